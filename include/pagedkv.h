@@ -1,0 +1,220 @@
+/*
+ * pagedkv.h -- C ABI of the MI355X (gfx950) paged KV-cache attention library.
+ *
+ * What the library computes, and where the pages describe it:
+ *
+ *  - KV cache in fixed-size blocks of 16 tokens held in one physical pool and
+ *    reached through a per-sequence block table ("vLLM — PagedAttention and
+ *    Continuous Batching", §2.2; "vLLM and PagedAttention", §2, block-table figure
+ *    and bullets; "How vLLM Works?", section 03).
+ *  - Cache tensor layout [num_blocks, block_size, num_kv_heads, head_dim], the
+ *    layout of the simplified kernel sketch in "vLLM and PagedAttention", §2, with
+ *    its head count read as the number of KV heads.  A block is therefore one
+ *    contiguous slab and one token's K (or V) row is one contiguous
+ *    num_kv_heads*head_dim vector.
+ *  - Decode attention that walks the table block by block and accumulates the
+ *    per-block results ("vLLM and PagedAttention", §2 "Reworking the Attention
+ *    Computation"; "vLLM — PagedAttention and Continuous Batching", §2.4).
+ *  - Copy-on-write sharing of prefix blocks ("vLLM and PagedAttention", §2 bullets;
+ *    "How vLLM Works?", section 03).
+ *
+ * Conventions for every call below:
+ *  - Device buffers are allocated and owned by the caller; the library keeps no
+ *    device memory.  Pointers named "device" must be device-accessible, 16-byte
+ *    aligned and contiguous in the stated layout.
+ *  - Calls only enqueue work on `stream` (a hipStream_t; NULL = the null stream)
+ *    and never synchronize.
+ *  - Every call returns PKV_OK or a negative code.  On an error nothing is
+ *    launched and no buffer is touched.  pkv_last_error() gives a message for the
+ *    last failing call on the calling thread.
+ *  - Device data (tables, lengths, slots) is trusted for values but never for
+ *    memory safety: kernels do not dereference block ids outside [0, num_blocks)
+ *    or table entries past max_blocks_per_seq.
+ *  - dtype: PKV_F32 (IEEE float) or PKV_BF16 (bfloat16 bit patterns).  Queries,
+ *    caches and outputs share one dtype; accumulation is fp32.
+ */
+#ifndef PAGEDKV_H
+#define PAGEDKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { PKV_F32 = 0, PKV_BF16 = 1 } pkv_dtype;
+
+enum {
+  PKV_OK = 0,
+  PKV_EINVAL = -1,       /* bad argument (null pointer, bad shape, misalignment) */
+  PKV_EUNSUPPORTED = -2, /* valid but not built: block_size != 16, head_dim, GQA group */
+  PKV_ENOMEM = -3,       /* allocator: not enough free blocks (state unchanged) */
+  PKV_ELAUNCH = -4,      /* the HIP runtime rejected a launch */
+  PKV_ENOSEQ = -5,       /* allocator: unknown sequence id */
+  PKV_EWORKSPACE = -6    /* workspace missing or smaller than the query says */
+};
+
+#define PKV_BLOCK_SIZE 16        /* tokens per block; the only size built */
+#define PKV_PARTITION_TOKENS 512 /* tokens per split-context partition */
+
+/* Message for the last failing call on this thread ("" if none).  Static storage. */
+const char* pkv_last_error(void);
+/* Short name of a status code. */
+const char* pkv_strerror(int code);
+
+/* ------------------------------------------------------------------------ */
+/* KV write: store each new token's K and V row into its slot.
+ *
+ * The cache keeps every token's key and value for reuse on later steps ("How vLLM
+ * Works?", section 01); a token's slot is block_table[pos / 16] * 16 + pos % 16,
+ * decided by the allocator below.
+ *
+ *   key_cache, value_cache  device, [num_blocks, block_size, num_kv_heads, head_dim], dtype dt
+ *   k, v                    device, [num_tokens, num_kv_heads, head_dim], dtype dt
+ *   slot_mapping            device int32 [num_tokens]; slot s -> block s / 16,
+ *                           offset s % 16.  Slots < 0 or >= num_blocks*16 are skipped.
+ *                           Duplicate slots in one call race (caller error).
+ * Bit copy: the written rows equal the inputs byte for byte; nothing else changes.
+ * num_tokens == 0 launches nothing.  Errors: PKV_EINVAL, PKV_EUNSUPPORTED, PKV_ELAUNCH. */
+int pkv_write(void* key_cache, void* value_cache, const void* k, const void* v,
+              const int32_t* slot_mapping, int32_t num_tokens, int32_t num_blocks,
+              int32_t block_size, int32_t num_kv_heads, int32_t head_dim, pkv_dtype dt,
+              void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Decode attention for one new token per sequence, over the paged cache.
+ *
+ *   out[s, h, :] = softmax_j(scale * q[s, h, :] . K_s[j, h / G, :]) . V_s[j, h / G, :]
+ *
+ * where K_s, V_s are sequence s's first context_lens[s] tokens gathered through
+ * block_tables[s] ("vLLM and PagedAttention", §2: attention computed per block
+ * through the block table and accumulated), and G = num_q_heads / num_kv_heads
+ * (consecutive q heads share a KV head).  Contexts longer than
+ * PKV_PARTITION_TOKENS are split into partitions whose softmax statistics
+ * (max, sum, normalized partial output) are merged by log-sum-exp; the result is
+ * the same softmax up to fp32 rounding.  context_lens[s] == 0 gives zeros.
+ *
+ *   out, q               device, [num_seqs, num_q_heads, head_dim], dtype dt
+ *   key_cache, value_cache  as for pkv_write
+ *   block_tables         device int32 [num_seqs, max_blocks_per_seq] row-major;
+ *                        entries past ceil(context_len/16) are never read
+ *   context_lens         device int32 [num_seqs]; must be <= max_context_len
+ *                        (larger values are clamped, never faulted on)
+ *   max_context_len      host-known bound on context_lens (no device sync);
+ *                        must be <= max_blocks_per_seq * 16
+ *   workspace            device, >= pkv_decode_workspace_bytes(...) bytes; may be
+ *                        NULL when that size is 0.  Scratch only; contents undefined.
+ * Supported: block_size 16; head_dim 64 or 128; G in {1, 2, 4, 8}; num_seqs <= 65535.
+ * Errors: PKV_EINVAL, PKV_EUNSUPPORTED, PKV_EWORKSPACE, PKV_ELAUNCH. */
+size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                                  int32_t max_context_len);
+int pkv_attention_decode(void* out, const void* q, const void* key_cache,
+                         const void* value_cache, const int32_t* block_tables,
+                         const int32_t* context_lens, float scale, int32_t block_size,
+                         int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                         int32_t num_seqs, int32_t max_blocks_per_seq, int32_t num_blocks,
+                         int32_t max_context_len, pkv_dtype dt, void* workspace,
+                         size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Log-sum-exp merge of partial softmax results, one output row per input row.
+ *
+ * The accumulation of separately computed attention pieces ("vLLM and
+ * PagedAttention", §2 "Reworking the Attention Computation"): with maxima m_p in
+ * base-2 units (scores already multiplied by log2(e)), sums l_p and normalized
+ * partial outputs o_p,
+ *   M = max_p m_p,  w_p = l_p * 2^(m_p - M),  out = sum_p w_p o_p / sum_p w_p.
+ * Partials with m_p = -inf or l_p = 0 weigh 0; a row with no live partial is 0.
+ *
+ *   out        device [rows, head_dim], dtype out_dt
+ *   part_m, part_l  device float [rows, max_parts]
+ *   part_o     device float [rows, max_parts, head_dim]
+ *   num_parts  device int32 [rows]; row r merges its first num_parts[r] partials
+ *              (clamped to [0, max_parts])
+ * Errors: PKV_EINVAL, PKV_EUNSUPPORTED (head_dim not 64/128), PKV_ELAUNCH. */
+int pkv_lse_merge(void* out, const float* part_m, const float* part_l, const float* part_o,
+                  const int32_t* num_parts, int32_t rows, int32_t max_parts, int32_t head_dim,
+                  pkv_dtype out_dt, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Copy-on-write block copies: for each pair (src, dst), block dst of both caches
+ * becomes a byte copy of block src ("vLLM and PagedAttention", §2 shareable
+ * prefixes with copy-on-write).  Run the pairs returned by pkv_alloc_append before
+ * writing new tokens.
+ *
+ *   pairs   device int32 [num_pairs, 2]; pairs whose ids fall outside
+ *           [0, num_blocks) are skipped.  A dst that is also a src in the same call
+ *           races (caller error).
+ * num_pairs == 0 launches nothing.  Errors: PKV_EINVAL, PKV_EUNSUPPORTED, PKV_ELAUNCH. */
+int pkv_copy_blocks(void* key_cache, void* value_cache, const int32_t* pairs,
+                    int32_t num_pairs, int32_t num_blocks, int32_t block_size,
+                    int32_t num_kv_heads, int32_t head_dim, pkv_dtype dt, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Host-side debug checks (no device access).
+ * pkv_check_tables: every entry a sequence uses (the first ceil(context_lens[s]/16)
+ * of its row) lies in [0, num_blocks), and context_lens are in [0, max_blocks*16].
+ * pkv_check_slots: no two non-negative slots are equal (a duplicate is a write race)
+ * and all lie below num_blocks*16.  Both return PKV_OK or PKV_EINVAL. */
+int pkv_check_tables(const int32_t* host_block_tables, const int32_t* host_context_lens,
+                     int32_t num_seqs, int32_t max_blocks_per_seq, int32_t num_blocks);
+int pkv_check_slots(const int32_t* host_slot_mapping, int32_t num_tokens, int32_t num_blocks,
+                    int32_t block_size);
+
+/* ------------------------------------------------------------------------ */
+/* Host block allocator (no device memory; not thread-safe; one pool per object).
+ *
+ * A sequence takes a new block only when its last block is full, so only the last
+ * block can be partly empty ("How vLLM Works?", section 03; "vLLM and
+ * PagedAttention", §2 on-demand allocation bullet).  Sequences forked from a parent
+ * share its blocks with reference counts; appending into a shared, partly filled
+ * last block first copies it (copy-on-write) and reports the (src, dst) pair for
+ * pkv_copy_blocks ("vLLM and PagedAttention", §2; "vLLM — PagedAttention and
+ * Continuous Batching", §2.3).  Full shared blocks are never copied.
+ *
+ * The free list is shuffled once at creation with the splitmix64 generator seeded
+ * by shuffle_seed (seed 0 keeps ids in order 0, 1, 2, ...), which scatters each
+ * sequence's blocks through the pool.  Every operation is all-or-nothing: on
+ * PKV_ENOMEM nothing changes. */
+typedef struct pkv_allocator pkv_allocator;
+
+/* NULL on bad arguments (num_blocks <= 0, block_size != 16) or allocation failure. */
+pkv_allocator* pkv_alloc_create(int32_t num_blocks, int32_t block_size, uint64_t shuffle_seed);
+void pkv_alloc_destroy(pkv_allocator* a);
+/* New empty sequence.  PKV_EINVAL if the id exists. */
+int pkv_alloc_add_seq(pkv_allocator* a, int64_t seq_id);
+/* child shares all of parent's blocks and length.  PKV_ENOSEQ / PKV_EINVAL (child exists). */
+int pkv_alloc_fork(pkv_allocator* a, int64_t parent, int64_t child);
+/* Reserve n_tokens slots at the end of seq_id.  slots_out[n_tokens] receives each
+ * new token's slot; cow_pairs_out (capacity 2 ints) receives at most one (src, dst)
+ * pair, *num_cow_out its count (0 or 1). */
+int pkv_alloc_append(pkv_allocator* a, int64_t seq_id, int32_t n_tokens, int32_t* slots_out,
+                     int32_t* cow_pairs_out, int32_t* num_cow_out);
+/* Batched append, all-or-nothing over the batch.  seq_ids must be distinct.
+ * slots_out receives sum(n_tokens) slots in batch order (capacity slots_cap);
+ * cow_pairs_out receives up to cow_cap pairs (2 ints each), *num_cow_out the count. */
+int pkv_alloc_append_batch(pkv_allocator* a, const int64_t* seq_ids, const int32_t* n_tokens,
+                           int32_t num_seqs, int32_t* slots_out, int64_t slots_cap,
+                           int32_t* cow_pairs_out, int32_t cow_cap, int32_t* num_cow_out);
+/* Drop a sequence; blocks whose count reaches 0 return to the free list. */
+int pkv_alloc_free_seq(pkv_allocator* a, int64_t seq_id);
+/* Copy seq_id's table into out (capacity cap); *len_out = its block count. */
+int pkv_alloc_block_table(const pkv_allocator* a, int64_t seq_id, int32_t* out, int32_t cap,
+                          int32_t* len_out);
+/* Dense row-major [num_seqs, max_blocks] tables (unused entries = fill) and lengths. */
+int pkv_alloc_block_tables(const pkv_allocator* a, const int64_t* seq_ids, int32_t num_seqs,
+                           int32_t* tables_out, int32_t max_blocks, int32_t fill,
+                           int32_t* context_lens_out);
+/* Tokens held by seq_id, or PKV_ENOSEQ. */
+int64_t pkv_alloc_seq_len(const pkv_allocator* a, int64_t seq_id);
+int32_t pkv_alloc_num_free(const pkv_allocator* a);
+int32_t pkv_alloc_num_blocks(const pkv_allocator* a);
+/* Reference count of a block (number of table entries holding it); -1 if out of range. */
+int32_t pkv_alloc_refcount(const pkv_allocator* a, int32_t block_id);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDKV_H */

@@ -1,0 +1,104 @@
+"""Python handle over the C++ block allocator (``pkv_alloc_*`` in the C ABI)."""
+
+import ctypes
+
+import numpy as np
+
+from ._lib import PKV_ENOMEM, PagedKVError, check, lib
+
+
+class BlockAllocator:
+    """Refcounted block pool with per-sequence tables and copy-on-write appends.
+
+    Methods mirror the C ABI; ``append`` returns ``(slots, cow_pairs)`` as lists.
+    Out-of-blocks raises ``MemoryError`` (state unchanged); other failures raise
+    ``PagedKVError``.
+    """
+
+    def __init__(self, num_blocks, block_size=16, shuffle_seed=0):
+        self._h = lib().pkv_alloc_create(int(num_blocks), int(block_size), int(shuffle_seed))
+        if not self._h:
+            raise PagedKVError("pkv_alloc_create", -1)
+        self.num_blocks = int(num_blocks)
+        self.block_size = int(block_size)
+
+    def close(self):
+        if self._h:
+            lib().pkv_alloc_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    @staticmethod
+    def _check(name, code):
+        if code == PKV_ENOMEM:
+            raise MemoryError(f"{name}: block pool exhausted")
+        check(name, code)
+
+    def add_seq(self, seq):
+        self._check("pkv_alloc_add_seq", lib().pkv_alloc_add_seq(self._h, int(seq)))
+
+    def fork(self, parent, child):
+        self._check("pkv_alloc_fork", lib().pkv_alloc_fork(self._h, int(parent), int(child)))
+
+    def append(self, seq, n_tokens):
+        slots = np.empty(max(1, n_tokens), dtype=np.int32)
+        pairs = np.empty(2, dtype=np.int32)
+        ncow = ctypes.c_int32(0)
+        self._check("pkv_alloc_append", lib().pkv_alloc_append(
+            self._h, int(seq), int(n_tokens), slots.ctypes.data, pairs.ctypes.data,
+            ctypes.addressof(ncow)))
+        cow = [(int(pairs[0]), int(pairs[1]))] if ncow.value else []
+        return slots[:n_tokens].tolist(), cow
+
+    def append_batch(self, seq_ids, n_tokens):
+        """All-or-nothing append for distinct sequences; returns (slots ndarray, pairs [n,2] ndarray)."""
+        ids = np.ascontiguousarray(seq_ids, dtype=np.int64)
+        ns = np.ascontiguousarray(n_tokens, dtype=np.int32)
+        total = int(ns.sum())
+        slots = np.empty(max(1, total), dtype=np.int32)
+        pairs = np.empty((max(1, len(ids)), 2), dtype=np.int32)
+        ncow = ctypes.c_int32(0)
+        self._check("pkv_alloc_append_batch", lib().pkv_alloc_append_batch(
+            self._h, ids.ctypes.data, ns.ctypes.data, len(ids), slots.ctypes.data, total,
+            pairs.ctypes.data, pairs.shape[0], ctypes.addressof(ncow)))
+        return slots[:total], pairs[:ncow.value]
+
+    def free_seq(self, seq):
+        self._check("pkv_alloc_free_seq", lib().pkv_alloc_free_seq(self._h, int(seq)))
+
+    def block_table(self, seq):
+        n = ctypes.c_int32(0)
+        code = lib().pkv_alloc_block_table(self._h, int(seq), None, 0, ctypes.addressof(n))
+        if code not in (0, -1):
+            self._check("pkv_alloc_block_table", code)
+        out = np.empty(max(1, n.value), dtype=np.int32)
+        self._check("pkv_alloc_block_table", lib().pkv_alloc_block_table(
+            self._h, int(seq), out.ctypes.data, out.shape[0], ctypes.addressof(n)))
+        return out[:n.value].tolist()
+
+    def block_tables(self, seq_ids, max_blocks, fill=-1):
+        """Dense int32 tables [S, max_blocks] and int32 context lengths [S]."""
+        ids = np.ascontiguousarray(seq_ids, dtype=np.int64)
+        tables = np.empty((len(ids), max_blocks), dtype=np.int32)
+        lens = np.empty(len(ids), dtype=np.int32)
+        self._check("pkv_alloc_block_tables", lib().pkv_alloc_block_tables(
+            self._h, ids.ctypes.data, len(ids), tables.ctypes.data, int(max_blocks), int(fill),
+            lens.ctypes.data))
+        return tables, lens
+
+    def seq_len(self, seq):
+        v = lib().pkv_alloc_seq_len(self._h, int(seq))
+        if v < 0:
+            self._check("pkv_alloc_seq_len", int(v))
+        return int(v)
+
+    def num_free(self):
+        return int(lib().pkv_alloc_num_free(self._h))
+
+    def refcount(self, block):
+        return int(lib().pkv_alloc_refcount(self._h, int(block)))

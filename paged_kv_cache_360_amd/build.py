@@ -1,0 +1,72 @@
+"""Build ``libpagedkv.so`` in-tree with hipcc for gfx950.
+
+Usage: ``python -m paged_kv_cache_360_amd.build`` (or ``build()`` from Python).
+Objects go to ``_build/`` at the repository root; the shared library is written
+next to this file, where the binding loads it.  Always recompiles.
+"""
+
+import os
+import shutil
+import subprocess
+import sys
+from concurrent.futures import ThreadPoolExecutor
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+OUT = os.path.join(PKG, "libpagedkv.so")
+BUILD_DIR = os.path.join(ROOT, "_build")
+
+ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
+HIPCC = os.path.join(ROCM, "bin", "hipcc")
+ARCH = "gfx950"
+
+# Device code: gfx950 only; packed-fp32 instruction selection is switched off
+# (ordinary scalar fp32 code is generated instead).
+HIP_FLAGS = [
+    "-O3", "-fPIC", "-std=c++17", f"--offload-arch={ARCH}", "-mcode-object-version=5",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall", "-Wno-unused-function", "-Wno-unused-command-line-argument",
+]
+HOST_FLAGS = ["-O2", "-fPIC", "-std=c++17", "-Wall", "-D__HIP_PLATFORM_AMD__",
+              f"-I{ROCM}/include"]
+
+HIP_SOURCES = ["kernels/cache_ops.hip", "kernels/decode.hip"]
+HOST_SOURCES = ["api.cpp", "allocator.cpp"]
+
+
+def _run(cmd, verbose):
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        sys.stderr.write(r.stdout + r.stderr)
+        raise RuntimeError(f"build step failed: {' '.join(cmd[:3])} ... ({r.returncode})")
+    return r
+
+
+def build(verbose=False, jobs=8):
+    """Compile every source and link ``libpagedkv.so``.  Returns the library path."""
+    if not os.path.exists(HIPCC):
+        raise RuntimeError(f"hipcc not found at {HIPCC}")
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    cmds, objs = [], []
+    for src in HIP_SOURCES:
+        obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
+        cmds.append([HIPCC, *HIP_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
+        objs.append(obj)
+    for src in HOST_SOURCES:
+        obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
+        cmds.append([HIPCC, *HOST_FLAGS, "-x", "c++", "-c", os.path.join(CSRC, src), "-o", obj])
+        objs.append(obj)
+    with ThreadPoolExecutor(max_workers=max(1, min(jobs, len(cmds)))) as ex:
+        list(ex.map(lambda c: _run(c, verbose), cmds))
+    tmp = OUT + ".tmp"
+    _run([HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp, *objs,
+          "-Wl,-soname,libpagedkv.so", f"-Wl,-rpath,{ROCM}/lib"], verbose)
+    shutil.move(tmp, OUT)
+    return OUT
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

@@ -1,0 +1,232 @@
+// C ABI: argument validation, workspace layout and launch dispatch.
+//
+// Every entry point validates its arguments on the host before any HIP call, so
+// an error launches nothing and touches no buffer.  Launch failures reported by
+// the runtime map to PKV_ELAUNCH.
+
+#include <hip/hip_runtime_api.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdio>
+#include <cstdint>
+#include <cstring>
+#include <vector>
+
+#include "../../include/pagedkv.h"
+#include "pkv_internal.hpp"
+
+namespace pkv {
+
+namespace {
+thread_local char g_last_error[256] = "";
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+inline int64_t elem_size(pkv_dtype dt) { return dt == PKV_BF16 ? 2 : 4; }
+inline bool dtype_ok(pkv_dtype dt) { return dt == PKV_F32 || dt == PKV_BF16; }
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+int64_t parts_for(int64_t max_ctx) { return (max_ctx + PKV_PARTITION_TOKENS - 1) / PKV_PARTITION_TOKENS; }
+
+int launched(int hip_status, const char* who) {
+  if (hip_status == 0) return PKV_OK;
+  char buf[256];
+  std::snprintf(buf, sizeof(buf), "%s: launch failed: %s", who,
+                hipGetErrorString((hipError_t)hip_status));
+  set_error(buf);
+  return PKV_ELAUNCH;
+}
+}  // namespace
+
+void set_error(const char* msg) {
+  std::strncpy(g_last_error, msg, sizeof(g_last_error) - 1);
+  g_last_error[sizeof(g_last_error) - 1] = '\0';
+}
+
+}  // namespace pkv
+
+using pkv::fail;
+
+extern "C" {
+
+const char* pkv_last_error(void) { return pkv::g_last_error; }
+
+const char* pkv_strerror(int code) {
+  switch (code) {
+    case PKV_OK: return "PKV_OK";
+    case PKV_EINVAL: return "PKV_EINVAL";
+    case PKV_EUNSUPPORTED: return "PKV_EUNSUPPORTED";
+    case PKV_ENOMEM: return "PKV_ENOMEM";
+    case PKV_ELAUNCH: return "PKV_ELAUNCH";
+    case PKV_ENOSEQ: return "PKV_ENOSEQ";
+    case PKV_EWORKSPACE: return "PKV_EWORKSPACE";
+    default: return "PKV_UNKNOWN";
+  }
+}
+
+int pkv_write(void* key_cache, void* value_cache, const void* k, const void* v,
+              const int32_t* slot_mapping, int32_t num_tokens, int32_t num_blocks,
+              int32_t block_size, int32_t num_kv_heads, int32_t head_dim, pkv_dtype dt,
+              void* stream) {
+  if (!pkv::dtype_ok(dt)) return fail(PKV_EUNSUPPORTED, "pkv_write: unsupported dtype");
+  if (block_size != PKV_BLOCK_SIZE) return fail(PKV_EUNSUPPORTED, "pkv_write: block_size must be 16");
+  if (num_tokens < 0 || num_blocks <= 0 || num_kv_heads <= 0 || head_dim <= 0)
+    return fail(PKV_EINVAL, "pkv_write: bad sizes");
+  const int64_t row_bytes = (int64_t)num_kv_heads * head_dim * pkv::elem_size(dt);
+  if (row_bytes % 16 != 0 || row_bytes > INT32_MAX)
+    return fail(PKV_EUNSUPPORTED, "pkv_write: row bytes must be a multiple of 16");
+  if (num_tokens == 0) return PKV_OK;
+  if (!key_cache || !value_cache || !k || !v || !slot_mapping)
+    return fail(PKV_EINVAL, "pkv_write: null pointer");
+  if (!pkv::aligned16(key_cache) || !pkv::aligned16(value_cache) || !pkv::aligned16(k) ||
+      !pkv::aligned16(v))
+    return fail(PKV_EINVAL, "pkv_write: pointers must be 16-byte aligned");
+  return pkv::launched(pkv::launch_kv_write(key_cache, value_cache, k, v, slot_mapping, num_tokens,
+                                            (int64_t)num_blocks * block_size, (int32_t)row_bytes,
+                                            stream),
+                       "pkv_write");
+}
+
+size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                                  int32_t max_context_len) {
+  if (num_seqs <= 0 || num_q_heads <= 0 || head_dim <= 0 || max_context_len <= 0) return 0;
+  const int64_t P = pkv::parts_for(max_context_len);
+  if (P <= 1) return 0;
+  const size_t rows = (size_t)num_seqs * num_q_heads;
+  return pkv::align256(rows * P * sizeof(float)) * 2 + pkv::align256(rows * P * head_dim * sizeof(float));
+}
+
+int pkv_attention_decode(void* out, const void* q, const void* key_cache,
+                         const void* value_cache, const int32_t* block_tables,
+                         const int32_t* context_lens, float scale, int32_t block_size,
+                         int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                         int32_t num_seqs, int32_t max_blocks_per_seq, int32_t num_blocks,
+                         int32_t max_context_len, pkv_dtype dt, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  if (!pkv::dtype_ok(dt)) return fail(PKV_EUNSUPPORTED, "pkv_attention_decode: unsupported dtype");
+  if (block_size != PKV_BLOCK_SIZE)
+    return fail(PKV_EUNSUPPORTED, "pkv_attention_decode: block_size must be 16");
+  if (head_dim != 64 && head_dim != 128)
+    return fail(PKV_EUNSUPPORTED, "pkv_attention_decode: head_dim must be 64 or 128");
+  if (num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0)
+    return fail(PKV_EINVAL, "pkv_attention_decode: num_q_heads must be a positive multiple of num_kv_heads");
+  const int32_t G = num_q_heads / num_kv_heads;
+  if (G != 1 && G != 2 && G != 4 && G != 8)
+    return fail(PKV_EUNSUPPORTED, "pkv_attention_decode: q heads per KV head must be 1, 2, 4 or 8");
+  if (num_seqs < 0 || num_seqs > 65535 || max_blocks_per_seq <= 0 || num_blocks <= 0 ||
+      max_context_len < 0 || num_kv_heads > 65535)
+    return fail(PKV_EINVAL, "pkv_attention_decode: bad sizes");
+  if ((int64_t)max_context_len > (int64_t)max_blocks_per_seq * PKV_BLOCK_SIZE)
+    return fail(PKV_EINVAL, "pkv_attention_decode: max_context_len exceeds the table width");
+  if (!std::isfinite(scale)) return fail(PKV_EINVAL, "pkv_attention_decode: scale must be finite");
+  if (num_seqs == 0) return PKV_OK;
+  if (!out || !q || !key_cache || !value_cache || !block_tables || !context_lens)
+    return fail(PKV_EINVAL, "pkv_attention_decode: null pointer");
+  if (!pkv::aligned16(out) || !pkv::aligned16(q) || !pkv::aligned16(key_cache) ||
+      !pkv::aligned16(value_cache))
+    return fail(PKV_EINVAL, "pkv_attention_decode: pointers must be 16-byte aligned");
+  const int64_t P = std::max<int64_t>(1, pkv::parts_for(max_context_len));
+  if (P > 65535) return fail(PKV_EUNSUPPORTED, "pkv_attention_decode: context too long");
+  const size_t need = pkv_decode_workspace_bytes(num_seqs, num_q_heads, head_dim, max_context_len);
+  if (need > 0 && (!workspace || workspace_bytes < need || !pkv::aligned16(workspace)))
+    return fail(PKV_EWORKSPACE, "pkv_attention_decode: workspace missing or too small");
+
+  pkv::DecodeArgs a{};
+  a.out = out;
+  a.q = q;
+  a.kc = key_cache;
+  a.vc = value_cache;
+  a.tables = block_tables;
+  a.ctx = context_lens;
+  a.scale_log2 = scale * 1.4426950408889634f;  // log2(e)
+  a.num_seqs = num_seqs;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.head_dim = head_dim;
+  a.max_blocks = max_blocks_per_seq;
+  a.num_blocks = num_blocks;
+  a.max_parts = (int32_t)P;
+  a.bf16 = dt == PKV_BF16;
+  if (need > 0) {
+    const size_t rows = (size_t)num_seqs * num_q_heads;
+    char* ws = static_cast<char*>(workspace);
+    a.part_m = reinterpret_cast<float*>(ws);
+    a.part_l = reinterpret_cast<float*>(ws + pkv::align256(rows * P * sizeof(float)));
+    a.part_o = reinterpret_cast<float*>(ws + 2 * pkv::align256(rows * P * sizeof(float)));
+  }
+  return pkv::launched(pkv::launch_decode(a, stream), "pkv_attention_decode");
+}
+
+int pkv_lse_merge(void* out, const float* part_m, const float* part_l, const float* part_o,
+                  const int32_t* num_parts, int32_t rows, int32_t max_parts, int32_t head_dim,
+                  pkv_dtype out_dt, void* stream) {
+  if (!pkv::dtype_ok(out_dt)) return fail(PKV_EUNSUPPORTED, "pkv_lse_merge: unsupported dtype");
+  if (head_dim != 64 && head_dim != 128)
+    return fail(PKV_EUNSUPPORTED, "pkv_lse_merge: head_dim must be 64 or 128");
+  if (rows < 0 || max_parts <= 0) return fail(PKV_EINVAL, "pkv_lse_merge: bad sizes");
+  if (rows == 0) return PKV_OK;
+  if (!out || !part_m || !part_l || !part_o || !num_parts)
+    return fail(PKV_EINVAL, "pkv_lse_merge: null pointer");
+  return pkv::launched(pkv::launch_lse_merge(out, part_m, part_l, part_o, num_parts, rows, max_parts,
+                                             head_dim, out_dt == PKV_BF16, stream),
+                       "pkv_lse_merge");
+}
+
+int pkv_copy_blocks(void* key_cache, void* value_cache, const int32_t* pairs,
+                    int32_t num_pairs, int32_t num_blocks, int32_t block_size,
+                    int32_t num_kv_heads, int32_t head_dim, pkv_dtype dt, void* stream) {
+  if (!pkv::dtype_ok(dt)) return fail(PKV_EUNSUPPORTED, "pkv_copy_blocks: unsupported dtype");
+  if (block_size != PKV_BLOCK_SIZE)
+    return fail(PKV_EUNSUPPORTED, "pkv_copy_blocks: block_size must be 16");
+  if (num_pairs < 0 || num_blocks <= 0 || num_kv_heads <= 0 || head_dim <= 0)
+    return fail(PKV_EINVAL, "pkv_copy_blocks: bad sizes");
+  const int64_t block_bytes = (int64_t)block_size * num_kv_heads * head_dim * pkv::elem_size(dt);
+  if (block_bytes % 16 != 0)
+    return fail(PKV_EUNSUPPORTED, "pkv_copy_blocks: block bytes must be a multiple of 16");
+  if (num_pairs == 0) return PKV_OK;
+  if (!key_cache || !value_cache || !pairs) return fail(PKV_EINVAL, "pkv_copy_blocks: null pointer");
+  if (!pkv::aligned16(key_cache) || !pkv::aligned16(value_cache))
+    return fail(PKV_EINVAL, "pkv_copy_blocks: caches must be 16-byte aligned");
+  if (num_pairs > 2147483647 / 2) return fail(PKV_EINVAL, "pkv_copy_blocks: too many pairs");
+  return pkv::launched(pkv::launch_copy_blocks(key_cache, value_cache, pairs, num_pairs, num_blocks,
+                                               block_bytes, stream),
+                       "pkv_copy_blocks");
+}
+
+int pkv_check_tables(const int32_t* host_block_tables, const int32_t* host_context_lens,
+                     int32_t num_seqs, int32_t max_blocks_per_seq, int32_t num_blocks) {
+  if (num_seqs < 0 || max_blocks_per_seq <= 0 || num_blocks <= 0)
+    return fail(PKV_EINVAL, "pkv_check_tables: bad sizes");
+  if (num_seqs > 0 && (!host_block_tables || !host_context_lens))
+    return fail(PKV_EINVAL, "pkv_check_tables: null pointer");
+  for (int32_t s = 0; s < num_seqs; ++s) {
+    const int64_t n = host_context_lens[s];
+    if (n < 0 || n > (int64_t)max_blocks_per_seq * PKV_BLOCK_SIZE)
+      return fail(PKV_EINVAL, "pkv_check_tables: context length out of range");
+    const int64_t nb = (n + PKV_BLOCK_SIZE - 1) / PKV_BLOCK_SIZE;
+    const int32_t* row = host_block_tables + (int64_t)s * max_blocks_per_seq;
+    for (int64_t b = 0; b < nb; ++b) {
+      if (row[b] < 0 || row[b] >= num_blocks) return fail(PKV_EINVAL, "pkv_check_tables: block id out of range");
+    }
+  }
+  return PKV_OK;
+}
+
+int pkv_check_slots(const int32_t* host_slot_mapping, int32_t num_tokens, int32_t num_blocks,
+                    int32_t block_size) {
+  if (num_tokens < 0 || num_blocks <= 0 || block_size != PKV_BLOCK_SIZE)
+    return fail(PKV_EINVAL, "pkv_check_slots: bad sizes");
+  if (num_tokens > 0 && !host_slot_mapping) return fail(PKV_EINVAL, "pkv_check_slots: null pointer");
+  const int64_t nslots = (int64_t)num_blocks * block_size;
+  std::vector<uint8_t> seen((size_t)nslots, 0);
+  for (int32_t i = 0; i < num_tokens; ++i) {
+    const int32_t s = host_slot_mapping[i];
+    if (s < 0) continue;
+    if (s >= nslots) return fail(PKV_EINVAL, "pkv_check_slots: slot beyond the pool");
+    if (seen[(size_t)s]) return fail(PKV_EINVAL, "pkv_check_slots: duplicate slot (write race)");
+    seen[(size_t)s] = 1;
+  }
+  return PKV_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,393 @@
+// Split-context paged decode attention and the log-sum-exp merge, for gfx950.
+//
+// Attention over K/V reached block by block through a block table, with each
+// block's contribution computed separately and accumulated ("vLLM and
+// PagedAttention", §2 "Reworking the Attention Computation"; cache layout from
+// the kernel sketch there: [num_blocks, 16, num_kv_heads, head_dim]).
+//
+// Work decomposition (one workgroup = 4 wavefronts of 64 lanes):
+//   grid = (kv head g, partition p, sequence s); partition p covers tokens
+//   [512 p, 512 p + 512) of the sequence, i.e. 32 blocks.  The workgroup serves
+//   all G = Hq / Hkv query heads of KV head g, so every K/V byte is read once.
+//   Wave w takes blocks p*32 + w, + 4, + 8, ... and keeps its own online-softmax
+//   state; the four waves merge through LDS at the end.
+//
+// Lane mapping for one 16-token block of one KV head (the slab is 16 rows of
+// head_dim elements, rows num_kv_heads*head_dim apart): a token row is split
+// over LPT lanes that each load 16 contiguous bytes (dwordx4), so one wave-wide
+// load covers TPL = 64 / LPT whole rows and NL = 16 / TPL loads cover the block.
+// For bf16, head_dim 128: 16 lanes x 16 B = one 256-B row, 4 rows per load, 4
+// loads per block for K and 4 for V.  The q.k dot product is a per-lane partial
+// over 8 dims followed by a butterfly sum across the row's 16 lanes.
+//
+// Online softmax in base 2: q is pre-multiplied by scale*log2(e) so scores are
+// log2-domain and every exponential is one v_exp_f32.  The running max m is
+// uniform across the wave; the running sum l and the accumulator acc stay
+// lane-local (each lane sums only its own tokens) and are reduced once at the end.
+//
+// Masking: tokens past the context in the last block get score -inf and their V
+// values are replaced by 0 before the multiply, so NaN/Inf left in unused slots
+// never reaches the output.  Block ids outside [0, num_blocks) are not
+// dereferenced: such a block counts as fully masked.
+//
+// Memory-level parallelism: each wave double-buffers two blocks (K and V) in
+// registers, issuing block i+1's loads before computing block i.
+
+#include <hip/hip_runtime.h>
+
+#include "../pkv_internal.hpp"
+#include "device_common.hpp"
+
+namespace pkv {
+
+namespace {
+
+constexpr int kDecodeThreads = 256;
+constexpr int kDecodeWaves = kDecodeThreads / kWave;
+
+struct DecodeParams {
+  void* out;
+  const void* q;
+  const char* kc;
+  const char* vc;
+  const int32_t* tables;
+  const int32_t* ctx;
+  float scale_log2;
+  int32_t Hkv;
+  int32_t MB;
+  int32_t NB;
+  int32_t max_parts;
+  float* part_m;
+  float* part_l;
+  float* part_o;
+};
+
+template <bool BF16>
+__device__ __forceinline__ void store_out(void* out, int64_t idx, float v) {
+  if constexpr (BF16) {
+    reinterpret_cast<uint16_t*>(out)[idx] = f32_to_bf16(v);
+  } else {
+    reinterpret_cast<float*>(out)[idx] = v;
+  }
+}
+
+template <bool BF16, int D, int G>
+__global__ __launch_bounds__(kDecodeThreads) void decode_partition_kernel(DecodeParams p) {
+  constexpr int ES = BF16 ? 2 : 4;                 // bytes per element
+  constexpr int EPL = 16 / ES;                     // elements per lane per load
+  constexpr int LPT = D * ES / 16;                 // lanes per token row
+  constexpr int TPL = kWave / LPT;                 // token rows per wave-wide load
+  constexpr int NL = kBlockTokens / TPL;           // loads per block (per cache)
+  constexpr int NW = kDecodeWaves;
+  static_assert(LPT >= 1 && LPT <= kWave && kWave % LPT == 0, "row must split over lanes");
+  static_assert(kBlockTokens % TPL == 0, "block must split over loads");
+
+  const int g = blockIdx.x;
+  const int part = blockIdx.y;
+  const int s = blockIdx.z;
+  const int Hq = p.Hkv * G;
+
+  int ctx = p.ctx[s];
+  ctx = max(0, min(ctx, min(p.MB * kBlockTokens, p.max_parts * kPartTokens)));
+  const int nparts = (ctx + kPartTokens - 1) / kPartTokens;
+  if (part >= max(nparts, 1)) return;
+  const int64_t row0 = (int64_t)s * Hq + (int64_t)g * G;  // first q head of this group
+
+  if (ctx == 0) {  // empty context: zero output
+    for (int i = threadIdx.x; i < G * D; i += kDecodeThreads) store_out<BF16>(p.out, row0 * D + i, 0.f);
+    return;
+  }
+
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int dim0 = (lane % LPT) * EPL;
+  const int tl = lane / LPT;
+
+  // q for this lane's dims, all G heads, scaled into the log2 domain.
+  float qv[G][EPL];
+#pragma unroll
+  for (int j = 0; j < G; ++j) {
+    const uint4 r = load16(reinterpret_cast<const char*>(p.q) + ((row0 + j) * D + dim0) * ES);
+    widen16<BF16>(r, qv[j]);
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) qv[j][e] *= p.scale_log2;
+  }
+
+  float m[G], l[G], acc[G][EPL];
+#pragma unroll
+  for (int j = 0; j < G; ++j) {
+    m[j] = -INFINITY;
+    l[j] = 0.f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[j][e] = 0.f;
+  }
+
+  const int nblk = (ctx + kBlockTokens - 1) / kBlockTokens;
+  const int b_begin = part * kPartBlocks;
+  const int b_end = min(b_begin + kPartBlocks, nblk);
+  const int32_t* trow = p.tables + (int64_t)s * p.MB;
+  const int64_t tok_bytes = (int64_t)p.Hkv * D * ES;
+  const int64_t blk_bytes = tok_bytes * kBlockTokens;
+  const int64_t lane_off = (int64_t)tl * tok_bytes + ((int64_t)g * D + dim0) * ES;
+
+  auto issue = [&](int b, uint4 (&kr)[NL], uint4 (&vr)[NL], int& valid) {
+    const int pb = trow[b];
+    const bool ok = (unsigned)pb < (unsigned)p.NB;
+    valid = ok ? min(kBlockTokens, ctx - b * kBlockTokens) : 0;
+    const int64_t base = (int64_t)(ok ? pb : 0) * blk_bytes + lane_off;
+#pragma unroll
+    for (int i = 0; i < NL; ++i) kr[i] = load16(p.kc + base + (int64_t)i * TPL * tok_bytes);
+#pragma unroll
+    for (int i = 0; i < NL; ++i) vr[i] = load16(p.vc + base + (int64_t)i * TPL * tok_bytes);
+  };
+
+  auto compute = [&](const uint4 (&kr)[NL], const uint4 (&vr)[NL], int valid) {
+    float sc[NL][G];
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      float kf[EPL];
+      widen16<BF16>(kr[i], kf);
+#pragma unroll
+      for (int j = 0; j < G; ++j) {
+        float d = 0.f;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) d = fmaf(qv[j][e], kf[e], d);
+        sc[i][j] = xor_sum<1, LPT>(d);
+      }
+    }
+    const bool partial = valid < kBlockTokens;
+    if (partial) {
+#pragma unroll
+      for (int i = 0; i < NL; ++i) {
+        if (i * TPL + tl >= valid) {
+#pragma unroll
+          for (int j = 0; j < G; ++j) sc[i][j] = -INFINITY;
+        }
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+      float mb = sc[0][j];
+#pragma unroll
+      for (int i = 1; i < NL; ++i) mb = fmaxf(mb, sc[i][j]);
+      mb = xor_max<LPT, kWave>(mb);
+      const float mn = fmaxf(m[j], mb);
+      const float ms = (mn == -INFINITY) ? 0.f : mn;
+      const float alpha = exp2_fast(m[j] - ms);
+      m[j] = mn;
+      l[j] *= alpha;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[j][e] *= alpha;
+#pragma unroll
+      for (int i = 0; i < NL; ++i) {
+        sc[i][j] = exp2_fast(sc[i][j] - ms);
+        l[j] += sc[i][j];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      float vf[EPL];
+      widen16<BF16>(vr[i], vf);
+      if (partial && i * TPL + tl >= valid) {
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) vf[e] = 0.f;
+      }
+#pragma unroll
+      for (int j = 0; j < G; ++j) {
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[j][e] = fmaf(sc[i][j], vf[e], acc[j][e]);
+      }
+    }
+  };
+
+  uint4 ka[NL], va[NL], kb[NL], vb[NL];
+  int valid_a = 0, valid_b = 0;
+  int b = b_begin + wave;
+  if (b < b_end) issue(b, ka, va, valid_a);
+  while (b < b_end) {
+    int bn = b + NW;
+    if (bn < b_end) issue(bn, kb, vb, valid_b);
+    compute(ka, va, valid_a);
+    b = bn;
+    if (b >= b_end) break;
+    bn = b + NW;
+    if (bn < b_end) issue(bn, ka, va, valid_a);
+    compute(kb, vb, valid_b);
+    b = bn;
+  }
+
+  // Wave totals: sum l and acc over the TPL token groups (m is already uniform).
+#pragma unroll
+  for (int j = 0; j < G; ++j) {
+    l[j] = xor_sum<LPT, kWave>(l[j]);
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[j][e] = xor_sum<LPT, kWave>(acc[j][e]);
+  }
+
+  __shared__ float s_m[NW][G];
+  __shared__ float s_l[NW][G];
+  __shared__ float s_o[NW][G][D];
+  if (tl == 0) {
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) s_o[wave][j][dim0 + e] = acc[j][e];
+    }
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+      s_m[wave][j] = m[j];
+      s_l[wave][j] = l[j];
+    }
+  }
+  __syncthreads();
+
+  for (int idx = threadIdx.x; idx < G * D; idx += kDecodeThreads) {
+    const int j = idx / D;
+    const int d = idx % D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, s_m[w][j]);
+    float L = 0.f, O = 0.f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        const float f = exp2_fast(s_m[w][j] - M);
+        L = fmaf(s_l[w][j], f, L);
+        O = fmaf(s_o[w][j][d], f, O);
+      }
+    }
+    const float r = L > 0.f ? O / L : 0.f;
+    if (nparts == 1) {
+      store_out<BF16>(p.out, (row0 + j) * D + d, r);
+    } else {
+      const int64_t pr = (row0 + j) * p.max_parts + part;
+      p.part_o[pr * D + d] = r;
+      if (d == 0) {
+        p.part_m[pr] = M;
+        p.part_l[pr] = L;
+      }
+    }
+  }
+}
+
+// One wave per output row.  FROM_CTX: the row count comes from the sequence's
+// context length (decode path; rows with a single partition were already
+// written by the partition kernel and are skipped); otherwise from num_parts[row].
+template <bool BF16, int D, bool FROM_CTX>
+__global__ __launch_bounds__(kWave) void lse_merge_kernel(
+    void* __restrict__ out, const float* __restrict__ pm, const float* __restrict__ pl,
+    const float* __restrict__ po, const int32_t* __restrict__ counts, int32_t Hq,
+    int32_t max_parts, int32_t ctx_cap) {
+  constexpr int PER = D / kWave;
+  const int64_t row = blockIdx.x;
+  int n;
+  if constexpr (FROM_CTX) {
+    const int ctx = max(0, min(counts[row / Hq], ctx_cap));
+    n = (ctx + kPartTokens - 1) / kPartTokens;
+    if (n <= 1) return;
+  } else {
+    n = max(0, min(counts[row], max_parts));
+  }
+  const int lane = threadIdx.x;
+  const float* rm = pm + row * max_parts;
+  const float* rl = pl + row * max_parts;
+  const float* ro = po + row * max_parts * D;
+  float M = -INFINITY;
+  for (int i = 0; i < n; ++i) {
+    if (rl[i] > 0.f) M = fmaxf(M, rm[i]);
+  }
+  float L = 0.f;
+  float o[PER];
+#pragma unroll
+  for (int k = 0; k < PER; ++k) o[k] = 0.f;
+  if (M != -INFINITY) {
+    for (int i = 0; i < n; ++i) {
+      const float mi = rm[i], li = rl[i];
+      if (!(li > 0.f) || mi == -INFINITY) continue;
+      const float w = li * exp2_fast(mi - M);
+      L += w;
+#pragma unroll
+      for (int k = 0; k < PER; ++k) o[k] = fmaf(w, ro[(int64_t)i * D + lane + k * kWave], o[k]);
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    store_out<BF16>(out, row * D + lane + k * kWave, L > 0.f ? o[k] / L : 0.f);
+  }
+}
+
+template <bool BF16, int D, int G>
+void launch_decode_t(const DecodeArgs& a, hipStream_t st) {
+  DecodeParams p;
+  p.out = a.out;
+  p.q = a.q;
+  p.kc = reinterpret_cast<const char*>(a.kc);
+  p.vc = reinterpret_cast<const char*>(a.vc);
+  p.tables = a.tables;
+  p.ctx = a.ctx;
+  p.scale_log2 = a.scale_log2;
+  p.Hkv = a.num_kv_heads;
+  p.MB = a.max_blocks;
+  p.NB = a.num_blocks;
+  p.max_parts = a.max_parts;
+  p.part_m = a.part_m;
+  p.part_l = a.part_l;
+  p.part_o = a.part_o;
+  hipLaunchKernelGGL((decode_partition_kernel<BF16, D, G>),
+                     dim3(a.num_kv_heads, a.max_parts, a.num_seqs), dim3(kDecodeThreads), 0, st, p);
+  if (a.max_parts > 1) {
+    hipLaunchKernelGGL((lse_merge_kernel<BF16, D, true>), dim3(a.num_seqs * a.num_q_heads),
+                       dim3(kWave), 0, st, a.out, a.part_m, a.part_l, a.part_o, a.ctx,
+                       a.num_q_heads, a.max_parts,
+                       min(a.max_blocks * kBlockTokens, a.max_parts * kPartTokens));
+  }
+}
+
+template <bool BF16, int D>
+int launch_decode_g(const DecodeArgs& a, hipStream_t st) {
+  switch (a.num_q_heads / a.num_kv_heads) {
+    case 1: launch_decode_t<BF16, D, 1>(a, st); break;
+    case 2: launch_decode_t<BF16, D, 2>(a, st); break;
+    case 4: launch_decode_t<BF16, D, 4>(a, st); break;
+    case 8: launch_decode_t<BF16, D, 8>(a, st); break;
+    default: return (int)hipErrorInvalidValue;
+  }
+  return (int)hipGetLastError();
+}
+
+}  // namespace
+
+int launch_decode(const DecodeArgs& a, void* stream) {
+  hipStream_t st = (hipStream_t)stream;
+  if (a.bf16) {
+    return a.head_dim == 64 ? launch_decode_g<true, 64>(a, st) : launch_decode_g<true, 128>(a, st);
+  }
+  return a.head_dim == 64 ? launch_decode_g<false, 64>(a, st) : launch_decode_g<false, 128>(a, st);
+}
+
+int launch_lse_merge(void* out, const float* part_m, const float* part_l, const float* part_o,
+                     const int32_t* num_parts, int32_t rows, int32_t max_parts, int32_t head_dim,
+                     bool bf16, void* stream) {
+  hipStream_t st = (hipStream_t)stream;
+  const dim3 grid(rows), block(kWave);
+  if (bf16) {
+    if (head_dim == 64)
+      hipLaunchKernelGGL((lse_merge_kernel<true, 64, false>), grid, block, 0, st, out, part_m,
+                         part_l, part_o, num_parts, 1, max_parts, 0);
+    else
+      hipLaunchKernelGGL((lse_merge_kernel<true, 128, false>), grid, block, 0, st, out, part_m,
+                         part_l, part_o, num_parts, 1, max_parts, 0);
+  } else {
+    if (head_dim == 64)
+      hipLaunchKernelGGL((lse_merge_kernel<false, 64, false>), grid, block, 0, st, out, part_m,
+                         part_l, part_o, num_parts, 1, max_parts, 0);
+    else
+      hipLaunchKernelGGL((lse_merge_kernel<false, 128, false>), grid, block, 0, st, out, part_m,
+                         part_l, part_o, num_parts, 1, max_parts, 0);
+  }
+  return (int)hipGetLastError();
+}
+
+}  // namespace pkv

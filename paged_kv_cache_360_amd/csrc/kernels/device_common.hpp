@@ -1,0 +1,62 @@
+// Device helpers shared by the gfx950 kernels: bf16 <-> fp32, 16-byte vector
+// access, wavefront reductions and the log2-domain exponential.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pkv {
+
+constexpr int kWave = 64;           // CDNA wavefront width
+constexpr int kBlockTokens = 16;    // tokens per KV block
+constexpr int kPartTokens = 512;    // tokens per split-context partition
+constexpr int kPartBlocks = kPartTokens / kBlockTokens;
+
+// bf16 is the upper half of an fp32: widening is a shift (low half) or a mask (high half).
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// fp32 -> bf16, round to nearest even; NaN stays NaN (quiet).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x0040u);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// 2^x on the hardware exponential unit (v_exp_f32); 2^-inf = 0.
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Widen one 16-byte load of storage into fp32 values (8 for bf16, 4 for fp32).
+template <bool BF16>
+__device__ __forceinline__ void widen16(const uint4& r, float* f) {
+  if constexpr (BF16) {
+    f[0] = bf16_lo(r.x); f[1] = bf16_hi(r.x);
+    f[2] = bf16_lo(r.y); f[3] = bf16_hi(r.y);
+    f[4] = bf16_lo(r.z); f[5] = bf16_hi(r.z);
+    f[6] = bf16_lo(r.w); f[7] = bf16_hi(r.w);
+  } else {
+    f[0] = __uint_as_float(r.x); f[1] = __uint_as_float(r.y);
+    f[2] = __uint_as_float(r.z); f[3] = __uint_as_float(r.w);
+  }
+}
+
+__device__ __forceinline__ uint4 load16(const void* p) {
+  return *reinterpret_cast<const uint4*>(p);
+}
+
+// Butterfly sum / max over lanes that differ only in the bits of [lo_mask, 64).
+template <int FROM, int TO>
+__device__ __forceinline__ float xor_sum(float v) {
+#pragma unroll
+  for (int off = FROM; off < TO; off <<= 1) v += __shfl_xor(v, off, kWave);
+  return v;
+}
+template <int FROM, int TO>
+__device__ __forceinline__ float xor_max(float v) {
+#pragma unroll
+  for (int off = FROM; off < TO; off <<= 1) v = fmaxf(v, __shfl_xor(v, off, kWave));
+  return v;
+}
+
+}  // namespace pkv

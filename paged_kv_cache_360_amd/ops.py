@@ -1,0 +1,129 @@
+"""Python entry points with the C ABI's names: argument marshalling only.
+
+Every step of the hot path runs in the HIP kernels behind ``libpagedkv.so``;
+these wrappers read shapes, device pointers and the current stream from torch
+tensors and pass them through.  torch supplies device memory and streams only.
+"""
+
+import torch
+
+from ._lib import (BLOCK_SIZE, PKV_BF16, PKV_F32, check, lib)
+
+_DTYPES = {torch.float32: PKV_F32, torch.bfloat16: PKV_BF16}
+
+
+def _dt(t):
+    try:
+        return _DTYPES[t.dtype]
+    except KeyError:
+        raise TypeError(f"unsupported dtype {t.dtype}; use float32 or bfloat16") from None
+
+
+def _dev(t, name, dtype=None):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return getattr(stream, "cuda_stream", stream)
+
+
+def pkv_write(key_cache, value_cache, k, v, slot_mapping, stream=None):
+    """Scatter new tokens' K/V rows ``[T, Hkv, D]`` into their slots (bit copy)."""
+    nb, bs, hkv, d = key_cache.shape
+    if value_cache.shape != key_cache.shape or k.shape != v.shape or k.shape[1:] != (hkv, d):
+        raise ValueError("shape mismatch between caches and k/v")
+    if k.dtype != key_cache.dtype or v.dtype != key_cache.dtype or value_cache.dtype != key_cache.dtype:
+        raise TypeError("caches and k/v must share one dtype")
+    t = k.shape[0]
+    if slot_mapping.shape != (t,):
+        raise ValueError("slot_mapping must be [num_tokens]")
+    check("pkv_write", lib().pkv_write(
+        _dev(key_cache, "key_cache"), _dev(value_cache, "value_cache"), _dev(k, "k"), _dev(v, "v"),
+        _dev(slot_mapping, "slot_mapping", torch.int32), t, nb, bs, hkv, d, _dt(key_cache),
+        _stream(stream)))
+
+
+def pkv_decode_workspace_bytes(num_seqs, num_q_heads, head_dim, max_context_len):
+    return int(lib().pkv_decode_workspace_bytes(num_seqs, num_q_heads, head_dim, max_context_len))
+
+
+def decode_workspace(num_seqs, num_q_heads, head_dim, max_context_len, device="cuda"):
+    """A device buffer of the size ``pkv_attention_decode`` needs (None if 0 bytes)."""
+    n = pkv_decode_workspace_bytes(num_seqs, num_q_heads, head_dim, max_context_len)
+    return torch.empty(n, dtype=torch.uint8, device=device) if n else None
+
+
+def pkv_attention_decode(out, q, key_cache, value_cache, block_tables, context_lens, scale,
+                         max_context_len, workspace=None, stream=None):
+    """Paged decode attention for one new token per sequence; writes ``out`` [S, Hq, D]."""
+    s, hq, d = q.shape
+    nb, bs, hkv, dk = key_cache.shape
+    if out.shape != q.shape or dk != d or value_cache.shape != key_cache.shape:
+        raise ValueError("shape mismatch")
+    if out.dtype != q.dtype or key_cache.dtype != q.dtype or value_cache.dtype != q.dtype:
+        raise TypeError("q, caches and out must share one dtype")
+    if block_tables.dim() != 2 or block_tables.shape[0] != s or context_lens.shape != (s,):
+        raise ValueError("block_tables must be [S, MB] and context_lens [S]")
+    mb = block_tables.shape[1]
+    if workspace is None:
+        workspace = decode_workspace(s, hq, d, max_context_len, q.device)
+    ws_ptr = 0 if workspace is None else _dev(workspace, "workspace")
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    check("pkv_attention_decode", lib().pkv_attention_decode(
+        _dev(out, "out"), _dev(q, "q"), _dev(key_cache, "key_cache"), _dev(value_cache, "value_cache"),
+        _dev(block_tables, "block_tables", torch.int32), _dev(context_lens, "context_lens", torch.int32),
+        float(scale), bs, hq, hkv, d, s, mb, nb, int(max_context_len), _dt(q), ws_ptr, ws_bytes,
+        _stream(stream)))
+    return out
+
+
+def pkv_lse_merge(out, part_m, part_l, part_o, num_parts, stream=None):
+    """Merge partial softmax results (base-2 maxima); ``out`` [rows, D]."""
+    rows, maxp, d = part_o.shape
+    if part_m.shape != (rows, maxp) or part_l.shape != (rows, maxp) or num_parts.shape != (rows,):
+        raise ValueError("shape mismatch")
+    if out.shape != (rows, d):
+        raise ValueError("out must be [rows, head_dim]")
+    check("pkv_lse_merge", lib().pkv_lse_merge(
+        _dev(out, "out"), _dev(part_m, "part_m", torch.float32), _dev(part_l, "part_l", torch.float32),
+        _dev(part_o, "part_o", torch.float32), _dev(num_parts, "num_parts", torch.int32), rows, maxp, d,
+        _dt(out), _stream(stream)))
+    return out
+
+
+def pkv_copy_blocks(key_cache, value_cache, pairs, stream=None):
+    """Copy-on-write block copies; ``pairs`` is a device int32 [n, 2] of (src, dst)."""
+    nb, bs, hkv, d = key_cache.shape
+    n = pairs.shape[0] if pairs.numel() else 0
+    if n and tuple(pairs.shape) != (n, 2):
+        raise ValueError("pairs must be [n, 2]")
+    if n == 0:
+        return
+    check("pkv_copy_blocks", lib().pkv_copy_blocks(
+        _dev(key_cache, "key_cache"), _dev(value_cache, "value_cache"), _dev(pairs, "pairs", torch.int32),
+        n, nb, bs, hkv, d, _dt(key_cache), _stream(stream)))
+
+
+def pkv_check_tables(block_tables, context_lens, num_blocks):
+    """Host-side table validation (numpy int32 arrays).  Raises PagedKVError on a bad entry."""
+    import numpy as np
+    t = np.ascontiguousarray(block_tables, dtype=np.int32)
+    c = np.ascontiguousarray(context_lens, dtype=np.int32)
+    check("pkv_check_tables", lib().pkv_check_tables(
+        t.ctypes.data, c.ctypes.data, t.shape[0], t.shape[1], int(num_blocks)))
+
+
+def pkv_check_slots(slot_mapping, num_blocks):
+    """Host-side slot validation: in range and no duplicates (numpy int32)."""
+    import numpy as np
+    s = np.ascontiguousarray(slot_mapping, dtype=np.int32)
+    check("pkv_check_slots", lib().pkv_check_slots(s.ctypes.data, s.shape[0], int(num_blocks),
+                                                   BLOCK_SIZE))

@@ -71,12 +71,15 @@ def f32_to_bf16_bits(x):
     NaN inputs become a quiet NaN with the input's sign.
     """
     x = np.ascontiguousarray(x, dtype=np.float32)
-    u = x.view(np.uint32).astype(np.uint64)
-    rounded = ((u + np.uint64(0x7FFF) + ((u >> np.uint64(16)) & np.uint64(1))) >> np.uint64(16))
-    out = (rounded & np.uint64(0xFFFF)).astype(np.uint16)
+    u = x.view(np.uint32)
+    # add 0x7FFF plus the lowest kept bit, then keep the top half; the uint32 sum
+    # wraps only for negative NaN patterns, which are replaced below
+    with np.errstate(over="ignore"):
+        r = u + (np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1)))
+    out = (r >> np.uint32(16)).astype(np.uint16)
     nan = np.isnan(x)
     if nan.any():
-        out[nan] = ((u[nan] >> np.uint64(16)).astype(np.uint16) | np.uint16(0x0040))
+        out[nan] = (u[nan] >> np.uint32(16)).astype(np.uint16) | np.uint16(0x0040)
     return out
 
 
