@@ -1,0 +1,332 @@
+#!/usr/bin/env python3
+"""Decode-step benchmark of the paged KV-cache hot path on one MI355X.
+
+One step = one decode iteration for a batch of sequences, every stage of the
+path included:
+  1. host block allocator: one new token per sequence (a new block when the last
+     one is full), slot of each new token, refreshed block tables and lengths,
+     written into a pinned staging buffer (C++ allocator behind the C ABI);
+  2. one H2D copy of that metadata on a side stream (default priority), joined
+     to the compute stream by an event;
+  3. pkv_copy_blocks for any copy-on-write pairs (none for unshared batches);
+  4. pkv_write of the new tokens' K/V;
+  5. pkv_attention_decode_partitions (split-context decode, the dominant kernel);
+  6. pkv_attention_decode_merge (log-sum-exp merge of multi-partition sequences).
+Contexts grow by one token per step, as in real decoding.  Inputs (pool, q, new
+K/V rows) are resident in HBM before timing starts.  R copies of the KV pool are
+rotated step to step so each step's KV reads come from HBM, not the 256 MiB
+last-level cache.
+
+Prints ONE JSON line.  Per-kernel durations come from HIP events recorded on
+the compute stream around each launch inside the timed region.
+"""
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "decode tokens/s + KV-read HBM GB/s (% of MI355X peak), bf16 GQA ctx 2k–8k"
+HBM_PEAK_GBPS = 8000.0
+DEFAULT_WORKLOAD = "gqa32x8_bf16_s128_ctx512_8192"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_partitions_traffic.json")
+KERNEL_SOURCES = ["paged_kv_cache_360_amd/csrc/kernels/decode.hip",
+                  "paged_kv_cache_360_amd/csrc/kernels/device_common.hpp"]
+
+
+def parse_args():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--seed", type=int, default=1002)
+    ap.add_argument("--pool-copies", type=int, default=4)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="only run a plain block copy of known size (counter calibration)")
+    ap.add_argument("--json-out", default=None)
+    return ap.parse_args()
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def copy_probe(torch, pkv):
+    """pkv_copy_blocks over 2 x 512 MiB: reads 1 GiB, writes 1 GiB (both caches)."""
+    nb, hkv, d = 2 * 8192, 8, 128                     # 32 KiB bf16 blocks
+    kc = torch.zeros((nb, 16, hkv, d), dtype=torch.bfloat16, device="cuda")
+    vc = torch.zeros_like(kc)
+    half = nb // 2
+    pairs = torch.stack([torch.arange(half), torch.arange(half) + half], 1).to(torch.int32).cuda()
+    for _ in range(3):
+        pkv.pkv_copy_blocks(kc, vc, pairs)
+    torch.cuda.synchronize()
+    moved = 2 * half * 16 * hkv * d * 2
+    print(json.dumps({"probe": "pkv_copy_blocks", "bytes_read_per_launch": moved,
+                      "bytes_written_per_launch": moved, "launches": 3}))
+
+
+def main():
+    args = parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only: --gpus {args.gpus} (WORLD_SIZE={world}) is not "
+              "supported; this paged-attention path runs on a single MI355X and has no "
+              "multi-GPU code.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_360_amd as pkv
+    from workloads import SPECS, draw_context_lens, normal_values_parallel, pool_blocks_for
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.copy_probe:
+        copy_probe(torch, pkv)
+        return
+
+    spec = SPECS[args.workload]
+    if spec.chunk_rows or spec.ctx_kind == "prefix":
+        raise SystemExit(f"workload {spec.name} is not a plain decode batch")
+    S, Hq, Hkv, D = spec.num_seqs, spec.num_q_heads, spec.num_kv_heads, spec.head_dim
+    es = 2 if spec.dtype == "bf16" else 4
+    tdt = torch.bfloat16 if spec.dtype == "bf16" else torch.float32
+    W, K, R = args.warmup, args.steps, max(1, args.pool_copies)
+    n_steps = W + K
+
+    # ---- workload: lengths, allocator state, pool, queries ------------------
+    t0 = time.time()
+    rng = np.random.default_rng(args.seed)
+    ctx0 = draw_context_lens(rng, spec)                 # context at the first step (new token included)
+    final_ctx = ctx0.astype(np.int64) + n_steps - 1
+    MB = int(-(-final_ctx.max() // 16))
+    max_ctx_bound = int(final_ctx.max())
+    nb = pool_blocks_for(spec, final_ctx)
+    alloc = pkv.BlockAllocator(nb, 16, shuffle_seed=args.seed)
+    ids = np.arange(S, dtype=np.int64)
+    for s in range(S):
+        alloc.add_seq(int(s))
+    alloc.append_batch(ids, ctx0 - 1)                   # prefilled tokens; the pool holds their K/V
+
+    pool_host_k = normal_values_parallel(args.seed * 10 + 1, (nb, 16, Hkv, D), spec.dtype)
+    pool_host_v = normal_values_parallel(args.seed * 10 + 2, (nb, 16, Hkv, D), spec.dtype)
+
+    def up(a):
+        a = np.ascontiguousarray(a)
+        t = torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a).cuda()
+        return t.view(tdt) if a.dtype == np.uint16 else t
+
+    kcs, vcs = [up(pool_host_k)], [up(pool_host_v)]
+    for _ in range(R - 1):
+        kcs.append(kcs[0].clone())
+        vcs.append(vcs[0].clone())
+    q_host = normal_values_parallel(args.seed * 10 + 3, (n_steps, S, Hq, D), spec.dtype)
+    qs = up(q_host)
+    knew = up(normal_values_parallel(args.seed * 10 + 4, (n_steps, S, Hkv, D), spec.dtype))
+    vnew = up(normal_values_parallel(args.seed * 10 + 5, (n_steps, S, Hkv, D), spec.dtype))
+    out = torch.empty((S, Hq, D), dtype=tdt, device="cuda")
+    ws = pkv.decode_workspace(S, Hq, D, max_ctx_bound)
+    scale = float(np.float32(1.0 / math.sqrt(D)))
+
+    # pinned staging: [slots S | lens S | tables S*MB] int32, two sets
+    meta_len = 2 * S + S * MB
+    stage = [torch.empty(meta_len, dtype=torch.int32, pin_memory=True) for _ in range(2)]
+    dmeta = [torch.empty(meta_len, dtype=torch.int32, device="cuda") for _ in range(2)]
+    views = []
+    for b in range(2):
+        h = stage[b].numpy()
+        views.append((h[:S], h[S:2 * S], h[2 * S:].reshape(S, MB)))
+    ones = np.ones(S, dtype=np.int32)
+    main = torch.cuda.current_stream()
+    side = torch.cuda.Stream()                          # default priority
+    h2d_done = [torch.cuda.Event() for _ in range(2)]
+    kern_done = [torch.cuda.Event() for _ in range(2)]
+    log(f"[bench] setup {time.time() - t0:.1f}s: {spec.name} S={S} Hq={Hq} Hkv={Hkv} D={D} "
+        f"pool={nb} blocks x{R} MB={MB}")
+
+    step_lens = []
+    host_alloc_s = []
+    events = []
+
+    def step(i, timed):
+        b = i % 2
+        slots_h, lens_h, tables_h = views[b]
+        h2d_done[b].synchronize()                       # staging set b is free again (copy of step i-2 done)
+        ta = time.perf_counter()
+        _, pairs = alloc.append_batch(ids, ones, slots_out=slots_h)
+        alloc.block_tables(ids, MB, fill=-1, tables_out=tables_h, lens_out=lens_h)
+        host_alloc_s.append(time.perf_counter() - ta)
+        if timed:
+            step_lens.append(lens_h.copy())
+        with torch.cuda.stream(side):
+            side.wait_event(kern_done[b])               # device set b no longer read by step i-2
+            dmeta[b].copy_(stage[b], non_blocking=True)
+            h2d_done[b].record(side)
+        main.wait_event(h2d_done[b])
+        d_slots, d_lens = dmeta[b][:S], dmeta[b][S:2 * S]
+        d_tables = dmeta[b][2 * S:].view(S, MB)
+        r = i % R
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)] if timed else None
+        if timed:
+            ev[0].record(main)
+        if len(pairs):
+            pkv.pkv_copy_blocks(kcs[r], vcs[r], torch.from_numpy(pairs).cuda())
+        pkv.pkv_write(kcs[r], vcs[r], knew[i], vnew[i], d_slots)
+        if timed:
+            ev[1].record(main)
+        pkv.pkv_attention_decode_partitions(out, qs[i], kcs[r], vcs[r], d_tables, d_lens, scale,
+                                            max_ctx_bound, workspace=ws)
+        if timed:
+            ev[2].record(main)
+        pkv.pkv_attention_decode_merge(out, qs[i], kcs[r], vcs[r], d_tables, d_lens, scale,
+                                       max_ctx_bound, workspace=ws)
+        if timed:
+            ev[3].record(main)
+            events.append(ev)
+        kern_done[b].record(main)
+
+    for i in range(W):
+        step(i, False)
+    torch.cuda.synchronize()
+    log(f"[bench] warmup {W} steps done")
+    t_start = time.perf_counter()
+    for i in range(W, W + K):
+        step(i, True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    log(f"[bench] timed {K} steps: {wall * 1e3:.2f} ms")
+
+    # ---- per-kernel durations and algorithmic bytes --------------------------
+    t_write = [e[0].elapsed_time(e[1]) * 1e-3 for e in events]
+    t_part = [e[1].elapsed_time(e[2]) * 1e-3 for e in events]
+    t_merge = [e[2].elapsed_time(e[3]) * 1e-3 for e in events]
+    kv_b, part_b, merge_b = [], [], []
+    for lens in step_lens:
+        lens = lens.astype(np.int64)
+        nparts = -(-lens // 512)
+        kv = int(lens.sum()) * 2 * Hkv * D * es
+        q_out = S * Hq * D * es + int((nparts == 1).sum()) * Hq * D * es
+        meta = int((4 * -(-lens // 16)).sum()) + 4 * S
+        partials = int(nparts[nparts > 1].sum()) * Hq * (D + 2) * 4
+        kv_b.append(kv)
+        part_b.append(kv + q_out + meta + partials)
+        merge_b.append(partials + int((nparts > 1).sum()) * Hq * D * es + 4 * S)
+    sum_tp = sum(t_part)
+    achieved = sum(part_b) / sum_tp / 1e9
+    kv_gbps = sum(kv_b) / sum_tp / 1e9
+    ms_per_step = wall / K * 1e3
+    value = S * K / wall
+
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        with open(TRAFFIC_FILE) as f:
+            tr = json.load(f)
+        if tr.get("kernel_source_sha256") == kernel_source_hash() and tr.get("workload") == spec.name:
+            traffic = tr.get("traffic_bytes_per_launch")
+
+    roofline = {
+        "kernel": "decode_partition_kernel (pkv_attention_decode_partitions)",
+        "bound": "hbm",
+        "achieved": round(achieved, 1),
+        "peak": HBM_PEAK_GBPS,
+        "unit": "GB/s",
+        "frac": round(achieved / HBM_PEAK_GBPS, 4),
+        "traffic": traffic,
+        "algorithmic_bytes_per_launch": int(np.mean(part_b)),
+        "avg_launch_us": round(sum_tp / K * 1e6, 2),
+    }
+
+    # ---- CPU oracle baseline (bounded sample of the same batch) --------------
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(np, spec, q_host[W + K - 1], pool_host_k, pool_host_v, alloc, ids, MB,
+                           scale, args.cpu_seconds)
+
+    res = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": spec.dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": spec.name,
+            "num_seqs": S, "num_q_heads": Hq, "num_kv_heads": Hkv, "head_dim": D,
+            "block_size": 16, "partition_tokens": 512,
+            "context": f"{spec.ctx_kind}[{spec.ctx_lo},{spec.ctx_hi}] + 1 per step",
+            "mean_context": round(float(np.mean([l.mean() for l in step_lens])), 1),
+            "pool_blocks": nb, "pool_copies": R, "seed": args.seed,
+        },
+        "kv_read_GBps": round(kv_gbps, 1),
+        "kv_read_frac_of_peak": round(kv_gbps / HBM_PEAK_GBPS, 4),
+        "kernels_us": {
+            "write": round(float(np.mean(t_write)) * 1e6, 2),
+            "decode_partitions": round(float(np.mean(t_part)) * 1e6, 2),
+            "merge": round(float(np.mean(t_merge)) * 1e6, 2),
+        },
+        "host_alloc_us": round(float(np.mean(host_alloc_s[W:])) * 1e6, 2),
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    line = json.dumps(res)
+    print(line, flush=True)
+    if args.json_out:
+        with open(args.json_out, "w") as f:
+            f.write(line + "\n")
+
+
+def cpu_baseline(np, spec, q_last, pool_k, pool_v, alloc, ids, MB, scale, budget_s):
+    """The fp64 oracle on the host, sequence by sequence, for about ``budget_s`` seconds."""
+    import oracle
+    from threadpoolctl import threadpool_limits
+
+    tables, lens = alloc.block_tables(ids, MB)
+    done, t0 = 0, time.perf_counter()
+    with threadpool_limits(limits=1):
+        for s in range(len(ids)):
+            oracle.decode_attention(q_last[s:s + 1], pool_k, pool_v, tables[s:s + 1], lens[s:s + 1], scale)
+            done += 1
+            if time.perf_counter() - t0 >= budget_s:
+                break
+    el = time.perf_counter() - t0
+    kv = int(lens[:done].astype(np.int64).sum()) * 2 * spec.num_kv_heads * spec.head_dim * (
+        2 if spec.dtype == "bf16" else 4)
+    return {
+        "value": round(done / el, 3),
+        "unit": "tokens/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"first {done} of {len(ids)} sequences of the last timed step's batch "
+                  f"(mean context {float(lens[:done].mean()):.0f}), fp64 NumPy, 1 BLAS thread, "
+                  f"{el:.1f} s; host {os.cpu_count()} logical CPUs",
+        "kv_GBps": round(kv / el / 1e9, 4),
+    }
+
+
+if __name__ == "__main__":
+    main()

@@ -117,6 +117,29 @@ int pkv_attention_decode(void* out, const void* q, const void* key_cache,
                          int32_t max_context_len, pkv_dtype dt, void* workspace,
                          size_t workspace_bytes, void* stream);
 
+/* The two launches pkv_attention_decode makes, callable one at a time with the
+ * same arguments (so each can be timed or overlapped on its own).
+ * _partitions: one workgroup per (sequence, KV head, 512-token partition); writes
+ * `out` for sequences with a single partition and the partials (max, sum,
+ * normalized output) of the others to the workspace.
+ * _merge: log-sum-exp merge of those partials into `out` (launches nothing when
+ * max_context_len <= PKV_PARTITION_TOKENS).  Run _partitions first on the same
+ * stream.  Errors as pkv_attention_decode. */
+int pkv_attention_decode_partitions(void* out, const void* q, const void* key_cache,
+                                    const void* value_cache, const int32_t* block_tables,
+                                    const int32_t* context_lens, float scale, int32_t block_size,
+                                    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                    int32_t num_seqs, int32_t max_blocks_per_seq,
+                                    int32_t num_blocks, int32_t max_context_len, pkv_dtype dt,
+                                    void* workspace, size_t workspace_bytes, void* stream);
+int pkv_attention_decode_merge(void* out, const void* q, const void* key_cache,
+                               const void* value_cache, const int32_t* block_tables,
+                               const int32_t* context_lens, float scale, int32_t block_size,
+                               int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                               int32_t num_seqs, int32_t max_blocks_per_seq, int32_t num_blocks,
+                               int32_t max_context_len, pkv_dtype dt, void* workspace,
+                               size_t workspace_bytes, void* stream);
+
 /* ------------------------------------------------------------------------ */
 /* Log-sum-exp merge of partial softmax results, one output row per input row.
  *

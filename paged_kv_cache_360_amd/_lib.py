@@ -36,6 +36,10 @@ SIGNATURES = {
     "pkv_decode_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32]),
     "pkv_attention_decode": (ctypes.c_int, [_p, _p, _p, _p, _p, _p, _f32, _i32, _i32, _i32, _i32, _i32,
                                             _i32, _i32, _i32, ctypes.c_int, _p, _sz, _p]),
+    "pkv_attention_decode_partitions": (ctypes.c_int, [_p, _p, _p, _p, _p, _p, _f32, _i32, _i32, _i32, _i32,
+                                                       _i32, _i32, _i32, _i32, ctypes.c_int, _p, _sz, _p]),
+    "pkv_attention_decode_merge": (ctypes.c_int, [_p, _p, _p, _p, _p, _p, _f32, _i32, _i32, _i32, _i32,
+                                                  _i32, _i32, _i32, _i32, ctypes.c_int, _p, _sz, _p]),
     "pkv_lse_merge": (ctypes.c_int, [_p, _p, _p, _p, _p, _i32, _i32, _i32, ctypes.c_int, _p]),
     "pkv_copy_blocks": (ctypes.c_int, [_p, _p, _p, _i32, _i32, _i32, _i32, _i32, ctypes.c_int, _p]),
     "pkv_check_tables": (ctypes.c_int, [_p, _p, _i32, _i32, _i32]),
@@ -64,7 +68,7 @@ def lib():
     if _lib is None:
         if not os.path.exists(LIB_PATH):
             raise ImportError(
-                f"{LIB_PATH} is missing: build it with `python -m paged_kv_cache_360_amd.build` "
+                f"{LIB_PATH} is missing: build it with `python paged_kv_cache_360_amd/build.py` "
                 "(the paged-attention path has no fallback)")
         handle = ctypes.CDLL(LIB_PATH)
         for name, (res, args) in SIGNATURES.items():

@@ -55,16 +55,26 @@ class BlockAllocator:
         cow = [(int(pairs[0]), int(pairs[1]))] if ncow.value else []
         return slots[:n_tokens].tolist(), cow
 
-    def append_batch(self, seq_ids, n_tokens):
-        """All-or-nothing append for distinct sequences; returns (slots ndarray, pairs [n,2] ndarray)."""
+    def append_batch(self, seq_ids, n_tokens, slots_out=None):
+        """All-or-nothing append for distinct sequences.
+
+        Returns (slots, pairs): int32 slots in batch order (written into
+        ``slots_out`` when given, e.g. a pinned staging buffer) and an int32 [n, 2]
+        array of copy-on-write pairs.
+        """
         ids = np.ascontiguousarray(seq_ids, dtype=np.int64)
         ns = np.ascontiguousarray(n_tokens, dtype=np.int32)
         total = int(ns.sum())
-        slots = np.empty(max(1, total), dtype=np.int32)
+        if slots_out is None:
+            slots = np.empty(max(1, total), dtype=np.int32)
+        else:
+            slots = slots_out
+            if slots.dtype != np.int32 or not slots.flags.c_contiguous or slots.size < total:
+                raise ValueError("slots_out must be a contiguous int32 array of sum(n_tokens) entries")
         pairs = np.empty((max(1, len(ids)), 2), dtype=np.int32)
         ncow = ctypes.c_int32(0)
         self._check("pkv_alloc_append_batch", lib().pkv_alloc_append_batch(
-            self._h, ids.ctypes.data, ns.ctypes.data, len(ids), slots.ctypes.data, total,
+            self._h, ids.ctypes.data, ns.ctypes.data, len(ids), slots.ctypes.data, max(total, slots.size),
             pairs.ctypes.data, pairs.shape[0], ctypes.addressof(ncow)))
         return slots[:total], pairs[:ncow.value]
 
@@ -81,11 +91,18 @@ class BlockAllocator:
             self._h, int(seq), out.ctypes.data, out.shape[0], ctypes.addressof(n)))
         return out[:n.value].tolist()
 
-    def block_tables(self, seq_ids, max_blocks, fill=-1):
-        """Dense int32 tables [S, max_blocks] and int32 context lengths [S]."""
+    def block_tables(self, seq_ids, max_blocks, fill=-1, tables_out=None, lens_out=None):
+        """Dense int32 tables [S, max_blocks] and int32 context lengths [S].
+
+        ``tables_out`` / ``lens_out`` (contiguous int32, e.g. pinned staging
+        buffers) receive the result in place when given.
+        """
         ids = np.ascontiguousarray(seq_ids, dtype=np.int64)
-        tables = np.empty((len(ids), max_blocks), dtype=np.int32)
-        lens = np.empty(len(ids), dtype=np.int32)
+        tables = np.empty((len(ids), max_blocks), dtype=np.int32) if tables_out is None else tables_out
+        lens = np.empty(len(ids), dtype=np.int32) if lens_out is None else lens_out
+        for a, shape in ((tables, (len(ids), max_blocks)), (lens, (len(ids),))):
+            if a.dtype != np.int32 or not a.flags.c_contiguous or a.shape != shape:
+                raise ValueError(f"output must be a contiguous int32 array of shape {shape}")
         self._check("pkv_alloc_block_tables", lib().pkv_alloc_block_tables(
             self._h, ids.ctypes.data, len(ids), tables.ctypes.data, int(max_blocks), int(fill),
             lens.ctypes.data))

@@ -1,6 +1,7 @@
 """Build ``libpagedkv.so`` in-tree with hipcc for gfx950.
 
-Usage: ``python -m paged_kv_cache_360_amd.build`` (or ``build()`` from Python).
+Usage: ``python paged_kv_cache_360_amd/build.py`` (or ``__graft_entry__.build()``); the
+script does not import the package, so a stale library never blocks a rebuild.
 Objects go to ``_build/`` at the repository root; the shared library is written
 next to this file, where the binding loads it.  Always recompiles.
 """

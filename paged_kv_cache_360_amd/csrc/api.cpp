@@ -96,42 +96,48 @@ size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t
   return pkv::align256(rows * P * sizeof(float)) * 2 + pkv::align256(rows * P * head_dim * sizeof(float));
 }
 
-int pkv_attention_decode(void* out, const void* q, const void* key_cache,
-                         const void* value_cache, const int32_t* block_tables,
-                         const int32_t* context_lens, float scale, int32_t block_size,
-                         int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
-                         int32_t num_seqs, int32_t max_blocks_per_seq, int32_t num_blocks,
-                         int32_t max_context_len, pkv_dtype dt, void* workspace,
-                         size_t workspace_bytes, void* stream) {
-  if (!pkv::dtype_ok(dt)) return fail(PKV_EUNSUPPORTED, "pkv_attention_decode: unsupported dtype");
-  if (block_size != PKV_BLOCK_SIZE)
-    return fail(PKV_EUNSUPPORTED, "pkv_attention_decode: block_size must be 16");
-  if (head_dim != 64 && head_dim != 128)
-    return fail(PKV_EUNSUPPORTED, "pkv_attention_decode: head_dim must be 64 or 128");
+}  // extern "C"
+
+namespace {
+
+// Shared validation of the decode arguments; fills `a` on success.
+int prepare_decode(const char* who, pkv::DecodeArgs& a, void* out, const void* q,
+                   const void* key_cache, const void* value_cache, const int32_t* block_tables,
+                   const int32_t* context_lens, float scale, int32_t block_size, int32_t num_q_heads,
+                   int32_t num_kv_heads, int32_t head_dim, int32_t num_seqs, int32_t max_blocks_per_seq,
+                   int32_t num_blocks, int32_t max_context_len, pkv_dtype dt, void* workspace,
+                   size_t workspace_bytes) {
+  char msg[160];
+  auto bad = [&](int code, const char* what) {
+    std::snprintf(msg, sizeof(msg), "%s: %s", who, what);
+    return fail(code, msg);
+  };
+  if (!pkv::dtype_ok(dt)) return bad(PKV_EUNSUPPORTED, "unsupported dtype");
+  if (block_size != PKV_BLOCK_SIZE) return bad(PKV_EUNSUPPORTED, "block_size must be 16");
+  if (head_dim != 64 && head_dim != 128) return bad(PKV_EUNSUPPORTED, "head_dim must be 64 or 128");
   if (num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0)
-    return fail(PKV_EINVAL, "pkv_attention_decode: num_q_heads must be a positive multiple of num_kv_heads");
+    return bad(PKV_EINVAL, "num_q_heads must be a positive multiple of num_kv_heads");
   const int32_t G = num_q_heads / num_kv_heads;
   if (G != 1 && G != 2 && G != 4 && G != 8)
-    return fail(PKV_EUNSUPPORTED, "pkv_attention_decode: q heads per KV head must be 1, 2, 4 or 8");
+    return bad(PKV_EUNSUPPORTED, "q heads per KV head must be 1, 2, 4 or 8");
   if (num_seqs < 0 || num_seqs > 65535 || max_blocks_per_seq <= 0 || num_blocks <= 0 ||
       max_context_len < 0 || num_kv_heads > 65535)
-    return fail(PKV_EINVAL, "pkv_attention_decode: bad sizes");
+    return bad(PKV_EINVAL, "bad sizes");
   if ((int64_t)max_context_len > (int64_t)max_blocks_per_seq * PKV_BLOCK_SIZE)
-    return fail(PKV_EINVAL, "pkv_attention_decode: max_context_len exceeds the table width");
-  if (!std::isfinite(scale)) return fail(PKV_EINVAL, "pkv_attention_decode: scale must be finite");
+    return bad(PKV_EINVAL, "max_context_len exceeds the table width");
+  if (!std::isfinite(scale)) return bad(PKV_EINVAL, "scale must be finite");
   if (num_seqs == 0) return PKV_OK;
   if (!out || !q || !key_cache || !value_cache || !block_tables || !context_lens)
-    return fail(PKV_EINVAL, "pkv_attention_decode: null pointer");
+    return bad(PKV_EINVAL, "null pointer");
   if (!pkv::aligned16(out) || !pkv::aligned16(q) || !pkv::aligned16(key_cache) ||
       !pkv::aligned16(value_cache))
-    return fail(PKV_EINVAL, "pkv_attention_decode: pointers must be 16-byte aligned");
+    return bad(PKV_EINVAL, "pointers must be 16-byte aligned");
   const int64_t P = std::max<int64_t>(1, pkv::parts_for(max_context_len));
-  if (P > 65535) return fail(PKV_EUNSUPPORTED, "pkv_attention_decode: context too long");
+  if (P > 65535) return bad(PKV_EUNSUPPORTED, "context too long");
   const size_t need = pkv_decode_workspace_bytes(num_seqs, num_q_heads, head_dim, max_context_len);
   if (need > 0 && (!workspace || workspace_bytes < need || !pkv::aligned16(workspace)))
-    return fail(PKV_EWORKSPACE, "pkv_attention_decode: workspace missing or too small");
+    return bad(PKV_EWORKSPACE, "workspace missing or too small");
 
-  pkv::DecodeArgs a{};
   a.out = out;
   a.q = q;
   a.kc = key_cache;
@@ -154,7 +160,48 @@ int pkv_attention_decode(void* out, const void* q, const void* key_cache,
     a.part_l = reinterpret_cast<float*>(ws + pkv::align256(rows * P * sizeof(float)));
     a.part_o = reinterpret_cast<float*>(ws + 2 * pkv::align256(rows * P * sizeof(float)));
   }
-  return pkv::launched(pkv::launch_decode(a, stream), "pkv_attention_decode");
+  return PKV_OK;
+}
+
+}  // namespace
+
+#define PKV_DECODE_ARGS                                                                        \
+  void *out, const void *q, const void *key_cache, const void *value_cache,                    \
+      const int32_t *block_tables, const int32_t *context_lens, float scale, int32_t block_size, \
+      int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t num_seqs,           \
+      int32_t max_blocks_per_seq, int32_t num_blocks, int32_t max_context_len, pkv_dtype dt,   \
+      void *workspace, size_t workspace_bytes, void *stream
+#define PKV_DECODE_FWD                                                                          \
+  out, q, key_cache, value_cache, block_tables, context_lens, scale, block_size, num_q_heads,  \
+      num_kv_heads, head_dim, num_seqs, max_blocks_per_seq, num_blocks, max_context_len, dt,   \
+      workspace, workspace_bytes
+
+extern "C" {
+
+int pkv_attention_decode_partitions(PKV_DECODE_ARGS) {
+  pkv::DecodeArgs a{};
+  const char* who = "pkv_attention_decode_partitions";
+  int rc = prepare_decode(who, a, PKV_DECODE_FWD);
+  if (rc != PKV_OK || num_seqs == 0) return rc;
+  return pkv::launched(pkv::launch_decode_partitions(a, stream), who);
+}
+
+int pkv_attention_decode_merge(PKV_DECODE_ARGS) {
+  pkv::DecodeArgs a{};
+  const char* who = "pkv_attention_decode_merge";
+  int rc = prepare_decode(who, a, PKV_DECODE_FWD);
+  if (rc != PKV_OK || num_seqs == 0) return rc;
+  return pkv::launched(pkv::launch_decode_merge(a, stream), who);
+}
+
+int pkv_attention_decode(PKV_DECODE_ARGS) {
+  pkv::DecodeArgs a{};
+  const char* who = "pkv_attention_decode";
+  int rc = prepare_decode(who, a, PKV_DECODE_FWD);
+  if (rc != PKV_OK || num_seqs == 0) return rc;
+  rc = pkv::launched(pkv::launch_decode_partitions(a, stream), who);
+  if (rc != PKV_OK) return rc;
+  return pkv::launched(pkv::launch_decode_merge(a, stream), who);
 }
 
 int pkv_lse_merge(void* out, const float* part_m, const float* part_l, const float* part_o,

@@ -319,7 +319,7 @@ __global__ __launch_bounds__(kWave) void lse_merge_kernel(
 }
 
 template <bool BF16, int D, int G>
-void launch_decode_t(const DecodeArgs& a, hipStream_t st) {
+void launch_partitions_t(const DecodeArgs& a, hipStream_t st) {
   DecodeParams p;
   p.out = a.out;
   p.q = a.q;
@@ -337,34 +337,46 @@ void launch_decode_t(const DecodeArgs& a, hipStream_t st) {
   p.part_o = a.part_o;
   hipLaunchKernelGGL((decode_partition_kernel<BF16, D, G>),
                      dim3(a.num_kv_heads, a.max_parts, a.num_seqs), dim3(kDecodeThreads), 0, st, p);
-  if (a.max_parts > 1) {
-    hipLaunchKernelGGL((lse_merge_kernel<BF16, D, true>), dim3(a.num_seqs * a.num_q_heads),
-                       dim3(kWave), 0, st, a.out, a.part_m, a.part_l, a.part_o, a.ctx,
-                       a.num_q_heads, a.max_parts,
-                       min(a.max_blocks * kBlockTokens, a.max_parts * kPartTokens));
-  }
 }
 
 template <bool BF16, int D>
-int launch_decode_g(const DecodeArgs& a, hipStream_t st) {
+int launch_partitions_g(const DecodeArgs& a, hipStream_t st) {
   switch (a.num_q_heads / a.num_kv_heads) {
-    case 1: launch_decode_t<BF16, D, 1>(a, st); break;
-    case 2: launch_decode_t<BF16, D, 2>(a, st); break;
-    case 4: launch_decode_t<BF16, D, 4>(a, st); break;
-    case 8: launch_decode_t<BF16, D, 8>(a, st); break;
+    case 1: launch_partitions_t<BF16, D, 1>(a, st); break;
+    case 2: launch_partitions_t<BF16, D, 2>(a, st); break;
+    case 4: launch_partitions_t<BF16, D, 4>(a, st); break;
+    case 8: launch_partitions_t<BF16, D, 8>(a, st); break;
     default: return (int)hipErrorInvalidValue;
   }
   return (int)hipGetLastError();
 }
 
+template <bool BF16, int D>
+void launch_merge_t(const DecodeArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL((lse_merge_kernel<BF16, D, true>), dim3(a.num_seqs * a.num_q_heads), dim3(kWave),
+                     0, st, a.out, a.part_m, a.part_l, a.part_o, a.ctx, a.num_q_heads, a.max_parts,
+                     min(a.max_blocks * kBlockTokens, a.max_parts * kPartTokens));
+}
+
 }  // namespace
 
-int launch_decode(const DecodeArgs& a, void* stream) {
+int launch_decode_partitions(const DecodeArgs& a, void* stream) {
   hipStream_t st = (hipStream_t)stream;
   if (a.bf16) {
-    return a.head_dim == 64 ? launch_decode_g<true, 64>(a, st) : launch_decode_g<true, 128>(a, st);
+    return a.head_dim == 64 ? launch_partitions_g<true, 64>(a, st) : launch_partitions_g<true, 128>(a, st);
   }
-  return a.head_dim == 64 ? launch_decode_g<false, 64>(a, st) : launch_decode_g<false, 128>(a, st);
+  return a.head_dim == 64 ? launch_partitions_g<false, 64>(a, st) : launch_partitions_g<false, 128>(a, st);
+}
+
+int launch_decode_merge(const DecodeArgs& a, void* stream) {
+  if (a.max_parts <= 1) return 0;  // every sequence fits one partition: nothing to merge
+  hipStream_t st = (hipStream_t)stream;
+  if (a.bf16) {
+    if (a.head_dim == 64) launch_merge_t<true, 64>(a, st); else launch_merge_t<true, 128>(a, st);
+  } else {
+    if (a.head_dim == 64) launch_merge_t<false, 64>(a, st); else launch_merge_t<false, 128>(a, st);
+  }
+  return (int)hipGetLastError();
 }
 
 int launch_lse_merge(void* out, const float* part_m, const float* part_l, const float* part_o,

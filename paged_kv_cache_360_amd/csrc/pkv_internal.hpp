@@ -42,8 +42,11 @@ struct DecodeArgs {
   float* part_o;         // [S*Hq, max_parts, D]
 };
 
-// Split-context decode partitions, then (max_parts > 1) the log-sum-exp merge.
-int launch_decode(const DecodeArgs& a, void* stream);
+// Split-context decode partitions: writes the output of single-partition
+// sequences and the partials of the others.
+int launch_decode_partitions(const DecodeArgs& a, void* stream);
+// Log-sum-exp merge of the partials of multi-partition sequences.
+int launch_decode_merge(const DecodeArgs& a, void* stream);
 
 int launch_lse_merge(void* out, const float* part_m, const float* part_l, const float* part_o,
                      const int32_t* num_parts, int32_t rows, int32_t max_parts, int32_t head_dim,

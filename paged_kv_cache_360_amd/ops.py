@@ -61,9 +61,8 @@ def decode_workspace(num_seqs, num_q_heads, head_dim, max_context_len, device="c
     return torch.empty(n, dtype=torch.uint8, device=device) if n else None
 
 
-def pkv_attention_decode(out, q, key_cache, value_cache, block_tables, context_lens, scale,
-                         max_context_len, workspace=None, stream=None):
-    """Paged decode attention for one new token per sequence; writes ``out`` [S, Hq, D]."""
+def _decode_call(cname, out, q, key_cache, value_cache, block_tables, context_lens, scale,
+                 max_context_len, workspace, stream):
     s, hq, d = q.shape
     nb, bs, hkv, dk = key_cache.shape
     if out.shape != q.shape or dk != d or value_cache.shape != key_cache.shape:
@@ -77,12 +76,33 @@ def pkv_attention_decode(out, q, key_cache, value_cache, block_tables, context_l
         workspace = decode_workspace(s, hq, d, max_context_len, q.device)
     ws_ptr = 0 if workspace is None else _dev(workspace, "workspace")
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    check("pkv_attention_decode", lib().pkv_attention_decode(
+    check(cname, getattr(lib(), cname)(
         _dev(out, "out"), _dev(q, "q"), _dev(key_cache, "key_cache"), _dev(value_cache, "value_cache"),
         _dev(block_tables, "block_tables", torch.int32), _dev(context_lens, "context_lens", torch.int32),
         float(scale), bs, hq, hkv, d, s, mb, nb, int(max_context_len), _dt(q), ws_ptr, ws_bytes,
         _stream(stream)))
     return out
+
+
+def pkv_attention_decode(out, q, key_cache, value_cache, block_tables, context_lens, scale,
+                         max_context_len, workspace=None, stream=None):
+    """Paged decode attention for one new token per sequence; writes ``out`` [S, Hq, D]."""
+    return _decode_call("pkv_attention_decode", out, q, key_cache, value_cache, block_tables,
+                        context_lens, scale, max_context_len, workspace, stream)
+
+
+def pkv_attention_decode_partitions(out, q, key_cache, value_cache, block_tables, context_lens,
+                                    scale, max_context_len, workspace=None, stream=None):
+    """First launch of ``pkv_attention_decode`` alone (partition kernel)."""
+    return _decode_call("pkv_attention_decode_partitions", out, q, key_cache, value_cache,
+                        block_tables, context_lens, scale, max_context_len, workspace, stream)
+
+
+def pkv_attention_decode_merge(out, q, key_cache, value_cache, block_tables, context_lens, scale,
+                               max_context_len, workspace=None, stream=None):
+    """Second launch of ``pkv_attention_decode`` alone (log-sum-exp merge)."""
+    return _decode_call("pkv_attention_decode_merge", out, q, key_cache, value_cache, block_tables,
+                        context_lens, scale, max_context_len, workspace, stream)
 
 
 def pkv_lse_merge(out, part_m, part_l, part_o, num_parts, stream=None):

@@ -14,6 +14,7 @@ from .gen import (  # noqa: F401
     SPECS,
     f32_to_bf16_bits,
     normal_values,
+    normal_values_parallel,
     draw_context_lens,
     pool_blocks_for,
     random_block_tables,
