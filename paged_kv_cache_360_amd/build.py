@@ -32,7 +32,7 @@ HIP_FLAGS = [
 HOST_FLAGS = ["-O2", "-fPIC", "-std=c++17", "-Wall", "-D__HIP_PLATFORM_AMD__",
               f"-I{ROCM}/include"]
 
-HIP_SOURCES = ["kernels/cache_ops.hip", "kernels/decode.hip"]
+HIP_SOURCES = ["kernels/cache_ops.hip", "kernels/decode.hip", "kernels/decode_mfma.hip"]
 HOST_SOURCES = ["api.cpp", "allocator.cpp"]
 
 

@@ -1,4 +1,7 @@
-// Split-context paged decode attention and the log-sum-exp merge, for gfx950.
+// fp32 split-context paged decode attention on the vector ALUs, and the
+// log-sum-exp merge of partition results (both dtypes), for gfx950.  The bf16
+// partition kernel runs on the matrix cores (decode_mfma.hip); fp32 stays here
+// because fp32 data carries half the flops per byte and the vector ALUs keep up.
 //
 // Attention over K/V reached block by block through a block table, with each
 // block's contribution computed separately and accumulated ("vLLM and
@@ -16,9 +19,9 @@
 // head_dim elements, rows num_kv_heads*head_dim apart): a token row is split
 // over LPT lanes that each load 16 contiguous bytes (dwordx4), so one wave-wide
 // load covers TPL = 64 / LPT whole rows and NL = 16 / TPL loads cover the block.
-// For bf16, head_dim 128: 16 lanes x 16 B = one 256-B row, 4 rows per load, 4
-// loads per block for K and 4 for V.  The q.k dot product is a per-lane partial
-// over 8 dims followed by a butterfly sum across the row's 16 lanes.
+// For head_dim 128: 32 lanes x 16 B = one 512-B row, 2 rows per load, 8 loads per
+// block for K and 8 for V.  The q.k dot product is a per-lane partial over 4
+// dims followed by a butterfly sum across the row's lanes.
 //
 // Online softmax in base 2: q is pre-multiplied by scale*log2(e) so scores are
 // log2-domain and every exponential is one v_exp_f32.  The running max m is
@@ -36,44 +39,15 @@
 #include <hip/hip_runtime.h>
 
 #include "../pkv_internal.hpp"
-#include "device_common.hpp"
+#include "decode_common.hpp"
 
 namespace pkv {
 
 namespace {
 
-constexpr int kDecodeThreads = 256;
-constexpr int kDecodeWaves = kDecodeThreads / kWave;
-
-struct DecodeParams {
-  void* out;
-  const void* q;
-  const char* kc;
-  const char* vc;
-  const int32_t* tables;
-  const int32_t* ctx;
-  float scale_log2;
-  int32_t Hkv;
-  int32_t MB;
-  int32_t NB;
-  int32_t max_parts;
-  float* part_m;
-  float* part_l;
-  float* part_o;
-};
-
-template <bool BF16>
-__device__ __forceinline__ void store_out(void* out, int64_t idx, float v) {
-  if constexpr (BF16) {
-    reinterpret_cast<uint16_t*>(out)[idx] = f32_to_bf16(v);
-  } else {
-    reinterpret_cast<float*>(out)[idx] = v;
-  }
-}
-
-template <bool BF16, int D, int G>
+template <int D, int G>
 __global__ __launch_bounds__(kDecodeThreads) void decode_partition_kernel(DecodeParams p) {
-  constexpr int ES = BF16 ? 2 : 4;                 // bytes per element
+  constexpr int ES = 4;                            // bytes per element (fp32)
   constexpr int EPL = 16 / ES;                     // elements per lane per load
   constexpr int LPT = D * ES / 16;                 // lanes per token row
   constexpr int TPL = kWave / LPT;                 // token rows per wave-wide load
@@ -87,14 +61,13 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_partition_kernel(Decode
   const int s = blockIdx.z;
   const int Hq = p.Hkv * G;
 
-  int ctx = p.ctx[s];
-  ctx = max(0, min(ctx, min(p.MB * kBlockTokens, p.max_parts * kPartTokens)));
+  const int ctx = clamped_ctx(p, s);
   const int nparts = (ctx + kPartTokens - 1) / kPartTokens;
   if (part >= max(nparts, 1)) return;
   const int64_t row0 = (int64_t)s * Hq + (int64_t)g * G;  // first q head of this group
 
   if (ctx == 0) {  // empty context: zero output
-    for (int i = threadIdx.x; i < G * D; i += kDecodeThreads) store_out<BF16>(p.out, row0 * D + i, 0.f);
+    for (int i = threadIdx.x; i < G * D; i += kDecodeThreads) store_out<false>(p.out, row0 * D + i, 0.f);
     return;
   }
 
@@ -108,7 +81,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_partition_kernel(Decode
 #pragma unroll
   for (int j = 0; j < G; ++j) {
     const uint4 r = load16(reinterpret_cast<const char*>(p.q) + ((row0 + j) * D + dim0) * ES);
-    widen16<BF16>(r, qv[j]);
+    widen16<false>(r, qv[j]);
 #pragma unroll
     for (int e = 0; e < EPL; ++e) qv[j][e] *= p.scale_log2;
   }
@@ -146,7 +119,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_partition_kernel(Decode
 #pragma unroll
     for (int i = 0; i < NL; ++i) {
       float kf[EPL];
-      widen16<BF16>(kr[i], kf);
+      widen16<false>(kr[i], kf);
 #pragma unroll
       for (int j = 0; j < G; ++j) {
         float d = 0.f;
@@ -187,7 +160,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_partition_kernel(Decode
 #pragma unroll
     for (int i = 0; i < NL; ++i) {
       float vf[EPL];
-      widen16<BF16>(vr[i], vf);
+      widen16<false>(vr[i], vf);
       if (partial && i * TPL + tl >= valid) {
 #pragma unroll
         for (int e = 0; e < EPL; ++e) vf[e] = 0.f;
@@ -260,7 +233,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_partition_kernel(Decode
     }
     const float r = L > 0.f ? O / L : 0.f;
     if (nparts == 1) {
-      store_out<BF16>(p.out, (row0 + j) * D + d, r);
+      store_out<false>(p.out, (row0 + j) * D + d, r);
     } else {
       const int64_t pr = (row0 + j) * p.max_parts + part;
       p.part_o[pr * D + d] = r;
@@ -318,8 +291,7 @@ __global__ __launch_bounds__(kWave) void lse_merge_kernel(
   }
 }
 
-template <bool BF16, int D, int G>
-void launch_partitions_t(const DecodeArgs& a, hipStream_t st) {
+DecodeParams make_params(const DecodeArgs& a) {
   DecodeParams p;
   p.out = a.out;
   p.q = a.q;
@@ -335,17 +307,22 @@ void launch_partitions_t(const DecodeArgs& a, hipStream_t st) {
   p.part_m = a.part_m;
   p.part_l = a.part_l;
   p.part_o = a.part_o;
-  hipLaunchKernelGGL((decode_partition_kernel<BF16, D, G>),
+  return p;
+}
+
+template <int D, int G>
+void launch_partitions_t(const DecodeParams& p, const DecodeArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL((decode_partition_kernel<D, G>),
                      dim3(a.num_kv_heads, a.max_parts, a.num_seqs), dim3(kDecodeThreads), 0, st, p);
 }
 
-template <bool BF16, int D>
-int launch_partitions_g(const DecodeArgs& a, hipStream_t st) {
+template <int D>
+int launch_partitions_g(const DecodeParams& p, const DecodeArgs& a, hipStream_t st) {
   switch (a.num_q_heads / a.num_kv_heads) {
-    case 1: launch_partitions_t<BF16, D, 1>(a, st); break;
-    case 2: launch_partitions_t<BF16, D, 2>(a, st); break;
-    case 4: launch_partitions_t<BF16, D, 4>(a, st); break;
-    case 8: launch_partitions_t<BF16, D, 8>(a, st); break;
+    case 1: launch_partitions_t<D, 1>(p, a, st); break;
+    case 2: launch_partitions_t<D, 2>(p, a, st); break;
+    case 4: launch_partitions_t<D, 4>(p, a, st); break;
+    case 8: launch_partitions_t<D, 8>(p, a, st); break;
     default: return (int)hipErrorInvalidValue;
   }
   return (int)hipGetLastError();
@@ -361,11 +338,10 @@ void launch_merge_t(const DecodeArgs& a, hipStream_t st) {
 }  // namespace
 
 int launch_decode_partitions(const DecodeArgs& a, void* stream) {
+  const DecodeParams p = make_params(a);
+  if (a.bf16) return launch_decode_partitions_bf16(p, a, stream);  // matrix cores
   hipStream_t st = (hipStream_t)stream;
-  if (a.bf16) {
-    return a.head_dim == 64 ? launch_partitions_g<true, 64>(a, st) : launch_partitions_g<true, 128>(a, st);
-  }
-  return a.head_dim == 64 ? launch_partitions_g<false, 64>(a, st) : launch_partitions_g<false, 128>(a, st);
+  return a.head_dim == 64 ? launch_partitions_g<64>(p, a, st) : launch_partitions_g<128>(p, a, st);
 }
 
 int launch_decode_merge(const DecodeArgs& a, void* stream) {

@@ -45,6 +45,25 @@ __device__ __forceinline__ uint4 load16(const void* p) {
   return *reinterpret_cast<const uint4*>(p);
 }
 
+// Raw buffer resources (gfx9 descriptor, stride 0): loads at byte offsets at or
+// past the resource's range return zeros without a memory access.
+constexpr int kRawBufferWord3 = 0x00020000;
+
+__device__ __forceinline__ uint4 buffer_load16(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+
+template <typename T>
+__device__ __forceinline__ T buffer_load_piece(__amdgpu_buffer_rsrc_t r, int voff, int soff);
+template <>
+__device__ __forceinline__ uint4 buffer_load_piece<uint4>(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+  return buffer_load16(r, voff, soff);
+}
+template <>
+__device__ __forceinline__ uint2 buffer_load_piece<uint2>(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+  return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0));
+}
+
 // Butterfly sum / max over lanes that differ only in the bits of [lo_mask, 64).
 template <int FROM, int TO>
 __device__ __forceinline__ float xor_sum(float v) {
