@@ -70,7 +70,7 @@ def log(*a):
 
 
 def copy_probe(torch, pkv):
-    """pkv_copy_blocks over 2 x 512 MiB: reads 1 GiB, writes 1 GiB (both caches)."""
+    """pkv_copy_blocks over 8192 pairs of 32 KiB blocks per cache: reads 512 MiB, writes 512 MiB."""
     nb, hkv, d = 2 * 8192, 8, 128                     # 32 KiB bf16 blocks
     kc = torch.zeros((nb, 16, hkv, d), dtype=torch.bfloat16, device="cuda")
     vc = torch.zeros_like(kc)
