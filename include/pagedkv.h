@@ -103,9 +103,14 @@ int pkv_write(void* key_cache, void* value_cache, const void* k, const void* v,
  *                        (larger values are clamped, never faulted on)
  *   max_context_len      host-known bound on context_lens (no device sync);
  *                        must be <= max_blocks_per_seq * 16
- *   workspace            device, >= pkv_decode_workspace_bytes(...) bytes; may be
- *                        NULL when that size is 0.  Scratch only; contents undefined.
+ *   workspace            device, >= pkv_decode_workspace_bytes(...) bytes, 256-byte
+ *                        aligned.  Scratch only: a work list the call builds on the
+ *                        device from context_lens, and the partition partials.
+ *                        Contents undefined between calls; calls sharing one
+ *                        workspace must be ordered on one stream.
  * Supported: block_size 16; head_dim 64 or 128; G in {1, 2, 4, 8}; num_seqs <= 65535.
+ * bf16 runs on the matrix cores as a persistent kernel fed from that work list;
+ * fp32 runs on the vector ALUs.
  * Errors: PKV_EINVAL, PKV_EUNSUPPORTED, PKV_EWORKSPACE, PKV_ELAUNCH. */
 size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
                                   int32_t max_context_len);
@@ -119,9 +124,9 @@ int pkv_attention_decode(void* out, const void* q, const void* key_cache,
 
 /* The two launches pkv_attention_decode makes, callable one at a time with the
  * same arguments (so each can be timed or overlapped on its own).
- * _partitions: one workgroup per (sequence, KV head, 512-token partition); writes
- * `out` for sequences with a single partition and the partials (max, sum,
- * normalized output) of the others to the workspace.
+ * _partitions: builds the work list, then computes every (sequence, KV head,
+ * 512-token partition); writes `out` for sequences with a single partition and
+ * the partials (max, sum, normalized output) of the others to the workspace.
  * _merge: log-sum-exp merge of those partials into `out` (launches nothing when
  * max_context_len <= PKV_PARTITION_TOKENS).  Run _partitions first on the same
  * stream.  Errors as pkv_attention_decode. */

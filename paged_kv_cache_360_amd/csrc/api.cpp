@@ -25,6 +25,21 @@ inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 
 inline int64_t elem_size(pkv_dtype dt) { return dt == PKV_BF16 ? 2 : 4; }
 inline bool dtype_ok(pkv_dtype dt) { return dt == PKV_F32 || dt == PKV_BF16; }
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+constexpr size_t kSchedBytes = 256;  // decode workspace header
+constexpr size_t kRecBytes = 4 * sizeof(int32_t);  // work-list record: sequence, partition, context, partitions
+
+// Compute units of the current device, queried once per device.
+int32_t device_cus() {
+  static int32_t cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+  if (dev < 64 && cache[dev] > 0) return cache[dev];
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    n = 256;
+  if (dev < 64) cache[dev] = n;
+  return n;
+}
 
 int64_t parts_for(int64_t max_ctx) { return (max_ctx + PKV_PARTITION_TOKENS - 1) / PKV_PARTITION_TOKENS; }
 
@@ -89,11 +104,14 @@ int pkv_write(void* key_cache, void* value_cache, const void* k, const void* v,
 
 size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
                                   int32_t max_context_len) {
-  if (num_seqs <= 0 || num_q_heads <= 0 || head_dim <= 0 || max_context_len <= 0) return 0;
-  const int64_t P = pkv::parts_for(max_context_len);
-  if (P <= 1) return 0;
+  if (num_seqs <= 0 || num_q_heads <= 0 || head_dim <= 0 || max_context_len < 0) return 0;
+  const int64_t P = std::max<int64_t>(1, pkv::parts_for(max_context_len));
   const size_t rows = (size_t)num_seqs * num_q_heads;
-  return pkv::align256(rows * P * sizeof(float)) * 2 + pkv::align256(rows * P * head_dim * sizeof(float));
+  // header (ticket counter, ticket count) + work list, one record per (sequence, partition)
+  size_t n = pkv::kSchedBytes + pkv::align256((size_t)num_seqs * P * pkv::kRecBytes);
+  if (P > 1)  // partials (max, sum, normalized output) of multi-partition sequences
+    n += pkv::align256(rows * P * sizeof(float)) * 2 + pkv::align256(rows * P * head_dim * sizeof(float));
+  return n;
 }
 
 }  // extern "C"
@@ -135,8 +153,8 @@ int prepare_decode(const char* who, pkv::DecodeArgs& a, void* out, const void* q
   const int64_t P = std::max<int64_t>(1, pkv::parts_for(max_context_len));
   if (P > 65535) return bad(PKV_EUNSUPPORTED, "context too long");
   const size_t need = pkv_decode_workspace_bytes(num_seqs, num_q_heads, head_dim, max_context_len);
-  if (need > 0 && (!workspace || workspace_bytes < need || !pkv::aligned16(workspace)))
-    return bad(PKV_EWORKSPACE, "workspace missing or too small");
+  if (!workspace || workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    return bad(PKV_EWORKSPACE, "workspace missing, too small or not 256-byte aligned");
 
   a.out = out;
   a.q = q;
@@ -153,12 +171,16 @@ int prepare_decode(const char* who, pkv::DecodeArgs& a, void* out, const void* q
   a.num_blocks = num_blocks;
   a.max_parts = (int32_t)P;
   a.bf16 = dt == PKV_BF16;
-  if (need > 0) {
+  a.num_cus = pkv::device_cus();
+  char* ws = static_cast<char*>(workspace);
+  a.sched = reinterpret_cast<int32_t*>(ws);
+  a.recs = reinterpret_cast<int32_t*>(ws + pkv::kSchedBytes);
+  if (P > 1) {
     const size_t rows = (size_t)num_seqs * num_q_heads;
-    char* ws = static_cast<char*>(workspace);
-    a.part_m = reinterpret_cast<float*>(ws);
-    a.part_l = reinterpret_cast<float*>(ws + pkv::align256(rows * P * sizeof(float)));
-    a.part_o = reinterpret_cast<float*>(ws + 2 * pkv::align256(rows * P * sizeof(float)));
+    char* parts = ws + pkv::kSchedBytes + pkv::align256((size_t)num_seqs * P * pkv::kRecBytes);
+    a.part_m = reinterpret_cast<float*>(parts);
+    a.part_l = reinterpret_cast<float*>(parts + pkv::align256(rows * P * sizeof(float)));
+    a.part_o = reinterpret_cast<float*>(parts + 2 * pkv::align256(rows * P * sizeof(float)));
   }
   return PKV_OK;
 }

@@ -38,6 +38,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+
 #include "../pkv_internal.hpp"
 #include "decode_common.hpp"
 
@@ -248,12 +250,18 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_partition_kernel(Decode
 // One wave per output row.  FROM_CTX: the row count comes from the sequence's
 // context length (decode path; rows with a single partition were already
 // written by the partition kernel and are skipped); otherwise from num_parts[row].
+// Latency is one round trip per kMergeUnroll partitions: the first group's
+// partial outputs are loaded before the maxima are reduced, and the maxima and
+// sums are read lane-parallel (64 partitions per load).
+constexpr int kMergeUnroll = 8;
+
 template <bool BF16, int D, bool FROM_CTX>
 __global__ __launch_bounds__(kWave) void lse_merge_kernel(
     void* __restrict__ out, const float* __restrict__ pm, const float* __restrict__ pl,
     const float* __restrict__ po, const int32_t* __restrict__ counts, int32_t Hq,
     int32_t max_parts, int32_t ctx_cap) {
   constexpr int PER = D / kWave;
+  constexpr int U = kMergeUnroll;
   const int64_t row = blockIdx.x;
   int n;
   if constexpr (FROM_CTX) {
@@ -267,22 +275,51 @@ __global__ __launch_bounds__(kWave) void lse_merge_kernel(
   const float* rm = pm + row * max_parts;
   const float* rl = pl + row * max_parts;
   const float* ro = po + row * max_parts * D;
-  float M = -INFINITY;
-  for (int i = 0; i < n; ++i) {
-    if (rl[i] > 0.f) M = fmaxf(M, rm[i]);
+
+  float ov[U][PER];  // first group of partial outputs, in flight during the reductions
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+#pragma unroll
+    for (int k = 0; k < PER; ++k) ov[u][k] = u < n ? ro[(int64_t)u * D + lane + k * kWave] : 0.f;
   }
-  float L = 0.f;
+
+  // live partial: l > 0 and a finite max; the rest weigh 0
+  float M = -INFINITY;
+  for (int base = 0; base < n; base += kWave) {
+    const int i = base + lane;
+    if (i < n && rl[i] > 0.f) M = fmaxf(M, rm[i]);
+  }
+  M = xor_max<1, kWave>(M);
   float o[PER];
 #pragma unroll
   for (int k = 0; k < PER; ++k) o[k] = 0.f;
+  float L = 0.f;
   if (M != -INFINITY) {
-    for (int i = 0; i < n; ++i) {
+    // a dead partial is skipped, not weighted by 0: its output may hold NaN
+    auto add = [&](int i, const float (&v)[PER]) {
       const float mi = rm[i], li = rl[i];
-      if (!(li > 0.f) || mi == -INFINITY) continue;
-      const float w = li * exp2_fast(mi - M);
-      L += w;
+      if (li > 0.f && mi != -INFINITY) {
+        const float w = li * exp2_fast(mi - M);
+        L += w;
 #pragma unroll
-      for (int k = 0; k < PER; ++k) o[k] = fmaf(w, ro[(int64_t)i * D + lane + k * kWave], o[k]);
+        for (int k = 0; k < PER; ++k) o[k] = fmaf(w, v[k], o[k]);
+      }
+    };
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (u < n) add(u, ov[u]);
+    }
+    for (int base = U; base < n; base += U) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+#pragma unroll
+        for (int k = 0; k < PER; ++k)
+          ov[u][k] = base + u < n ? ro[(int64_t)(base + u) * D + lane + k * kWave] : 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (base + u < n) add(base + u, ov[u]);
+      }
     }
   }
 #pragma unroll
@@ -300,10 +337,14 @@ DecodeParams make_params(const DecodeArgs& a) {
   p.tables = a.tables;
   p.ctx = a.ctx;
   p.scale_log2 = a.scale_log2;
+  p.num_seqs = a.num_seqs;
   p.Hkv = a.num_kv_heads;
   p.MB = a.max_blocks;
   p.NB = a.num_blocks;
   p.max_parts = a.max_parts;
+  p.ctx_cap = std::min(a.max_blocks * kBlockTokens, a.max_parts * kPartTokens);
+  p.sched = a.sched;
+  p.recs = reinterpret_cast<const int4*>(a.recs);
   p.part_m = a.part_m;
   p.part_l = a.part_l;
   p.part_o = a.part_o;
@@ -332,7 +373,7 @@ template <bool BF16, int D>
 void launch_merge_t(const DecodeArgs& a, hipStream_t st) {
   hipLaunchKernelGGL((lse_merge_kernel<BF16, D, true>), dim3(a.num_seqs * a.num_q_heads), dim3(kWave),
                      0, st, a.out, a.part_m, a.part_l, a.part_o, a.ctx, a.num_q_heads, a.max_parts,
-                     min(a.max_blocks * kBlockTokens, a.max_parts * kPartTokens));
+                     std::min(a.max_blocks * kBlockTokens, a.max_parts * kPartTokens));
 }
 
 }  // namespace

@@ -12,6 +12,7 @@ namespace pkv {
 
 constexpr int kDecodeThreads = 256;                 // 4 wavefronts per workgroup
 constexpr int kDecodeWaves = kDecodeThreads / kWave;
+constexpr int kPlanThreads = 1024;                  // work-list builder: one workgroup
 
 struct DecodeParams {
   void* out;
@@ -21,10 +22,14 @@ struct DecodeParams {
   const int32_t* tables;
   const int32_t* ctx;
   float scale_log2;
+  int32_t num_seqs;
   int32_t Hkv;
   int32_t MB;
   int32_t NB;
   int32_t max_parts;
+  int32_t ctx_cap;       // min(MB * 16, max_parts * 512): larger lengths are clamped
+  int32_t* sched;        // [0] next ticket, [1] tickets of this launch
+  const int4* recs;      // work list: {sequence, partition, context, partitions} records
   float* part_m;
   float* part_l;
   float* part_o;
@@ -42,8 +47,7 @@ __device__ __forceinline__ void store_out(void* out, int64_t idx, float v) {
 // Context length of sequence s, clamped to what the table width and the
 // workspace can hold (a larger value is never faulted on).
 __device__ __forceinline__ int clamped_ctx(const DecodeParams& p, int s) {
-  const int c = p.ctx[s];
-  return max(0, min(c, min(p.MB * kBlockTokens, p.max_parts * kPartTokens)));
+  return max(0, min(p.ctx[s], p.ctx_cap));
 }
 
 }  // namespace pkv

@@ -46,11 +46,16 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+
 #include "../pkv_internal.hpp"
 #include "decode_common.hpp"
 
 #ifndef PKV_MFMA_NBUF
 #define PKV_MFMA_NBUF 2
+#endif
+#ifndef PKV_MFMA_WG_PER_CU
+#define PKV_MFMA_WG_PER_CU 1
 #endif
 #ifndef PKV_MFMA_WAVES
 #define PKV_MFMA_WAVES 3
@@ -69,6 +74,10 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 // sized for (waves per SIMD).
 constexpr int kMfmaPipelineDepth = PKV_MFMA_NBUF;
 constexpr int kMfmaWavesPerSimd = PKV_MFMA_WAVES;
+// Persistent workgroups per compute unit (capped by what fits).  Fewer, deeper
+// pipelined workgroups keep the same bytes in flight and finish each item
+// sooner, which shortens the end-of-run tail of the ticket schedule.
+constexpr int kMfmaWgPerCu = PKV_MFMA_WG_PER_CU;
 
 // One lane's share of a V row load: head_dim / 16 bf16 values.
 template <int D> struct VPiece;
@@ -89,6 +98,78 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
+// Work list of the persistent kernel, built on the device from context_lens
+// (no host round trip).  One record {sequence, partition, clamped context
+// length, partition count} per (sequence, partition).  Every partition but a
+// sequence's last (all of them full, 32 blocks) comes first; then each
+// sequence's last partition, in decreasing block count (a counting sort over
+// the 33 possible counts), so the run ends on the shortest items.  A ticket t
+// names record t / Hkv and KV head t % Hkv: consecutive tickets read the
+// different heads' slices of the same blocks.  Also resets the ticket counter.
+// One workgroup.
+__global__ __launch_bounds__(kPlanThreads) void decode_plan_kernel(
+    const int32_t* __restrict__ ctx, int32_t S, int32_t ctx_cap, int32_t Hkv,
+    int32_t* __restrict__ sched, int4* __restrict__ recs) {
+  constexpr int NB = kPartBlocks + 1;       // buckets: last-partition block count 32 .. 0
+  __shared__ int32_t s_sum[kPlanThreads];
+  __shared__ int32_t s_bucket[NB];
+  const int t = threadIdx.x;
+  const int per = (S + kPlanThreads - 1) / kPlanThreads;
+  const int s0 = min(S, t * per);
+  const int s1 = min(S, s0 + per);
+  auto ctx_of = [&](int s) { return max(0, min(ctx[s], ctx_cap)); };
+  auto nparts_of = [&](int c) { return max(1, (c + kPartTokens - 1) / kPartTokens); };
+  auto last_bucket = [&](int c, int n) {  // 0 for a full last partition, 32 for an empty one
+    return kPartBlocks - ((c + kBlockTokens - 1) / kBlockTokens - (n - 1) * kPartBlocks);
+  };
+  if (t < NB) s_bucket[t] = 0;
+  __syncthreads();
+  int full = 0;
+  for (int s = s0; s < s1; ++s) {
+    const int c = ctx_of(s);
+    const int n = nparts_of(c);
+    full += n - 1;
+    atomicAdd(&s_bucket[last_bucket(c, n)], 1);
+  }
+  s_sum[t] = full;
+  __syncthreads();
+  for (int off = 1; off < kPlanThreads; off <<= 1) {  // inclusive scan (Hillis-Steele)
+    const int v = t >= off ? s_sum[t - off] : 0;
+    __syncthreads();
+    s_sum[t] += v;
+    __syncthreads();
+  }
+  const int num_full = s_sum[kPlanThreads - 1];
+  if (t == 0) {  // bucket start offsets in the tail region
+    int acc = num_full;
+    for (int k = 0; k < NB; ++k) {
+      const int c = s_bucket[k];
+      s_bucket[k] = acc;
+      acc += c;
+    }
+  }
+  __syncthreads();
+  int o = s_sum[t] - full;
+  for (int s = s0; s < s1; ++s) {
+    const int c = ctx_of(s);
+    const int n = nparts_of(c);
+    for (int q = 0; q < n - 1; ++q) recs[o++] = make_int4(s, q, c, n);
+    recs[atomicAdd(&s_bucket[last_bucket(c, n)], 1)] = make_int4(s, n - 1, c, n);
+  }
+  if (t == 0) {
+    sched[0] = 0;                    // next ticket
+    sched[1] = (num_full + S) * Hkv; // tickets in this launch
+  }
+}
+
+// Persistent partition kernel: each workgroup takes tickets from the counter
+// until none are left.  After the last block of an item each wave already holds
+// the next item's record (its ticket was passed through LDS at the previous
+// item's epilogue barrier and its record loaded right after), so it issues
+// that item's first blocks before the barrier and the cross-wave merge of the
+// current item: the merge and the output writes overlap with loads in flight.
+// LDS state is double-buffered by item parity: a wave may start writing item
+// i+1's state while others still read item i's.
 template <int D, int G>
 __global__ __launch_bounds__(kDecodeThreads, kMfmaWavesPerSimd) void decode_partition_mfma_kernel(
     DecodeParams p) {
@@ -100,45 +181,55 @@ __global__ __launch_bounds__(kDecodeThreads, kMfmaWavesPerSimd) void decode_part
   using VT = typename VPiece<D>::T;
   static_assert(G >= 1 && G <= 16, "the q heads of one KV head fill at most 16 MFMA columns");
 
-  const int g = blockIdx.x;
-  const int part = blockIdx.y;
-  const int s = blockIdx.z;
-  const int Hq = p.Hkv * G;
-  const int ctx = clamped_ctx(p, s);
-  const int nparts = (ctx + kPartTokens - 1) / kPartTokens;
-  if (part >= max(nparts, 1)) return;
-  const int64_t row0 = (int64_t)s * Hq + (int64_t)g * G;  // first q head of this group
-
-  if (ctx == 0) {  // empty context: zero output
-    for (int i = threadIdx.x; i < G * D; i += kDecodeThreads) store_out<true>(p.out, row0 * D + i, 0.f);
-    return;
-  }
-
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int h = lane & 15;
   const int j = lane >> 4;
+  const int Hq = p.Hkv * G;
+  const int64_t tok_bytes = (int64_t)p.Hkv * D * 2;
+  const int64_t blk_bytes = tok_bytes * kBlockTokens;
+  // tickets of this launch, bounded by the work-list capacity
+  const int total = min(p.sched[1], p.num_seqs * p.max_parts * p.Hkv);
+
+  // One work item as this wave sees it.
+  struct Item {
+    int s, part, g, ctx, nparts, b_begin, nmine;
+    int64_t row0;       // first q head (row of q / out) of the KV head group
+    int my_id;          // lane k < nmine: id of the wave's k-th block
+    int k_lane, v_lane; // this lane's byte offsets inside a block
+  };
+  // record of ticket tk (a scalar load: tk is wave-uniform)
+  auto load_rec = [&](int tk) { return p.recs[tk / p.Hkv]; };
+  auto make_item = [&](int tk, int4 r, Item& it) {
+    it.g = tk % p.Hkv;
+    it.s = r.x;
+    it.part = r.y;
+    it.ctx = r.z;
+    it.nparts = r.w;
+    const int nblk = (it.ctx + kBlockTokens - 1) / kBlockTokens;
+    it.b_begin = it.part * kPartBlocks;
+    const int in_part = min(kPartBlocks, nblk - it.b_begin);
+    it.nmine = max(0, (in_part - wave + NWAVE - 1) / NWAVE);
+    it.row0 = (int64_t)it.s * Hq + (int64_t)it.g * G;
+    it.k_lane = (int)(h * tok_bytes + (it.g * D + 8 * j) * 2);
+    it.v_lane = (int)(4 * j * tok_bytes + (it.g * D + EPL * h) * 2);
+  };
+  // ids of the wave's blocks b_begin + wave + NWAVE*k, one per lane (a vector load)
+  auto load_ids = [&](Item& it) {
+    const int32_t* trow = p.tables + (int64_t)it.s * p.MB;
+    it.my_id = lane < it.nmine ? trow[it.b_begin + wave + NWAVE * lane] : -1;
+  };
 
   // q as the B operand of the score MFMAs (columns >= G are zero).
   bf16x8 qf[NKC];
-  {
-    const char* qrow = reinterpret_cast<const char*>(p.q) + (row0 + min(h, G - 1)) * D * 2;
+  auto load_q = [&](const Item& it) {
+    const char* qrow = reinterpret_cast<const char*>(p.q) + (it.row0 + min(h, G - 1)) * D * 2;
 #pragma unroll
     for (int c = 0; c < NKC; ++c) {
       const uint4 r = h < G ? load16(qrow + (32 * c + 8 * j) * 2) : make_uint4(0, 0, 0, 0);
       qf[c] = __builtin_bit_cast(bf16x8, r);
     }
-  }
-
-  const int nblk = (ctx + kBlockTokens - 1) / kBlockTokens;
-  const int b_begin = part * kPartBlocks;
-  const int b_end = min(b_begin + kPartBlocks, nblk);
-  const int32_t* trow = p.tables + (int64_t)s * p.MB;
-  const int64_t tok_bytes = (int64_t)p.Hkv * D * 2;
-  const int64_t blk_bytes = tok_bytes * kBlockTokens;
-  // byte offsets of this lane's pieces inside a block (blocks are < 2 GiB)
-  const int k_lane = (int)(h * tok_bytes + (g * D + 8 * j) * 2);
-  const int v_lane = (int)(4 * j * tok_bytes + (g * D + EPL * h) * 2);
+  };
 
   struct Blk {
     uint4 k[NKC];
@@ -146,20 +237,15 @@ __global__ __launch_bounds__(kDecodeThreads, kMfmaWavesPerSimd) void decode_part
     int valid;
   };
 
-  // Block ids of this wave's blocks b_begin + wave + NWAVE*k (k < kPartBlocks /
-  // NWAVE), one per lane, fetched once: the per-block id is then a lane read.
-  const int nmine = max(0, (b_end - b_begin - wave + NWAVE - 1) / NWAVE);
-  const int my_id = lane < nmine ? trow[b_begin + wave + NWAVE * lane] : -1;
-
-  // Loads of the wave's k-th block through buffer resources sized to the block:
-  // k past the wave's share or an id outside the pool gets a zero-sized
-  // resource, so its loads return zeros without touching memory and the
-  // prefetch of later blocks needs no branch.
-  auto issue = [&](int k, Blk& B) {
-    const int pb = k < nmine ? __builtin_amdgcn_readlane(my_id, k) : -1;
+  // Loads of the wave's k-th block of an item through buffer resources sized to
+  // the block: k past the wave's share or an id outside the pool gets a
+  // zero-sized resource, so its loads return zeros without touching memory and
+  // the prefetch of later blocks needs no branch.
+  auto issue = [&](const Item& it, int k, Blk& B) {
+    const int pb = k < it.nmine ? __builtin_amdgcn_readlane(it.my_id, k) : -1;
     const bool ok = (unsigned)pb < (unsigned)p.NB;
-    const int b = b_begin + wave + NWAVE * k;
-    B.valid = ok ? min(kBlockTokens, ctx - b * kBlockTokens) : 0;
+    const int b = it.b_begin + wave + NWAVE * k;
+    B.valid = ok ? min(kBlockTokens, it.ctx - b * kBlockTokens) : 0;
     const int64_t base = (int64_t)(ok ? pb : 0) * blk_bytes;
     const int nrec = ok ? (int)blk_bytes : 0;
     const __amdgpu_buffer_rsrc_t kr =
@@ -167,16 +253,13 @@ __global__ __launch_bounds__(kDecodeThreads, kMfmaWavesPerSimd) void decode_part
     const __amdgpu_buffer_rsrc_t vr =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(p.vc + base), (short)0, nrec, kRawBufferWord3);
 #pragma unroll
-    for (int c = 0; c < NKC; ++c) B.k[c] = buffer_load16(kr, k_lane + 64 * c, 0);
+    for (int c = 0; c < NKC; ++c) B.k[c] = buffer_load16(kr, it.k_lane + 64 * c, 0);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) B.v[i] = buffer_load_piece<VT>(vr, v_lane, i * tok_bytes);
+    for (int i = 0; i < 4; ++i) B.v[i] = buffer_load_piece<VT>(vr, it.v_lane, i * tok_bytes);
   };
 
-  float m = -INFINITY;   // running max of head h (log2 domain), uniform over j
-  float l = 0.f;         // running sum of this lane's tokens' weights
+  float m, l;            // running max of head h (log2 domain, uniform over j); this lane's sum
   f32x4 acc[EPL];
-#pragma unroll
-  for (int e = 0; e < EPL; ++e) acc[e] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   auto compute = [&](Blk& B) {
     f32x4 sc = {0.f, 0.f, 0.f, 0.f};
@@ -226,87 +309,150 @@ __global__ __launch_bounds__(kDecodeThreads, kMfmaWavesPerSimd) void decode_part
     }
   };
 
-  // NBUF-deep software pipeline: blocks k+1 .. k+NBUF-1 are in flight while
-  // block k is computed.  The trip count is rounded up to whole rounds; the
-  // extra blocks have zero-sized resources and are fully masked, so they leave
-  // the running state unchanged.
-  Blk buf[NBUF];
-#pragma unroll
-  for (int u = 0; u < NBUF - 1; ++u) issue(u, buf[u]);
-  const int rounds = (nmine + NBUF - 1) / NBUF;
-  for (int r = 0; r < rounds; ++r) {
-#pragma unroll
-    for (int u = 0; u < NBUF; ++u) {
-      issue(r * NBUF + u + NBUF - 1, buf[(u + NBUF - 1) % NBUF]);
-      compute(buf[u]);
-    }
-  }
+  __shared__ float s_m[2][NWAVE][G];
+  __shared__ float s_l[2][NWAVE][G];
+  __shared__ float s_o[2][NWAVE][G][D];
+  __shared__ int s_ticket[4];  // [0], [1]: by item parity; [2], [3]: the first two
 
-  // Wave totals of head h: l summed over the four lane groups (m is already uniform).
-  l += __shfl_xor(l, 16, kWave);
-  l += __shfl_xor(l, 32, kWave);
-
-  __shared__ float s_m[NWAVE][G];
-  __shared__ float s_l[NWAVE][G];
-  __shared__ float s_o[NWAVE][G][D];
-  if (h < G) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) s_o[wave][h][EPL * (4 * j + i) + e] = acc[e][i];
-    }
-    if (j == 0) {
-      s_m[wave][h] = m;
-      s_l[wave][h] = l;
-    }
+  // Tickets run two items ahead: while item i is computed the wave already
+  // holds item i+1's record and block ids, and thread 0 is fetching ticket i+2.
+  if (threadIdx.x == 0) {
+    s_ticket[2] = atomicAdd(&p.sched[0], 1);
+    s_ticket[3] = atomicAdd(&p.sched[0], 1);
   }
   __syncthreads();
+  const int tk0 = __builtin_amdgcn_readfirstlane(s_ticket[2]);
+  if (tk0 >= total) return;
+  int tk1 = __builtin_amdgcn_readfirstlane(s_ticket[3]);
+  bool have1 = tk1 < total;
 
-  for (int idx = threadIdx.x; idx < G * D; idx += kDecodeThreads) {
-    const int hh = idx / D;
-    const int d = idx % D;
-    float M = -INFINITY;
+  // NBUF-deep software pipeline over an item's blocks: blocks k+1 .. k+NBUF-1
+  // are in flight while block k is computed.  The trip count is rounded up to
+  // whole rounds; the extra blocks have zero-sized resources and are fully
+  // masked, so they leave the running state unchanged.
+  Blk buf[NBUF];
+  Item cur, nxt;
+  make_item(tk0, load_rec(tk0), cur);
+  load_ids(cur);
+  load_q(cur);
 #pragma unroll
-    for (int w = 0; w < NWAVE; ++w) M = fmaxf(M, s_m[w][hh]);
-    float L = 0.f, O = 0.f;
-    if (M != -INFINITY) {
+  for (int u = 0; u < NBUF - 1; ++u) issue(cur, u, buf[u]);
+  int4 rec1 = have1 ? load_rec(tk1) : make_int4(0, 0, 0, 0);
+
+  for (int parity = 0;; parity ^= 1) {
+    if (have1) {
+      make_item(tk1, rec1, nxt);
+      load_ids(nxt);
+    }
+    int tk2 = 0;
+    if (threadIdx.x == 0) tk2 = atomicAdd(&p.sched[0], 1);
+
+    m = -INFINITY;
+    l = 0.f;
 #pragma unroll
-      for (int w = 0; w < NWAVE; ++w) {
-        const float f = exp2_fast(s_m[w][hh] - M);
-        L = fmaf(s_l[w][hh], f, L);
-        O = fmaf(s_o[w][hh][d], f, O);
+    for (int e = 0; e < EPL; ++e) acc[e] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int rounds = (cur.nmine + NBUF - 1) / NBUF;
+    for (int r = 0; r < rounds; ++r) {
+#pragma unroll
+      for (int u = 0; u < NBUF; ++u) {
+        issue(cur, r * NBUF + u + NBUF - 1, buf[(u + NBUF - 1) % NBUF]);
+        compute(buf[u]);
       }
     }
-    const float r = L > 0.f ? O / L : 0.f;
-    if (nparts == 1) {
-      store_out<true>(p.out, (row0 + hh) * D + d, r);
-    } else {
-      const int64_t pr = (row0 + hh) * p.max_parts + part;
-      p.part_o[pr * D + d] = r;
-      if (d == 0) {
-        p.part_m[pr] = M;
-        p.part_l[pr] = L;
+
+    // The next item's q and first blocks go out before this item's merge.
+    const Item done = cur;
+    if (have1) {
+      cur = nxt;
+      load_q(cur);
+#pragma unroll
+      for (int u = 0; u < NBUF - 1; ++u) issue(cur, u, buf[u]);
+    }
+
+    // Wave totals of head h: l summed over the four lane groups (m is uniform).
+    l += __shfl_xor(l, 16, kWave);
+    l += __shfl_xor(l, 32, kWave);
+    if (h < G) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) s_o[parity][wave][h][EPL * (4 * j + i) + e] = acc[e][i];
+      }
+      if (j == 0) {
+        s_m[parity][wave][h] = m;
+        s_l[parity][wave][h] = l;
       }
     }
+    if (threadIdx.x == 0) s_ticket[parity] = tk2;
+    __syncthreads();
+    tk2 = __builtin_amdgcn_readfirstlane(s_ticket[parity]);
+    const bool have2 = have1 && tk2 < total;
+    const int4 rec2 = have2 ? load_rec(tk2) : make_int4(0, 0, 0, 0);
+
+    for (int idx = threadIdx.x; idx < G * D; idx += kDecodeThreads) {
+      const int hh = idx / D;
+      const int d = idx % D;
+      float M = -INFINITY;
+#pragma unroll
+      for (int w = 0; w < NWAVE; ++w) M = fmaxf(M, s_m[parity][w][hh]);
+      float L = 0.f, O = 0.f;
+      if (M != -INFINITY) {
+#pragma unroll
+        for (int w = 0; w < NWAVE; ++w) {
+          const float f = exp2_fast(s_m[parity][w][hh] - M);
+          L = fmaf(s_l[parity][w][hh], f, L);
+          O = fmaf(s_o[parity][w][hh][d], f, O);
+        }
+      }
+      const float r = L > 0.f ? O / L : 0.f;
+      if (done.nparts == 1) {
+        store_out<true>(p.out, (done.row0 + hh) * D + d, r);
+      } else {
+        const int64_t pr = (done.row0 + hh) * p.max_parts + done.part;
+        p.part_o[pr * D + d] = r;
+        if (d == 0) {
+          p.part_m[pr] = M;
+          p.part_l[pr] = L;
+        }
+      }
+    }
+    if (!have1) break;
+    tk1 = tk2;
+    have1 = have2;
+    rec1 = rec2;
   }
 }
 
 template <int D, int G>
-void launch_mfma_t(const DecodeParams& p, const DecodeArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL((decode_partition_mfma_kernel<D, G>),
-                     dim3(a.num_kv_heads, a.max_parts, a.num_seqs), dim3(kDecodeThreads), 0, st, p);
+int launch_mfma_t(const DecodeParams& p, const DecodeArgs& a, hipStream_t st) {
+  static int per_cu = 0;  // resident workgroups per CU for this instantiation (queried once)
+  if (per_cu == 0) {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_partition_mfma_kernel<D, G>,
+                                                     kDecodeThreads, 0) != hipSuccess || n < 1)
+      n = 1;
+    per_cu = n;
+  }
+  const int64_t items = (int64_t)a.num_seqs * a.max_parts * a.num_kv_heads;  // upper bound
+  const int64_t grid = std::min<int64_t>(items, (int64_t)a.num_cus * std::min(per_cu, kMfmaWgPerCu));
+  hipLaunchKernelGGL(decode_plan_kernel, dim3(1), dim3(kPlanThreads), 0, st, a.ctx, a.num_seqs,
+                     p.ctx_cap, a.num_kv_heads, p.sched, reinterpret_cast<int4*>(a.recs));
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return (int)e;  // the work list would be stale: launch nothing more
+  hipLaunchKernelGGL((decode_partition_mfma_kernel<D, G>), dim3((unsigned)grid), dim3(kDecodeThreads),
+                     0, st, p);
+  return (int)hipGetLastError();
 }
 
 template <int D>
 int launch_mfma_g(const DecodeParams& p, const DecodeArgs& a, hipStream_t st) {
   switch (a.num_q_heads / a.num_kv_heads) {
-    case 1: launch_mfma_t<D, 1>(p, a, st); break;
-    case 2: launch_mfma_t<D, 2>(p, a, st); break;
-    case 4: launch_mfma_t<D, 4>(p, a, st); break;
-    case 8: launch_mfma_t<D, 8>(p, a, st); break;
+    case 1: return launch_mfma_t<D, 1>(p, a, st);
+    case 2: return launch_mfma_t<D, 2>(p, a, st);
+    case 4: return launch_mfma_t<D, 4>(p, a, st);
+    case 8: return launch_mfma_t<D, 8>(p, a, st);
     default: return (int)hipErrorInvalidValue;
   }
-  return (int)hipGetLastError();
 }
 
 }  // namespace

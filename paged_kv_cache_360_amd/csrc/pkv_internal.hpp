@@ -37,6 +37,9 @@ struct DecodeArgs {
   int32_t num_blocks;    // pool size (ids outside [0, num_blocks) are not read)
   int32_t max_parts;     // partitions per sequence the workspace holds
   bool bf16;
+  int32_t num_cus;       // compute units of the current device
+  int32_t* sched;        // workspace header: ticket counter and ticket count
+  int32_t* recs;         // workspace: work list, [S * max_parts, 4] int32 records
   float* part_m;         // [S*Hq, max_parts]
   float* part_l;         // [S*Hq, max_parts]
   float* part_o;         // [S*Hq, max_parts, D]

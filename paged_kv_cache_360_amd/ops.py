@@ -56,7 +56,10 @@ def pkv_decode_workspace_bytes(num_seqs, num_q_heads, head_dim, max_context_len)
 
 
 def decode_workspace(num_seqs, num_q_heads, head_dim, max_context_len, device="cuda"):
-    """A device buffer of the size ``pkv_attention_decode`` needs (None if 0 bytes)."""
+    """A device buffer of the size ``pkv_attention_decode`` needs (None if 0 bytes).
+
+    torch's allocator returns blocks aligned to at least 256 bytes, as the call
+    requires."""
     n = pkv_decode_workspace_bytes(num_seqs, num_q_heads, head_dim, max_context_len)
     return torch.empty(n, dtype=torch.uint8, device=device) if n else None
 

@@ -77,11 +77,16 @@ def test_decode_argument_errors(kw, code):
 
 def test_decode_workspace_sizes():
     f = lib().pkv_decode_workspace_bytes
-    assert f(64, 32, 128, 512) == 0                # one partition: no workspace
+    one = f(64, 32, 128, 512)                      # one partition: header + work list only
+    assert 256 + 64 * 4 * 4 <= one < 4096
     n = f(128, 32, 128, 8192)                      # 16 partitions
     rows = 128 * 32 * 16
-    assert n >= rows * (128 + 2) * 4
+    assert n >= rows * (128 + 2) * 4 + 128 * 16 * 4 * 4
     assert f(0, 32, 128, 8192) == 0
+
+
+def test_decode_workspace_alignment_is_checked():
+    assert _decode(ws=FAKE + 16) == PKV_EWORKSPACE
 
 
 def test_write_and_copy_argument_errors():

@@ -254,11 +254,12 @@ def test_gqa_equals_repeated_mha_on_gpu():
 
 
 # ------------------------------------------------------------------ LSE merge
-@pytest.mark.parametrize("dtype,d", [("f32", 128), ("bf16", 128), ("f32", 64)])
-def test_lse_merge_isolated(dtype, d):
-    say(f"lse merge {dtype} d={d}")
-    rng = np.random.default_rng(12)
-    rows, maxp = 40, 9
+@pytest.mark.parametrize("dtype,d,maxp", [("f32", 128, 9), ("bf16", 128, 9), ("f32", 64, 9),
+                                          ("f32", 128, 70), ("bf16", 64, 70)])
+def test_lse_merge_isolated(dtype, d, maxp):
+    say(f"lse merge {dtype} d={d} maxp={maxp}")
+    rng = np.random.default_rng(12 + maxp)
+    rows = 40
     counts = rng.integers(0, maxp + 1, rows).astype(np.int32)
     counts[0], counts[1] = 1, maxp
     pm = np.full((rows, maxp), -np.inf)
