@@ -129,7 +129,8 @@ int pkv_attention_decode(void* out, const void* q, const void* key_cache,
  * the partials (max, sum, normalized output) of the others to the workspace.
  * _merge: log-sum-exp merge of those partials into `out` (launches nothing when
  * max_context_len <= PKV_PARTITION_TOKENS).  Run _partitions first on the same
- * stream.  Errors as pkv_attention_decode. */
+ * stream with the same workspace (the merge reads the work list's per-row key
+ * counts).  Errors as pkv_attention_decode. */
 int pkv_attention_decode_partitions(void* out, const void* q, const void* key_cache,
                                     const void* value_cache, const int32_t* block_tables,
                                     const int32_t* context_lens, float scale, int32_t block_size,
@@ -144,6 +145,41 @@ int pkv_attention_decode_merge(void* out, const void* q, const void* key_cache,
                                int32_t num_seqs, int32_t max_blocks_per_seq, int32_t num_blocks,
                                int32_t max_context_len, pkv_dtype dt, void* workspace,
                                size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Variable-length attention over the paged cache: decode rows and chunked
+ * prefill rows in one call (bf16 only).
+ *
+ * Sequence s owns query rows query_start_loc[s] .. query_start_loc[s+1]-1 of q
+ * and out.  With q_s rows and ctx_s = context_lens[s] keys (the rows' own
+ * tokens included: write them with pkv_write first), row r attends causally to
+ * keys 0 .. ctx_s - q_s + r:
+ *   out[row, h, :] = softmax_j(scale * q[row, h, :] . K_s[j, h / G, :]) . V_s[j, h / G, :]
+ * A long prompt split into chunks and batched with decode steps is the pages'
+ * chunked prefill ("How vLLM Works?", section 04; "vLLM and PagedAttention",
+ * key engineering optimizations); a sequence with one row is a decode step.
+ * One-row sequences run the decode kernels; longer ones run 64/G-row tiles on
+ * the matrix cores.  Both split keys into 512-token partitions merged by
+ * log-sum-exp.  A row that sees no key (q_s > ctx_s) gets zeros.
+ *
+ *   out, q            device [num_tokens, num_q_heads, head_dim] bf16
+ *   query_start_loc   device int32 [num_seqs + 1], non-decreasing, values in
+ *                     [0, num_tokens] (out-of-range values are clamped)
+ *   max_query_len     host bound on rows per sequence (>= 1)
+ *   max_context_len   host bound on context_lens, <= max_blocks_per_seq * 16
+ *   workspace         device, >= pkv_varlen_workspace_bytes(...) bytes, 256-byte aligned
+ * Other arguments as pkv_attention_decode.
+ * Errors: PKV_EINVAL, PKV_EUNSUPPORTED (fp32, shapes), PKV_EWORKSPACE, PKV_ELAUNCH. */
+size_t pkv_varlen_workspace_bytes(int32_t num_seqs, int32_t num_tokens, int32_t num_q_heads,
+                                  int32_t num_kv_heads, int32_t head_dim, int32_t max_query_len,
+                                  int32_t max_context_len);
+int pkv_attention_varlen(void* out, const void* q, const void* key_cache, const void* value_cache,
+                         const int32_t* block_tables, const int32_t* context_lens,
+                         const int32_t* query_start_loc, int32_t num_tokens, int32_t max_query_len,
+                         float scale, int32_t block_size, int32_t num_q_heads, int32_t num_kv_heads,
+                         int32_t head_dim, int32_t num_seqs, int32_t max_blocks_per_seq,
+                         int32_t num_blocks, int32_t max_context_len, pkv_dtype dt, void* workspace,
+                         size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------ */
 /* Log-sum-exp merge of partial softmax results, one output row per input row.

@@ -1,7 +1,7 @@
 """MI355X-native paged KV-cache attention: a thin binding over ``libpagedkv.so``.
 
 The hot path (slot write, copy-on-write block copy, split-context decode
-attention, log-sum-exp merge) runs in hand-written HIP kernels for gfx950 behind
+attention, chunked-prefill attention, log-sum-exp merge) runs in hand-written HIP kernels for gfx950 behind
 the C ABI declared in ``include/pagedkv.h``; the block allocator is C++ in the
 same library.  This package only marshals arguments.  Importing it loads the
 library and raises if it has not been built.
@@ -17,6 +17,9 @@ from .ops import (  # noqa: F401
     pkv_attention_decode_merge,
     pkv_decode_workspace_bytes,
     decode_workspace,
+    pkv_attention_varlen,
+    pkv_varlen_workspace_bytes,
+    varlen_workspace,
     pkv_lse_merge,
     pkv_copy_blocks,
     pkv_check_tables,

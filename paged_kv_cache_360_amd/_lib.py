@@ -40,6 +40,9 @@ SIGNATURES = {
                                                        _i32, _i32, _i32, _i32, ctypes.c_int, _p, _sz, _p]),
     "pkv_attention_decode_merge": (ctypes.c_int, [_p, _p, _p, _p, _p, _p, _f32, _i32, _i32, _i32, _i32,
                                                   _i32, _i32, _i32, _i32, ctypes.c_int, _p, _sz, _p]),
+    "pkv_varlen_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32, _i32]),
+    "pkv_attention_varlen": (ctypes.c_int, [_p, _p, _p, _p, _p, _p, _p, _i32, _i32, _f32, _i32, _i32, _i32,
+                                            _i32, _i32, _i32, _i32, _i32, ctypes.c_int, _p, _sz, _p]),
     "pkv_lse_merge": (ctypes.c_int, [_p, _p, _p, _p, _p, _i32, _i32, _i32, ctypes.c_int, _p]),
     "pkv_copy_blocks": (ctypes.c_int, [_p, _p, _p, _i32, _i32, _i32, _i32, _i32, ctypes.c_int, _p]),
     "pkv_check_tables": (ctypes.c_int, [_p, _p, _i32, _i32, _i32]),

@@ -32,7 +32,8 @@ HIP_FLAGS = [
 HOST_FLAGS = ["-O2", "-fPIC", "-std=c++17", "-Wall", "-D__HIP_PLATFORM_AMD__",
               f"-I{ROCM}/include"]
 
-HIP_SOURCES = ["kernels/cache_ops.hip", "kernels/decode.hip", "kernels/decode_mfma.hip"]
+HIP_SOURCES = ["kernels/cache_ops.hip", "kernels/plan.hip", "kernels/decode.hip", "kernels/decode_mfma.hip",
+               "kernels/prefill_mfma.hip"]
 HOST_SOURCES = ["api.cpp", "allocator.cpp"]
 
 

@@ -25,8 +25,38 @@ inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 
 inline int64_t elem_size(pkv_dtype dt) { return dt == PKV_BF16 ? 2 : 4; }
 inline bool dtype_ok(pkv_dtype dt) { return dt == PKV_F32 || dt == PKV_BF16; }
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
-constexpr size_t kSchedBytes = 256;  // decode workspace header
-constexpr size_t kRecBytes = 4 * sizeof(int32_t);  // work-list record: sequence, partition, context, partitions
+int64_t parts_for(int64_t max_ctx) { return (max_ctx + PKV_PARTITION_TOKENS - 1) / PKV_PARTITION_TOKENS; }
+
+constexpr size_t kSchedBytes = 256;  // decode workspace header: ticket counters and counts
+constexpr size_t kDecRecBytes = 4 * sizeof(int32_t);  // {sequence, partition, context, query row}
+constexpr size_t kPreRecBytes = 8 * sizeof(int32_t);  // two int4 (see plan.hip)
+
+// Workspace of one attention call: header, the two work lists, per-row key
+// counts and (when a row can span several partitions) the partials.
+struct WsLayout {
+  size_t dec, pre, keys, pm, pl, po, total;
+  int64_t P, dec_cap, pre_cap;
+};
+WsLayout workspace_layout(int64_t S, int64_t T, int64_t Hq, int64_t G, int64_t D, int64_t max_qlen,
+                          int64_t max_ctx) {
+  WsLayout w{};
+  w.P = std::max<int64_t>(1, parts_for(max_ctx));
+  w.dec_cap = S * w.P;
+  const int64_t rpi = prefill_rows_per_item((int32_t)G);
+  w.pre_cap = max_qlen > 1 ? ((T + rpi - 1) / rpi + S) * w.P : 0;
+  size_t off = kSchedBytes;
+  w.dec = off; off += align256((size_t)w.dec_cap * kDecRecBytes);
+  w.pre = off; off += align256((size_t)w.pre_cap * kPreRecBytes);
+  w.keys = off; off += align256((size_t)T * sizeof(int32_t));
+  if (w.P > 1) {
+    const size_t rows = (size_t)T * Hq;
+    w.pm = off; off += align256(rows * w.P * sizeof(float));
+    w.pl = off; off += align256(rows * w.P * sizeof(float));
+    w.po = off; off += align256(rows * w.P * D * sizeof(float));
+  }
+  w.total = off;
+  return w;
+}
 
 // Compute units of the current device, queried once per device.
 int32_t device_cus() {
@@ -41,7 +71,6 @@ int32_t device_cus() {
   return n;
 }
 
-int64_t parts_for(int64_t max_ctx) { return (max_ctx + PKV_PARTITION_TOKENS - 1) / PKV_PARTITION_TOKENS; }
 
 int launched(int hip_status, const char* who) {
   if (hip_status == 0) return PKV_OK;
@@ -105,13 +134,19 @@ int pkv_write(void* key_cache, void* value_cache, const void* k, const void* v,
 size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
                                   int32_t max_context_len) {
   if (num_seqs <= 0 || num_q_heads <= 0 || head_dim <= 0 || max_context_len < 0) return 0;
-  const int64_t P = std::max<int64_t>(1, pkv::parts_for(max_context_len));
-  const size_t rows = (size_t)num_seqs * num_q_heads;
-  // header (ticket counter, ticket count) + work list, one record per (sequence, partition)
-  size_t n = pkv::kSchedBytes + pkv::align256((size_t)num_seqs * P * pkv::kRecBytes);
-  if (P > 1)  // partials (max, sum, normalized output) of multi-partition sequences
-    n += pkv::align256(rows * P * sizeof(float)) * 2 + pkv::align256(rows * P * head_dim * sizeof(float));
-  return n;
+  return pkv::workspace_layout(num_seqs, num_seqs, num_q_heads, 1, head_dim, 1, max_context_len).total;
+}
+
+size_t pkv_varlen_workspace_bytes(int32_t num_seqs, int32_t num_tokens, int32_t num_q_heads,
+                                  int32_t num_kv_heads, int32_t head_dim, int32_t max_query_len,
+                                  int32_t max_context_len) {
+  if (num_seqs <= 0 || num_tokens < 0 || num_q_heads <= 0 || num_kv_heads <= 0 ||
+      num_q_heads % num_kv_heads != 0 || head_dim <= 0 || max_query_len < 1 || max_context_len < 0)
+    return 0;
+  const int32_t G = num_q_heads / num_kv_heads;
+  if (G != 1 && G != 2 && G != 4 && G != 8) return 0;
+  return pkv::workspace_layout(num_seqs, num_tokens, num_q_heads, G, head_dim, max_query_len,
+                               max_context_len).total;
 }
 
 }  // extern "C"
@@ -119,12 +154,14 @@ size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t
 namespace {
 
 // Shared validation of the decode arguments; fills `a` on success.
-int prepare_decode(const char* who, pkv::DecodeArgs& a, void* out, const void* q,
-                   const void* key_cache, const void* value_cache, const int32_t* block_tables,
-                   const int32_t* context_lens, float scale, int32_t block_size, int32_t num_q_heads,
-                   int32_t num_kv_heads, int32_t head_dim, int32_t num_seqs, int32_t max_blocks_per_seq,
-                   int32_t num_blocks, int32_t max_context_len, pkv_dtype dt, void* workspace,
-                   size_t workspace_bytes) {
+// qsl == nullptr: decode (query row s is sequence s, num_tokens == num_seqs).
+int prepare_attention(const char* who, pkv::DecodeArgs& a, void* out, const void* q,
+                      const void* key_cache, const void* value_cache, const int32_t* block_tables,
+                      const int32_t* context_lens, const int32_t* qsl, int32_t num_tokens,
+                      int32_t max_query_len, float scale, int32_t block_size, int32_t num_q_heads,
+                      int32_t num_kv_heads, int32_t head_dim, int32_t num_seqs,
+                      int32_t max_blocks_per_seq, int32_t num_blocks, int32_t max_context_len,
+                      pkv_dtype dt, void* workspace, size_t workspace_bytes) {
   char msg[160];
   auto bad = [&](int code, const char* what) {
     std::snprintf(msg, sizeof(msg), "%s: %s", who, what);
@@ -144,7 +181,8 @@ int prepare_decode(const char* who, pkv::DecodeArgs& a, void* out, const void* q
   if ((int64_t)max_context_len > (int64_t)max_blocks_per_seq * PKV_BLOCK_SIZE)
     return bad(PKV_EINVAL, "max_context_len exceeds the table width");
   if (!std::isfinite(scale)) return bad(PKV_EINVAL, "scale must be finite");
-  if (num_seqs == 0) return PKV_OK;
+  if (num_tokens < 0 || max_query_len < 1) return bad(PKV_EINVAL, "bad query sizes");
+  if (num_seqs == 0 || num_tokens == 0) return PKV_OK;
   if (!out || !q || !key_cache || !value_cache || !block_tables || !context_lens)
     return bad(PKV_EINVAL, "null pointer");
   if (!pkv::aligned16(out) || !pkv::aligned16(q) || !pkv::aligned16(key_cache) ||
@@ -152,8 +190,12 @@ int prepare_decode(const char* who, pkv::DecodeArgs& a, void* out, const void* q
     return bad(PKV_EINVAL, "pointers must be 16-byte aligned");
   const int64_t P = std::max<int64_t>(1, pkv::parts_for(max_context_len));
   if (P > 65535) return bad(PKV_EUNSUPPORTED, "context too long");
-  const size_t need = pkv_decode_workspace_bytes(num_seqs, num_q_heads, head_dim, max_context_len);
-  if (!workspace || workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+  const pkv::WsLayout w = pkv::workspace_layout(num_seqs, num_tokens, num_q_heads, G, head_dim,
+                                                max_query_len, max_context_len);
+  if ((int64_t)num_tokens * num_q_heads * w.P > INT32_MAX || w.dec_cap * num_kv_heads > INT32_MAX ||
+      w.pre_cap * num_kv_heads > INT32_MAX)
+    return bad(PKV_EUNSUPPORTED, "batch too large");
+  if (!workspace || workspace_bytes < w.total || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
     return bad(PKV_EWORKSPACE, "workspace missing, too small or not 256-byte aligned");
 
   a.out = out;
@@ -162,8 +204,11 @@ int prepare_decode(const char* who, pkv::DecodeArgs& a, void* out, const void* q
   a.vc = value_cache;
   a.tables = block_tables;
   a.ctx = context_lens;
+  a.qsl = qsl;
   a.scale_log2 = scale * 1.4426950408889634f;  // log2(e)
   a.num_seqs = num_seqs;
+  a.num_tokens = num_tokens;
+  a.max_query_len = max_query_len;
   a.num_q_heads = num_q_heads;
   a.num_kv_heads = num_kv_heads;
   a.head_dim = head_dim;
@@ -174,13 +219,15 @@ int prepare_decode(const char* who, pkv::DecodeArgs& a, void* out, const void* q
   a.num_cus = pkv::device_cus();
   char* ws = static_cast<char*>(workspace);
   a.sched = reinterpret_cast<int32_t*>(ws);
-  a.recs = reinterpret_cast<int32_t*>(ws + pkv::kSchedBytes);
-  if (P > 1) {
-    const size_t rows = (size_t)num_seqs * num_q_heads;
-    char* parts = ws + pkv::kSchedBytes + pkv::align256((size_t)num_seqs * P * pkv::kRecBytes);
-    a.part_m = reinterpret_cast<float*>(parts);
-    a.part_l = reinterpret_cast<float*>(parts + pkv::align256(rows * P * sizeof(float)));
-    a.part_o = reinterpret_cast<float*>(parts + 2 * pkv::align256(rows * P * sizeof(float)));
+  a.dec_recs = reinterpret_cast<int32_t*>(ws + w.dec);
+  a.pre_recs = reinterpret_cast<int32_t*>(ws + w.pre);
+  a.row_keys = reinterpret_cast<int32_t*>(ws + w.keys);
+  a.dec_cap = (int32_t)w.dec_cap;
+  a.pre_cap = (int32_t)w.pre_cap;
+  if (w.P > 1) {
+    a.part_m = reinterpret_cast<float*>(ws + w.pm);
+    a.part_l = reinterpret_cast<float*>(ws + w.pl);
+    a.part_o = reinterpret_cast<float*>(ws + w.po);
   }
   return PKV_OK;
 }
@@ -194,24 +241,26 @@ int prepare_decode(const char* who, pkv::DecodeArgs& a, void* out, const void* q
       int32_t max_blocks_per_seq, int32_t num_blocks, int32_t max_context_len, pkv_dtype dt,   \
       void *workspace, size_t workspace_bytes, void *stream
 #define PKV_DECODE_FWD                                                                          \
-  out, q, key_cache, value_cache, block_tables, context_lens, scale, block_size, num_q_heads,  \
-      num_kv_heads, head_dim, num_seqs, max_blocks_per_seq, num_blocks, max_context_len, dt,   \
-      workspace, workspace_bytes
+  out, q, key_cache, value_cache, block_tables, context_lens, nullptr, num_seqs, 1, scale,     \
+      block_size, num_q_heads, num_kv_heads, head_dim, num_seqs, max_blocks_per_seq, num_blocks, \
+      max_context_len, dt, workspace, workspace_bytes
 
 extern "C" {
 
 int pkv_attention_decode_partitions(PKV_DECODE_ARGS) {
   pkv::DecodeArgs a{};
   const char* who = "pkv_attention_decode_partitions";
-  int rc = prepare_decode(who, a, PKV_DECODE_FWD);
+  int rc = prepare_attention(who, a, PKV_DECODE_FWD);
   if (rc != PKV_OK || num_seqs == 0) return rc;
+  rc = pkv::launched(pkv::launch_plan(a, stream), who);
+  if (rc != PKV_OK) return rc;
   return pkv::launched(pkv::launch_decode_partitions(a, stream), who);
 }
 
 int pkv_attention_decode_merge(PKV_DECODE_ARGS) {
   pkv::DecodeArgs a{};
   const char* who = "pkv_attention_decode_merge";
-  int rc = prepare_decode(who, a, PKV_DECODE_FWD);
+  int rc = prepare_attention(who, a, PKV_DECODE_FWD);
   if (rc != PKV_OK || num_seqs == 0) return rc;
   return pkv::launched(pkv::launch_decode_merge(a, stream), who);
 }
@@ -219,9 +268,37 @@ int pkv_attention_decode_merge(PKV_DECODE_ARGS) {
 int pkv_attention_decode(PKV_DECODE_ARGS) {
   pkv::DecodeArgs a{};
   const char* who = "pkv_attention_decode";
-  int rc = prepare_decode(who, a, PKV_DECODE_FWD);
+  int rc = prepare_attention(who, a, PKV_DECODE_FWD);
   if (rc != PKV_OK || num_seqs == 0) return rc;
+  rc = pkv::launched(pkv::launch_plan(a, stream), who);
+  if (rc != PKV_OK) return rc;
   rc = pkv::launched(pkv::launch_decode_partitions(a, stream), who);
+  if (rc != PKV_OK) return rc;
+  return pkv::launched(pkv::launch_decode_merge(a, stream), who);
+}
+
+int pkv_attention_varlen(void* out, const void* q, const void* key_cache, const void* value_cache,
+                         const int32_t* block_tables, const int32_t* context_lens,
+                         const int32_t* query_start_loc, int32_t num_tokens, int32_t max_query_len,
+                         float scale, int32_t block_size, int32_t num_q_heads, int32_t num_kv_heads,
+                         int32_t head_dim, int32_t num_seqs, int32_t max_blocks_per_seq,
+                         int32_t num_blocks, int32_t max_context_len, pkv_dtype dt, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  pkv::DecodeArgs a{};
+  const char* who = "pkv_attention_varlen";
+  if (dt != PKV_BF16) return fail(PKV_EUNSUPPORTED, "pkv_attention_varlen: bf16 only");
+  if (num_tokens > 0 && num_seqs > 0 && !query_start_loc)
+    return fail(PKV_EINVAL, "pkv_attention_varlen: null query_start_loc");
+  int rc = prepare_attention(who, a, out, q, key_cache, value_cache, block_tables, context_lens,
+                             query_start_loc, num_tokens, max_query_len, scale, block_size, num_q_heads,
+                             num_kv_heads, head_dim, num_seqs, max_blocks_per_seq, num_blocks,
+                             max_context_len, dt, workspace, workspace_bytes);
+  if (rc != PKV_OK || num_seqs == 0 || num_tokens == 0) return rc;
+  rc = pkv::launched(pkv::launch_plan(a, stream), who);
+  if (rc != PKV_OK) return rc;
+  rc = pkv::launched(pkv::launch_decode_partitions(a, stream), who);
+  if (rc != PKV_OK) return rc;
+  rc = pkv::launched(pkv::launch_prefill(a, stream), who);
   if (rc != PKV_OK) return rc;
   return pkv::launched(pkv::launch_decode_merge(a, stream), who);
 }

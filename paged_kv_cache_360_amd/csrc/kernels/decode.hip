@@ -247,26 +247,27 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_partition_kernel(Decode
   }
 }
 
-// One wave per output row.  FROM_CTX: the row count comes from the sequence's
-// context length (decode path; rows with a single partition were already
-// written by the partition kernel and are skipped); otherwise from num_parts[row].
+// One wave per output row (query row x q head).  FROM_KEYS: the partition count
+// comes from the keys the query row sees (counts = the plan's row_keys; rows
+// with a single partition were already written by the partition kernels and
+// are skipped); otherwise from num_parts[row].
 // Latency is one round trip per kMergeUnroll partitions: the first group's
 // partial outputs are loaded before the maxima are reduced, and the maxima and
 // sums are read lane-parallel (64 partitions per load).
 constexpr int kMergeUnroll = 8;
 
-template <bool BF16, int D, bool FROM_CTX>
+template <bool BF16, int D, bool FROM_KEYS>
 __global__ __launch_bounds__(kWave) void lse_merge_kernel(
     void* __restrict__ out, const float* __restrict__ pm, const float* __restrict__ pl,
     const float* __restrict__ po, const int32_t* __restrict__ counts, int32_t Hq,
-    int32_t max_parts, int32_t ctx_cap) {
+    int32_t max_parts) {
   constexpr int PER = D / kWave;
   constexpr int U = kMergeUnroll;
   const int64_t row = blockIdx.x;
   int n;
-  if constexpr (FROM_CTX) {
-    const int ctx = max(0, min(counts[row / Hq], ctx_cap));
-    n = (ctx + kPartTokens - 1) / kPartTokens;
+  if constexpr (FROM_KEYS) {
+    const int keys = max(0, counts[row / Hq]);
+    n = min((keys + kPartTokens - 1) / kPartTokens, max_parts);
     if (n <= 1) return;
   } else {
     n = max(0, min(counts[row], max_parts));
@@ -328,29 +329,6 @@ __global__ __launch_bounds__(kWave) void lse_merge_kernel(
   }
 }
 
-DecodeParams make_params(const DecodeArgs& a) {
-  DecodeParams p;
-  p.out = a.out;
-  p.q = a.q;
-  p.kc = reinterpret_cast<const char*>(a.kc);
-  p.vc = reinterpret_cast<const char*>(a.vc);
-  p.tables = a.tables;
-  p.ctx = a.ctx;
-  p.scale_log2 = a.scale_log2;
-  p.num_seqs = a.num_seqs;
-  p.Hkv = a.num_kv_heads;
-  p.MB = a.max_blocks;
-  p.NB = a.num_blocks;
-  p.max_parts = a.max_parts;
-  p.ctx_cap = std::min(a.max_blocks * kBlockTokens, a.max_parts * kPartTokens);
-  p.sched = a.sched;
-  p.recs = reinterpret_cast<const int4*>(a.recs);
-  p.part_m = a.part_m;
-  p.part_l = a.part_l;
-  p.part_o = a.part_o;
-  return p;
-}
-
 template <int D, int G>
 void launch_partitions_t(const DecodeParams& p, const DecodeArgs& a, hipStream_t st) {
   hipLaunchKernelGGL((decode_partition_kernel<D, G>),
@@ -371,12 +349,40 @@ int launch_partitions_g(const DecodeParams& p, const DecodeArgs& a, hipStream_t 
 
 template <bool BF16, int D>
 void launch_merge_t(const DecodeArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL((lse_merge_kernel<BF16, D, true>), dim3(a.num_seqs * a.num_q_heads), dim3(kWave),
-                     0, st, a.out, a.part_m, a.part_l, a.part_o, a.ctx, a.num_q_heads, a.max_parts,
-                     std::min(a.max_blocks * kBlockTokens, a.max_parts * kPartTokens));
+  hipLaunchKernelGGL((lse_merge_kernel<BF16, D, true>), dim3(a.num_tokens * a.num_q_heads), dim3(kWave),
+                     0, st, a.out, a.part_m, a.part_l, a.part_o, a.row_keys, a.num_q_heads, a.max_parts);
 }
 
 }  // namespace
+
+DecodeParams make_params(const DecodeArgs& a) {
+  DecodeParams p;
+  p.out = a.out;
+  p.q = a.q;
+  p.kc = reinterpret_cast<const char*>(a.kc);
+  p.vc = reinterpret_cast<const char*>(a.vc);
+  p.tables = a.tables;
+  p.ctx = a.ctx;
+  p.qsl = a.qsl;
+  p.scale_log2 = a.scale_log2;
+  p.num_seqs = a.num_seqs;
+  p.num_tokens = a.num_tokens;
+  p.Hkv = a.num_kv_heads;
+  p.MB = a.max_blocks;
+  p.NB = a.num_blocks;
+  p.max_parts = a.max_parts;
+  p.ctx_cap = std::min(a.max_blocks * kBlockTokens, a.max_parts * kPartTokens);
+  p.sched = a.sched;
+  p.dec_recs = reinterpret_cast<const int4*>(a.dec_recs);
+  p.pre_recs = reinterpret_cast<const int4*>(a.pre_recs);
+  p.row_keys = a.row_keys;
+  p.dec_cap = a.dec_cap;
+  p.pre_cap = a.pre_cap;
+  p.part_m = a.part_m;
+  p.part_l = a.part_l;
+  p.part_o = a.part_o;
+  return p;
+}
 
 int launch_decode_partitions(const DecodeArgs& a, void* stream) {
   const DecodeParams p = make_params(a);
@@ -386,7 +392,7 @@ int launch_decode_partitions(const DecodeArgs& a, void* stream) {
 }
 
 int launch_decode_merge(const DecodeArgs& a, void* stream) {
-  if (a.max_parts <= 1) return 0;  // every sequence fits one partition: nothing to merge
+  if (a.max_parts <= 1) return 0;  // every row fits one partition: nothing to merge
   hipStream_t st = (hipStream_t)stream;
   if (a.bf16) {
     if (a.head_dim == 64) launch_merge_t<true, 64>(a, st); else launch_merge_t<true, 128>(a, st);
@@ -404,17 +410,17 @@ int launch_lse_merge(void* out, const float* part_m, const float* part_l, const 
   if (bf16) {
     if (head_dim == 64)
       hipLaunchKernelGGL((lse_merge_kernel<true, 64, false>), grid, block, 0, st, out, part_m,
-                         part_l, part_o, num_parts, 1, max_parts, 0);
+                         part_l, part_o, num_parts, 1, max_parts);
     else
       hipLaunchKernelGGL((lse_merge_kernel<true, 128, false>), grid, block, 0, st, out, part_m,
-                         part_l, part_o, num_parts, 1, max_parts, 0);
+                         part_l, part_o, num_parts, 1, max_parts);
   } else {
     if (head_dim == 64)
       hipLaunchKernelGGL((lse_merge_kernel<false, 64, false>), grid, block, 0, st, out, part_m,
-                         part_l, part_o, num_parts, 1, max_parts, 0);
+                         part_l, part_o, num_parts, 1, max_parts);
     else
       hipLaunchKernelGGL((lse_merge_kernel<false, 128, false>), grid, block, 0, st, out, part_m,
-                         part_l, part_o, num_parts, 1, max_parts, 0);
+                         part_l, part_o, num_parts, 1, max_parts);
   }
   return (int)hipGetLastError();
 }

@@ -21,15 +21,20 @@ struct DecodeParams {
   const char* vc;
   const int32_t* tables;
   const int32_t* ctx;
+  const int32_t* qsl;    // [S+1] or null (row s is sequence s)
   float scale_log2;
   int32_t num_seqs;
+  int32_t num_tokens;    // query rows T
   int32_t Hkv;
   int32_t MB;
   int32_t NB;
   int32_t max_parts;
   int32_t ctx_cap;       // min(MB * 16, max_parts * 512): larger lengths are clamped
-  int32_t* sched;        // [0] next ticket, [1] tickets of this launch
-  const int4* recs;      // work list: {sequence, partition, context, partitions} records
+  int32_t* sched;        // [0] next decode ticket, [1] decode tickets; [2], [3] prefill
+  const int4* dec_recs;  // decode records {sequence, partition, context, query row}
+  const int4* pre_recs;  // prefill records, two int4 each (see plan.hip)
+  const int32_t* row_keys;
+  int32_t dec_cap, pre_cap;
   float* part_m;
   float* part_l;
   float* part_o;
@@ -54,6 +59,7 @@ __device__ __forceinline__ int clamped_ctx(const DecodeParams& p, int s) {
 
 namespace pkv {
 struct DecodeArgs;
+DecodeParams make_params(const DecodeArgs& a);
 // bf16 partition kernel on the matrix cores (decode_mfma.hip).
 int launch_decode_partitions_bf16(const DecodeParams& p, const DecodeArgs& a, void* stream);
 }  // namespace pkv

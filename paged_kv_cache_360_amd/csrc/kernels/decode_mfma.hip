@@ -98,70 +98,6 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
-// Work list of the persistent kernel, built on the device from context_lens
-// (no host round trip).  One record {sequence, partition, clamped context
-// length, partition count} per (sequence, partition).  Every partition but a
-// sequence's last (all of them full, 32 blocks) comes first; then each
-// sequence's last partition, in decreasing block count (a counting sort over
-// the 33 possible counts), so the run ends on the shortest items.  A ticket t
-// names record t / Hkv and KV head t % Hkv: consecutive tickets read the
-// different heads' slices of the same blocks.  Also resets the ticket counter.
-// One workgroup.
-__global__ __launch_bounds__(kPlanThreads) void decode_plan_kernel(
-    const int32_t* __restrict__ ctx, int32_t S, int32_t ctx_cap, int32_t Hkv,
-    int32_t* __restrict__ sched, int4* __restrict__ recs) {
-  constexpr int NB = kPartBlocks + 1;       // buckets: last-partition block count 32 .. 0
-  __shared__ int32_t s_sum[kPlanThreads];
-  __shared__ int32_t s_bucket[NB];
-  const int t = threadIdx.x;
-  const int per = (S + kPlanThreads - 1) / kPlanThreads;
-  const int s0 = min(S, t * per);
-  const int s1 = min(S, s0 + per);
-  auto ctx_of = [&](int s) { return max(0, min(ctx[s], ctx_cap)); };
-  auto nparts_of = [&](int c) { return max(1, (c + kPartTokens - 1) / kPartTokens); };
-  auto last_bucket = [&](int c, int n) {  // 0 for a full last partition, 32 for an empty one
-    return kPartBlocks - ((c + kBlockTokens - 1) / kBlockTokens - (n - 1) * kPartBlocks);
-  };
-  if (t < NB) s_bucket[t] = 0;
-  __syncthreads();
-  int full = 0;
-  for (int s = s0; s < s1; ++s) {
-    const int c = ctx_of(s);
-    const int n = nparts_of(c);
-    full += n - 1;
-    atomicAdd(&s_bucket[last_bucket(c, n)], 1);
-  }
-  s_sum[t] = full;
-  __syncthreads();
-  for (int off = 1; off < kPlanThreads; off <<= 1) {  // inclusive scan (Hillis-Steele)
-    const int v = t >= off ? s_sum[t - off] : 0;
-    __syncthreads();
-    s_sum[t] += v;
-    __syncthreads();
-  }
-  const int num_full = s_sum[kPlanThreads - 1];
-  if (t == 0) {  // bucket start offsets in the tail region
-    int acc = num_full;
-    for (int k = 0; k < NB; ++k) {
-      const int c = s_bucket[k];
-      s_bucket[k] = acc;
-      acc += c;
-    }
-  }
-  __syncthreads();
-  int o = s_sum[t] - full;
-  for (int s = s0; s < s1; ++s) {
-    const int c = ctx_of(s);
-    const int n = nparts_of(c);
-    for (int q = 0; q < n - 1; ++q) recs[o++] = make_int4(s, q, c, n);
-    recs[atomicAdd(&s_bucket[last_bucket(c, n)], 1)] = make_int4(s, n - 1, c, n);
-  }
-  if (t == 0) {
-    sched[0] = 0;                    // next ticket
-    sched[1] = (num_full + S) * Hkv; // tickets in this launch
-  }
-}
-
 // Persistent partition kernel: each workgroup takes tickets from the counter
 // until none are left.  After the last block of an item each wave already holds
 // the next item's record (its ticket was passed through LDS at the previous
@@ -189,28 +125,28 @@ __global__ __launch_bounds__(kDecodeThreads, kMfmaWavesPerSimd) void decode_part
   const int64_t tok_bytes = (int64_t)p.Hkv * D * 2;
   const int64_t blk_bytes = tok_bytes * kBlockTokens;
   // tickets of this launch, bounded by the work-list capacity
-  const int total = min(p.sched[1], p.num_seqs * p.max_parts * p.Hkv);
+  const int total = min(p.sched[1], p.dec_cap * p.Hkv);
 
   // One work item as this wave sees it.
   struct Item {
-    int s, part, g, ctx, nparts, b_begin, nmine;
+    int s, part, g, ctx, nparts, b_begin, nmine;  // nparts: of the query row
     int64_t row0;       // first q head (row of q / out) of the KV head group
     int my_id;          // lane k < nmine: id of the wave's k-th block
     int k_lane, v_lane; // this lane's byte offsets inside a block
   };
   // record of ticket tk (a scalar load: tk is wave-uniform)
-  auto load_rec = [&](int tk) { return p.recs[tk / p.Hkv]; };
+  auto load_rec = [&](int tk) { return p.dec_recs[tk / p.Hkv]; };
   auto make_item = [&](int tk, int4 r, Item& it) {
     it.g = tk % p.Hkv;
     it.s = r.x;
     it.part = r.y;
     it.ctx = r.z;
-    it.nparts = r.w;
+    it.nparts = max(1, (it.ctx + kPartTokens - 1) / kPartTokens);
     const int nblk = (it.ctx + kBlockTokens - 1) / kBlockTokens;
     it.b_begin = it.part * kPartBlocks;
     const int in_part = min(kPartBlocks, nblk - it.b_begin);
     it.nmine = max(0, (in_part - wave + NWAVE - 1) / NWAVE);
-    it.row0 = (int64_t)it.s * Hq + (int64_t)it.g * G;
+    it.row0 = (int64_t)r.w * Hq + (int64_t)it.g * G;  // r.w: the sequence's query row
     it.k_lane = (int)(h * tok_bytes + (it.g * D + 8 * j) * 2);
     it.v_lane = (int)(4 * j * tok_bytes + (it.g * D + EPL * h) * 2);
   };
@@ -433,12 +369,8 @@ int launch_mfma_t(const DecodeParams& p, const DecodeArgs& a, hipStream_t st) {
       n = 1;
     per_cu = n;
   }
-  const int64_t items = (int64_t)a.num_seqs * a.max_parts * a.num_kv_heads;  // upper bound
+  const int64_t items = (int64_t)a.dec_cap * a.num_kv_heads;  // upper bound
   const int64_t grid = std::min<int64_t>(items, (int64_t)a.num_cus * std::min(per_cu, kMfmaWgPerCu));
-  hipLaunchKernelGGL(decode_plan_kernel, dim3(1), dim3(kPlanThreads), 0, st, a.ctx, a.num_seqs,
-                     p.ctx_cap, a.num_kv_heads, p.sched, reinterpret_cast<int4*>(a.recs));
-  const hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return (int)e;  // the work list would be stale: launch nothing more
   hipLaunchKernelGGL((decode_partition_mfma_kernel<D, G>), dim3((unsigned)grid), dim3(kDecodeThreads),
                      0, st, p);
   return (int)hipGetLastError();

@@ -1,0 +1,149 @@
+// Work-list plan for the persistent attention kernels, built on the device from
+// context_lens (and query_start_loc for variable-length batches), so the host
+// never waits for the device.
+//
+// A sequence with one query row is a decode sequence; one with more rows is a
+// chunked-prefill sequence whose rows sit at the end of its context: with q
+// rows and ctx keys (the chunk's own tokens included), row r sees keys
+// 0 .. ctx - q + r ("How vLLM Works?", section 04 on chunked prefill; the usual
+// causal mask).  Keys are split into 512-token partitions merged by
+// log-sum-exp.
+//
+// Outputs (all in the caller's workspace):
+//  * decode records {sequence, partition, context, query row}: every decode
+//    partition but a sequence's last (all full, 32 blocks) first, then each
+//    sequence's last partition in decreasing block count (a counting sort over
+//    the 33 possible counts), so the persistent run ends on its shortest items;
+//  * prefill records, two int4 each: {sequence, partition, context, first query
+//    row} and {rows, ctx - q + r0 + 1, 0, 0} (row i of the group sees max(0, that
+//    + i) keys; negative when the chunk is longer than the context); one per (group of
+//    rows_per_item consecutive rows, partition the group's last row reaches);
+//  * row_keys[T]: the keys each query row sees (its partition count for the
+//    merge);
+//  * sched: both ticket counters reset, and each list's ticket count (records
+//    times KV heads: ticket t is record t / Hkv, KV head t % Hkv).
+// One workgroup; sequence chunks are scanned in LDS.
+
+#include <hip/hip_runtime.h>
+
+#include "../pkv_internal.hpp"
+#include "decode_common.hpp"
+
+namespace pkv {
+
+namespace {
+
+__global__ __launch_bounds__(kPlanThreads) void plan_kernel(
+    const int32_t* __restrict__ ctx, const int32_t* __restrict__ qsl, int32_t S, int32_t T,
+    int32_t ctx_cap, int32_t Hkv, int32_t rows_per_item, int32_t dec_cap, int32_t pre_cap,
+    int32_t* __restrict__ sched, int4* __restrict__ dec, int4* __restrict__ pre,
+    int32_t* __restrict__ row_keys) {
+  constexpr int NBK = kPartBlocks + 1;  // buckets: last-partition block count 32 .. 0
+  __shared__ int32_t s_full[kPlanThreads];
+  __shared__ int32_t s_pre[kPlanThreads];
+  __shared__ int32_t s_bucket[NBK];
+  const int t = threadIdx.x;
+  const int per = (S + kPlanThreads - 1) / kPlanThreads;
+  const int s0 = min(S, t * per);
+  const int s1 = min(S, s0 + per);
+
+  auto ctx_of = [&](int s) { return max(0, min(ctx[s], ctx_cap)); };
+  auto parts_of = [&](int keys) { return max(1, (keys + kPartTokens - 1) / kPartTokens); };
+  auto first_row = [&](int s) { return qsl ? min(max(qsl[s], 0), T) : s; };
+  auto rows_of = [&](int s) { return qsl ? max(0, min(qsl[s + 1], T) - first_row(s)) : 1; };
+  auto last_bucket = [&](int c, int n) {  // 0 for a full last partition, 32 for an empty one
+    return kPartBlocks - ((c + kBlockTokens - 1) / kBlockTokens - (n - 1) * kPartBlocks);
+  };
+  // prefill: the keys seen by row r of a sequence with q rows and c keys
+  auto row_keys_of = [&](int c, int q, int r) { return max(0, c - q + r + 1); };
+
+  if (t < NBK) s_bucket[t] = 0;
+  for (int r = t; r < T; r += kPlanThreads) row_keys[r] = 0;  // rows no sequence owns see nothing
+  __syncthreads();
+  int full = 0, npre = 0;
+  for (int s = s0; s < s1; ++s) {
+    const int c = ctx_of(s);
+    const int q = rows_of(s);
+    if (q == 1) {
+      const int n = parts_of(c);
+      full += n - 1;
+      atomicAdd(&s_bucket[last_bucket(c, n)], 1);
+    } else if (q > 1) {
+      for (int r0 = 0; r0 < q; r0 += rows_per_item)
+        npre += parts_of(row_keys_of(c, q, min(q, r0 + rows_per_item) - 1));
+    }
+  }
+  s_full[t] = full;
+  s_pre[t] = npre;
+  __syncthreads();
+  for (int off = 1; off < kPlanThreads; off <<= 1) {  // inclusive scans (Hillis-Steele)
+    const int vf = t >= off ? s_full[t - off] : 0;
+    const int vp = t >= off ? s_pre[t - off] : 0;
+    __syncthreads();
+    s_full[t] += vf;
+    s_pre[t] += vp;
+    __syncthreads();
+  }
+  const int num_full = s_full[kPlanThreads - 1];
+  const int num_pre = s_pre[kPlanThreads - 1];
+  if (t == 0) {  // bucket start offsets in the decode tail region
+    int acc = num_full;
+    for (int k = 0; k < NBK; ++k) {
+      const int c = s_bucket[k];
+      s_bucket[k] = acc;
+      acc += c;
+    }
+  }
+  __syncthreads();
+
+  int od = s_full[t] - full;
+  int op = s_pre[t] - npre;
+  for (int s = s0; s < s1; ++s) {
+    const int c = ctx_of(s);
+    const int q = rows_of(s);
+    const int row0 = first_row(s);
+    if (q == 1) {
+      const int n = parts_of(c);
+      for (int k = 0; k < n - 1; ++k)
+        if (od < dec_cap) dec[od++] = make_int4(s, k, c, row0);
+      const int at = atomicAdd(&s_bucket[last_bucket(c, n)], 1);
+      if (at < dec_cap) dec[at] = make_int4(s, n - 1, c, row0);
+      row_keys[row0] = c;
+    } else if (q > 1) {
+      for (int r0 = 0; r0 < q; r0 += rows_per_item) {
+        const int nr = min(q, r0 + rows_per_item) - r0;
+        const int n = parts_of(row_keys_of(c, q, r0 + nr - 1));
+        for (int k = 0; k < n; ++k, ++op) {
+          if (op < pre_cap) {
+            pre[2 * op] = make_int4(s, k, c, row0 + r0);
+            pre[2 * op + 1] = make_int4(nr, c - q + r0 + 1, 0, 0);  // unclamped: row i sees max(0, this + i)
+          }
+        }
+      }
+      for (int r = 0; r < q; ++r) row_keys[row0 + r] = row_keys_of(c, q, r);
+    }
+  }
+  __syncthreads();
+  if (t == 0) {
+    // every bucket cursor has advanced past its records: the last one ends the list
+    const int num_dec_recs = s_bucket[NBK - 1];
+    sched[0] = 0;
+    sched[1] = min(num_dec_recs, dec_cap) * Hkv;
+    sched[2] = 0;
+    sched[3] = min(num_pre, pre_cap) * Hkv;
+  }
+}
+
+}  // namespace
+
+int launch_plan(const DecodeArgs& a, void* stream) {
+  const DecodeParams p = make_params(a);
+  const int32_t G = a.num_q_heads / a.num_kv_heads;
+  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, (hipStream_t)stream, a.ctx, a.qsl,
+                     a.num_seqs, a.num_tokens, p.ctx_cap, a.num_kv_heads, prefill_rows_per_item(G),
+                     a.dec_cap, a.pre_cap, a.sched, reinterpret_cast<int4*>(a.dec_recs),
+                     reinterpret_cast<int4*>(a.pre_recs), a.row_keys);
+  return (int)hipGetLastError();
+}
+
+}  // namespace pkv

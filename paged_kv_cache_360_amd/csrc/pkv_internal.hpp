@@ -25,30 +25,45 @@ int launch_copy_blocks(void* kc, void* vc, const int32_t* pairs, int32_t num_pai
                        int32_t num_blocks, int64_t block_bytes, void* stream);
 
 struct DecodeArgs {
-  void* out;
-  const void* q;
+  void* out;             // [T, Hq, D]
+  const void* q;         // [T, Hq, D]
   const void* kc;
   const void* vc;
   const int32_t* tables;
   const int32_t* ctx;
+  const int32_t* qsl;    // [S+1] first query row of each sequence; null: row s is sequence s
   float scale_log2;      // softmax scale times log2(e)
-  int32_t num_seqs, num_q_heads, num_kv_heads, head_dim;
+  int32_t num_seqs, num_tokens, num_q_heads, num_kv_heads, head_dim;
   int32_t max_blocks;    // table row width
   int32_t num_blocks;    // pool size (ids outside [0, num_blocks) are not read)
-  int32_t max_parts;     // partitions per sequence the workspace holds
+  int32_t max_parts;     // partitions per query row the workspace holds
+  int32_t max_query_len; // host bound on query rows per sequence (1 for decode)
   bool bf16;
   int32_t num_cus;       // compute units of the current device
-  int32_t* sched;        // workspace header: ticket counter and ticket count
-  int32_t* recs;         // workspace: work list, [S * max_parts, 4] int32 records
-  float* part_m;         // [S*Hq, max_parts]
-  float* part_l;         // [S*Hq, max_parts]
-  float* part_o;         // [S*Hq, max_parts, D]
+  // workspace (see workspace_layout in api.cpp)
+  int32_t* sched;        // [0], [1]: decode ticket counter, tickets; [2], [3]: prefill
+  int32_t* dec_recs;     // decode work list, dec_cap records of 4 int32
+  int32_t* pre_recs;     // prefill work list, pre_cap records of 8 int32
+  int32_t* row_keys;     // [T] keys each query row sees (written by the plan)
+  int32_t dec_cap, pre_cap;
+  float* part_m;         // [T*Hq, max_parts]
+  float* part_l;         // [T*Hq, max_parts]
+  float* part_o;         // [T*Hq, max_parts, D]
 };
 
-// Split-context decode partitions: writes the output of single-partition
-// sequences and the partials of the others.
+// Rows of one prefill work item (one wavefront): four 16-column MFMA tiles of
+// 16/G rows x G heads.
+inline int32_t prefill_rows_per_item(int32_t G) { return 64 / G; }
+
+// Work-list plan: decode records, prefill records and per-row key counts.
+int launch_plan(const DecodeArgs& a, void* stream);
+// Chunked-prefill rows (sequences with more than one query row), bf16 only.
+int launch_prefill(const DecodeArgs& a, void* stream);
+
+// Split-context decode partitions of the one-row sequences: writes the output
+// of single-partition rows and the partials of the others.  Expects the plan.
 int launch_decode_partitions(const DecodeArgs& a, void* stream);
-// Log-sum-exp merge of the partials of multi-partition sequences.
+// Log-sum-exp merge of the partials of multi-partition rows (any query length).
 int launch_decode_merge(const DecodeArgs& a, void* stream);
 
 int launch_lse_merge(void* out, const float* part_m, const float* part_l, const float* part_o,

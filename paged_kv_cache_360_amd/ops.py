@@ -108,6 +108,49 @@ def pkv_attention_decode_merge(out, q, key_cache, value_cache, block_tables, con
                         context_lens, scale, max_context_len, workspace, stream)
 
 
+def pkv_varlen_workspace_bytes(num_seqs, num_tokens, num_q_heads, num_kv_heads, head_dim,
+                               max_query_len, max_context_len):
+    return int(lib().pkv_varlen_workspace_bytes(num_seqs, num_tokens, num_q_heads, num_kv_heads,
+                                                head_dim, max_query_len, max_context_len))
+
+
+def varlen_workspace(num_seqs, num_tokens, num_q_heads, num_kv_heads, head_dim, max_query_len,
+                     max_context_len, device="cuda"):
+    """A device buffer of the size ``pkv_attention_varlen`` needs (None if 0 bytes)."""
+    n = pkv_varlen_workspace_bytes(num_seqs, num_tokens, num_q_heads, num_kv_heads, head_dim,
+                                   max_query_len, max_context_len)
+    return torch.empty(n, dtype=torch.uint8, device=device) if n else None
+
+
+def pkv_attention_varlen(out, q, key_cache, value_cache, block_tables, context_lens,
+                         query_start_loc, scale, max_query_len, max_context_len, workspace=None,
+                         stream=None):
+    """Causal attention for variable query lengths (decode rows and prefill chunks), bf16.
+
+    ``q``/``out`` [T, Hq, D]; ``query_start_loc`` int32 [S+1] on the device.
+    """
+    t, hq, d = q.shape
+    nb, bs, hkv, dk = key_cache.shape
+    if out.shape != q.shape or dk != d or value_cache.shape != key_cache.shape:
+        raise ValueError("shape mismatch")
+    if out.dtype != q.dtype or key_cache.dtype != q.dtype or value_cache.dtype != q.dtype:
+        raise TypeError("q, caches and out must share one dtype")
+    s = context_lens.shape[0]
+    if block_tables.dim() != 2 or block_tables.shape[0] != s or query_start_loc.shape != (s + 1,):
+        raise ValueError("block_tables must be [S, MB] and query_start_loc [S+1]")
+    mb = block_tables.shape[1]
+    if workspace is None:
+        workspace = varlen_workspace(s, t, hq, hkv, d, max_query_len, max_context_len, q.device)
+    ws_ptr = 0 if workspace is None else _dev(workspace, "workspace")
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    check("pkv_attention_varlen", lib().pkv_attention_varlen(
+        _dev(out, "out"), _dev(q, "q"), _dev(key_cache, "key_cache"), _dev(value_cache, "value_cache"),
+        _dev(block_tables, "block_tables", torch.int32), _dev(context_lens, "context_lens", torch.int32),
+        _dev(query_start_loc, "query_start_loc", torch.int32), t, int(max_query_len), float(scale), bs,
+        hq, hkv, d, s, mb, nb, int(max_context_len), _dt(q), ws_ptr, ws_bytes, _stream(stream)))
+    return out
+
+
 def pkv_lse_merge(out, part_m, part_l, part_o, num_parts, stream=None):
     """Merge partial softmax results (base-2 maxima); ``out`` [rows, D]."""
     rows, maxp, d = part_o.shape

@@ -89,6 +89,45 @@ def test_decode_workspace_alignment_is_checked():
     assert _decode(ws=FAKE + 16) == PKV_EWORKSPACE
 
 
+def _varlen(**kw):
+    a = dict(out=FAKE, q=FAKE, kc=FAKE, vc=FAKE, tables=FAKE, ctx=FAKE, qsl=FAKE, t=40, mq=32,
+             scale=0.125, bs=16, hq=32, hkv=8, d=128, s=4, mb=128, nb=1000, maxctx=2048, dt=PKV_BF16,
+             ws=FAKE, wsb=1 << 30)
+    a.update(kw)
+    return lib().pkv_attention_varlen(a["out"], a["q"], a["kc"], a["vc"], a["tables"], a["ctx"],
+                                      a["qsl"], a["t"], a["mq"], a["scale"], a["bs"], a["hq"], a["hkv"],
+                                      a["d"], a["s"], a["mb"], a["nb"], a["maxctx"], a["dt"], a["ws"],
+                                      a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dt=PKV_F32), PKV_EUNSUPPORTED),          # matrix-core path: bf16 only
+    (dict(qsl=0), PKV_EINVAL),
+    (dict(mq=0), PKV_EINVAL),
+    (dict(t=-1), PKV_EINVAL),
+    (dict(hq=48, hkv=3), PKV_EUNSUPPORTED),
+    (dict(d=96), PKV_EUNSUPPORTED),
+    (dict(ws=0), PKV_EWORKSPACE),
+    (dict(wsb=1000), PKV_EWORKSPACE),
+    (dict(maxctx=128 * 16 + 1), PKV_EINVAL),
+    (dict(t=0), PKV_OK),                            # no query rows: nothing to launch
+    (dict(s=0), PKV_OK),
+])
+def test_varlen_argument_errors(kw, code):
+    assert _varlen(**kw) == code
+
+
+def test_varlen_workspace_sizes():
+    f = lib().pkv_varlen_workspace_bytes
+    dec = lib().pkv_decode_workspace_bytes(193, 32, 128, 4096)
+    assert f(193, 193, 32, 8, 128, 1, 4096) == dec     # all one-row sequences: the decode layout
+    big = f(193, 704, 32, 8, 128, 512, 4096)            # a 512-row chunk + 192 decode rows
+    rows, parts = 704 * 32, 8
+    assert big >= rows * parts * (128 + 2) * 4
+    assert f(193, 704, 32, 8, 128, 0, 4096) == 0        # max_query_len must be >= 1
+    assert f(4, 40, 12, 8, 128, 8, 512) == 0            # 12 q heads over 8 KV heads
+
+
 def test_write_and_copy_argument_errors():
     w = lib().pkv_write
     assert w(FAKE, FAKE, FAKE, FAKE, FAKE, 0, 8, 16, 2, 64, PKV_BF16, None) == PKV_OK

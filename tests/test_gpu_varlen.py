@@ -1,0 +1,174 @@
+"""GPU parity for variable-length attention: decode rows and chunked-prefill rows.
+
+``pkv_attention_varlen`` through the C ABI against ``oracle.causal_chunk_attention``
+(row r of a chunk of q rows over ctx keys sees keys 0 .. ctx - q + r), at sizes
+that span several 16-column tiles, 16-token blocks and 512-token partitions with
+ragged tails; and at the full mixed-step size (one 512-row chunk at the end of a
+4096-token context plus 192 decode sequences) on sampled rows, where each
+sampled row is the decode of its own truncated context in the oracle.
+"""
+
+import math
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_util import assert_close, dev, host, host_f64, say
+from workloads import (BLOCK_SIZE, SPECS, draw_context_lens, f32_to_bf16_bits, normal_values,
+                       normal_values_parallel, pool_blocks_for, random_block_tables)
+
+pytestmark = pytest.mark.gpu
+
+pkv = pytest.importorskip("paged_kv_cache_360_amd") if torch.cuda.is_available() else None
+
+
+def mixed_case(seed, Hq, Hkv, D, qlens, ctxs, spare=5):
+    rng = np.random.default_rng(seed)
+    ctx = np.asarray(ctxs, np.int32)
+    qlens = np.asarray(qlens, np.int32)
+    nb = int(sum(-(-c // BLOCK_SIZE) for c in ctx)) + spare
+    mb = max(1, int(-(-ctx.max() // BLOCK_SIZE)) + 1)
+    tables = random_block_tables(rng, ctx, nb, mb)
+    T = int(qlens.sum())
+    return {
+        "context_lens": ctx, "block_tables": tables, "num_blocks": nb,
+        "qsl": np.concatenate([[0], np.cumsum(qlens)]).astype(np.int32),
+        "key_cache": normal_values(rng, (nb, BLOCK_SIZE, Hkv, D), "bf16"),
+        "value_cache": normal_values(rng, (nb, BLOCK_SIZE, Hkv, D), "bf16"),
+        "q": normal_values(rng, (T, Hq, D), "bf16"),
+        "scale": np.float32(1.0 / math.sqrt(D)),
+        "max_query_len": int(qlens.max()),
+    }
+
+
+def gpu_varlen(inp, kc=None, vc=None):
+    q = dev(inp["q"])
+    out = torch.full_like(q, float("nan"))
+    kc = dev(inp["key_cache"]) if kc is None else kc
+    vc = dev(inp["value_cache"]) if vc is None else vc
+    ctx = inp["context_lens"]
+    pkv.pkv_attention_varlen(out, q, kc, vc, dev(inp["block_tables"]), dev(ctx), dev(inp["qsl"]),
+                             float(inp["scale"]), inp["max_query_len"], int(ctx.max()))
+    torch.cuda.synchronize()
+    return out
+
+
+def oracle_varlen(inp):
+    return oracle.causal_chunk_attention(inp["q"], inp["key_cache"], inp["value_cache"],
+                                         inp["block_tables"], inp["context_lens"], inp["qsl"],
+                                         inp["scale"])
+
+
+VARLEN_CASES = {
+    # name: (Hq, Hkv, D, query lengths, context lengths)
+    "gqa4_d128": (32, 8, 128, [1, 40, 1, 17, 3, 130], [600, 40, 1, 530, 1100, 1500]),
+    "gqa4_d128_long_chunk": (32, 8, 128, [300, 1, 1], [1300, 2048, 77]),
+    "mha_d64": (8, 8, 64, [1, 70, 2, 65], [90, 800, 513, 65]),
+    "gqa8_d128": (16, 2, 128, [9, 1, 33, 8], [1024, 517, 600, 8]),
+    "gqa2_d64": (8, 4, 64, [31, 1, 12], [700, 1000, 12]),
+}
+
+
+@pytest.mark.parametrize("name", sorted(VARLEN_CASES))
+def test_varlen_matches_oracle(name):
+    hq, hkv, d, qlens, ctxs = VARLEN_CASES[name]
+    say(f"varlen {name}: hq={hq} hkv={hkv} d={d} q={qlens} ctx={ctxs}")
+    inp = mixed_case(zlib.crc32(name.encode()) % 1000, hq, hkv, d, qlens, ctxs)
+    got = host_f64(gpu_varlen(inp))
+    assert_close(got, oracle_varlen(inp), "bf16", name)
+
+
+def test_varlen_unit_scale_zero_query():
+    """q = 0: row r's output is the mean of V over its visible keys (|out| ~ 1)."""
+    say("varlen zero-query unit scale")
+    inp = mixed_case(41, 32, 8, 128, [100, 1, 37], [700, 1200, 37])
+    rng = np.random.default_rng(41)
+    sign = np.where(rng.random((8, 128)) < 0.5, -1.0, 1.0).astype(np.float32)
+    noise = 0.05 * rng.standard_normal(inp["value_cache"].shape).astype(np.float32)
+    inp["value_cache"] = f32_to_bf16_bits(sign[None, None] + noise)
+    inp["q"] = np.zeros_like(inp["q"])
+    ref = oracle_varlen(inp)
+    assert np.min(np.abs(ref)) > 0.5
+    assert_close(host_f64(gpu_varlen(inp)), ref, "bf16", "zero-query")
+
+
+def test_varlen_poisoned_unused_memory_changes_nothing():
+    say("varlen poison")
+    inp = mixed_case(43, 32, 8, 128, [20, 1, 5], [530, 300, 17], spare=9)
+    clean = host(gpu_varlen(inp))
+    used = np.zeros((inp["num_blocks"], 16), bool)
+    for s, c in enumerate(inp["context_lens"]):
+        for jj in range(c):
+            used[inp["block_tables"][s, jj // 16], jj % 16] = True
+    kc, vc = inp["key_cache"].copy(), inp["value_cache"].copy()
+    kc[~used] = np.uint16(0x7F80)
+    vc[~used] = np.uint16(0x7FC0)
+    got = host(gpu_varlen(inp, kc=dev(kc), vc=dev(vc)))
+    assert got.tobytes() == clean.tobytes()
+
+
+def test_varlen_one_row_sequences_equal_decode():
+    """All sequences with one query row: the decode path, bit for bit."""
+    say("varlen decode rows == decode")
+    ctx = [1, 15, 600, 2000, 513, 4000]
+    inp = mixed_case(45, 32, 8, 128, [1] * len(ctx), ctx)
+    a = host(gpu_varlen(inp))
+    q = dev(inp["q"])
+    out = torch.empty_like(q)
+    pkv.pkv_attention_decode(out, q, dev(inp["key_cache"]), dev(inp["value_cache"]),
+                             dev(inp["block_tables"]), dev(inp["context_lens"]), float(inp["scale"]),
+                             max(ctx))
+    torch.cuda.synchronize()
+    assert a.tobytes() == host(out).tobytes()
+
+
+def test_varlen_rows_past_context_are_zero():
+    """More query rows than keys: rows that see no key get zeros; row r >= 4 of a
+    10-row chunk over 6 keys sees keys 0 .. r - 4 (the decode of that prefix)."""
+    say("varlen q > ctx")
+    inp = mixed_case(47, 8, 8, 64, [10, 1], [6, 30])
+    got = host_f64(gpu_varlen(inp))
+    assert np.all(got[:4] == 0)
+    keys = np.arange(4, 10) - 3
+    ref = oracle.decode_attention(inp["q"][4:10], inp["key_cache"], inp["value_cache"],
+                                  np.repeat(inp["block_tables"][:1], 6, 0), keys, inp["scale"])
+    assert_close(got[4:10], ref, "bf16", "rows with keys")
+
+
+def test_varlen_full_size_mixed_step_sampled():
+    spec = SPECS["mixed_chunk512_ctx4096_gqa32x8_bf16_s192"]
+    seed = 1004
+    say(f"full-size mixed step {spec.name}")
+    rng = np.random.default_rng(seed)
+    Hq, Hkv, D = spec.num_q_heads, spec.num_kv_heads, spec.head_dim
+    dec_ctx = draw_context_lens(rng, spec)
+    ctx = np.concatenate([[spec.chunk_ctx], dec_ctx]).astype(np.int32)
+    qlens = np.concatenate([[spec.chunk_rows], np.ones(len(dec_ctx), np.int32)]).astype(np.int32)
+    nb = pool_blocks_for(spec, ctx)
+    tables = random_block_tables(rng, ctx, nb, spec.max_blocks_per_seq)
+    T = int(qlens.sum())
+    inp = {
+        "context_lens": ctx, "block_tables": tables, "num_blocks": nb,
+        "qsl": np.concatenate([[0], np.cumsum(qlens)]).astype(np.int32),
+        "key_cache": normal_values_parallel(seed * 10 + 1, (nb, BLOCK_SIZE, Hkv, D), "bf16"),
+        "value_cache": normal_values_parallel(seed * 10 + 2, (nb, BLOCK_SIZE, Hkv, D), "bf16"),
+        "q": normal_values_parallel(seed * 10 + 3, (T, Hq, D), "bf16"),
+        "scale": np.float32(1.0 / math.sqrt(D)),
+        "max_query_len": int(qlens.max()),
+    }
+    got = host_f64(gpu_varlen(inp))
+    again = host_f64(gpu_varlen(inp))
+    assert np.array_equal(got, again), "two runs differ"
+    # prefill rows: row r sees keys 0 .. 3584 + r, the decode of a truncated context
+    rows = np.array([0, 1, 15, 16, 100, 255, 256, 300, 447, 510, 511])
+    keys = spec.chunk_ctx - spec.chunk_rows + rows + 1
+    ref = oracle.decode_attention(inp["q"][rows], inp["key_cache"], inp["value_cache"],
+                                  np.repeat(tables[:1], len(rows), 0), keys, inp["scale"])
+    assert_close(got[rows], ref, "bf16", "prefill rows")
+    seqs = np.unique(np.concatenate([np.argsort(dec_ctx)[[0, -1]], rng.choice(len(dec_ctx), 6, replace=False)])) + 1
+    dref = oracle.decode_attention(inp["q"][inp["qsl"][seqs]], inp["key_cache"], inp["value_cache"],
+                                   tables[seqs], ctx[seqs], inp["scale"])
+    assert_close(got[inp["qsl"][seqs]], dref, "bf16", "decode rows")
