@@ -105,7 +105,9 @@ def main():
         return
 
     spec = SPECS[args.workload]
-    if spec.chunk_rows or spec.ctx_kind == "prefix":
+    if spec.chunk_rows:
+        return mixed_main(args, spec)
+    if spec.ctx_kind == "prefix":
         raise SystemExit(f"workload {spec.name} is not a plain decode batch")
     S, Hq, Hkv, D = spec.num_seqs, spec.num_q_heads, spec.num_kv_heads, spec.head_dim
     es = 2 if spec.dtype == "bf16" else 4
@@ -292,6 +294,138 @@ def main():
         "host_alloc_us": round(float(np.mean(host_alloc_s[W:])) * 1e6, 2),
         "roofline": roofline,
         "cpu_baseline": cpu,
+    }
+    line = json.dumps(res)
+    print(line, flush=True)
+    if args.json_out:
+        with open(args.json_out, "w") as f:
+            f.write(line + "\n")
+
+
+def mixed_main(args, spec):
+    """Chunked-prefill mixed step: one prefill chunk batched with decode sequences.
+
+    Sequence 0 holds a context of spec.chunk_ctx tokens whose last spec.chunk_rows
+    are the chunk's query rows (written every step into the same slots, so each
+    step has the same shape); sequences 1..S append one decode token per step.
+    One step = host allocation + metadata H2D + pkv_write of all new rows +
+    pkv_attention_varlen (plan, decode partitions, prefill tiles, merge).
+    """
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_360_amd as pkv
+    from workloads import draw_context_lens, normal_values_parallel, pool_blocks_for
+
+    S, Hq, Hkv, D = spec.num_seqs, spec.num_q_heads, spec.num_kv_heads, spec.head_dim
+    C, CC = spec.chunk_rows, spec.chunk_ctx
+    W, K, R = args.warmup, args.steps, max(1, args.pool_copies)
+    n_steps = W + K
+    rng = np.random.default_rng(args.seed)
+    dec0 = draw_context_lens(rng, spec)
+    final = dec0.astype(np.int64) + n_steps - 1
+    MB = int(-(-max(int(final.max()), CC) // 16))
+    nb = pool_blocks_for(spec, np.concatenate([[CC], final]))
+    alloc = pkv.BlockAllocator(nb, 16, shuffle_seed=args.seed)
+    ids = np.arange(S + 1, dtype=np.int64)
+    for s in ids:
+        alloc.add_seq(int(s))
+    chunk_slots, _ = alloc.append(0, CC)
+    chunk_slots = np.asarray(chunk_slots[CC - C:], np.int32)
+    alloc.append_batch(ids[1:], dec0 - 1)
+    tdt = torch.bfloat16
+
+    def up(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(tdt)
+
+    kcs = [up(normal_values_parallel(args.seed * 10 + 1, (nb, 16, Hkv, D), "bf16"))]
+    vcs = [up(normal_values_parallel(args.seed * 10 + 2, (nb, 16, Hkv, D), "bf16"))]
+    for _ in range(R - 1):
+        kcs.append(kcs[0].clone())
+        vcs.append(vcs[0].clone())
+    T = C + S
+    qs = up(normal_values_parallel(args.seed * 10 + 3, (n_steps, T, Hq, D), "bf16"))
+    knew = up(normal_values_parallel(args.seed * 10 + 4, (n_steps, T, Hkv, D), "bf16"))
+    vnew = up(normal_values_parallel(args.seed * 10 + 5, (n_steps, T, Hkv, D), "bf16"))
+    out = torch.empty((T, Hq, D), dtype=tdt, device="cuda")
+    max_ctx = max(int(final.max()), CC)
+    ws = pkv.varlen_workspace(S + 1, T, Hq, Hkv, D, C, max_ctx)
+    scale = float(np.float32(1.0 / math.sqrt(D)))
+    qsl = torch.from_numpy(np.concatenate([[0], C + np.arange(S + 1)]).astype(np.int32)).cuda()
+    slots_h = np.empty(T, np.int32)
+    slots_h[:C] = chunk_slots
+    main = torch.cuda.current_stream()
+    events, lens_log = [], []
+
+    def step(i, timed):
+        _, pairs = alloc.append_batch(ids[1:], np.ones(S, np.int32), slots_out=slots_h[C:])
+        tables, lens = alloc.block_tables(ids, MB)
+        d_slots = torch.from_numpy(slots_h).cuda(non_blocking=False)
+        d_tables = torch.from_numpy(tables).cuda()
+        d_lens = torch.from_numpy(lens).cuda()
+        r = i % R
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)] if timed else None
+        if timed:
+            lens_log.append(lens.copy())
+            ev[0].record(main)
+        pkv.pkv_write(kcs[r], vcs[r], knew[i], vnew[i], d_slots)
+        if timed:
+            ev[1].record(main)
+        pkv.pkv_attention_varlen(out, qs[i], kcs[r], vcs[r], d_tables, d_lens, qsl, scale, C, max_ctx,
+                                 workspace=ws)
+        if timed:
+            ev[2].record(main)
+            events.append(ev)
+
+    for i in range(W):
+        step(i, False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(W, W + K):
+        step(i, True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    t_write = [e[0].elapsed_time(e[1]) * 1e-3 for e in events]
+    t_attn = [e[1].elapsed_time(e[2]) * 1e-3 for e in events]
+    # algorithmic bytes of the attention call: K/V each row group reads once
+    # (decode rows: their context; the chunk: its 4096-token context), q, out,
+    # and the partials of rows spanning several partitions
+    es, row_kv = 2, 2 * Hkv * D * 2
+    keys_chunk = CC - C + np.arange(C) + 1
+    flops_prefill = 4 * D * Hq * int(keys_chunk.sum())
+    att_b = []
+    for lens in lens_log:
+        dec = lens[1:].astype(np.int64)
+        nparts = -(-dec // 512)
+        b = int(dec.sum()) * row_kv + CC * row_kv
+        b += 2 * T * Hq * D * es
+        pc = -(-keys_chunk // 512)
+        b += 2 * (int(nparts[nparts > 1].sum()) + int(pc[pc > 1].sum())) * Hq * (D + 2) * 4
+        att_b.append(b)
+    ta = float(np.mean(t_attn))
+    res = {
+        "metric": "mixed chunked-prefill step: query rows/s (prefill chunk + decode rows), bf16 GQA",
+        "value": round(T * K / wall, 1),
+        "unit": "query rows/s",
+        "n_gpus": 1, "steps": K, "warmup": W,
+        "ms_per_step": round(wall / K * 1e3, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": spec.name, "chunk_rows": C, "chunk_context": CC, "decode_seqs": S,
+                   "num_q_heads": Hq, "num_kv_heads": Hkv, "head_dim": D, "block_size": 16,
+                   "partition_tokens": 512, "pool_blocks": nb, "pool_copies": R, "seed": args.seed},
+        "kernels_us": {"write": round(float(np.mean(t_write)) * 1e6, 2),
+                       "varlen_call": round(ta * 1e6, 2)},
+        "decode_tokens_per_s": round(S * K / wall, 1),
+        "prefill_gflop_per_step": round(flops_prefill / 1e9, 2),
+        "roofline": {
+            "kernel": "pkv_attention_varlen (plan + decode partitions + prefill tiles + merge)",
+            "bound": "hbm", "achieved": round(float(np.mean(att_b)) / ta / 1e9, 1),
+            "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+            "frac": round(float(np.mean(att_b)) / ta / 1e9 / HBM_PEAK_GBPS, 4), "traffic": None,
+            "algorithmic_bytes_per_launch": int(np.mean(att_b)), "avg_launch_us": round(ta * 1e6, 2),
+        },
+        "cpu_baseline": None,
     }
     line = json.dumps(res)
     print(line, flush=True)

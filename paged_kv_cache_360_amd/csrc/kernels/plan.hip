@@ -61,9 +61,13 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(
   for (int r = t; r < T; r += kPlanThreads) row_keys[r] = 0;  // rows no sequence owns see nothing
   __syncthreads();
   int full = 0, npre = 0;
+  int own_c = 0, own_q = 0, own_row0 = 0;  // this thread's (last) sequence, for the write loop
   for (int s = s0; s < s1; ++s) {
     const int c = ctx_of(s);
     const int q = rows_of(s);
+    own_c = c;
+    own_q = q;
+    own_row0 = first_row(s);
     if (q == 1) {
       const int n = parts_of(c);
       full += n - 1;
@@ -96,31 +100,55 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(
   }
   __syncthreads();
 
+  // Writes.  Decode sequences (at most a few records each): every thread writes
+  // its own.  Prefill sequences (hundreds of rows and records each): the wave
+  // takes them one at a time, in each owner's order, and all 64 lanes write.
+  const int lane = t & (kWave - 1);
   int od = s_full[t] - full;
-  int op = s_pre[t] - npre;
   for (int s = s0; s < s1; ++s) {
+    const int c = per == 1 ? own_c : ctx_of(s);
+    const int q = per == 1 ? own_q : rows_of(s);
+    if (q != 1) continue;
+    const int row0 = per == 1 ? own_row0 : first_row(s);
+    const int n = parts_of(c);
+    for (int k = 0; k < n - 1; ++k, ++od)
+      if (od < dec_cap) dec[od] = make_int4(s, k, c, row0);
+    const int at = atomicAdd(&s_bucket[last_bucket(c, n)], 1);
+    if (at < dec_cap) dec[at] = make_int4(s, n - 1, c, row0);
+    row_keys[row0] = c;
+  }
+  auto next_prefill = [&](int from) {
+    for (int s = from; s < s1; ++s)
+      if ((per == 1 ? own_q : rows_of(s)) > 1) return s;
+    return s1;
+  };
+  int op = s_pre[t] - npre;
+  int ps = next_prefill(s0);
+  for (;;) {
+    const unsigned long long pending = __ballot(ps < s1);
+    if (pending == 0) break;
+    const int src = __ffsll(pending) - 1;
+    const int s = __shfl(ps, src, kWave);
+    int cop = __shfl(op, src, kWave);
     const int c = ctx_of(s);
     const int q = rows_of(s);
     const int row0 = first_row(s);
-    if (q == 1) {
-      const int n = parts_of(c);
-      for (int k = 0; k < n - 1; ++k)
-        if (od < dec_cap) dec[od++] = make_int4(s, k, c, row0);
-      const int at = atomicAdd(&s_bucket[last_bucket(c, n)], 1);
-      if (at < dec_cap) dec[at] = make_int4(s, n - 1, c, row0);
-      row_keys[row0] = c;
-    } else if (q > 1) {
-      for (int r0 = 0; r0 < q; r0 += rows_per_item) {
-        const int nr = min(q, r0 + rows_per_item) - r0;
-        const int n = parts_of(row_keys_of(c, q, r0 + nr - 1));
-        for (int k = 0; k < n; ++k, ++op) {
-          if (op < pre_cap) {
-            pre[2 * op] = make_int4(s, k, c, row0 + r0);
-            pre[2 * op + 1] = make_int4(nr, c - q + r0 + 1, 0, 0);  // unclamped: row i sees max(0, this + i)
-          }
+    for (int r0 = 0; r0 < q; r0 += rows_per_item) {
+      const int nr = min(q, r0 + rows_per_item) - r0;
+      const int n = parts_of(row_keys_of(c, q, r0 + nr - 1));
+      for (int k = lane; k < n; k += kWave) {
+        if (cop + k < pre_cap) {
+          pre[2 * (cop + k)] = make_int4(s, k, c, row0 + r0);
+          // unclamped: row i of the group sees max(0, this + i) keys
+          pre[2 * (cop + k) + 1] = make_int4(nr, c - q + r0 + 1, 0, 0);
         }
       }
-      for (int r = 0; r < q; ++r) row_keys[row0 + r] = row_keys_of(c, q, r);
+      cop += n;
+    }
+    for (int r = lane; r < q; r += kWave) row_keys[row0 + r] = row_keys_of(c, q, r);
+    if (lane == src) {
+      op = cop;
+      ps = next_prefill(ps + 1);
     }
   }
   __syncthreads();
