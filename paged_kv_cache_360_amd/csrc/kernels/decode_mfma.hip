@@ -194,7 +194,7 @@ __global__ __launch_bounds__(kDecodeThreads, kMfmaWavesPerSimd) void decode_part
     for (int i = 0; i < 4; ++i) B.v[i] = buffer_load_piece<VT>(vr, it.v_lane, i * tok_bytes);
   };
 
-  float m, l;            // running max of head h (log2 domain, uniform over j); this lane's sum
+  float m, l;            // reference max of head h (log2 domain, uniform over j); this lane's sum
   f32x4 acc[EPL];
 
   auto compute = [&](Blk& B) {
@@ -214,12 +214,11 @@ __global__ __launch_bounds__(kDecodeThreads, kMfmaWavesPerSimd) void decode_part
         }
       }
     }
-    float mb = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-    mb = fmaxf(mb, __shfl_xor(mb, 16, kWave));
-    mb = fmaxf(mb, __shfl_xor(mb, 32, kWave));
-    const float mn = fmaxf(m, mb);
+    const float mb = max_over_rows(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])));
+    const bool up = mb > m + kRescaleLog2;  // lazy reference max (-inf + 8 = -inf)
+    const float mn = up ? mb : m;
     const float ms = (mn == -INFINITY) ? 0.f : mn;
-    if (__ballot(mn != m)) {  // some head's max grew: rescale what was accumulated
+    if (__ballot(up)) {  // some head's reference moved: rescale what was accumulated
       const float alpha = exp2_fast(m - ms);
       l *= alpha;
 #pragma unroll
@@ -306,8 +305,7 @@ __global__ __launch_bounds__(kDecodeThreads, kMfmaWavesPerSimd) void decode_part
     }
 
     // Wave totals of head h: l summed over the four lane groups (m is uniform).
-    l += __shfl_xor(l, 16, kWave);
-    l += __shfl_xor(l, 32, kWave);
+    l = sum_over_rows(l);
     if (h < G) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {

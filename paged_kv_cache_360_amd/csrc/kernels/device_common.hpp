@@ -24,6 +24,13 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   return (uint16_t)(u >> 16);
 }
 
+// Lazy rescaling of the online softmax: the running reference max moves only
+// when a block's max exceeds it by more than this many powers of two, so
+// weights 2^(x - ref) stay below 2^8 and the accumulators are rescaled rarely.
+// The result is the same softmax: the reference cancels between the weighted
+// sum and the sum of weights (and between partials in the log-sum-exp merge).
+constexpr float kRescaleLog2 = 8.f;
+
 // 2^x on the hardware exponential unit (v_exp_f32); 2^-inf = 0.
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -62,6 +69,24 @@ __device__ __forceinline__ uint4 buffer_load_piece<uint4>(__amdgpu_buffer_rsrc_t
 template <>
 __device__ __forceinline__ uint2 buffer_load_piece<uint2>(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
   return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0));
+}
+
+// Reductions over the four 16-lane rows of a wave (lanes l, l^16, l^32, l^48)
+// with the gfx950 lane-swap instructions (vector ALU, no LDS round trip).
+// v_permlane16_swap(x, x) yields, per lane, the lane's own value and its xor-16
+// partner's in its two results; v_permlane32_swap(x, x) the same for xor 32.
+// All 64 lanes must be active.
+__device__ __forceinline__ float max_over_rows(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float sum_over_rows(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
 // Butterfly sum / max over lanes that differ only in the bits of [lo_mask, 64).

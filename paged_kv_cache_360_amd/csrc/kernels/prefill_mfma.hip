@@ -8,24 +8,23 @@
 // §2 "Reworking the Attention Computation"), split into 512-token partitions
 // whose partial softmax results the log-sum-exp merge combines.
 //
-// Unlike a decode row, a chunk's rows make a real dense tile: one wavefront
-// takes a work item of 64/G consecutive rows x the G q heads of one KV head =
-// four 16-column MFMA tiles (column n of tile c = row c*16/G + n/G, head n%G),
-// over one partition of keys.  Per 16-token block the K operand (A of
+// Unlike a decode row, a chunk's rows make a real dense tile.  A workgroup takes
+// a work item of 256/G consecutive rows x the G q heads of one KV head over one
+// partition of keys; each of its four waves owns 64/G rows = four 16-column
+// MFMA tiles (column n of tile c = row c*16/G + n/G, head n%G).  Each
+// 16-token block of K and V is loaded once per workgroup (coalesced 16-byte
+// pieces, a few blocks in flight in registers), staged through a double-buffered
+// LDS slab with padded rows, and read by every wave as the K operand (A of
 // v_mfma_f32_16x16x32_bf16, token = lane & 15) and the V^T operand (A of
-// v_mfma_f32_16x16x16bf16_1k, regrouped from coalesced rows by 16-bit
-// permutes) are loaded once and used by all four tiles; the score tile's lane
-// layout is the P^T operand of the value product, as in the decode kernel.
-// Each column keeps its own online softmax and causal mask (token < the keys
-// its row sees), so the diagonal block needs no special case.
+// v_mfma_f32_16x16x16bf16_1k, regrouped by 16-bit permutes), each used by all
+// four of the wave's tiles; the score tile's lane layout is the P^T operand of
+// the value product, as in the decode kernel.  Each column keeps its own
+// online softmax and causal mask (token < the keys its row sees), so the
+// diagonal block needs no special case.
 //
-// The waves of a workgroup are independent: each takes tickets from the
-// prefill counter (a ticket names a work record and a KV head), holds the next
-// record while computing the current one, and issues the next item's q and
-// first blocks before writing the current item's partials, so the memory
-// pipeline does not drain between items.  A row whose keys fit one partition
-// gets its output written directly; other rows' partials go to the workspace
-// for the merge.
+// Workgroups take tickets from the prefill counter (a ticket names a work
+// record and a KV head).  A row whose keys fit one partition gets its output
+// written directly; other rows' partials go to the workspace for the merge.
 
 #include <hip/hip_runtime.h>
 
@@ -35,7 +34,7 @@
 #include "decode_common.hpp"
 
 #ifndef PKV_PREFILL_NBUF
-#define PKV_PREFILL_NBUF 2
+#define PKV_PREFILL_NBUF 4
 #endif
 
 namespace pkv {
@@ -47,7 +46,7 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kPrefillNbuf = PKV_PREFILL_NBUF;  // blocks in flight per wave
+constexpr int kPrefillNbuf = PKV_PREFILL_NBUF;  // blocks in flight per workgroup
 constexpr int kTiles = 4;                        // 16-column MFMA tiles per work item
 
 template <int D> struct VPiece;
@@ -63,15 +62,20 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
 
 template <int D, int G>
 __global__ __launch_bounds__(kDecodeThreads, 1) void prefill_mfma_kernel(DecodeParams p) {
-  constexpr int EPL = D / 16;            // dims per lane in one V row load
-  constexpr int WPL = EPL / 2;           // 32-bit words per V row load
+  constexpr int EPL = D / 16;            // dims per lane in one V row piece
+  constexpr int WPL = EPL / 2;           // 32-bit words per V row piece
   constexpr int NKC = D / 32;            // 16x16x32 MFMAs per tile per block for the scores
   constexpr int R = 16 / G;              // rows per tile
-  constexpr int NBUF = kPrefillNbuf;
+  constexpr int RPW = kTiles * R;        // rows per wave
+  constexpr int NPF = kPrefillNbuf;      // blocks in flight (cooperative loads)
+  constexpr int RS = D * 2 + 16;         // LDS row stride in bytes (16-byte pad: no bank conflicts)
   using VT = typename VPiece<D>::T;
   static_assert(G >= 1 && G <= 16 && 16 % G == 0, "a tile holds whole rows of G heads");
+  static_assert(kDecodeThreads == kBlockTokens * 16, "16 threads per token row load a block");
 
-  const int lane = threadIdx.x & (kWave - 1);
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int n = lane & 15;               // MFMA column (row n / G, head n % G of a tile)
   const int j = lane >> 4;
   const int Hq = p.Hkv * G;
@@ -79,50 +83,38 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void prefill_mfma_kernel(DecodeP
   const int64_t blk_bytes = tok_bytes * kBlockTokens;
   const int total = min(p.sched[3], p.pre_cap * p.Hkv);
 
-  auto ticket = [&]() {  // one ticket per wave
-    int t = 0;
-    if (lane == 0) t = atomicAdd(&p.sched[2], 1);
-    return __builtin_amdgcn_readfirstlane(t);
-  };
-  struct Rec {
-    int4 a, b;  // {sequence, partition, context, first query row}, {rows, key0}: row i sees max(0, key0 + i)
-  };
-  auto load_rec = [&](int tk) {
-    Rec r;
-    r.a = p.pre_recs[2 * (tk / p.Hkv)];
-    r.b = p.pre_recs[2 * (tk / p.Hkv) + 1];
-    return r;
-  };
+  // [buffer][K, V][16 rows x RS bytes]
+  __shared__ __attribute__((aligned(16))) char s_kv[2][2][kBlockTokens * RS];
+  __shared__ int s_ticket[2];
 
   struct Item {
-    int s, part, g, ctx, qrow0, nrows, key0, b_begin, nblk;
-    int ids;             // lane k < nblk: physical id of the item's k-th block
-    int k_lane, v_lane;
+    int s, part, g, ctx, qrow0, nrows, key0, b_begin, nblk, ids;
   };
-  auto make_item = [&](int tk, const Rec& r, Item& it) {
+  auto make_item = [&](int tk, Item& it) {
+    const int4 ra = p.pre_recs[2 * (tk / p.Hkv)];
+    const int4 rb = p.pre_recs[2 * (tk / p.Hkv) + 1];
     it.g = tk % p.Hkv;
-    it.s = r.a.x;
-    it.part = r.a.y;
-    it.ctx = r.a.z;
-    it.qrow0 = r.a.w;
-    it.nrows = r.b.x;
-    it.key0 = r.b.y;
+    it.s = ra.x;
+    it.part = ra.y;
+    it.ctx = ra.z;
+    it.qrow0 = ra.w;
+    it.nrows = rb.x;
+    it.key0 = rb.y;                                      // row i sees max(0, key0 + i) keys
     const int key_last = max(0, it.key0 + it.nrows - 1);  // keys the item's last row sees
     const int k_begin = it.part * kPartTokens;
     const int k_end = min(k_begin + kPartTokens, key_last);
     it.b_begin = it.part * kPartBlocks;
     it.nblk = max(0, (k_end - k_begin + kBlockTokens - 1) / kBlockTokens);
     it.ids = lane < it.nblk ? p.tables[(int64_t)it.s * p.MB + it.b_begin + lane] : -1;
-    it.k_lane = (int)(n * tok_bytes + (it.g * D + 8 * j) * 2);
-    it.v_lane = (int)(4 * j * tok_bytes + (it.g * D + EPL * n) * 2);
   };
 
-  // q operands (B of the score MFMAs): tile c, column n = row c*R + n/G, head n%G
+  // q operands (B of the score MFMAs) of this wave's rows: tile c, column n =
+  // row wave*RPW + c*R + n/G of the item, head n%G
   bf16x8 qf[kTiles][NKC];
   auto load_q = [&](const Item& it) {
 #pragma unroll
     for (int c = 0; c < kTiles; ++c) {
-      const int r = c * R + n / G;
+      const int r = wave * RPW + c * R + n / G;
       const bool ok = r < it.nrows;
       const char* qrow = reinterpret_cast<const char*>(p.q) +
                          ((int64_t)(it.qrow0 + (ok ? r : 0)) * Hq + it.g * G + n % G) * D * 2;
@@ -134,141 +126,176 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void prefill_mfma_kernel(DecodeP
     }
   };
 
-  struct Blk {
-    uint4 k[NKC];
-    VT v[4];
-    int valid;   // tokens of the block inside the context
-    int t0;      // first token of the block
+  // cooperative block loads: thread t loads the same piece of K and of V, row
+  // t / 16 of the block, bytes (t % 16) * PS .. + PS of KV head g's slice
+  // (PS = D / 8: one coalesced 16-lane row per token), so every load uses one
+  // resource and the pipeline needs no per-thread selection
+  constexpr int PS = D / 8;
+  const int st_row = tid / 16;
+  const int st_col = (tid % 16) * PS;
+  struct Stage {
+    VT k, v;
   };
-  auto issue = [&](const Item& it, int k, Blk& B) {
-    const int b = it.b_begin + k;
+  auto issue = [&](const Item& it, int k, Stage& st) {
     const int pb = k < it.nblk ? __builtin_amdgcn_readlane(it.ids, k) : -1;
     const bool ok = (unsigned)pb < (unsigned)p.NB;
-    B.t0 = b * kBlockTokens;
-    B.valid = ok ? min(kBlockTokens, it.ctx - B.t0) : 0;
     const int64_t base = (int64_t)(ok ? pb : 0) * blk_bytes;
     const int nrec = ok ? (int)blk_bytes : 0;
     const __amdgpu_buffer_rsrc_t kr =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(p.kc + base), (short)0, nrec, kRawBufferWord3);
     const __amdgpu_buffer_rsrc_t vr =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(p.vc + base), (short)0, nrec, kRawBufferWord3);
-#pragma unroll
-    for (int kc = 0; kc < NKC; ++kc) B.k[kc] = buffer_load16(kr, it.k_lane + 64 * kc, 0);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) B.v[i] = buffer_load_piece<VT>(vr, it.v_lane, i * tok_bytes);
+    const int off = (int)(st_row * tok_bytes + it.g * D * 2 + st_col);
+    st.k = buffer_load_piece<VT>(kr, off, 0);
+    st.v = buffer_load_piece<VT>(vr, off, 0);
+  };
+  auto stage_to_lds = [&](const Stage& st, int buf) {
+    *reinterpret_cast<VT*>(&s_kv[buf][0][st_row * RS + st_col]) = st.k;
+    *reinterpret_cast<VT*>(&s_kv[buf][1][st_row * RS + st_col]) = st.v;
   };
 
   float m[kTiles], l[kTiles];
   f32x4 acc[kTiles][EPL];
   int col_keys[kTiles];  // keys the column's row sees (0 for a column past the item's rows)
 
-  auto compute = [&](Blk& B) {
-    if (B.valid < kBlockTokens) {  // tokens past the context: V rows to zero (0 * NaN)
+  // one block from LDS buffer buf: tokens t0 .. t0+15, of which `valid` are in the context
+  auto compute = [&](int buf, int t0, int valid) {
+    const char* kb = s_kv[buf][0];
+    const char* vb = s_kv[buf][1];
+    uint4 kf[NKC];
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (4 * j + i >= B.valid) B.v[i] = VT{};
+    for (int kc = 0; kc < NKC; ++kc) kf[kc] = *reinterpret_cast<const uint4*>(kb + n * RS + 64 * kc + 16 * j);
+    VT vp[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      vp[i] = *reinterpret_cast<const VT*>(vb + (4 * j + i) * RS + EPL * 2 * n);
+      if (4 * j + i >= valid) vp[i] = VT{};  // past the context: zero (0 * NaN)
     }
-    const uint32_t* w0 = reinterpret_cast<const uint32_t*>(&B.v[0]);
-    const uint32_t* w1 = reinterpret_cast<const uint32_t*>(&B.v[1]);
-    const uint32_t* w2 = reinterpret_cast<const uint32_t*>(&B.v[2]);
-    const uint32_t* w3 = reinterpret_cast<const uint32_t*>(&B.v[3]);
+    const uint32_t* w0 = reinterpret_cast<const uint32_t*>(&vp[0]);
+    const uint32_t* w1 = reinterpret_cast<const uint32_t*>(&vp[1]);
+    const uint32_t* w2 = reinterpret_cast<const uint32_t*>(&vp[2]);
+    const uint32_t* w3 = reinterpret_cast<const uint32_t*>(&vp[3]);
     i16x4 av[EPL];  // V^T operand tiles, shared by the four column tiles
 #pragma unroll
     for (int w = 0; w < WPL; ++w) {
       av[2 * w] = __builtin_bit_cast(i16x4, make_uint2(pair_lo(w0[w], w1[w]), pair_lo(w2[w], w3[w])));
       av[2 * w + 1] = __builtin_bit_cast(i16x4, make_uint2(pair_hi(w0[w], w1[w]), pair_hi(w2[w], w3[w])));
     }
+    // In phases over the four tiles, so independent tiles overlap: scores,
+    // block maxima, one rescale decision, probabilities, value products.
+    f32x4 sc[kTiles];
+#pragma unroll
+    for (int c = 0; c < kTiles; ++c) sc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kc = 0; kc < NKC; ++kc) {
+#pragma unroll
+      for (int c = 0; c < kTiles; ++c)
+        sc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kf[kc]), qf[c][kc],
+                                                        sc[c], 0, 0, 0);
+    }
+    float x[kTiles][4], ms[kTiles];
+    bool grew = false;
 #pragma unroll
     for (int c = 0; c < kTiles; ++c) {
-      f32x4 sc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kc = 0; kc < NKC; ++kc)
-        sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, B.k[kc]), qf[c][kc], sc,
-                                                     0, 0, 0);
-      float x[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int t = B.t0 + 4 * j + i;
-        x[i] = t < col_keys[c] ? sc[i] * p.scale_log2 : -INFINITY;
+        const int t = t0 + 4 * j + i;
+        x[c][i] = t < col_keys[c] ? sc[c][i] * p.scale_log2 : -INFINITY;
       }
-      float mb = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-      mb = fmaxf(mb, __shfl_xor(mb, 16, kWave));
-      mb = fmaxf(mb, __shfl_xor(mb, 32, kWave));
-      const float mn = fmaxf(m[c], mb);
-      const float ms = (mn == -INFINITY) ? 0.f : mn;
-      if (__ballot(mn != m[c])) {
-        const float alpha = exp2_fast(m[c] - ms);
+      const float mb = max_over_rows(fmaxf(fmaxf(x[c][0], x[c][1]), fmaxf(x[c][2], x[c][3])));
+      const bool up = mb > m[c] + kRescaleLog2;  // -inf + 8 = -inf: the first live block moves it
+      const float mn = up ? mb : m[c];
+      ms[c] = (mn == -INFINITY) ? 0.f : mn;
+      grew |= up;
+      x[c][0] -= ms[c];
+      x[c][1] -= ms[c];
+      x[c][2] -= ms[c];
+      x[c][3] -= ms[c];
+      const float old = m[c];
+      m[c] = mn;
+      ms[c] = old - ms[c];  // exponent of the rescale factor
+    }
+    if (__ballot(grew)) {  // some column's reference moved: rescale what was accumulated
+#pragma unroll
+      for (int c = 0; c < kTiles; ++c) {
+        const float alpha = exp2_fast(ms[c]);
         l[c] *= alpha;
 #pragma unroll
         for (int e = 0; e < EPL; ++e) acc[c][e] *= alpha;
       }
-      m[c] = mn;
-      const uint32_t p01 = pack_bf16x2(exp2_fast(x[0] - ms), exp2_fast(x[1] - ms));
-      const uint32_t p23 = pack_bf16x2(exp2_fast(x[2] - ms), exp2_fast(x[3] - ms));
-      l[c] += (bf16_lo(p01) + bf16_hi(p01)) + (bf16_lo(p23) + bf16_hi(p23));
-      const i16x4 pt = __builtin_bit_cast(i16x4, make_uint2(p01, p23));
+    }
+    i16x4 pt[kTiles];
 #pragma unroll
-      for (int e = 0; e < EPL; ++e)
-        acc[c][e] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av[e], pt, acc[c][e], 0, 0, 0);
+    for (int c = 0; c < kTiles; ++c) {
+      const uint32_t p01 = pack_bf16x2(exp2_fast(x[c][0]), exp2_fast(x[c][1]));
+      const uint32_t p23 = pack_bf16x2(exp2_fast(x[c][2]), exp2_fast(x[c][3]));
+      l[c] += (bf16_lo(p01) + bf16_hi(p01)) + (bf16_lo(p23) + bf16_hi(p23));
+      pt[c] = __builtin_bit_cast(i16x4, make_uint2(p01, p23));
+    }
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+#pragma unroll
+      for (int c = 0; c < kTiles; ++c)
+        acc[c][e] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av[e], pt[c], acc[c][e], 0, 0, 0);
     }
   };
 
-  // per-wave ticket pipeline: the current and the next record are held
-  int tk = ticket();
-  int tk_next = ticket();
-  if (tk >= total) return;
-  Rec rec = load_rec(tk);
-  Rec rec_next = tk_next < total ? load_rec(tk_next) : Rec{};
+  if (tid == 0) s_ticket[0] = atomicAdd(&p.sched[2], 1);
+  __syncthreads();
+  int tk = __builtin_amdgcn_readfirstlane(s_ticket[0]);
 
-  Blk buf[NBUF];
-  Item cur;
-  make_item(tk, rec, cur);
-  load_q(cur);
+  Stage stg[NPF];
+  int buf = 0;
+  for (int parity = 1; tk < total; parity ^= 1) {
+    int next_tk = 0;
+    if (tid == 0) next_tk = atomicAdd(&p.sched[2], 1);
+    Item it;
+    make_item(tk, it);
+    load_q(it);
 #pragma unroll
-  for (int u = 0; u < NBUF - 1; ++u) issue(cur, u, buf[u]);
-
-  for (;;) {
-    const int tk_after = ticket();
+    for (int u = 0; u < NPF; ++u) issue(it, u, stg[u]);
 #pragma unroll
     for (int c = 0; c < kTiles; ++c) {
       m[c] = -INFINITY;
       l[c] = 0.f;
-      const int r = c * R + n / G;
-      col_keys[c] = r < cur.nrows ? max(0, cur.key0 + r) : 0;
+      const int r = wave * RPW + c * R + n / G;
+      col_keys[c] = r < it.nrows ? max(0, it.key0 + r) : 0;
 #pragma unroll
       for (int e = 0; e < EPL; ++e) acc[c][e] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    const int rounds = (cur.nblk + NBUF - 1) / NBUF;
+
+    // Blocks in rounds of NPF: block k's staged registers go to LDS buffer
+    // k % 2, the slot is refilled with block k + NPF (a zero-range load past the
+    // item), one barrier makes the block visible, and every wave computes it.
+    // Two LDS buffers suffice: a wave writing buffer k % 2 has passed block
+    // k-1's barrier, which every wave reached after computing block k-2.
+    const int rounds = (it.nblk + NPF - 1) / NPF;
     for (int rr = 0; rr < rounds; ++rr) {
 #pragma unroll
-      for (int u = 0; u < NBUF; ++u) {
-        issue(cur, rr * NBUF + u + NBUF - 1, buf[(u + NBUF - 1) % NBUF]);
-        compute(buf[u]);
+      for (int u = 0; u < NPF; ++u) {
+        const int k = rr * NPF + u;
+        const bool live = k < it.nblk;  // uniform over the workgroup
+        if (live) stage_to_lds(stg[u], buf);
+        issue(it, k + NPF, stg[u]);      // unconditional: the wait counts stay static
+        if (live) {
+          __syncthreads();
+          const int t0 = (it.b_begin + k) * kBlockTokens;
+          compute(buf, t0, min(kBlockTokens, it.ctx - t0));
+          buf ^= 1;
+        }
       }
-    }
-
-    // next item's q and first blocks before this item's writes
-    const Item done = cur;
-    const bool more = tk_next < total;
-    if (more) {
-      make_item(tk_next, rec_next, cur);
-      load_q(cur);
-#pragma unroll
-      for (int u = 0; u < NBUF - 1; ++u) issue(cur, u, buf[u]);
     }
 
 #pragma unroll
     for (int c = 0; c < kTiles; ++c) {
-      float lt = l[c];
-      lt += __shfl_xor(lt, 16, kWave);
-      lt += __shfl_xor(lt, 32, kWave);
-      const int r = c * R + n / G;
-      const int keys = max(0, done.key0 + r);
+      const float lt = sum_over_rows(l[c]);
+      const int r = wave * RPW + c * R + n / G;
+      const int keys = max(0, it.key0 + r);
       const int nparts = max(1, (keys + kPartTokens - 1) / kPartTokens);
       // a row that ends before this partition has nothing here (its own items
       // cover its partitions); only partition 0 of a one-partition row is output
-      if (r < done.nrows && done.part < nparts) {
-        const int64_t orow = (int64_t)(done.qrow0 + r) * Hq + done.g * G + n % G;
+      if (r < it.nrows && it.part < nparts) {
+        const int64_t orow = (int64_t)(it.qrow0 + r) * Hq + it.g * G + n % G;
         const float inv = lt > 0.f ? 1.f / lt : 0.f;
         if (nparts == 1) {
           uint16_t* o = reinterpret_cast<uint16_t*>(p.out) + orow * D;
@@ -278,7 +305,7 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void prefill_mfma_kernel(DecodeP
             for (int e = 0; e < EPL; ++e) o[EPL * (4 * j + i) + e] = f32_to_bf16(acc[c][e][i] * inv);
           }
         } else {
-          const int64_t pr = orow * p.max_parts + done.part;
+          const int64_t pr = orow * p.max_parts + it.part;
           float* o = p.part_o + pr * D;
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
@@ -292,9 +319,9 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void prefill_mfma_kernel(DecodeP
         }
       }
     }
-    if (!more) break;
-    tk_next = tk_after;
-    rec_next = tk_next < total ? load_rec(tk_next) : Rec{};
+    if (tid == 0) s_ticket[parity] = next_tk;
+    __syncthreads();
+    tk = __builtin_amdgcn_readfirstlane(s_ticket[parity]);
   }
 }
 
@@ -309,9 +336,8 @@ int launch_prefill_t(const DecodeArgs& a, hipStream_t st) {
       nb = 1;
     per_cu = nb;
   }
-  const int64_t waves = (int64_t)a.pre_cap * a.num_kv_heads;                    // upper bound on items
-  const int64_t grid = std::min<int64_t>((waves + kDecodeWaves - 1) / kDecodeWaves,
-                                         (int64_t)a.num_cus * per_cu);
+  const int64_t items = (int64_t)a.pre_cap * a.num_kv_heads;  // upper bound
+  const int64_t grid = std::min<int64_t>(items, (int64_t)a.num_cus * per_cu);
   hipLaunchKernelGGL((prefill_mfma_kernel<D, G>), dim3((unsigned)std::max<int64_t>(grid, 1)),
                      dim3(kDecodeThreads), 0, st, p);
   return (int)hipGetLastError();

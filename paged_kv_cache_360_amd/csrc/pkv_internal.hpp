@@ -51,9 +51,9 @@ struct DecodeArgs {
   float* part_o;         // [T*Hq, max_parts, D]
 };
 
-// Rows of one prefill work item (one wavefront): four 16-column MFMA tiles of
-// 16/G rows x G heads.
-inline int32_t prefill_rows_per_item(int32_t G) { return 64 / G; }
+// Rows of one prefill work item (one workgroup of four wavefronts, each with
+// four 16-column MFMA tiles of 16/G rows x G heads).
+inline int32_t prefill_rows_per_item(int32_t G) { return 256 / G; }
 
 // Work-list plan: decode records, prefill records and per-row key counts.
 int launch_plan(const DecodeArgs& a, void* stream);
