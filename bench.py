@@ -6,8 +6,9 @@ path included:
   1. host block allocator: one new token per sequence (a new block when the last
      one is full), slot of each new token, refreshed block tables and lengths,
      written into a pinned staging buffer (C++ allocator behind the C ABI);
-  2. one H2D copy of that metadata on a side stream (default priority), joined
-     to the compute stream by an event;
+  2. one H2D copy of that metadata on a side stream (default priority), then
+     pkv_attention_decode_plan (work list from the lengths) on the same side
+     stream, joined to the compute stream by events, so the plan overlaps 3-4;
   3. pkv_copy_blocks for any copy-on-write pairs (none for unshared batches);
   4. pkv_write of the new tokens' K/V;
   5. pkv_attention_decode_partitions (split-context decode, the dominant kernel);
@@ -146,7 +147,9 @@ def main():
     knew = up(normal_values_parallel(args.seed * 10 + 4, (n_steps, S, Hkv, D), spec.dtype))
     vnew = up(normal_values_parallel(args.seed * 10 + 5, (n_steps, S, Hkv, D), spec.dtype))
     out = torch.empty((S, Hq, D), dtype=tdt, device="cuda")
-    ws = pkv.decode_workspace(S, Hq, D, max_ctx_bound)
+    # one workspace per staging set: step i's plan (side stream) may run while
+    # step i-1's partitions and merge still read the other one
+    wss = [pkv.decode_workspace(S, Hq, D, max_ctx_bound) for _ in range(2)]
     scale = float(np.float32(1.0 / math.sqrt(D)))
 
     # pinned staging: [slots S | lens S | tables S*MB] int32, two sets
@@ -161,6 +164,7 @@ def main():
     main = torch.cuda.current_stream()
     side = torch.cuda.Stream()                          # default priority
     h2d_done = [torch.cuda.Event() for _ in range(2)]
+    plan_done = [torch.cuda.Event() for _ in range(2)]
     kern_done = [torch.cuda.Event() for _ in range(2)]
     log(f"[bench] setup {time.time() - t0:.1f}s: {spec.name} S={S} Hq={Hq} Hkv={Hkv} D={D} "
         f"pool={nb} blocks x{R} MB={MB}")
@@ -179,20 +183,26 @@ def main():
         host_alloc_s.append(time.perf_counter() - ta)
         if timed:
             step_lens.append(lens_h.copy())
+        d_slots, d_lens = dmeta[b][:S], dmeta[b][S:2 * S]
+        d_tables = dmeta[b][2 * S:].view(S, MB)
+        r = i % R
+        ws = wss[b]
         with torch.cuda.stream(side):
             side.wait_event(kern_done[b])               # device set b no longer read by step i-2
             dmeta[b].copy_(stage[b], non_blocking=True)
             h2d_done[b].record(side)
+            # the work list needs only the lengths: it runs beside the write
+            pkv.pkv_attention_decode_plan(out, qs[i], kcs[r], vcs[r], d_tables, d_lens, scale,
+                                          max_ctx_bound, workspace=ws, stream=side)
+            plan_done[b].record(side)
         main.wait_event(h2d_done[b])
-        d_slots, d_lens = dmeta[b][:S], dmeta[b][S:2 * S]
-        d_tables = dmeta[b][2 * S:].view(S, MB)
-        r = i % R
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)] if timed else None
         if timed:
             ev[0].record(main)
         if len(pairs):
             pkv.pkv_copy_blocks(kcs[r], vcs[r], torch.from_numpy(pairs).cuda())
         pkv.pkv_write(kcs[r], vcs[r], knew[i], vnew[i], d_slots)
+        main.wait_event(plan_done[b])
         if timed:
             ev[1].record(main)
         pkv.pkv_attention_decode_partitions(out, qs[i], kcs[r], vcs[r], d_tables, d_lens, scale,
@@ -246,7 +256,7 @@ def main():
             traffic = tr.get("traffic_bytes_per_launch")
 
     roofline = {
-        "kernel": "decode_partition_kernel (pkv_attention_decode_partitions)",
+        "kernel": "decode_partition_mfma_kernel (pkv_attention_decode_partitions)",
         "bound": "hbm",
         "achieved": round(achieved, 1),
         "peak": HBM_PEAK_GBPS,

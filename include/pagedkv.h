@@ -122,15 +122,25 @@ int pkv_attention_decode(void* out, const void* q, const void* key_cache,
                          int32_t max_context_len, pkv_dtype dt, void* workspace,
                          size_t workspace_bytes, void* stream);
 
-/* The two launches pkv_attention_decode makes, callable one at a time with the
+/* The three launches pkv_attention_decode makes, callable one at a time with the
  * same arguments (so each can be timed or overlapped on its own).
- * _partitions: builds the work list, then computes every (sequence, KV head,
- * 512-token partition); writes `out` for sequences with a single partition and
- * the partials (max, sum, normalized output) of the others to the workspace.
+ * _plan: builds the work list in the workspace from context_lens (reads nothing
+ * else, writes only the workspace), so it may run on another stream -- e.g.
+ * beside pkv_write -- if the caller orders it before _partitions.
+ * _partitions: computes every (sequence, KV head, 512-token partition) of the
+ * planned work list; writes `out` for sequences with a single partition and the
+ * partials (max, sum, normalized output) of the others to the workspace.
  * _merge: log-sum-exp merge of those partials into `out` (launches nothing when
- * max_context_len <= PKV_PARTITION_TOKENS).  Run _partitions first on the same
- * stream with the same workspace (the merge reads the work list's per-row key
- * counts).  Errors as pkv_attention_decode. */
+ * max_context_len <= PKV_PARTITION_TOKENS).
+ * All three take the same workspace; run them in this order.  Errors as
+ * pkv_attention_decode. */
+int pkv_attention_decode_plan(void* out, const void* q, const void* key_cache,
+                              const void* value_cache, const int32_t* block_tables,
+                              const int32_t* context_lens, float scale, int32_t block_size,
+                              int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                              int32_t num_seqs, int32_t max_blocks_per_seq, int32_t num_blocks,
+                              int32_t max_context_len, pkv_dtype dt, void* workspace,
+                              size_t workspace_bytes, void* stream);
 int pkv_attention_decode_partitions(void* out, const void* q, const void* key_cache,
                                     const void* value_cache, const int32_t* block_tables,
                                     const int32_t* context_lens, float scale, int32_t block_size,

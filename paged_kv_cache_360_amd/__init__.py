@@ -13,6 +13,7 @@ from ._lib import (  # noqa: F401
 from .ops import (  # noqa: F401
     pkv_write,
     pkv_attention_decode,
+    pkv_attention_decode_plan,
     pkv_attention_decode_partitions,
     pkv_attention_decode_merge,
     pkv_decode_workspace_bytes,

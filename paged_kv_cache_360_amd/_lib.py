@@ -36,6 +36,8 @@ SIGNATURES = {
     "pkv_decode_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32]),
     "pkv_attention_decode": (ctypes.c_int, [_p, _p, _p, _p, _p, _p, _f32, _i32, _i32, _i32, _i32, _i32,
                                             _i32, _i32, _i32, ctypes.c_int, _p, _sz, _p]),
+    "pkv_attention_decode_plan": (ctypes.c_int, [_p, _p, _p, _p, _p, _p, _f32, _i32, _i32, _i32, _i32,
+                                                 _i32, _i32, _i32, _i32, ctypes.c_int, _p, _sz, _p]),
     "pkv_attention_decode_partitions": (ctypes.c_int, [_p, _p, _p, _p, _p, _p, _f32, _i32, _i32, _i32, _i32,
                                                        _i32, _i32, _i32, _i32, ctypes.c_int, _p, _sz, _p]),
     "pkv_attention_decode_merge": (ctypes.c_int, [_p, _p, _p, _p, _p, _p, _f32, _i32, _i32, _i32, _i32,

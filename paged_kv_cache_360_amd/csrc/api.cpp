@@ -247,13 +247,19 @@ int prepare_attention(const char* who, pkv::DecodeArgs& a, void* out, const void
 
 extern "C" {
 
+int pkv_attention_decode_plan(PKV_DECODE_ARGS) {
+  pkv::DecodeArgs a{};
+  const char* who = "pkv_attention_decode_plan";
+  int rc = prepare_attention(who, a, PKV_DECODE_FWD);
+  if (rc != PKV_OK || num_seqs == 0) return rc;
+  return pkv::launched(pkv::launch_plan(a, stream), who);
+}
+
 int pkv_attention_decode_partitions(PKV_DECODE_ARGS) {
   pkv::DecodeArgs a{};
   const char* who = "pkv_attention_decode_partitions";
   int rc = prepare_attention(who, a, PKV_DECODE_FWD);
   if (rc != PKV_OK || num_seqs == 0) return rc;
-  rc = pkv::launched(pkv::launch_plan(a, stream), who);
-  if (rc != PKV_OK) return rc;
   return pkv::launched(pkv::launch_decode_partitions(a, stream), who);
 }
 

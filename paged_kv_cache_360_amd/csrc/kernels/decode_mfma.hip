@@ -129,7 +129,8 @@ __global__ __launch_bounds__(kDecodeThreads, kMfmaWavesPerSimd) void decode_part
 
   // One work item as this wave sees it.
   struct Item {
-    int s, part, g, ctx, nparts, b_begin, nmine;  // nparts: of the query row
+    int s, part, g, ctx, nparts, b_begin, nmine;  // part: first of the item's partitions
+    bool two;                                      // the item has a second partition
     int64_t row0;       // first q head (row of q / out) of the KV head group
     int my_id;          // lane k < nmine: id of the wave's k-th block
     int k_lane, v_lane; // this lane's byte offsets inside a block
@@ -144,8 +145,9 @@ __global__ __launch_bounds__(kDecodeThreads, kMfmaWavesPerSimd) void decode_part
     it.nparts = max(1, (it.ctx + kPartTokens - 1) / kPartTokens);
     const int nblk = (it.ctx + kBlockTokens - 1) / kBlockTokens;
     it.b_begin = it.part * kPartBlocks;
-    const int in_part = min(kPartBlocks, nblk - it.b_begin);
-    it.nmine = max(0, (in_part - wave + NWAVE - 1) / NWAVE);
+    const int in_item = min(kItemBlocks, nblk - it.b_begin);
+    it.two = in_item > kPartBlocks;
+    it.nmine = max(0, (in_item - wave + NWAVE - 1) / NWAVE);
     it.row0 = (int64_t)r.w * Hq + (int64_t)it.g * G;  // r.w: the sequence's query row
     it.k_lane = (int)(h * tok_bytes + (it.g * D + 8 * j) * 2);
     it.v_lane = (int)(4 * j * tok_bytes + (it.g * D + EPL * h) * 2);
@@ -244,9 +246,10 @@ __global__ __launch_bounds__(kDecodeThreads, kMfmaWavesPerSimd) void decode_part
     }
   };
 
-  __shared__ float s_m[2][NWAVE][G];
-  __shared__ float s_l[2][NWAVE][G];
-  __shared__ float s_o[2][NWAVE][G][D];
+  // [item parity][partition of the item][wave]
+  __shared__ float s_m[2][kItemParts][NWAVE][G];
+  __shared__ float s_l[2][kItemParts][NWAVE][G];
+  __shared__ float s_o[2][kItemParts][NWAVE][G][D];
   __shared__ int s_ticket[4];  // [0], [1]: by item parity; [2], [3]: the first two
 
   // Tickets run two items ahead: while item i is computed the wave already
@@ -282,14 +285,41 @@ __global__ __launch_bounds__(kDecodeThreads, kMfmaWavesPerSimd) void decode_part
     int tk2 = 0;
     if (threadIdx.x == 0) tk2 = atomicAdd(&p.sched[0], 1);
 
-    m = -INFINITY;
-    l = 0.f;
+    // Wave state of one partition to LDS (the item's partitions meet at the
+    // barrier), then a fresh state.  The wave's k-th block is block wave + 4k of
+    // the item, so its blocks k < kSplit belong to the first partition.
+    constexpr int kSplit = kPartBlocks / NWAVE;
+    auto reset = [&]() {
+      m = -INFINITY;
+      l = 0.f;
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) acc[e] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int e = 0; e < EPL; ++e) acc[e] = f32x4{0.f, 0.f, 0.f, 0.f};
+    };
+    auto save = [&](int slot) {
+      const float lt = sum_over_rows(l);
+      if (h < G) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) s_o[parity][slot][wave][h][EPL * (4 * j + i) + e] = acc[e][i];
+        }
+        if (j == 0) {
+          s_m[parity][slot][wave][h] = m;
+          s_l[parity][slot][wave][h] = lt;
+        }
+      }
+      reset();
+    };
+    reset();
+    bool saved0 = false;
     const int rounds = (cur.nmine + NBUF - 1) / NBUF;
     for (int r = 0; r < rounds; ++r) {
 #pragma unroll
       for (int u = 0; u < NBUF; ++u) {
+        if (r * NBUF + u == kSplit) {  // uniform: first block of the second partition
+          save(0);
+          saved0 = true;
+        }
         issue(cur, r * NBUF + u + NBUF - 1, buf[(u + NBUF - 1) % NBUF]);
         compute(buf[u]);
       }
@@ -304,45 +334,36 @@ __global__ __launch_bounds__(kDecodeThreads, kMfmaWavesPerSimd) void decode_part
       for (int u = 0; u < NBUF - 1; ++u) issue(cur, u, buf[u]);
     }
 
-    // Wave totals of head h: l summed over the four lane groups (m is uniform).
-    l = sum_over_rows(l);
-    if (h < G) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) s_o[parity][wave][h][EPL * (4 * j + i) + e] = acc[e][i];
-      }
-      if (j == 0) {
-        s_m[parity][wave][h] = m;
-        s_l[parity][wave][h] = l;
-      }
-    }
+    if (!saved0) save(0);  // this wave ended inside the first partition
+    if (done.two) save(1);
     if (threadIdx.x == 0) s_ticket[parity] = tk2;
     __syncthreads();
     tk2 = __builtin_amdgcn_readfirstlane(s_ticket[parity]);
     const bool have2 = have1 && tk2 < total;
     const int4 rec2 = have2 ? load_rec(tk2) : make_int4(0, 0, 0, 0);
 
-    for (int idx = threadIdx.x; idx < G * D; idx += kDecodeThreads) {
-      const int hh = idx / D;
+    const int nslots = done.two ? 2 : 1;
+    for (int idx = threadIdx.x; idx < nslots * G * D; idx += kDecodeThreads) {
+      const int slot = idx / (G * D);
+      const int hh = (idx / D) % G;
       const int d = idx % D;
       float M = -INFINITY;
 #pragma unroll
-      for (int w = 0; w < NWAVE; ++w) M = fmaxf(M, s_m[parity][w][hh]);
+      for (int w = 0; w < NWAVE; ++w) M = fmaxf(M, s_m[parity][slot][w][hh]);
       float L = 0.f, O = 0.f;
       if (M != -INFINITY) {
 #pragma unroll
         for (int w = 0; w < NWAVE; ++w) {
-          const float f = exp2_fast(s_m[parity][w][hh] - M);
-          L = fmaf(s_l[parity][w][hh], f, L);
-          O = fmaf(s_o[parity][w][hh][d], f, O);
+          const float f = exp2_fast(s_m[parity][slot][w][hh] - M);
+          L = fmaf(s_l[parity][slot][w][hh], f, L);
+          O = fmaf(s_o[parity][slot][w][hh][d], f, O);
         }
       }
       const float r = L > 0.f ? O / L : 0.f;
       if (done.nparts == 1) {
         store_out<true>(p.out, (done.row0 + hh) * D + d, r);
       } else {
-        const int64_t pr = (done.row0 + hh) * p.max_parts + done.part;
+        const int64_t pr = (done.row0 + hh) * p.max_parts + done.part + slot;
         p.part_o[pr * D + d] = r;
         if (d == 0) {
           p.part_m[pr] = M;

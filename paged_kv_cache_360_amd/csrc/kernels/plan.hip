@@ -10,10 +10,11 @@
 // log-sum-exp.
 //
 // Outputs (all in the caller's workspace):
-//  * decode records {sequence, partition, context, query row}: every decode
-//    partition but a sequence's last (all full, 32 blocks) first, then each
-//    sequence's last partition in decreasing block count (a counting sort over
-//    the 33 possible counts), so the persistent run ends on its shortest items;
+//  * decode records {sequence, first partition, context, query row}, one per
+//    pair of consecutive partitions (kItemParts): every pair but a sequence's
+//    last (both full, 64 blocks) first, then each sequence's last item in
+//    decreasing block count (a counting sort over the 65 possible counts), so
+//    the persistent run ends on its shortest items;
 //  * prefill records, two int4 each: {sequence, partition, context, first query
 //    row} and {rows, ctx - q + r0 + 1, 0, 0} (row i of the group sees max(0, that
 //    + i) keys; negative when the chunk is longer than the context); one per (group of
@@ -38,7 +39,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(
     int32_t ctx_cap, int32_t Hkv, int32_t rows_per_item, int32_t dec_cap, int32_t pre_cap,
     int32_t* __restrict__ sched, int4* __restrict__ dec, int4* __restrict__ pre,
     int32_t* __restrict__ row_keys) {
-  constexpr int NBK = kPartBlocks + 1;  // buckets: last-partition block count 32 .. 0
+  constexpr int NBK = kItemBlocks + 1;  // buckets: last-item block count 64 .. 0
   __shared__ int32_t s_full[kPlanThreads];
   __shared__ int32_t s_pre[kPlanThreads];
   __shared__ int32_t s_bucket[NBK];
@@ -51,8 +52,9 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(
   auto parts_of = [&](int keys) { return max(1, (keys + kPartTokens - 1) / kPartTokens); };
   auto first_row = [&](int s) { return qsl ? min(max(qsl[s], 0), T) : s; };
   auto rows_of = [&](int s) { return qsl ? max(0, min(qsl[s + 1], T) - first_row(s)) : 1; };
-  auto last_bucket = [&](int c, int n) {  // 0 for a full last partition, 32 for an empty one
-    return kPartBlocks - ((c + kBlockTokens - 1) / kBlockTokens - (n - 1) * kPartBlocks);
+  auto items_of = [&](int n) { return (n + kItemParts - 1) / kItemParts; };
+  auto last_bucket = [&](int c, int n) {  // 0 for a full last item, 64 for an empty one
+    return kItemBlocks - ((c + kBlockTokens - 1) / kBlockTokens - (items_of(n) - 1) * kItemBlocks);
   };
   // prefill: the keys seen by row r of a sequence with q rows and c keys
   auto row_keys_of = [&](int c, int q, int r) { return max(0, c - q + r + 1); };
@@ -70,7 +72,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(
     own_row0 = first_row(s);
     if (q == 1) {
       const int n = parts_of(c);
-      full += n - 1;
+      full += items_of(n) - 1;
       atomicAdd(&s_bucket[last_bucket(c, n)], 1);
     } else if (q > 1) {
       for (int r0 = 0; r0 < q; r0 += rows_per_item)
@@ -111,10 +113,11 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(
     if (q != 1) continue;
     const int row0 = per == 1 ? own_row0 : first_row(s);
     const int n = parts_of(c);
-    for (int k = 0; k < n - 1; ++k, ++od)
-      if (od < dec_cap) dec[od] = make_int4(s, k, c, row0);
+    const int ni = items_of(n);
+    for (int k = 0; k < ni - 1; ++k, ++od)
+      if (od < dec_cap) dec[od] = make_int4(s, k * kItemParts, c, row0);
     const int at = atomicAdd(&s_bucket[last_bucket(c, n)], 1);
-    if (at < dec_cap) dec[at] = make_int4(s, n - 1, c, row0);
+    if (at < dec_cap) dec[at] = make_int4(s, (ni - 1) * kItemParts, c, row0);
     row_keys[row0] = c;
   }
   auto next_prefill = [&](int from) {

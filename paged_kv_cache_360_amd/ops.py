@@ -94,16 +94,23 @@ def pkv_attention_decode(out, q, key_cache, value_cache, block_tables, context_l
                         context_lens, scale, max_context_len, workspace, stream)
 
 
+def pkv_attention_decode_plan(out, q, key_cache, value_cache, block_tables, context_lens,
+                              scale, max_context_len, workspace=None, stream=None):
+    """First launch of ``pkv_attention_decode`` alone (work list from context_lens)."""
+    return _decode_call("pkv_attention_decode_plan", out, q, key_cache, value_cache,
+                        block_tables, context_lens, scale, max_context_len, workspace, stream)
+
+
 def pkv_attention_decode_partitions(out, q, key_cache, value_cache, block_tables, context_lens,
                                     scale, max_context_len, workspace=None, stream=None):
-    """First launch of ``pkv_attention_decode`` alone (partition kernel)."""
+    """Second launch of ``pkv_attention_decode`` alone (partition kernel; needs the plan)."""
     return _decode_call("pkv_attention_decode_partitions", out, q, key_cache, value_cache,
                         block_tables, context_lens, scale, max_context_len, workspace, stream)
 
 
 def pkv_attention_decode_merge(out, q, key_cache, value_cache, block_tables, context_lens, scale,
                                max_context_len, workspace=None, stream=None):
-    """Second launch of ``pkv_attention_decode`` alone (log-sum-exp merge)."""
+    """Third launch of ``pkv_attention_decode`` alone (log-sum-exp merge)."""
     return _decode_call("pkv_attention_decode_merge", out, q, key_cache, value_cache, block_tables,
                         context_lens, scale, max_context_len, workspace, stream)
 

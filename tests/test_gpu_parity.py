@@ -285,3 +285,27 @@ def test_lse_merge_isolated(dtype, d, maxp):
     live = counts > 0
     # inputs were rounded to fp32 before the merge; the bar is the fp32/bf16 one
     assert_close(got[live], ref[live], dtype, "merge")
+
+
+def test_three_call_form_equals_one_call():
+    """plan, partitions and merge called one at a time (plan on its own stream,
+    ordered by an event) give the one-call result bit for bit."""
+    say("plan / partitions / merge")
+    inp = explicit_case(13, "bf16", 32, 8, 128, [40, 513, 1100, 3000, 7])
+    ref = host(gpu_decode(inp))
+    q, kc, vc = dev(inp["q"]), dev(inp["key_cache"]), dev(inp["value_cache"])
+    tables, ctx = dev(inp["block_tables"]), dev(inp["context_lens"])
+    mx = int(inp["context_lens"].max())
+    out = torch.empty_like(q)
+    ws = pkv.decode_workspace(5, 32, 128, mx)
+    side = torch.cuda.Stream()
+    done = torch.cuda.Event()
+    with torch.cuda.stream(side):
+        pkv.pkv_attention_decode_plan(out, q, kc, vc, tables, ctx, float(inp["scale"]), mx, workspace=ws,
+                                      stream=side)
+        done.record(side)
+    torch.cuda.current_stream().wait_event(done)
+    pkv.pkv_attention_decode_partitions(out, q, kc, vc, tables, ctx, float(inp["scale"]), mx, workspace=ws)
+    pkv.pkv_attention_decode_merge(out, q, kc, vc, tables, ctx, float(inp["scale"]), mx, workspace=ws)
+    torch.cuda.synchronize()
+    assert host(out).tobytes() == ref.tobytes()
