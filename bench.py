@@ -38,8 +38,10 @@ METRIC = "decode tokens/s + KV-read HBM GB/s (% of MI355X peak), bf16 GQA ctx 2k
 HBM_PEAK_GBPS = 8000.0
 DEFAULT_WORKLOAD = "gqa32x8_bf16_s128_ctx512_8192"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_partitions_traffic.json")
-KERNEL_SOURCES = ["paged_kv_cache_360_amd/csrc/kernels/decode.hip",
+KERNEL_SOURCES = ["paged_kv_cache_360_amd/csrc/kernels/decode_mfma.hip",
+                  "paged_kv_cache_360_amd/csrc/kernels/decode_common.hpp",
                   "paged_kv_cache_360_amd/csrc/kernels/device_common.hpp"]
+COPY_PROBE_BYTES = 512 * 1024 * 1024   # pkv_copy_blocks in --copy-probe: read and written per launch
 
 
 def parse_args():
@@ -55,7 +57,42 @@ def parse_args():
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain block copy of known size (counter calibration)")
     ap.add_argument("--json-out", default=None)
+    ap.add_argument("--traffic-from", nargs=4, metavar="CSV", default=None,
+                    help="rocprofv3 counter_collection CSVs: FETCH_SIZE and WRITE_SIZE of a "
+                         "--steps run, then of a --copy-probe run; writes the per-launch HBM "
+                         "traffic of the partition kernel for later bench lines, and exits")
     return ap.parse_args()
+
+
+def traffic_from_counters(paths, workload):
+    """Per-launch HBM bytes of the partition kernel from rocprofv3 --pmc CSVs.
+
+    FETCH_SIZE / WRITE_SIZE (KiB per dispatch) are scaled by what they read for
+    the copy probe, whose bytes are known (COPY_PROBE_BYTES each way).
+    """
+    import csv
+
+    def mean_kib(path, kernel_part):
+        vals = [float(r["Counter_Value"]) for r in csv.DictReader(open(path))
+                if kernel_part in r["Kernel_Name"]]
+        if not vals:
+            raise SystemExit(f"{path}: no dispatch of {kernel_part}")
+        return sum(vals) / len(vals)
+
+    fetch, write, cfetch, cwrite = paths
+    kf = COPY_PROBE_BYTES / (mean_kib(cfetch, "copy_blocks_kernel") * 1024)
+    kw = COPY_PROBE_BYTES / (mean_kib(cwrite, "copy_blocks_kernel") * 1024)
+    fb = mean_kib(fetch, "decode_partition_mfma_kernel") * 1024 * kf
+    wb = mean_kib(write, "decode_partition_mfma_kernel") * 1024 * kw
+    out = {"kernel": "decode_partition_mfma_kernel", "workload": workload,
+           "kernel_source_sha256": kernel_source_hash(),
+           "fetch_bytes_per_launch": int(fb), "write_bytes_per_launch": int(wb),
+           "traffic_bytes_per_launch": int(fb + wb),
+           "fetch_scale": round(kf, 4), "write_scale": round(kw, 4)}
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+    print(json.dumps(out))
 
 
 def kernel_source_hash():
@@ -87,6 +124,8 @@ def copy_probe(torch, pkv):
 
 def main():
     args = parse_args()
+    if args.traffic_from:
+        return traffic_from_counters(args.traffic_from, args.workload)
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU only: --gpus {args.gpus} (WORLD_SIZE={world}) is not "

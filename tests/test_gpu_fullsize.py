@@ -22,8 +22,9 @@ pytestmark = pytest.mark.gpu
 pkv = pytest.importorskip("paged_kv_cache_360_amd") if torch.cuda.is_available() else None
 
 
-def full_case(name, seed):
+def full_case(name, seed, dtype=None):
     spec = SPECS[name]
+    dt = dtype or spec.dtype
     rng = np.random.default_rng(seed)
     S, Hq, Hkv, D = spec.num_seqs, spec.num_q_heads, spec.num_kv_heads, spec.head_dim
     ctx = draw_context_lens(rng, spec)
@@ -31,11 +32,11 @@ def full_case(name, seed):
     tables = random_block_tables(rng, ctx, nb, spec.max_blocks_per_seq)
     return {
         "context_lens": ctx, "block_tables": tables, "num_blocks": nb,
-        "key_cache": normal_values_parallel(seed * 10 + 1, (nb, BLOCK_SIZE, Hkv, D), spec.dtype),
-        "value_cache": normal_values_parallel(seed * 10 + 2, (nb, BLOCK_SIZE, Hkv, D), spec.dtype),
-        "q": normal_values_parallel(seed * 10 + 3, (S, Hq, D), spec.dtype),
+        "key_cache": normal_values_parallel(seed * 10 + 1, (nb, BLOCK_SIZE, Hkv, D), dt),
+        "value_cache": normal_values_parallel(seed * 10 + 2, (nb, BLOCK_SIZE, Hkv, D), dt),
+        "q": normal_values_parallel(seed * 10 + 3, (S, Hq, D), dt),
         "scale": np.float32(1.0 / math.sqrt(D)),
-        "dtype": spec.dtype,
+        "dtype": dt,
     }
 
 
@@ -55,14 +56,17 @@ def run(inp, kc, vc):
     return out
 
 
-@pytest.mark.parametrize("name,seed", [
-    ("gqa32x8_bf16_s128_ctx512_8192", 1002),
-    ("llama2_7b_mha_bf16_s64_ctx1_2048", 1001),
-    ("gqa32x8_bf16_s128_ctx8192", 1007),
+@pytest.mark.parametrize("name,seed,dtype", [
+    ("gqa32x8_bf16_s128_ctx512_8192", 1002, None),
+    ("llama2_7b_mha_bf16_s64_ctx1_2048", 1001, None),
+    ("gqa32x8_bf16_s128_ctx8192", 1007, None),
+    # fp32 variants at the same shapes: the tight (1e-5) structural check
+    ("gqa32x8_bf16_s128_ctx512_8192", 1002, "f32"),
+    ("llama2_7b_mha_bf16_s64_ctx1_2048", 1001, "f32"),
 ])
-def test_full_size_decode_sampled(name, seed):
-    say(f"full-size decode {name} seed={seed}")
-    inp = full_case(name, seed)
+def test_full_size_decode_sampled(name, seed, dtype):
+    say(f"full-size decode {name} seed={seed} dtype={dtype or 'spec'}")
+    inp = full_case(name, seed, dtype)
     kc, vc = dev(inp["key_cache"]), dev(inp["value_cache"])
     got = run(inp, kc, vc)
     again = run(inp, kc, vc)
