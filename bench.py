@@ -18,8 +18,11 @@ K/V rows) are resident in HBM before timing starts.  R copies of the KV pool are
 rotated step to step so each step's KV reads come from HBM, not the 256 MiB
 last-level cache.
 
-Prints ONE JSON line.  Per-kernel durations come from HIP events recorded on
-the compute stream around each launch inside the timed region.
+Prints ONE JSON line.  The partition kernel's duration comes from two HIP
+events recorded on the compute stream around it in every timed step (each
+timing event costs the stream a few microseconds, so the write and merge are
+not bracketed there); the write and merge durations come from a few extra
+steps after the timed region, with events around every launch.
 """
 
 import argparse
@@ -153,7 +156,8 @@ def main():
     es = 2 if spec.dtype == "bf16" else 4
     tdt = torch.bfloat16 if spec.dtype == "bf16" else torch.float32
     W, K, R = args.warmup, args.steps, max(1, args.pool_copies)
-    n_steps = W + K
+    P = 8                                               # detail steps after the timed region
+    n_steps = W + K + P
 
     # ---- workload: lengths, allocator state, pool, queries ------------------
     t0 = time.time()
@@ -209,10 +213,31 @@ def main():
         f"pool={nb} blocks x{R} MB={MB}")
 
     step_lens = []
-    host_alloc_s = []
-    events = []
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K + P)]
 
-    def step(i, timed):
+    # The step calls the C ABI directly with precomputed pointers: per-call
+    # tensor checks in the Python wrappers cost more host time than the
+    # kernels take, and the host must stay ahead of the device.
+    L = pkv.lib()
+    dt = pkv.PKV_BF16 if spec.dtype == "bf16" else pkv.PKV_F32
+    q_stride = S * Hq * D * es
+    kv_stride = S * Hkv * D * es
+    q0, knew0, vnew0, out_p = qs.data_ptr(), knew.data_ptr(), vnew.data_ptr(), out.data_ptr()
+    side_h, main_h = side.cuda_stream, main.cuda_stream
+    dptr = [m.data_ptr() for m in dmeta]
+    ws_arg = [(w.data_ptr(), w.numel()) for w in wss]
+    kc_p = [t.data_ptr() for t in kcs]
+    vc_p = [t.data_ptr() for t in vcs]
+    check = pkv.check
+    host_alloc_s = []
+    host_step_s = []
+
+    def attn_args(i, b, r, stream):
+        d = dptr[b]
+        return (out_p, q0 + i * q_stride, kc_p[r], vc_p[r], d + 8 * S, d + 4 * S, scale, 16, Hq, Hkv,
+                D, S, MB, nb, max_ctx_bound, dt, ws_arg[b][0], ws_arg[b][1], stream)
+
+    def step(i, timed, detail=False):
         b = i % 2
         slots_h, lens_h, tables_h = views[b]
         h2d_done[b].synchronize()                       # staging set b is free again (copy of step i-2 done)
@@ -222,38 +247,34 @@ def main():
         host_alloc_s.append(time.perf_counter() - ta)
         if timed:
             step_lens.append(lens_h.copy())
-        d_slots, d_lens = dmeta[b][:S], dmeta[b][S:2 * S]
-        d_tables = dmeta[b][2 * S:].view(S, MB)
         r = i % R
-        ws = wss[b]
         with torch.cuda.stream(side):
             side.wait_event(kern_done[b])               # device set b no longer read by step i-2
             dmeta[b].copy_(stage[b], non_blocking=True)
             h2d_done[b].record(side)
-            # the work list needs only the lengths: it runs beside the write
-            pkv.pkv_attention_decode_plan(out, qs[i], kcs[r], vcs[r], d_tables, d_lens, scale,
-                                          max_ctx_bound, workspace=ws, stream=side)
-            plan_done[b].record(side)
+        # the work list needs only the lengths: it runs beside the write
+        check("pkv_attention_decode_plan", L.pkv_attention_decode_plan(*attn_args(i, b, r, side_h)))
+        plan_done[b].record(side)
         main.wait_event(h2d_done[b])
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)] if timed else None
-        if timed:
+        ev = events[i - W] if timed or detail else None
+        if detail:
             ev[0].record(main)
         if len(pairs):
             pkv.pkv_copy_blocks(kcs[r], vcs[r], torch.from_numpy(pairs).cuda())
-        pkv.pkv_write(kcs[r], vcs[r], knew[i], vnew[i], d_slots)
+        check("pkv_write", L.pkv_write(kc_p[r], vc_p[r], knew0 + i * kv_stride, vnew0 + i * kv_stride,
+                                       dptr[b], S, nb, 16, Hkv, D, dt, main_h))
         main.wait_event(plan_done[b])
-        if timed:
+        if timed or detail:
             ev[1].record(main)
-        pkv.pkv_attention_decode_partitions(out, qs[i], kcs[r], vcs[r], d_tables, d_lens, scale,
-                                            max_ctx_bound, workspace=ws)
-        if timed:
+        args_m = attn_args(i, b, r, main_h)
+        check("pkv_attention_decode_partitions", L.pkv_attention_decode_partitions(*args_m))
+        if timed or detail:
             ev[2].record(main)
-        pkv.pkv_attention_decode_merge(out, qs[i], kcs[r], vcs[r], d_tables, d_lens, scale,
-                                       max_ctx_bound, workspace=ws)
-        if timed:
+        check("pkv_attention_decode_merge", L.pkv_attention_decode_merge(*args_m))
+        if detail:
             ev[3].record(main)
-            events.append(ev)
         kern_done[b].record(main)
+        host_step_s.append(time.perf_counter() - ta)
 
     for i in range(W):
         step(i, False)
@@ -265,11 +286,14 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
     log(f"[bench] timed {K} steps: {wall * 1e3:.2f} ms")
+    for i in range(W + K, W + K + P):
+        step(i, False, detail=True)
+    torch.cuda.synchronize()
 
     # ---- per-kernel durations and algorithmic bytes --------------------------
-    t_write = [e[0].elapsed_time(e[1]) * 1e-3 for e in events]
-    t_part = [e[1].elapsed_time(e[2]) * 1e-3 for e in events]
-    t_merge = [e[2].elapsed_time(e[3]) * 1e-3 for e in events]
+    t_part = [e[1].elapsed_time(e[2]) * 1e-3 for e in events[:K]]
+    t_write = [e[0].elapsed_time(e[1]) * 1e-3 for e in events[K:]]   # includes the wait for the plan
+    t_merge = [e[2].elapsed_time(e[3]) * 1e-3 for e in events[K:]]
     kv_b, part_b, merge_b = [], [], []
     for lens in step_lens:
         lens = lens.astype(np.int64)
@@ -340,7 +364,8 @@ def main():
             "decode_partitions": round(float(np.mean(t_part)) * 1e6, 2),
             "merge": round(float(np.mean(t_merge)) * 1e6, 2),
         },
-        "host_alloc_us": round(float(np.mean(host_alloc_s[W:])) * 1e6, 2),
+        "host_alloc_us": round(float(np.mean(host_alloc_s[W:W + K])) * 1e6, 2),
+        "host_step_us": round(float(np.mean(host_step_s[W:W + K])) * 1e6, 2),
         "roofline": roofline,
         "cpu_baseline": cpu,
     }

@@ -8,7 +8,7 @@ library and raises if it has not been built.
 """
 
 from ._lib import (  # noqa: F401
-    BLOCK_SIZE, PARTITION_TOKENS, PKV_BF16, PKV_F32, LIB_PATH, PagedKVError, lib,
+    BLOCK_SIZE, PARTITION_TOKENS, PKV_BF16, PKV_F32, LIB_PATH, PagedKVError, check, lib,
 )
 from .ops import (  # noqa: F401
     pkv_write,

@@ -27,6 +27,12 @@ ARCH = "gfx950"
 HIP_FLAGS = [
     "-O3", "-fPIC", "-std=c++17", f"--offload-arch={ARCH}", "-mcode-object-version=5",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # Work tickets are taken with one lane's atomic add whose result is only
+    # needed at the end of the current item.  The atomic optimizer rewrites such
+    # an add into a wave-wide form that reads the result at once, which stalls
+    # the wave for the round trip and, as vector memory operations complete in
+    # order, for every block load issued before it.
+    "-Xarch_device", "-mllvm=-amdgpu-atomic-optimizer-strategy=None",
     "-Wall", "-Wno-unused-function", "-Wno-unused-command-line-argument",
 ]
 HOST_FLAGS = ["-O2", "-fPIC", "-std=c++17", "-Wall", "-D__HIP_PLATFORM_AMD__",

@@ -35,7 +35,7 @@ struct DecodeParams {
   int32_t NB;
   int32_t max_parts;
   int32_t ctx_cap;       // min(MB * 16, max_parts * 512): larger lengths are clamped
-  int32_t* sched;        // [0] next decode ticket, [1] decode tickets; [2], [3] prefill
+  int32_t* sched;        // [0] decode tickets taken from the counter, [1] decode tickets; [2], [3] prefill
   const int4* dec_recs;  // decode records {sequence, partition, context, query row}
   const int4* pre_recs;  // prefill records, two int4 each (see plan.hip)
   const int32_t* row_keys;

@@ -58,7 +58,7 @@
 #define PKV_MFMA_WG_PER_CU 1
 #endif
 #ifndef PKV_MFMA_WAVES
-#define PKV_MFMA_WAVES 3
+#define PKV_MFMA_WAVES 2
 #endif
 
 namespace pkv {
@@ -101,11 +101,17 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
 // Persistent partition kernel: each workgroup takes tickets from the counter
 // until none are left.  After the last block of an item each wave already holds
 // the next item's record (its ticket was passed through LDS at the previous
-// item's epilogue barrier and its record loaded right after), so it issues
-// that item's first blocks before the barrier and the cross-wave merge of the
-// current item: the merge and the output writes overlap with loads in flight.
-// LDS state is double-buffered by item parity: a wave may start writing item
-// i+1's state while others still read item i's.
+// item's barrier and its record loaded right after), so it issues that item's
+// first blocks before the barrier.  The cross-wave merge of an item runs inside
+// the next item's block loop, where its LDS reads and output stores overlap
+// with loads in flight.  LDS state is double-buffered by item parity: item
+// i+1's state is written while item i's is still being merged.
+//
+// Nothing at an item boundary waits for the block loads in flight: records
+// come in on the scalar path, the block ids and the ticket land in registers
+// that only loads and the atomic write, and the ticket is consumed while only
+// the zero-sized tail loads are outstanding (vector memory operations complete
+// in order, so any earlier wait would drain the prefetch).
 template <int D, int G>
 __global__ __launch_bounds__(kDecodeThreads, kMfmaWavesPerSimd) void decode_partition_mfma_kernel(
     DecodeParams p) {
@@ -135,8 +141,16 @@ __global__ __launch_bounds__(kDecodeThreads, kMfmaWavesPerSimd) void decode_part
     int my_id;          // lane k < nmine: id of the wave's k-th block
     int k_lane, v_lane; // this lane's byte offsets inside a block
   };
-  // record of ticket tk (a scalar load: tk is wave-uniform)
-  auto load_rec = [&](int tk) { return p.dec_recs[tk / p.Hkv]; };
+  // Record of ticket tk.  The records are written by the plan launch and only
+  // read here, so they are read through the constant address space: with tk
+  // wave-uniform that is a scalar load, and waiting for it does not wait for
+  // the vector loads in flight (vector loads complete in order, so a record
+  // fetched with one would drain the block prefetch at every item).
+  auto load_rec = [&](int tk) {
+    const __attribute__((address_space(4))) int* r =
+        (const __attribute__((address_space(4))) int*)(const void*)p.dec_recs + 4 * (tk / p.Hkv);
+    return make_int4(r[0], r[1], r[2], r[3]);
+  };
   auto make_item = [&](int tk, int4 r, Item& it) {
     it.g = tk % p.Hkv;
     it.s = r.x;
@@ -152,21 +166,28 @@ __global__ __launch_bounds__(kDecodeThreads, kMfmaWavesPerSimd) void decode_part
     it.k_lane = (int)(h * tok_bytes + (it.g * D + 8 * j) * 2);
     it.v_lane = (int)(4 * j * tok_bytes + (it.g * D + EPL * h) * 2);
   };
-  // ids of the wave's blocks b_begin + wave + NWAVE*k, one per lane (a vector load)
+  // ids of the wave's blocks b_begin + wave + NWAVE*k, one per lane (a vector
+  // load through a resource over the sequence's table row; lanes past the row
+  // read 0).  Only lanes k < nmine are ever used, so the load needs no branch,
+  // and its register is written by loads alone, which complete in order: a
+  // conditional default value would make the compiler wait for every load in
+  // flight before overwriting it.
   auto load_ids = [&](Item& it) {
-    const int32_t* trow = p.tables + (int64_t)it.s * p.MB;
-    it.my_id = lane < it.nmine ? trow[it.b_begin + wave + NWAVE * lane] : -1;
+    const __amdgpu_buffer_rsrc_t tr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<int32_t*>(p.tables + (int64_t)it.s * p.MB), (short)0, p.MB * 4, kRawBufferWord3);
+    it.my_id = (int)__builtin_amdgcn_raw_buffer_load_b32(tr, (it.b_begin + wave + NWAVE * lane) * 4, 0, 0);
   };
 
-  // q as the B operand of the score MFMAs (columns >= G are zero).
+  // q as the B operand of the score MFMAs.  The resource covers the group's G
+  // rows; lanes of columns h >= G point past it and read zeros (no branch).
   bf16x8 qf[NKC];
   auto load_q = [&](const Item& it) {
-    const char* qrow = reinterpret_cast<const char*>(p.q) + (it.row0 + min(h, G - 1)) * D * 2;
+    const __amdgpu_buffer_rsrc_t qr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<char*>(reinterpret_cast<const char*>(p.q) + it.row0 * D * 2), (short)0, G * D * 2,
+        kRawBufferWord3);
+    const int off = h < G ? (h * D + 8 * j) * 2 : G * D * 2;
 #pragma unroll
-    for (int c = 0; c < NKC; ++c) {
-      const uint4 r = h < G ? load16(qrow + (32 * c + 8 * j) * 2) : make_uint4(0, 0, 0, 0);
-      qf[c] = __builtin_bit_cast(bf16x8, r);
-    }
+    for (int c = 0; c < NKC; ++c) qf[c] = __builtin_bit_cast(bf16x8, buffer_load16(qr, off + 64 * c, 0));
   };
 
   struct Blk {
@@ -250,18 +271,16 @@ __global__ __launch_bounds__(kDecodeThreads, kMfmaWavesPerSimd) void decode_part
   __shared__ float s_m[2][kItemParts][NWAVE][G];
   __shared__ float s_l[2][kItemParts][NWAVE][G];
   __shared__ float s_o[2][kItemParts][NWAVE][G][D];
-  __shared__ int s_ticket[4];  // [0], [1]: by item parity; [2], [3]: the first two
+  __shared__ int s_ticket[2];  // by item parity
 
   // Tickets run two items ahead: while item i is computed the wave already
   // holds item i+1's record and block ids, and thread 0 is fetching ticket i+2.
-  if (threadIdx.x == 0) {
-    s_ticket[2] = atomicAdd(&p.sched[0], 1);
-    s_ticket[3] = atomicAdd(&p.sched[0], 1);
-  }
-  __syncthreads();
-  const int tk0 = __builtin_amdgcn_readfirstlane(s_ticket[2]);
+  // Each workgroup's first two tickets are static (blockIdx.x and blockIdx.x +
+  // gridDim.x); the counter hands out the rest, from 2 * gridDim.x on, so the
+  // launch does not start with every workgroup queueing on one atomic.
+  const int tk0 = blockIdx.x;
   if (tk0 >= total) return;
-  int tk1 = __builtin_amdgcn_readfirstlane(s_ticket[3]);
+  int tk1 = blockIdx.x + gridDim.x;
   bool have1 = tk1 < total;
 
   // NBUF-deep software pipeline over an item's blocks: blocks k+1 .. k+NBUF-1
@@ -277,13 +296,58 @@ __global__ __launch_bounds__(kDecodeThreads, kMfmaWavesPerSimd) void decode_part
   for (int u = 0; u < NBUF - 1; ++u) issue(cur, u, buf[u]);
   int4 rec1 = have1 ? load_rec(tk1) : make_int4(0, 0, 0, 0);
 
-  for (int parity = 0;; parity ^= 1) {
+  // Cross-wave merge of a finished item whose wave states are in LDS half
+  // `par`: per (partition, head, dim), the four waves' states combined by
+  // log-sum-exp; written to out (single-partition context) or to the partials.
+  // Each wave takes a quarter of the elements.
+  auto merge = [&](const Item& it, int par) {
+    const int nslots = it.two ? 2 : 1;
+    for (int idx = threadIdx.x; idx < nslots * G * D; idx += kDecodeThreads) {
+      const int slot = idx / (G * D);
+      const int hh = (idx / D) % G;
+      const int d = idx % D;
+      float M = -INFINITY;
+#pragma unroll
+      for (int w = 0; w < NWAVE; ++w) M = fmaxf(M, s_m[par][slot][w][hh]);
+      float L = 0.f, O = 0.f;
+      if (M != -INFINITY) {
+#pragma unroll
+        for (int w = 0; w < NWAVE; ++w) {
+          const float f = exp2_fast(s_m[par][slot][w][hh] - M);
+          L = fmaf(s_l[par][slot][w][hh], f, L);
+          O = fmaf(s_o[par][slot][w][hh][d], f, O);
+        }
+      }
+      const float r = L > 0.f ? O / L : 0.f;
+      if (it.nparts == 1) {
+        store_out<true>(p.out, (it.row0 + hh) * D + d, r);
+      } else {
+        const int64_t pr = (it.row0 + hh) * p.max_parts + it.part + slot;
+        p.part_o[pr * D + d] = r;
+        if (d == 0) {
+          p.part_m[pr] = M;
+          p.part_l[pr] = L;
+        }
+      }
+    }
+  };
+
+  // The merge of item i runs inside item i+1's block loop, right after the
+  // wave's first block: there its LDS reads and output stores overlap with the
+  // loads in flight instead of holding the whole workgroup after the barrier.
+  // Item i+1's closing barrier orders it before item i+2 reuses LDS half i%2.
+  Item prev;
+  bool pending = false;
+  int parity = 0;
+  for (;; parity ^= 1) {
     if (have1) {
       make_item(tk1, rec1, nxt);
       load_ids(nxt);
     }
-    int tk2 = 0;
-    if (threadIdx.x == 0) tk2 = atomicAdd(&p.sched[0], 1);
+    // (left unset in other lanes: like the ids, its register is written by the
+    // atomic alone, so nothing waits for the loads in flight before it is issued)
+    int fetched;
+    if (threadIdx.x == 0) fetched = 2 * (int)gridDim.x + atomicAdd(&p.sched[0], 1);
 
     // Wave state of one partition to LDS (the item's partitions meet at the
     // barrier), then a fresh state.  The wave's k-th block is block wave + 4k of
@@ -322,8 +386,19 @@ __global__ __launch_bounds__(kDecodeThreads, kMfmaWavesPerSimd) void decode_part
         }
         issue(cur, r * NBUF + u + NBUF - 1, buf[(u + NBUF - 1) % NBUF]);
         compute(buf[u]);
+        if (u == 0 && r == 0 && pending) {
+          merge(prev, parity ^ 1);
+          pending = false;
+        }
       }
     }
+    if (pending) {  // the wave had no block in this item
+      merge(prev, parity ^ 1);
+      pending = false;
+    }
+    // The ticket goes to LDS while only the zero-sized tail loads are in
+    // flight: waiting for the atomic here waits for nothing else.
+    if (threadIdx.x == 0) s_ticket[parity] = fetched;
 
     // The next item's q and first blocks go out before this item's merge.
     const Item done = cur;
@@ -336,46 +411,19 @@ __global__ __launch_bounds__(kDecodeThreads, kMfmaWavesPerSimd) void decode_part
 
     if (!saved0) save(0);  // this wave ended inside the first partition
     if (done.two) save(1);
-    if (threadIdx.x == 0) s_ticket[parity] = tk2;
     __syncthreads();
-    tk2 = __builtin_amdgcn_readfirstlane(s_ticket[parity]);
+    const int tk2 = __builtin_amdgcn_readfirstlane(s_ticket[parity]);
     const bool have2 = have1 && tk2 < total;
     const int4 rec2 = have2 ? load_rec(tk2) : make_int4(0, 0, 0, 0);
 
-    const int nslots = done.two ? 2 : 1;
-    for (int idx = threadIdx.x; idx < nslots * G * D; idx += kDecodeThreads) {
-      const int slot = idx / (G * D);
-      const int hh = (idx / D) % G;
-      const int d = idx % D;
-      float M = -INFINITY;
-#pragma unroll
-      for (int w = 0; w < NWAVE; ++w) M = fmaxf(M, s_m[parity][slot][w][hh]);
-      float L = 0.f, O = 0.f;
-      if (M != -INFINITY) {
-#pragma unroll
-        for (int w = 0; w < NWAVE; ++w) {
-          const float f = exp2_fast(s_m[parity][slot][w][hh] - M);
-          L = fmaf(s_l[parity][slot][w][hh], f, L);
-          O = fmaf(s_o[parity][slot][w][hh][d], f, O);
-        }
-      }
-      const float r = L > 0.f ? O / L : 0.f;
-      if (done.nparts == 1) {
-        store_out<true>(p.out, (done.row0 + hh) * D + d, r);
-      } else {
-        const int64_t pr = (done.row0 + hh) * p.max_parts + done.part + slot;
-        p.part_o[pr * D + d] = r;
-        if (d == 0) {
-          p.part_m[pr] = M;
-          p.part_l[pr] = L;
-        }
-      }
-    }
+    prev = done;
+    pending = true;
     if (!have1) break;
     tk1 = tk2;
     have1 = have2;
     rec1 = rec2;
   }
+  merge(prev, parity);  // the last item (its closing barrier has passed)
 }
 
 template <int D, int G>
