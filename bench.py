@@ -19,10 +19,10 @@ rotated step to step so each step's KV reads come from HBM, not the 256 MiB
 last-level cache.
 
 Prints ONE JSON line.  The partition kernel's duration comes from two HIP
-events recorded on the compute stream around it in every timed step (each
-timing event costs the stream a few microseconds, so the write and merge are
-not bracketed there); the write and merge durations come from a few extra
-steps after the timed region, with events around every launch.
+events recorded on the compute stream around it in every EV_EVERY-th timed
+step (each timing event costs the stream a few microseconds, so the write and
+merge are not bracketed there); the write and merge durations come from a few
+extra steps after the timed region, with events around every launch.
 """
 
 import argparse
@@ -37,6 +37,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
+EV_EVERY = 4                                            # timed steps per event-bracketed launch
 METRIC = "decode tokens/s + KV-read HBM GB/s (% of MI355X peak), bf16 GQA ctx 2k–8k"
 HBM_PEAK_GBPS = 8000.0
 DEFAULT_WORKLOAD = "gqa32x8_bf16_s128_ctx512_8192"
@@ -50,7 +51,7 @@ COPY_PROBE_BYTES = 512 * 1024 * 1024   # pkv_copy_blocks in --copy-probe: read a
 def parse_args():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--seed", type=int, default=1002)
@@ -67,17 +68,27 @@ def parse_args():
     return ap.parse_args()
 
 
-def traffic_from_counters(paths, workload):
+def traffic_from_counters(paths, workload, W, K):
     """Per-launch HBM bytes of the partition kernel from rocprofv3 --pmc CSVs.
 
     FETCH_SIZE / WRITE_SIZE (KiB per dispatch) are scaled by what they read for
-    the copy probe, whose bytes are known (COPY_PROBE_BYTES each way).
+    the copy probe, whose bytes are known (COPY_PROBE_BYTES each way).  The
+    counted run must use the same --warmup W and --steps K as the bench line
+    that reports the figure: the average is taken over the same launches the
+    bench brackets with events (timed steps 0, EV_EVERY, ... after W warmup
+    steps), so it compares with their algorithmic bytes.
     """
     import csv
 
-    def mean_kib(path, kernel_part):
-        vals = [float(r["Counter_Value"]) for r in csv.DictReader(open(path))
-                if kernel_part in r["Kernel_Name"]]
+    def mean_kib(path, kernel_part, pick=None):
+        rows = sorted(((int(r["Dispatch_Id"]), float(r["Counter_Value"]))
+                       for r in csv.DictReader(open(path)) if kernel_part in r["Kernel_Name"]))
+        vals = [v for _, v in rows]
+        if pick is not None:
+            if len(vals) < W + K:
+                raise SystemExit(f"{path}: {len(vals)} dispatches of {kernel_part}, "
+                                 f"fewer than --warmup {W} + --steps {K}")
+            vals = [vals[W + k] for k in range(0, K, EV_EVERY)]
         if not vals:
             raise SystemExit(f"{path}: no dispatch of {kernel_part}")
         return sum(vals) / len(vals)
@@ -85,10 +96,10 @@ def traffic_from_counters(paths, workload):
     fetch, write, cfetch, cwrite = paths
     kf = COPY_PROBE_BYTES / (mean_kib(cfetch, "copy_blocks_kernel") * 1024)
     kw = COPY_PROBE_BYTES / (mean_kib(cwrite, "copy_blocks_kernel") * 1024)
-    fb = mean_kib(fetch, "decode_partition_mfma_kernel") * 1024 * kf
-    wb = mean_kib(write, "decode_partition_mfma_kernel") * 1024 * kw
+    fb = mean_kib(fetch, "decode_partition_mfma_kernel", pick=True) * 1024 * kf
+    wb = mean_kib(write, "decode_partition_mfma_kernel", pick=True) * 1024 * kw
     out = {"kernel": "decode_partition_mfma_kernel", "workload": workload,
-           "kernel_source_sha256": kernel_source_hash(),
+           "kernel_source_sha256": kernel_source_hash(), "warmup": W, "steps": K,
            "fetch_bytes_per_launch": int(fb), "write_bytes_per_launch": int(wb),
            "traffic_bytes_per_launch": int(fb + wb),
            "fetch_scale": round(kf, 4), "write_scale": round(kw, 4)}
@@ -128,7 +139,7 @@ def copy_probe(torch, pkv):
 def main():
     args = parse_args()
     if args.traffic_from:
-        return traffic_from_counters(args.traffic_from, args.workload)
+        return traffic_from_counters(args.traffic_from, args.workload, args.warmup, args.steps)
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU only: --gpus {args.gpus} (WORLD_SIZE={world}) is not "
@@ -256,7 +267,8 @@ def main():
         check("pkv_attention_decode_plan", L.pkv_attention_decode_plan(*attn_args(i, b, r, side_h)))
         plan_done[b].record(side)
         main.wait_event(h2d_done[b])
-        ev = events[i - W] if timed or detail else None
+        bracket = detail or (timed and (i - W) % EV_EVERY == 0)
+        ev = events[i - W] if bracket else None
         if detail:
             ev[0].record(main)
         if len(pairs):
@@ -264,11 +276,11 @@ def main():
         check("pkv_write", L.pkv_write(kc_p[r], vc_p[r], knew0 + i * kv_stride, vnew0 + i * kv_stride,
                                        dptr[b], S, nb, 16, Hkv, D, dt, main_h))
         main.wait_event(plan_done[b])
-        if timed or detail:
+        if bracket:
             ev[1].record(main)
         args_m = attn_args(i, b, r, main_h)
         check("pkv_attention_decode_partitions", L.pkv_attention_decode_partitions(*args_m))
-        if timed or detail:
+        if bracket:
             ev[2].record(main)
         check("pkv_attention_decode_merge", L.pkv_attention_decode_merge(*args_m))
         if detail:
@@ -291,7 +303,8 @@ def main():
     torch.cuda.synchronize()
 
     # ---- per-kernel durations and algorithmic bytes --------------------------
-    t_part = [e[1].elapsed_time(e[2]) * 1e-3 for e in events[:K]]
+    timed_ev = list(range(0, K, EV_EVERY))             # timed steps whose launch was bracketed
+    t_part = [events[k][1].elapsed_time(events[k][2]) * 1e-3 for k in timed_ev]
     t_write = [e[0].elapsed_time(e[1]) * 1e-3 for e in events[K:]]   # includes the wait for the plan
     t_merge = [e[2].elapsed_time(e[3]) * 1e-3 for e in events[K:]]
     kv_b, part_b, merge_b = [], [], []
@@ -306,8 +319,8 @@ def main():
         part_b.append(kv + q_out + meta + partials)
         merge_b.append(partials + int((nparts > 1).sum()) * Hq * D * es + 4 * S)
     sum_tp = sum(t_part)
-    achieved = sum(part_b) / sum_tp / 1e9
-    kv_gbps = sum(kv_b) / sum_tp / 1e9
+    achieved = sum(part_b[k] for k in timed_ev) / sum_tp / 1e9
+    kv_gbps = sum(kv_b[k] for k in timed_ev) / sum_tp / 1e9
     ms_per_step = wall / K * 1e3
     value = S * K / wall
 
@@ -315,7 +328,8 @@ def main():
     if os.path.exists(TRAFFIC_FILE):
         with open(TRAFFIC_FILE) as f:
             tr = json.load(f)
-        if tr.get("kernel_source_sha256") == kernel_source_hash() and tr.get("workload") == spec.name:
+        if (tr.get("kernel_source_sha256") == kernel_source_hash() and tr.get("workload") == spec.name
+                and tr.get("warmup") == W and tr.get("steps") == K):
             traffic = tr.get("traffic_bytes_per_launch")
 
     roofline = {
@@ -326,8 +340,9 @@ def main():
         "unit": "GB/s",
         "frac": round(achieved / HBM_PEAK_GBPS, 4),
         "traffic": traffic,
-        "algorithmic_bytes_per_launch": int(np.mean(part_b)),
-        "avg_launch_us": round(sum_tp / K * 1e6, 2),
+        "algorithmic_bytes_per_launch": int(np.mean([part_b[k] for k in timed_ev])),
+        "avg_launch_us": round(sum_tp / len(timed_ev) * 1e6, 2),
+        "launches_timed": len(timed_ev),
     }
 
     # ---- CPU oracle baseline (bounded sample of the same batch) --------------

@@ -60,6 +60,9 @@
 #ifndef PKV_MFMA_WAVES
 #define PKV_MFMA_WAVES 2
 #endif
+#ifndef PKV_MFMA_THREADS
+#define PKV_MFMA_THREADS 256
+#endif
 
 namespace pkv {
 
@@ -78,6 +81,8 @@ constexpr int kMfmaWavesPerSimd = PKV_MFMA_WAVES;
 // pipelined workgroups keep the same bytes in flight and finish each item
 // sooner, which shortens the end-of-run tail of the ticket schedule.
 constexpr int kMfmaWgPerCu = PKV_MFMA_WG_PER_CU;
+// Threads per workgroup: the waves of a workgroup split each item's blocks.
+constexpr int kMfmaThreads = PKV_MFMA_THREADS;
 
 // One lane's share of a V row load: head_dim / 16 bf16 values.
 template <int D> struct VPiece;
@@ -113,15 +118,17 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
 // the zero-sized tail loads are outstanding (vector memory operations complete
 // in order, so any earlier wait would drain the prefetch).
 template <int D, int G>
-__global__ __launch_bounds__(kDecodeThreads, kMfmaWavesPerSimd) void decode_partition_mfma_kernel(
+__global__ __launch_bounds__(kMfmaThreads, kMfmaWavesPerSimd) void decode_partition_mfma_kernel(
     DecodeParams p) {
   constexpr int EPL = D / 16;            // dims per lane in one V row load
   constexpr int WPL = EPL / 2;           // 32-bit words per V row load
   constexpr int NKC = D / 32;            // 16x16x32 MFMAs per block for the scores
-  constexpr int NWAVE = kDecodeWaves;
+  constexpr int NWAVE = kMfmaThreads / kWave;
   constexpr int NBUF = kMfmaPipelineDepth;
   using VT = typename VPiece<D>::T;
   static_assert(G >= 1 && G <= 16, "the q heads of one KV head fill at most 16 MFMA columns");
+  static_assert(kPartBlocks % NWAVE == 0 && kItemBlocks / NWAVE <= kWave,
+                "each wave holds its block ids of an item in one register");
 
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -136,7 +143,7 @@ __global__ __launch_bounds__(kDecodeThreads, kMfmaWavesPerSimd) void decode_part
   // One work item as this wave sees it.
   struct Item {
     int s, part, g, ctx, nparts, b_begin, nmine;  // part: first of the item's partitions
-    bool two;                                      // the item has a second partition
+    int nslots;                                    // partitions the item covers (1 .. kItemParts)
     int64_t row0;       // first q head (row of q / out) of the KV head group
     int my_id;          // lane k < nmine: id of the wave's k-th block
     int k_lane, v_lane; // this lane's byte offsets inside a block
@@ -160,7 +167,7 @@ __global__ __launch_bounds__(kDecodeThreads, kMfmaWavesPerSimd) void decode_part
     const int nblk = (it.ctx + kBlockTokens - 1) / kBlockTokens;
     it.b_begin = it.part * kPartBlocks;
     const int in_item = min(kItemBlocks, nblk - it.b_begin);
-    it.two = in_item > kPartBlocks;
+    it.nslots = max(1, (in_item + kPartBlocks - 1) / kPartBlocks);
     it.nmine = max(0, (in_item - wave + NWAVE - 1) / NWAVE);
     it.row0 = (int64_t)r.w * Hq + (int64_t)it.g * G;  // r.w: the sequence's query row
     it.k_lane = (int)(h * tok_bytes + (it.g * D + 8 * j) * 2);
@@ -301,8 +308,8 @@ __global__ __launch_bounds__(kDecodeThreads, kMfmaWavesPerSimd) void decode_part
   // log-sum-exp; written to out (single-partition context) or to the partials.
   // Each wave takes a quarter of the elements.
   auto merge = [&](const Item& it, int par) {
-    const int nslots = it.two ? 2 : 1;
-    for (int idx = threadIdx.x; idx < nslots * G * D; idx += kDecodeThreads) {
+    const int nslots = it.nslots;
+    for (int idx = threadIdx.x; idx < nslots * G * D; idx += kMfmaThreads) {
       const int slot = idx / (G * D);
       const int hh = (idx / D) % G;
       const int d = idx % D;
@@ -347,11 +354,12 @@ __global__ __launch_bounds__(kDecodeThreads, kMfmaWavesPerSimd) void decode_part
     // (left unset in other lanes: like the ids, its register is written by the
     // atomic alone, so nothing waits for the loads in flight before it is issued)
     int fetched;
-    if (threadIdx.x == 0) fetched = 2 * (int)gridDim.x + atomicAdd(&p.sched[0], 1);
+    if (threadIdx.x == 0) fetched = atomicAdd(&p.sched[0], 1);  // offset added where it is read
 
     // Wave state of one partition to LDS (the item's partitions meet at the
     // barrier), then a fresh state.  The wave's k-th block is block wave + 4k of
-    // the item, so its blocks k < kSplit belong to the first partition.
+    // the item, so its blocks kSplit*i .. kSplit*(i+1) - 1 belong to the item's
+    // partition i.
     constexpr int kSplit = kPartBlocks / NWAVE;
     auto reset = [&]() {
       m = -INFINITY;
@@ -375,15 +383,13 @@ __global__ __launch_bounds__(kDecodeThreads, kMfmaWavesPerSimd) void decode_part
       reset();
     };
     reset();
-    bool saved0 = false;
+    int saved = 0;  // partitions of this item whose state the wave has stored
     const int rounds = (cur.nmine + NBUF - 1) / NBUF;
     for (int r = 0; r < rounds; ++r) {
 #pragma unroll
       for (int u = 0; u < NBUF; ++u) {
-        if (r * NBUF + u == kSplit) {  // uniform: first block of the second partition
-          save(0);
-          saved0 = true;
-        }
+        const int k = r * NBUF + u;
+        if (k > 0 && k % kSplit == 0 && saved < kItemParts) save(saved++);  // uniform
         issue(cur, r * NBUF + u + NBUF - 1, buf[(u + NBUF - 1) % NBUF]);
         compute(buf[u]);
         if (u == 0 && r == 0 && pending) {
@@ -409,10 +415,10 @@ __global__ __launch_bounds__(kDecodeThreads, kMfmaWavesPerSimd) void decode_part
       for (int u = 0; u < NBUF - 1; ++u) issue(cur, u, buf[u]);
     }
 
-    if (!saved0) save(0);  // this wave ended inside the first partition
-    if (done.two) save(1);
+    // the partition the wave ended in, and empty states for any it never reached
+    while (saved < done.nslots) save(saved++);
     __syncthreads();
-    const int tk2 = __builtin_amdgcn_readfirstlane(s_ticket[parity]);
+    const int tk2 = 2 * (int)gridDim.x + __builtin_amdgcn_readfirstlane(s_ticket[parity]);
     const bool have2 = have1 && tk2 < total;
     const int4 rec2 = have2 ? load_rec(tk2) : make_int4(0, 0, 0, 0);
 
@@ -432,13 +438,13 @@ int launch_mfma_t(const DecodeParams& p, const DecodeArgs& a, hipStream_t st) {
   if (per_cu == 0) {
     int n = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_partition_mfma_kernel<D, G>,
-                                                     kDecodeThreads, 0) != hipSuccess || n < 1)
+                                                     kMfmaThreads, 0) != hipSuccess || n < 1)
       n = 1;
     per_cu = n;
   }
   const int64_t items = (int64_t)a.dec_cap * a.num_kv_heads;  // upper bound
   const int64_t grid = std::min<int64_t>(items, (int64_t)a.num_cus * std::min(per_cu, kMfmaWgPerCu));
-  hipLaunchKernelGGL((decode_partition_mfma_kernel<D, G>), dim3((unsigned)grid), dim3(kDecodeThreads),
+  hipLaunchKernelGGL((decode_partition_mfma_kernel<D, G>), dim3((unsigned)grid), dim3(kMfmaThreads),
                      0, st, p);
   return (int)hipGetLastError();
 }

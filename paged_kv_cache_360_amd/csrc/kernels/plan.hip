@@ -11,10 +11,10 @@
 //
 // Outputs (all in the caller's workspace):
 //  * decode records {sequence, first partition, context, query row}, one per
-//    pair of consecutive partitions (kItemParts): every pair but a sequence's
-//    last (both full, 64 blocks) first, then each sequence's last item in
-//    decreasing block count (a counting sort over the 65 possible counts), so
-//    the persistent run ends on its shortest items;
+//    kItemParts consecutive partitions: every item but a sequence's last (all
+//    full, kItemBlocks blocks) first, then each sequence's last item in
+//    decreasing block count (a counting sort over the kItemBlocks + 1 possible
+//    counts), so the persistent run ends on its shortest items;
 //  * prefill records, two int4 each: {sequence, partition, context, first query
 //    row} and {rows, ctx - q + r0 + 1, 0, 0} (row i of the group sees max(0, that
 //    + i) keys; negative when the chunk is longer than the context); one per (group of
@@ -39,7 +39,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(
     int32_t ctx_cap, int32_t Hkv, int32_t rows_per_item, int32_t dec_cap, int32_t pre_cap,
     int32_t* __restrict__ sched, int4* __restrict__ dec, int4* __restrict__ pre,
     int32_t* __restrict__ row_keys) {
-  constexpr int NBK = kItemBlocks + 1;  // buckets: last-item block count 64 .. 0
+  constexpr int NBK = kItemBlocks + 1;  // buckets: last-item block count kItemBlocks .. 0
   __shared__ int32_t s_full[kPlanThreads];
   __shared__ int32_t s_pre[kPlanThreads];
   __shared__ int32_t s_bucket[NBK];
@@ -53,7 +53,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(
   auto first_row = [&](int s) { return qsl ? min(max(qsl[s], 0), T) : s; };
   auto rows_of = [&](int s) { return qsl ? max(0, min(qsl[s + 1], T) - first_row(s)) : 1; };
   auto items_of = [&](int n) { return (n + kItemParts - 1) / kItemParts; };
-  auto last_bucket = [&](int c, int n) {  // 0 for a full last item, 64 for an empty one
+  auto last_bucket = [&](int c, int n) {  // 0 for a full last item, kItemBlocks for an empty one
     return kItemBlocks - ((c + kBlockTokens - 1) / kBlockTokens - (items_of(n) - 1) * kItemBlocks);
   };
   // prefill: the keys seen by row r of a sequence with q rows and c keys
