@@ -10,9 +10,10 @@ path included:
      pkv_attention_decode_plan (work list from the lengths) on the same side
      stream, joined to the compute stream by events, so the plan overlaps 3-4;
   3. pkv_copy_blocks for any copy-on-write pairs (none for unshared batches);
-  4. pkv_write of the new tokens' K/V;
-  5. pkv_attention_decode_partitions (split-context decode, the dominant kernel);
-  6. pkv_attention_decode_merge (log-sum-exp merge of multi-partition sequences).
+  4. bf16: pkv_attention_decode_partitions_append (split-context decode, the
+     dominant kernel, which also stores each sequence's new K/V row in the cache);
+     fp32: pkv_write of the new tokens' K/V, then pkv_attention_decode_partitions;
+  5. pkv_attention_decode_merge (log-sum-exp merge of multi-partition sequences).
 Contexts grow by one token per step, as in real decoding.  Inputs (pool, q, new
 K/V rows) are resident in HBM before timing starts.  R copies of the KV pool are
 rotated step to step so each step's KV reads come from HBM, not the 256 MiB
@@ -20,8 +21,8 @@ last-level cache.
 
 Prints ONE JSON line.  The partition kernel's duration comes from two HIP
 events recorded on the compute stream around it in every EV_EVERY-th timed
-step (each timing event costs the stream a few microseconds, so the write and
-merge are not bracketed there); the write and merge durations come from a few
+step (each timing event costs the stream a few microseconds, so the other
+launches are not bracketed there); the write (fp32) and merge durations come from a few
 extra steps after the timed region, with events around every launch.
 """
 
@@ -240,6 +241,7 @@ def main():
     kc_p = [t.data_ptr() for t in kcs]
     vc_p = [t.data_ptr() for t in vcs]
     check = pkv.check
+    fused = spec.dtype == "bf16"                        # the append form is bf16
     host_alloc_s = []
     host_step_s = []
 
@@ -266,20 +268,27 @@ def main():
         # the work list needs only the lengths: it runs beside the write
         check("pkv_attention_decode_plan", L.pkv_attention_decode_plan(*attn_args(i, b, r, side_h)))
         plan_done[b].record(side)
-        main.wait_event(h2d_done[b])
+        # (plan_done follows the copy on the side stream, so it orders both)
         bracket = detail or (timed and (i - W) % EV_EVERY == 0)
         ev = events[i - W] if bracket else None
         if detail:
             ev[0].record(main)
         if len(pairs):
             pkv.pkv_copy_blocks(kcs[r], vcs[r], torch.from_numpy(pairs).cuda())
-        check("pkv_write", L.pkv_write(kc_p[r], vc_p[r], knew0 + i * kv_stride, vnew0 + i * kv_stride,
-                                       dptr[b], S, nb, 16, Hkv, D, dt, main_h))
+        if not fused:
+            main.wait_event(h2d_done[b])                # the write reads the slots
+            check("pkv_write", L.pkv_write(kc_p[r], vc_p[r], knew0 + i * kv_stride, vnew0 + i * kv_stride,
+                                           dptr[b], S, nb, 16, Hkv, D, dt, main_h))
         main.wait_event(plan_done[b])
         if bracket:
             ev[1].record(main)
         args_m = attn_args(i, b, r, main_h)
-        check("pkv_attention_decode_partitions", L.pkv_attention_decode_partitions(*args_m))
+        if fused:   # the new K/V rows go to the cache inside the partition launch
+            a = args_m
+            check("pkv_attention_decode_partitions_append", L.pkv_attention_decode_partitions_append(
+                a[0], a[1], knew0 + i * kv_stride, vnew0 + i * kv_stride, *a[2:]))
+        else:
+            check("pkv_attention_decode_partitions", L.pkv_attention_decode_partitions(*args_m))
         if bracket:
             ev[2].record(main)
         check("pkv_attention_decode_merge", L.pkv_attention_decode_merge(*args_m))
@@ -305,7 +314,8 @@ def main():
     # ---- per-kernel durations and algorithmic bytes --------------------------
     timed_ev = list(range(0, K, EV_EVERY))             # timed steps whose launch was bracketed
     t_part = [events[k][1].elapsed_time(events[k][2]) * 1e-3 for k in timed_ev]
-    t_write = [e[0].elapsed_time(e[1]) * 1e-3 for e in events[K:]]   # includes the wait for the plan
+    # write (fp32) or nothing (bf16: fused), plus any wait for the plan on the side stream
+    t_write = [e[0].elapsed_time(e[1]) * 1e-3 for e in events[K:]]
     t_merge = [e[2].elapsed_time(e[3]) * 1e-3 for e in events[K:]]
     kv_b, part_b, merge_b = [], [], []
     for lens in step_lens:
@@ -315,8 +325,10 @@ def main():
         q_out = S * Hq * D * es + int((nparts == 1).sum()) * Hq * D * es
         meta = int((4 * -(-lens // 16)).sum()) + 4 * S
         partials = int(nparts[nparts > 1].sum()) * Hq * (D + 2) * 4
+        # append form: the new K/V rows are read from the inputs and stored to the cache
+        append = 4 * S * Hkv * D * es if fused else 0
         kv_b.append(kv)
-        part_b.append(kv + q_out + meta + partials)
+        part_b.append(kv + q_out + meta + partials + append)
         merge_b.append(partials + int((nparts > 1).sum()) * Hq * D * es + 4 * S)
     sum_tp = sum(t_part)
     achieved = sum(part_b[k] for k in timed_ev) / sum_tp / 1e9
@@ -333,7 +345,8 @@ def main():
             traffic = tr.get("traffic_bytes_per_launch")
 
     roofline = {
-        "kernel": "decode_partition_mfma_kernel (pkv_attention_decode_partitions)",
+        "kernel": ("decode_partition_mfma_kernel (pkv_attention_decode_partitions_append)" if fused
+                   else "decode_partition_kernel (pkv_attention_decode_partitions)"),
         "bound": "hbm",
         "achieved": round(achieved, 1),
         "peak": HBM_PEAK_GBPS,
@@ -375,7 +388,7 @@ def main():
         "kv_read_GBps": round(kv_gbps, 1),
         "kv_read_frac_of_peak": round(kv_gbps / HBM_PEAK_GBPS, 4),
         "kernels_us": {
-            "write": round(float(np.mean(t_write)) * 1e6, 2),
+            ("plan_wait" if fused else "write"): round(float(np.mean(t_write)) * 1e6, 2),
             "decode_partitions": round(float(np.mean(t_part)) * 1e6, 2),
             "merge": round(float(np.mean(t_merge)) * 1e6, 2),
         },

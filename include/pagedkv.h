@@ -156,6 +156,43 @@ int pkv_attention_decode_merge(void* out, const void* q, const void* key_cache,
                                int32_t max_context_len, pkv_dtype dt, void* workspace,
                                size_t workspace_bytes, void* stream);
 
+/* Decode step with the cache append in the same launch (bf16).
+ *
+ * Same result as pkv_write of each sequence's new token followed by
+ * pkv_attention_decode, byte for byte, in one launch fewer: the new token is
+ * the last of the context (position context_lens[s] - 1, slot
+ * block_tables[s][(ctx - 1) / 16] * 16 + (ctx - 1) % 16, the slot the allocator
+ * hands out for a decode append); the partition launch reads its K/V from
+ * k_new / v_new instead of the cache and writes them to that slot.  The pages
+ * write new K/V into the cache first and read them back ("How vLLM Works?",
+ * section 01; "vLLM and PagedAttention", §2); this folds the write into the
+ * work item that reads that block.
+ *
+ *   k_new, v_new          device [num_seqs, num_kv_heads, head_dim] bf16, 16-byte aligned
+ *   key_cache, value_cache  written at the new tokens' slots only
+ *   other arguments       as pkv_attention_decode (dt must be PKV_BF16)
+ * A sequence with context_lens[s] == 0 appends nothing; one whose context exceeds
+ * max_context_len (clamped) appends nothing.  The slot's block id must lie in
+ * [0, num_blocks), else nothing is written there.
+ * _partitions_append is the partition launch of this form (after
+ * pkv_attention_decode_plan, before pkv_attention_decode_merge, same workspace).
+ * Errors as pkv_attention_decode; PKV_EUNSUPPORTED for dt other than bf16. */
+int pkv_attention_decode_append(void* out, const void* q, const void* k_new, const void* v_new,
+                                void* key_cache, void* value_cache, const int32_t* block_tables,
+                                const int32_t* context_lens, float scale, int32_t block_size,
+                                int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                int32_t num_seqs, int32_t max_blocks_per_seq, int32_t num_blocks,
+                                int32_t max_context_len, pkv_dtype dt, void* workspace,
+                                size_t workspace_bytes, void* stream);
+int pkv_attention_decode_partitions_append(void* out, const void* q, const void* k_new,
+                                           const void* v_new, void* key_cache, void* value_cache,
+                                           const int32_t* block_tables, const int32_t* context_lens,
+                                           float scale, int32_t block_size, int32_t num_q_heads,
+                                           int32_t num_kv_heads, int32_t head_dim, int32_t num_seqs,
+                                           int32_t max_blocks_per_seq, int32_t num_blocks,
+                                           int32_t max_context_len, pkv_dtype dt, void* workspace,
+                                           size_t workspace_bytes, void* stream);
+
 /* ------------------------------------------------------------------------ */
 /* Variable-length attention over the paged cache: decode rows and chunked
  * prefill rows in one call (bf16 only).

@@ -16,6 +16,8 @@ from .ops import (  # noqa: F401
     pkv_attention_decode_plan,
     pkv_attention_decode_partitions,
     pkv_attention_decode_merge,
+    pkv_attention_decode_append,
+    pkv_attention_decode_partitions_append,
     pkv_decode_workspace_bytes,
     decode_workspace,
     pkv_attention_varlen,

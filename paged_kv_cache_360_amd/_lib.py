@@ -42,6 +42,11 @@ SIGNATURES = {
                                                        _i32, _i32, _i32, _i32, ctypes.c_int, _p, _sz, _p]),
     "pkv_attention_decode_merge": (ctypes.c_int, [_p, _p, _p, _p, _p, _p, _f32, _i32, _i32, _i32, _i32,
                                                   _i32, _i32, _i32, _i32, ctypes.c_int, _p, _sz, _p]),
+    "pkv_attention_decode_append": (ctypes.c_int, [_p, _p, _p, _p, _p, _p, _p, _p, _f32, _i32, _i32, _i32,
+                                                   _i32, _i32, _i32, _i32, _i32, ctypes.c_int, _p, _sz, _p]),
+    "pkv_attention_decode_partitions_append": (ctypes.c_int, [_p, _p, _p, _p, _p, _p, _p, _p, _f32, _i32, _i32,
+                                                              _i32, _i32, _i32, _i32, _i32, _i32, ctypes.c_int,
+                                                              _p, _sz, _p]),
     "pkv_varlen_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32, _i32]),
     "pkv_attention_varlen": (ctypes.c_int, [_p, _p, _p, _p, _p, _p, _p, _i32, _i32, _f32, _i32, _i32, _i32,
                                             _i32, _i32, _i32, _i32, _i32, ctypes.c_int, _p, _sz, _p]),

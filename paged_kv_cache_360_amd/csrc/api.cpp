@@ -283,6 +283,64 @@ int pkv_attention_decode(PKV_DECODE_ARGS) {
   return pkv::launched(pkv::launch_decode_merge(a, stream), who);
 }
 
+#define PKV_APPEND_ARGS                                                                         \
+  void *out, const void *q, const void *k_new, const void *v_new, void *key_cache,               \
+      void *value_cache, const int32_t *block_tables, const int32_t *context_lens, float scale,   \
+      int32_t block_size, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,           \
+      int32_t num_seqs, int32_t max_blocks_per_seq, int32_t num_blocks, int32_t max_context_len, \
+      pkv_dtype dt, void *workspace, size_t workspace_bytes, void *stream
+
+namespace {
+// Validation shared by the append entries: the decode checks plus the new rows.
+int prepare_append(const char* who, pkv::DecodeArgs& a, PKV_APPEND_ARGS) {
+  (void)stream;
+  char msg[160];
+  if (dt != PKV_BF16) {
+    std::snprintf(msg, sizeof(msg), "%s: bf16 only", who);
+    return fail(PKV_EUNSUPPORTED, msg);
+  }
+  int rc = prepare_attention(who, a, PKV_DECODE_FWD);
+  if (rc != PKV_OK || num_seqs == 0) return rc;
+  if (!k_new || !v_new) {
+    std::snprintf(msg, sizeof(msg), "%s: null k_new / v_new", who);
+    return fail(PKV_EINVAL, msg);
+  }
+  if (!pkv::aligned16(k_new) || !pkv::aligned16(v_new)) {
+    std::snprintf(msg, sizeof(msg), "%s: k_new / v_new must be 16-byte aligned", who);
+    return fail(PKV_EINVAL, msg);
+  }
+  a.knew = k_new;
+  a.vnew = v_new;
+  return PKV_OK;
+}
+}  // namespace
+
+int pkv_attention_decode_partitions_append(PKV_APPEND_ARGS) {
+  pkv::DecodeArgs a{};
+  const char* who = "pkv_attention_decode_partitions_append";
+  int rc = prepare_append(who, a, out, q, k_new, v_new, key_cache, value_cache, block_tables,
+                          context_lens, scale, block_size, num_q_heads, num_kv_heads, head_dim,
+                          num_seqs, max_blocks_per_seq, num_blocks, max_context_len, dt, workspace,
+                          workspace_bytes, stream);
+  if (rc != PKV_OK || num_seqs == 0) return rc;
+  return pkv::launched(pkv::launch_decode_partitions(a, stream), who);
+}
+
+int pkv_attention_decode_append(PKV_APPEND_ARGS) {
+  pkv::DecodeArgs a{};
+  const char* who = "pkv_attention_decode_append";
+  int rc = prepare_append(who, a, out, q, k_new, v_new, key_cache, value_cache, block_tables,
+                          context_lens, scale, block_size, num_q_heads, num_kv_heads, head_dim,
+                          num_seqs, max_blocks_per_seq, num_blocks, max_context_len, dt, workspace,
+                          workspace_bytes, stream);
+  if (rc != PKV_OK || num_seqs == 0) return rc;
+  rc = pkv::launched(pkv::launch_plan(a, stream), who);
+  if (rc != PKV_OK) return rc;
+  rc = pkv::launched(pkv::launch_decode_partitions(a, stream), who);
+  if (rc != PKV_OK) return rc;
+  return pkv::launched(pkv::launch_decode_merge(a, stream), who);
+}
+
 int pkv_attention_varlen(void* out, const void* q, const void* key_cache, const void* value_cache,
                          const int32_t* block_tables, const int32_t* context_lens,
                          const int32_t* query_start_loc, int32_t num_tokens, int32_t max_query_len,

@@ -381,6 +381,8 @@ DecodeParams make_params(const DecodeArgs& a) {
   p.part_m = a.part_m;
   p.part_l = a.part_l;
   p.part_o = a.part_o;
+  p.knew = reinterpret_cast<const char*>(a.knew);
+  p.vnew = reinterpret_cast<const char*>(a.vnew);
   return p;
 }
 

@@ -47,6 +47,8 @@ struct DecodeParams {
   float* part_m;
   float* part_l;
   float* part_o;
+  const char* knew;      // append form: the new tokens' K [S, Hkv, D] (else null)
+  const char* vnew;      // and V
 };
 
 template <bool BF16>

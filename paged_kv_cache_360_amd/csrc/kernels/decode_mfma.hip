@@ -97,6 +97,14 @@ __device__ __forceinline__ uint32_t pair_hi(uint32_t a, uint32_t b) {
   return (a >> 16) | (b & 0xFFFF0000u);
 }
 
+// Per-lane choice between two register pieces.
+__device__ __forceinline__ uint4 pick(bool t, uint4 a, uint4 b) {
+  return make_uint4(t ? a.x : b.x, t ? a.y : b.y, t ? a.z : b.z, t ? a.w : b.w);
+}
+__device__ __forceinline__ uint2 pick(bool t, uint2 a, uint2 b) {
+  return make_uint2(t ? a.x : b.x, t ? a.y : b.y);
+}
+
 // Two fp32 values to a packed bf16 pair (round to nearest even).
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   const bf16x2 v = {(__bf16)a, (__bf16)b};
@@ -147,7 +155,14 @@ __global__ __launch_bounds__(kMfmaThreads, kMfmaWavesPerSimd) void decode_partit
     int64_t row0;       // first q head (row of q / out) of the KV head group
     int my_id;          // lane k < nmine: id of the wave's k-th block
     int k_lane, v_lane; // this lane's byte offsets inside a block
+    // Append form: the wave's block k_new holds the sequence's new token (row
+    // new_row); k_new < 0: not this wave's, or no append.
+    int k_new, new_row;
   };
+  // This lane's pieces of the new token's K and V rows in the block-load layout
+  // (append form), for the current item and the next one.
+  uint4 kn_cur[NKC], kn_nxt[NKC];
+  VT vn_cur, vn_nxt;
   // Record of ticket tk.  The records are written by the plan launch and only
   // read here, so they are read through the constant address space: with tk
   // wave-uniform that is a scalar load, and waiting for it does not wait for
@@ -172,6 +187,17 @@ __global__ __launch_bounds__(kMfmaThreads, kMfmaWavesPerSimd) void decode_partit
     it.row0 = (int64_t)r.w * Hq + (int64_t)it.g * G;  // r.w: the sequence's query row
     it.k_lane = (int)(h * tok_bytes + (it.g * D + 8 * j) * 2);
     it.v_lane = (int)(4 * j * tok_bytes + (it.g * D + EPL * h) * 2);
+    it.k_new = -1;
+    it.new_row = 0;
+    if (p.knew != nullptr && it.ctx >= 1) {
+      // a context clamped to the workspace bound has no new token to append
+      const int raw = ((const __attribute__((address_space(4))) int*)(const void*)p.ctx)[it.s];
+      const int bn = (it.ctx - 1) / kBlockTokens - it.b_begin;  // item-relative block
+      if (raw == it.ctx && bn >= 0 && bn < in_item && bn % NWAVE == wave) {
+        it.k_new = bn / NWAVE;
+        it.new_row = (it.ctx - 1) % kBlockTokens;
+      }
+    }
   };
   // ids of the wave's blocks b_begin + wave + NWAVE*k, one per lane (a vector
   // load through a resource over the sequence's table row; lanes past the row
@@ -183,6 +209,17 @@ __global__ __launch_bounds__(kMfmaThreads, kMfmaWavesPerSimd) void decode_partit
     const __amdgpu_buffer_rsrc_t tr = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<int32_t*>(p.tables + (int64_t)it.s * p.MB), (short)0, p.MB * 4, kRawBufferWord3);
     it.my_id = (int)__builtin_amdgcn_raw_buffer_load_b32(tr, (it.b_begin + wave + NWAVE * lane) * 4, 0, 0);
+    // The new token's K/V pieces (append form), loaded with the ids through
+    // resources that are empty unless this wave holds the token's block.
+    const int nrec = it.k_new >= 0 ? D * 2 : 0;
+    const int64_t nrow = nrec ? ((int64_t)it.s * p.Hkv + it.g) * D * 2 : 0;
+    const __amdgpu_buffer_rsrc_t knr =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(p.knew + nrow), (short)0, nrec, kRawBufferWord3);
+    const __amdgpu_buffer_rsrc_t vnr =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(p.vnew + nrow), (short)0, nrec, kRawBufferWord3);
+#pragma unroll
+    for (int c = 0; c < NKC; ++c) kn_nxt[c] = buffer_load16(knr, 16 * j + 64 * c, 0);
+    vn_nxt = buffer_load_piece<VT>(vnr, EPL * h * 2, 0);
   };
 
   // q as the B operand of the score MFMAs.  The resource covers the group's G
@@ -226,6 +263,33 @@ __global__ __launch_bounds__(kMfmaThreads, kMfmaWavesPerSimd) void decode_partit
 
   float m, l;            // reference max of head h (log2 domain, uniform over j); this lane's sum
   f32x4 acc[EPL];
+
+  // Append form, the wave's k-th block of the current item holding the new
+  // token: that token's cache row is not written yet, so its K and V come from
+  // the inputs (the lanes of its row in the block-load layout), and those lanes
+  // write the row to the cache.  No other work item reads this (token, KV head)
+  // row.
+  auto append = [&](Blk& B, const Item& it, int k) {
+    const int pb = __builtin_amdgcn_readlane(it.my_id, k);
+    if ((unsigned)pb >= (unsigned)p.NB) return;  // block id outside the pool: nothing read or written
+    const int64_t base = (int64_t)pb * blk_bytes;
+    const int row = it.new_row;
+    const bool krow = h == row;
+    // V: lane (h, j) holds tokens 4j .. 4j+3; the new token is its piece i = row & 3
+    // when j == row / 4.  Per-lane selects keep the block in registers.
+    const int vsel = j == (row >> 2) ? (row & 3) : -1;
+#pragma unroll
+    for (int c = 0; c < NKC; ++c) B.k[c] = pick(krow, kn_cur[c], B.k[c]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) B.v[i] = pick(i == vsel, vn_cur, B.v[i]);
+    if (krow) {
+#pragma unroll
+      for (int c = 0; c < NKC; ++c)
+        *reinterpret_cast<uint4*>(const_cast<char*>(p.kc) + base + it.k_lane + 64 * c) = kn_cur[c];
+    }
+    if (vsel >= 0)
+      *reinterpret_cast<VT*>(const_cast<char*>(p.vc) + base + it.v_lane + vsel * tok_bytes) = vn_cur;
+  };
 
   auto compute = [&](Blk& B) {
     f32x4 sc = {0.f, 0.f, 0.f, 0.f};
@@ -298,6 +362,9 @@ __global__ __launch_bounds__(kMfmaThreads, kMfmaWavesPerSimd) void decode_partit
   Item cur, nxt;
   make_item(tk0, load_rec(tk0), cur);
   load_ids(cur);
+#pragma unroll
+  for (int c = 0; c < NKC; ++c) kn_cur[c] = kn_nxt[c];
+  vn_cur = vn_nxt;
   load_q(cur);
 #pragma unroll
   for (int u = 0; u < NBUF - 1; ++u) issue(cur, u, buf[u]);
@@ -391,6 +458,7 @@ __global__ __launch_bounds__(kMfmaThreads, kMfmaWavesPerSimd) void decode_partit
         const int k = r * NBUF + u;
         if (k > 0 && k % kSplit == 0 && saved < kItemParts) save(saved++);  // uniform
         issue(cur, r * NBUF + u + NBUF - 1, buf[(u + NBUF - 1) % NBUF]);
+        if (k == cur.k_new) append(buf[u], cur, k);  // uniform
         compute(buf[u]);
         if (u == 0 && r == 0 && pending) {
           merge(prev, parity ^ 1);
@@ -410,6 +478,9 @@ __global__ __launch_bounds__(kMfmaThreads, kMfmaWavesPerSimd) void decode_partit
     const Item done = cur;
     if (have1) {
       cur = nxt;
+#pragma unroll
+      for (int c = 0; c < NKC; ++c) kn_cur[c] = kn_nxt[c];
+      vn_cur = vn_nxt;
       load_q(cur);
 #pragma unroll
       for (int u = 0; u < NBUF - 1; ++u) issue(cur, u, buf[u]);

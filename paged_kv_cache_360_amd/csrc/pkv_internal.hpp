@@ -49,6 +49,11 @@ struct DecodeArgs {
   float* part_m;         // [T*Hq, max_parts]
   float* part_l;         // [T*Hq, max_parts]
   float* part_o;         // [T*Hq, max_parts, D]
+  // Append form of decode (bf16): each sequence's new token (position ctx - 1)
+  // is read from these [S, Hkv, D] rows instead of the cache, and written to
+  // the cache, by the partition launch.  Null otherwise.
+  const void* knew;
+  const void* vnew;
 };
 
 // Rows of one prefill work item (one workgroup of four wavefronts, each with

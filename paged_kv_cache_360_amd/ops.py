@@ -115,6 +115,49 @@ def pkv_attention_decode_merge(out, q, key_cache, value_cache, block_tables, con
                         context_lens, scale, max_context_len, workspace, stream)
 
 
+def _append_call(cname, out, q, k_new, v_new, key_cache, value_cache, block_tables, context_lens, scale,
+                 max_context_len, workspace, stream):
+    s, hq, d = q.shape
+    nb, bs, hkv, dk = key_cache.shape
+    if out.shape != q.shape or dk != d or value_cache.shape != key_cache.shape:
+        raise ValueError("shape mismatch")
+    if k_new.shape != (s, hkv, d) or v_new.shape != (s, hkv, d):
+        raise ValueError("k_new / v_new must be [num_seqs, num_kv_heads, head_dim]")
+    for t in (out, k_new, v_new, key_cache, value_cache):
+        if t.dtype != q.dtype:
+            raise TypeError("q, k_new, v_new, caches and out must share one dtype")
+    if block_tables.dim() != 2 or block_tables.shape[0] != s or context_lens.shape != (s,):
+        raise ValueError("block_tables must be [S, MB] and context_lens [S]")
+    mb = block_tables.shape[1]
+    if workspace is None:
+        workspace = decode_workspace(s, hq, d, max_context_len, q.device)
+    ws_ptr = 0 if workspace is None else _dev(workspace, "workspace")
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    check(cname, getattr(lib(), cname)(
+        _dev(out, "out"), _dev(q, "q"), _dev(k_new, "k_new"), _dev(v_new, "v_new"),
+        _dev(key_cache, "key_cache"), _dev(value_cache, "value_cache"),
+        _dev(block_tables, "block_tables", torch.int32), _dev(context_lens, "context_lens", torch.int32),
+        float(scale), bs, hq, hkv, d, s, mb, nb, int(max_context_len), _dt(q), ws_ptr, ws_bytes,
+        _stream(stream)))
+    return out
+
+
+def pkv_attention_decode_append(out, q, k_new, v_new, key_cache, value_cache, block_tables, context_lens,
+                                scale, max_context_len, workspace=None, stream=None):
+    """Decode step with each sequence's new token (position ctx - 1) appended to the cache
+    in the same launch: equals pkv_write of k_new / v_new at that slot, then decode (bf16)."""
+    return _append_call("pkv_attention_decode_append", out, q, k_new, v_new, key_cache, value_cache,
+                        block_tables, context_lens, scale, max_context_len, workspace, stream)
+
+
+def pkv_attention_decode_partitions_append(out, q, k_new, v_new, key_cache, value_cache, block_tables,
+                                           context_lens, scale, max_context_len, workspace=None,
+                                           stream=None):
+    """Partition launch of the append form (after the plan, before the merge)."""
+    return _append_call("pkv_attention_decode_partitions_append", out, q, k_new, v_new, key_cache,
+                        value_cache, block_tables, context_lens, scale, max_context_len, workspace, stream)
+
+
 def pkv_varlen_workspace_bytes(num_seqs, num_tokens, num_q_heads, num_kv_heads, head_dim,
                                max_query_len, max_context_len):
     return int(lib().pkv_varlen_workspace_bytes(num_seqs, num_tokens, num_q_heads, num_kv_heads,

@@ -75,6 +75,29 @@ def test_decode_argument_errors(kw, code):
     assert _decode(**kw) == code
 
 
+def _append(name="pkv_attention_decode_append", **kw):
+    a = dict(out=FAKE, q=FAKE, kn=FAKE, vn=FAKE, kc=FAKE, vc=FAKE, tables=FAKE, ctx=FAKE, scale=0.125,
+             bs=16, hq=32, hkv=8, d=128, s=4, mb=128, nb=1000, maxctx=2048, dt=PKV_BF16, ws=FAKE,
+             wsb=1 << 30)
+    a.update(kw)
+    return getattr(lib(), name)(a["out"], a["q"], a["kn"], a["vn"], a["kc"], a["vc"], a["tables"],
+                                a["ctx"], a["scale"], a["bs"], a["hq"], a["hkv"], a["d"], a["s"], a["mb"],
+                                a["nb"], a["maxctx"], a["dt"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("name", ["pkv_attention_decode_append", "pkv_attention_decode_partitions_append"])
+@pytest.mark.parametrize("kw,code", [
+    (dict(dt=PKV_F32), PKV_EUNSUPPORTED),         # bf16 only
+    (dict(kn=0), PKV_EINVAL),
+    (dict(vn=FAKE + 4), PKV_EINVAL),              # misaligned
+    (dict(bs=32), PKV_EUNSUPPORTED),              # the decode checks apply too
+    (dict(ws=FAKE + 16), PKV_EWORKSPACE),
+    (dict(s=0), PKV_OK),                          # empty batch: nothing launched
+])
+def test_append_argument_errors(name, kw, code):
+    assert _append(name, **kw) == code
+
+
 def test_decode_workspace_sizes():
     f = lib().pkv_decode_workspace_bytes
     one = f(64, 32, 128, 512)                      # one partition: header + work list only
