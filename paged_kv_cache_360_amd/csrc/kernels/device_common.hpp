@@ -89,6 +89,16 @@ __device__ __forceinline__ float sum_over_rows(float v) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
+// The same over the two 32-lane halves only (lane and lane ^ 32).
+__device__ __forceinline__ float max_over_halves(float v) {
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float sum_over_halves(float v) {
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 // Butterfly sum / max over lanes that differ only in the bits of [lo_mask, 64).
 template <int FROM, int TO>
 __device__ __forceinline__ float xor_sum(float v) {

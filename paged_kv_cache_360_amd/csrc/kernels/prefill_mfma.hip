@@ -8,23 +8,40 @@
 // §2 "Reworking the Attention Computation"), split into 512-token partitions
 // whose partial softmax results the log-sum-exp merge combines.
 //
-// Unlike a decode row, a chunk's rows make a real dense tile.  A workgroup takes
-// a work item of 256/G consecutive rows x the G q heads of one KV head over one
-// partition of keys; each of its four waves owns 64/G rows = four 16-column
-// MFMA tiles (column n of tile c = row c*16/G + n/G, head n%G).  Each
-// 16-token block of K and V is loaded once per workgroup (coalesced 16-byte
-// pieces, a few blocks in flight in registers), staged through a double-buffered
-// LDS slab with padded rows, and read by every wave as the K operand (A of
-// v_mfma_f32_16x16x32_bf16, token = lane & 15) and the V^T operand (A of
-// v_mfma_f32_16x16x16bf16_1k, regrouped by 16-bit permutes), each used by all
-// four of the wave's tiles; the score tile's lane layout is the P^T operand of
-// the value product, as in the decode kernel.  Each column keeps its own
-// online softmax and causal mask (token < the keys its row sees), so the
+// Unlike a decode row, a chunk's rows make a dense tile, so this kernel runs on
+// the 32x32x16 matrix instructions (the fastest bf16 shape here).  A workgroup
+// item is 256/G consecutive rows x the G q heads of one KV head over one
+// partition of keys; each of the eight waves owns one 32-column tile (column n
+// = row n/G of the wave's 32/G rows, head n%G).
+// Keys go in steps of 32 tokens (two blocks):
+//  * scores S^T[t][n] = sum_d K[t][d] q[n][d]: v_mfma_f32_32x32x16_bf16, D/16
+//    per tile; A = K (lane: token lane%32, dims 8*(lane/32) .. +7 of the
+//    16-dim step, read from LDS), B = q^T (lane: column lane%32, same dims).
+//    C: lane (n, h = lane/32), register i <-> token 8*(i/4) + 4h + i%4.
+//  * online softmax per column (base 2, lazy reference max as in decode);
+//  * values O^T[d][n] += sum_t V^T[d][t] P^T[t][n]: two 16-token k-steps of
+//    D/32 MFMAs per tile.  B = P^T is the score registers i = 8s .. 8s+7 of
+//    k-step s, rounded to bf16: element e <-> token 16s + 8*(e/4) + 4h + e%4.
+//    A = V^T takes the same tokens for the same elements: each lane reads
+//    those 8 token rows at dims NT*m .. NT*m + NT-1 (m = lane%32, NT = D/32)
+//    and regroups 16-bit halves, so tile e holds dim NT*m + e in row slot m.
+//    C: lane (n, h), register i <-> dim NT*(8*(i/4) + 4h + i%4) + e.
+// Each column keeps its own causal mask (token < the keys its row sees), so the
 // diagonal block needs no special case.
 //
-// Workgroups take tickets from the prefill counter (a ticket names a work
-// record and a KV head).  A row whose keys fit one partition gets its output
-// written directly; other rows' partials go to the workspace for the merge.
+// K and V of each step are loaded once per workgroup (one D/8-byte piece of K
+// and of V per thread and step row), staged through a three-buffer LDS slab
+// with rows padded to D*2 + 16 bytes, and read by every wave.  Each wave
+// computes the scores of step q + 1 while it runs step q's softmax and value
+// products, so the matrix cores work during the vector code.  The load stream
+// runs four steps ahead of the computation across item boundaries: the
+// workgroup keeps the record and the q operand of the next item, so a new item
+// starts with its first steps and q already loaded.
+//
+// Workgroups take items from the prefill tickets: the first two are static
+// (blockIdx.x and blockIdx.x + gridDim.x), the rest come from the counter.  A row whose
+// keys fit one partition gets its output written directly; other rows'
+// partials go to the workspace for the merge.
 
 #include <hip/hip_runtime.h>
 
@@ -33,111 +50,145 @@
 #include "../pkv_internal.hpp"
 #include "decode_common.hpp"
 
-#ifndef PKV_PREFILL_NBUF
-#define PKV_PREFILL_NBUF 4
-#endif
-
 namespace pkv {
 
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int kPrefillNbuf = PKV_PREFILL_NBUF;  // blocks in flight per workgroup
-constexpr int kTiles = 4;                        // 16-column MFMA tiles per work item
+constexpr int kStepTokens = 2 * kBlockTokens;  // tokens per step (two blocks)
+// Waves per workgroup; the item's 256 columns are split among them in 32-column
+// tiles.  Eight waves (two per SIMD) let one wave's softmax and LDS reads
+// overlap another's matrix products.
+#ifndef PKV_PREFILL_WAVES
+#define PKV_PREFILL_WAVES 8
+#endif
+constexpr int kPrefillWaves = PKV_PREFILL_WAVES;
+constexpr int kPrefillThreads = kPrefillWaves * kWave;
+constexpr int kColTiles = 8 / kPrefillWaves;   // 32-column tiles per wave
+#ifndef PKV_PREFILL_STEPS
+#define PKV_PREFILL_STEPS 2
+#endif
+constexpr int kPrefillSteps = PKV_PREFILL_STEPS;  // steps of K/V in flight
 
-template <int D> struct VPiece;
-template <> struct VPiece<128> { using T = uint4; };
-template <> struct VPiece<64> { using T = uint2; };
+// One thread's piece of a block row: D / 8 bytes.
+template <int D> struct KVPiece;
+template <> struct KVPiece<128> { using T = uint4; };
+template <> struct KVPiece<64> { using T = uint2; };
+// One lane's dims of a V row for the V^T operand: D / 32 bf16 values.
+template <int D> struct VDims;
+template <> struct VDims<128> { using T = uint2; };
+template <> struct VDims<64> { using T = uint32_t; };
 
-__device__ __forceinline__ uint32_t pair_lo(uint32_t a, uint32_t b) { return (a & 0xFFFFu) | (b << 16); }
-__device__ __forceinline__ uint32_t pair_hi(uint32_t a, uint32_t b) { return (a >> 16) | (b & 0xFFFF0000u); }
+// 16-bit halves of two words, one byte permute each: (low(a), low(b)) and
+// (high(a), high(b)).
+__device__ __forceinline__ uint32_t pair_lo(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x05040100u); }
+__device__ __forceinline__ uint32_t pair_hi(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x07060302u); }
+// Sum of a packed bf16 pair, added to acc (one dot-product instruction).
+__device__ __forceinline__ float add_bf16_pair(uint32_t w, float acc) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), __builtin_bit_cast(bf16x2, 0x3F803F80u), acc,
+                                         false);
+}
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   const bf16x2 v = {(__bf16)a, (__bf16)b};
   return __builtin_bit_cast(uint32_t, v);
 }
+__device__ __forceinline__ uint32_t word(uint2 v, int k) { return k == 0 ? v.x : v.y; }
+__device__ __forceinline__ uint32_t word(uint32_t v, int) { return v; }
 
 template <int D, int G>
-__global__ __launch_bounds__(kDecodeThreads, 1) void prefill_mfma_kernel(DecodeParams p) {
-  constexpr int EPL = D / 16;            // dims per lane in one V row piece
-  constexpr int WPL = EPL / 2;           // 32-bit words per V row piece
-  constexpr int NKC = D / 32;            // 16x16x32 MFMAs per tile per block for the scores
-  constexpr int R = 16 / G;              // rows per tile
-  constexpr int RPW = kTiles * R;        // rows per wave
-  constexpr int NPF = kPrefillNbuf;      // blocks in flight (cooperative loads)
-  constexpr int RS = D * 2 + 16;         // LDS row stride in bytes (16-byte pad: no bank conflicts)
-  using VT = typename VPiece<D>::T;
-  static_assert(G >= 1 && G <= 16 && 16 % G == 0, "a tile holds whole rows of G heads");
-  static_assert(kDecodeThreads == kBlockTokens * 16, "16 threads per token row load a block");
+__global__ __launch_bounds__(kPrefillThreads, 1) void prefill_mfma_kernel(DecodeParams p) {
+  constexpr int NT = D / 32;               // 32-dim tiles of the output; V dims per lane
+  constexpr int NKC = D / 16;              // 16-dim steps of the scores
+  constexpr int CT = kColTiles;
+  constexpr int R = 32 / G;                // rows per column tile
+  constexpr int RPW = CT * R;              // rows per wave
+  constexpr int RS = D * 2 + 16;           // LDS row stride in bytes (16-byte pad)
+  constexpr int PS = D / 8;                // bytes per thread and block row
+  constexpr int NS = kPrefillSteps;
+  using PT = typename KVPiece<D>::T;
+  using VD = typename VDims<D>::T;
+  static_assert(G >= 1 && G <= 32 && 32 % G == 0, "a tile holds whole rows of G heads");
+  constexpr int RPT = kStepTokens * 16 / kPrefillThreads;  // step rows each thread stages
+  static_assert(RPT >= 1 && kStepTokens * 16 % kPrefillThreads == 0, "16 threads per token row");
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
-  const int n = lane & 15;               // MFMA column (row n / G, head n % G of a tile)
-  const int j = lane >> 4;
+  const int n = lane & 31;                 // column of a tile; token / dim slot of operands
+  const int hh = lane >> 5;                // lane half
   const int Hq = p.Hkv * G;
   const int64_t tok_bytes = (int64_t)p.Hkv * D * 2;
   const int64_t blk_bytes = tok_bytes * kBlockTokens;
   const int total = min(p.sched[3], p.pre_cap * p.Hkv);
+  const int grid = (int)gridDim.x;
 
-  // [buffer][K, V][16 rows x RS bytes]
-  __shared__ __attribute__((aligned(16))) char s_kv[2][2][kBlockTokens * RS];
+  // [buffer][K, V][32 rows x RS bytes]: three buffers, step q in q % 3 (the
+  // scores of step q + 1 are computed while step q's values are)
+  __shared__ __attribute__((aligned(16))) char s_kv[3][2][kStepTokens * RS];
   __shared__ int s_ticket[2];
 
   struct Item {
-    int s, part, g, ctx, qrow0, nrows, key0, b_begin, nblk, ids;
+    int s, part, g, ctx, qrow0, nrows, key0, b_begin, nblk, nsteps;
+    bool valid;
   };
+  // Records are written by the plan launch and read-only here: read through the
+  // constant address space (scalar loads; waiting for them never waits for the
+  // vector loads in flight).
   auto make_item = [&](int tk, Item& it) {
-    const int4 ra = p.pre_recs[2 * (tk / p.Hkv)];
-    const int4 rb = p.pre_recs[2 * (tk / p.Hkv) + 1];
-    it.g = tk % p.Hkv;
-    it.s = ra.x;
-    it.part = ra.y;
-    it.ctx = ra.z;
-    it.qrow0 = ra.w;
-    it.nrows = rb.x;
-    it.key0 = rb.y;                                      // row i sees max(0, key0 + i) keys
+    it.valid = tk < total;
+    const int t = it.valid ? tk : 0;
+    const __attribute__((address_space(4))) int* r =
+        (const __attribute__((address_space(4))) int*)(const void*)p.pre_recs + 8 * (t / p.Hkv);
+    it.g = t % p.Hkv;
+    it.s = r[0];
+    it.part = r[1];
+    it.ctx = r[2];
+    it.qrow0 = r[3];
+    it.nrows = r[4];
+    it.key0 = r[5];                                       // row i sees max(0, key0 + i) keys
     const int key_last = max(0, it.key0 + it.nrows - 1);  // keys the item's last row sees
     const int k_begin = it.part * kPartTokens;
     const int k_end = min(k_begin + kPartTokens, key_last);
     it.b_begin = it.part * kPartBlocks;
-    it.nblk = max(0, (k_end - k_begin + kBlockTokens - 1) / kBlockTokens);
-    it.ids = lane < it.nblk ? p.tables[(int64_t)it.s * p.MB + it.b_begin + lane] : -1;
+    it.nblk = it.valid ? max(0, (k_end - k_begin + kBlockTokens - 1) / kBlockTokens) : 0;
+    // steps of two blocks, padded to a multiple of NS so that every item starts
+    // on stage slot 0, and to at least 2*NS so that the load stream (NS + 2
+    // steps ahead of the computation) never runs past the next item; padding
+    // steps load nothing and compute nothing
+    it.nsteps = max(2 * NS, (max(1, (it.nblk + 1) / 2) + NS - 1) / NS * NS);
   };
-
-  // q operands (B of the score MFMAs) of this wave's rows: tile c, column n =
-  // row wave*RPW + c*R + n/G of the item, head n%G
-  bf16x8 qf[kTiles][NKC];
-  auto load_q = [&](const Item& it) {
+  // q operands (B of the scores) of this wave's columns; rows past the item read
+  // zeros through the resource bound.
+  auto load_q = [&](const Item& it, bf16x8 (&qv)[CT][NKC]) {
+    const __amdgpu_buffer_rsrc_t qr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<char*>(reinterpret_cast<const char*>(p.q) + (int64_t)it.qrow0 * Hq * D * 2), (short)0,
+        it.valid ? it.nrows * Hq * D * 2 : 0, kRawBufferWord3);
 #pragma unroll
-    for (int c = 0; c < kTiles; ++c) {
+    for (int c = 0; c < CT; ++c) {
       const int r = wave * RPW + c * R + n / G;
-      const bool ok = r < it.nrows;
-      const char* qrow = reinterpret_cast<const char*>(p.q) +
-                         ((int64_t)(it.qrow0 + (ok ? r : 0)) * Hq + it.g * G + n % G) * D * 2;
+      const int off = ((r * Hq + it.g * G + n % G) * D + 8 * hh) * 2;
 #pragma unroll
-      for (int kc = 0; kc < NKC; ++kc) {
-        const uint4 v = ok ? load16(qrow + (32 * kc + 8 * j) * 2) : make_uint4(0, 0, 0, 0);
-        qf[c][kc] = __builtin_bit_cast(bf16x8, v);
-      }
+      for (int kc = 0; kc < NKC; ++kc) qv[c][kc] = __builtin_bit_cast(bf16x8, buffer_load16(qr, off + 32 * kc, 0));
     }
   };
 
-  // cooperative block loads: thread t loads the same piece of K and of V, row
-  // t / 16 of the block, bytes (t % 16) * PS .. + PS of KV head g's slice
-  // (PS = D / 8: one coalesced 16-lane row per token), so every load uses one
-  // resource and the pipeline needs no per-thread selection
-  constexpr int PS = D / 8;
+  // Cooperative loads: thread t holds the same piece of K and of V of step rows
+  // t / 16 + j * (threads / 16), j < RPT, bytes (t % 16) * PS .. + PS of KV head
+  // g's slice.  A wave's rows lie in one block, so its loads use one resource.
   const int st_row = tid / 16;
   const int st_col = (tid % 16) * PS;
+  constexpr int kRowStride = kPrefillThreads / 16;
   struct Stage {
-    VT k, v;
+    PT k[RPT], v[RPT];
   };
-  auto issue = [&](const Item& it, int k, Stage& st) {
-    const int pb = k < it.nblk ? __builtin_amdgcn_readlane(it.ids, k) : -1;
+  // Block k of a partition (block id pb; -1 past the partition): the loads go
+  // through resources sized to the block, empty for an id outside the pool.
+  // Row `row` (block row row % 16) of block id pb (-1 past the partition): the
+  // loads go through resources sized to the block, empty for an id outside the pool.
+  auto issue_row = [&](int g, int pb, int row, PT& kk, PT& vv) {
     const bool ok = (unsigned)pb < (unsigned)p.NB;
     const int64_t base = (int64_t)(ok ? pb : 0) * blk_bytes;
     const int nrec = ok ? (int)blk_bytes : 0;
@@ -145,150 +196,167 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void prefill_mfma_kernel(DecodeP
         __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(p.kc + base), (short)0, nrec, kRawBufferWord3);
     const __amdgpu_buffer_rsrc_t vr =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(p.vc + base), (short)0, nrec, kRawBufferWord3);
-    const int off = (int)(st_row * tok_bytes + it.g * D * 2 + st_col);
-    st.k = buffer_load_piece<VT>(kr, off, 0);
-    st.v = buffer_load_piece<VT>(vr, off, 0);
+    const int off = (int)((row % kBlockTokens) * tok_bytes + g * D * 2 + st_col);
+    kk = buffer_load_piece<PT>(kr, off, 0);
+    vv = buffer_load_piece<PT>(vr, off, 0);
+  };
+  // This thread's rows of step `step` of an item.  Block ids are scalar loads
+  // from the table (written before this launch, read-only here): they never
+  // wait for the vector loads in flight.
+  auto issue_step = [&](int s, int g, int b_begin, int nblk, int step, Stage& st) {
+    const __attribute__((address_space(4))) int* trow =
+        (const __attribute__((address_space(4))) int*)(const void*)(p.tables + (int64_t)s * p.MB + b_begin);
+#pragma unroll
+    for (int j = 0; j < RPT; ++j) {
+      const int row = st_row + j * kRowStride;                 // wave-uniform block
+      const int k = 2 * step + __builtin_amdgcn_readfirstlane(row / kBlockTokens);
+      const int id = k < nblk ? trow[k] : -1;
+      issue_row(g, id, row, st.k[j], st.v[j]);
+    }
   };
   auto stage_to_lds = [&](const Stage& st, int buf) {
-    *reinterpret_cast<VT*>(&s_kv[buf][0][st_row * RS + st_col]) = st.k;
-    *reinterpret_cast<VT*>(&s_kv[buf][1][st_row * RS + st_col]) = st.v;
+#pragma unroll
+    for (int j = 0; j < RPT; ++j) {
+      const int row = st_row + j * kRowStride;
+      *reinterpret_cast<PT*>(&s_kv[buf][0][row * RS + st_col]) = st.k[j];
+      *reinterpret_cast<PT*>(&s_kv[buf][1][row * RS + st_col]) = st.v[j];
+    }
   };
 
-  float m[kTiles], l[kTiles];
-  f32x4 acc[kTiles][EPL];
-  int col_keys[kTiles];  // keys the column's row sees (0 for a column past the item's rows)
+  bf16x8 qf[CT][NKC], qn[CT][NKC];   // q operands of the current and the next item
+  float m[CT], l[CT];
+  f32x16 acc[CT][NT];
+  int col_keys[CT];                   // keys the column's row sees (0 past the item's rows)
+  int min_keys;                       // the least of them over the wave (uniform)
 
-  // one block from LDS buffer buf: tokens t0 .. t0+15, of which `valid` are in the context
-  auto compute = [&](int buf, int t0, int valid) {
+  // Scores of the step in LDS buffer buf (the matrix products only).
+  auto scores = [&](int buf, f32x16 (&sc)[CT]) {
     const char* kb = s_kv[buf][0];
-    const char* vb = s_kv[buf][1];
-    uint4 kf[NKC];
 #pragma unroll
-    for (int kc = 0; kc < NKC; ++kc) kf[kc] = *reinterpret_cast<const uint4*>(kb + n * RS + 64 * kc + 16 * j);
-    VT vp[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      vp[i] = *reinterpret_cast<const VT*>(vb + (4 * j + i) * RS + EPL * 2 * n);
-      if (4 * j + i >= valid) vp[i] = VT{};  // past the context: zero (0 * NaN)
-    }
-    const uint32_t* w0 = reinterpret_cast<const uint32_t*>(&vp[0]);
-    const uint32_t* w1 = reinterpret_cast<const uint32_t*>(&vp[1]);
-    const uint32_t* w2 = reinterpret_cast<const uint32_t*>(&vp[2]);
-    const uint32_t* w3 = reinterpret_cast<const uint32_t*>(&vp[3]);
-    i16x4 av[EPL];  // V^T operand tiles, shared by the four column tiles
-#pragma unroll
-    for (int w = 0; w < WPL; ++w) {
-      av[2 * w] = __builtin_bit_cast(i16x4, make_uint2(pair_lo(w0[w], w1[w]), pair_lo(w2[w], w3[w])));
-      av[2 * w + 1] = __builtin_bit_cast(i16x4, make_uint2(pair_hi(w0[w], w1[w]), pair_hi(w2[w], w3[w])));
-    }
-    // In phases over the four tiles, so independent tiles overlap: scores,
-    // block maxima, one rescale decision, probabilities, value products.
-    f32x4 sc[kTiles];
-#pragma unroll
-    for (int c = 0; c < kTiles; ++c) sc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int c = 0; c < CT; ++c) sc[c] = f32x16{};
 #pragma unroll
     for (int kc = 0; kc < NKC; ++kc) {
+      const bf16x8 kf = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(kb + n * RS + 32 * kc + 16 * hh));
 #pragma unroll
-      for (int c = 0; c < kTiles; ++c)
-        sc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kf[kc]), qf[c][kc],
-                                                        sc[c], 0, 0, 0);
+      for (int c = 0; c < CT; ++c) sc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[c][kc], sc[c], 0, 0, 0);
     }
-    float x[kTiles][4], ms[kTiles];
+  };
+  // Softmax and value products of a step from its scores and LDS buffer buf:
+  // tokens t0 .. t0+31, of which `valid` are in the context (V rows past it
+  // are zeroed: 0 * NaN).
+  auto softmax_values = [&](f32x16 (&sc)[CT], int buf, int t0, int valid) {
+    const char* vb = s_kv[buf][1];
+    // softmax per column in base 2: register i holds token 8*(i/4) + 4*hh + i%4.
+    // Only steps that reach past some column's keys (the causal edge, the end
+    // of the context) need the per-element mask; the others take the scale into
+    // the exponent's fused multiply-add.
+    const bool masked = t0 + kStepTokens > min_keys;  // uniform over the wave
+    float ms[CT], mref[CT];
     bool grew = false;
 #pragma unroll
-    for (int c = 0; c < kTiles; ++c) {
+    for (int c = 0; c < CT; ++c) {
+      float mx;
+      if (masked) {
+        mx = -INFINITY;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int t = t0 + 4 * j + i;
-        x[c][i] = t < col_keys[c] ? sc[c][i] * p.scale_log2 : -INFINITY;
+        for (int i = 0; i < 16; ++i) {
+          const int t = t0 + 8 * (i / 4) + 4 * hh + (i % 4);
+          sc[c][i] = t < col_keys[c] ? sc[c][i] * p.scale_log2 : -INFINITY;
+          mx = fmaxf(mx, sc[c][i]);
+        }
+      } else {
+        float r = sc[c][0];
+#pragma unroll
+        for (int i = 1; i < 16; ++i) r = fmaxf(r, sc[c][i]);
+        mx = r * p.scale_log2;  // the scale is positive: the max commutes with it
       }
-      const float mb = max_over_rows(fmaxf(fmaxf(x[c][0], x[c][1]), fmaxf(x[c][2], x[c][3])));
-      const bool up = mb > m[c] + kRescaleLog2;  // -inf + 8 = -inf: the first live block moves it
+      const float mb = max_over_halves(mx);
+      const bool up = mb > m[c] + kRescaleLog2;  // -inf + 8 = -inf: the first live step moves it
       const float mn = up ? mb : m[c];
-      ms[c] = (mn == -INFINITY) ? 0.f : mn;
-      grew |= up;
-      x[c][0] -= ms[c];
-      x[c][1] -= ms[c];
-      x[c][2] -= ms[c];
-      x[c][3] -= ms[c];
-      const float old = m[c];
+      mref[c] = (mn == -INFINITY) ? 0.f : mn;
+      ms[c] = m[c] - mref[c];                     // exponent of the rescale factor
       m[c] = mn;
-      ms[c] = old - ms[c];  // exponent of the rescale factor
+      grew |= up;
     }
     if (__ballot(grew)) {  // some column's reference moved: rescale what was accumulated
 #pragma unroll
-      for (int c = 0; c < kTiles; ++c) {
+      for (int c = 0; c < CT; ++c) {
         const float alpha = exp2_fast(ms[c]);
         l[c] *= alpha;
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) acc[c][e] *= alpha;
+        for (int e = 0; e < NT; ++e) acc[c][e] *= alpha;
       }
     }
-    i16x4 pt[kTiles];
+    auto weight = [&](int c, int i) {
+      return masked ? exp2_fast(sc[c][i] - mref[c]) : exp2_fast(fmaf(sc[c][i], p.scale_log2, -mref[c]));
+    };
+    const bool ragged = valid < kStepTokens;  // uniform: V rows past the context are zeroed
 #pragma unroll
-    for (int c = 0; c < kTiles; ++c) {
-      const uint32_t p01 = pack_bf16x2(exp2_fast(x[c][0]), exp2_fast(x[c][1]));
-      const uint32_t p23 = pack_bf16x2(exp2_fast(x[c][2]), exp2_fast(x[c][3]));
-      l[c] += (bf16_lo(p01) + bf16_hi(p01)) + (bf16_lo(p23) + bf16_hi(p23));
-      pt[c] = __builtin_bit_cast(i16x4, make_uint2(p01, p23));
-    }
+    for (int s = 0; s < 2; ++s) {
+      // P^T operand of k-step s (rounded weights summed into l)
+      bf16x8 pt[CT];
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) {
+      for (int c = 0; c < CT; ++c) {
+        uint32_t w[4];
 #pragma unroll
-      for (int c = 0; c < kTiles; ++c)
-        acc[c][e] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av[e], pt[c], acc[c][e], 0, 0, 0);
+        for (int d = 0; d < 4; ++d) {
+          w[d] = pack_bf16x2(weight(c, 8 * s + 2 * d), weight(c, 8 * s + 2 * d + 1));
+          l[c] = add_bf16_pair(w[d], l[c]);
+        }
+        pt[c] = __builtin_bit_cast(bf16x8, make_uint4(w[0], w[1], w[2], w[3]));
+      }
+      // V^T operand: element e <-> token 16s + 8*(e/4) + 4*hh + e%4, dims NT*n ..
+      VD raw[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int tr = 16 * s + 8 * (e / 4) + 4 * hh + (e % 4);
+        raw[e] = *reinterpret_cast<const VD*>(vb + tr * RS + NT * 2 * n);
+      }
+      if (ragged) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int tr = 16 * s + 8 * (e / 4) + 4 * hh + (e % 4);
+          if (tr >= valid) raw[e] = VD{};
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < NT; ++e) {
+        // tile e: dim NT*n + e, i.e. 16-bit half (e & 1) of word (e >> 1)
+        uint32_t w[4];
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          const uint32_t a = word(raw[2 * d], e >> 1), b = word(raw[2 * d + 1], e >> 1);
+          w[d] = (e & 1) ? pair_hi(a, b) : pair_lo(a, b);
+        }
+        const bf16x8 av = __builtin_bit_cast(bf16x8, make_uint4(w[0], w[1], w[2], w[3]));
+#pragma unroll
+        for (int c = 0; c < CT; ++c) acc[c][e] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pt[c], acc[c][e], 0, 0, 0);
+      }
     }
   };
 
-  if (tid == 0) s_ticket[0] = atomicAdd(&p.sched[2], 1);
-  __syncthreads();
-  int tk = __builtin_amdgcn_readfirstlane(s_ticket[0]);
-
-  Stage stg[NPF];
-  int buf = 0;
-  for (int parity = 1; tk < total; parity ^= 1) {
-    int next_tk = 0;
-    if (tid == 0) next_tk = atomicAdd(&p.sched[2], 1);
-    Item it;
-    make_item(tk, it);
-    load_q(it);
+  auto begin_item = [&](const Item& it) {
 #pragma unroll
-    for (int u = 0; u < NPF; ++u) issue(it, u, stg[u]);
-#pragma unroll
-    for (int c = 0; c < kTiles; ++c) {
+    for (int c = 0; c < CT; ++c) {
       m[c] = -INFINITY;
       l[c] = 0.f;
       const int r = wave * RPW + c * R + n / G;
       col_keys[c] = r < it.nrows ? max(0, it.key0 + r) : 0;
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) acc[c][e] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int e = 0; e < NT; ++e) acc[c][e] = f32x16{};
     }
-
-    // Blocks in rounds of NPF: block k's staged registers go to LDS buffer
-    // k % 2, the slot is refilled with block k + NPF (a zero-range load past the
-    // item), one barrier makes the block visible, and every wave computes it.
-    // Two LDS buffers suffice: a wave writing buffer k % 2 has passed block
-    // k-1's barrier, which every wave reached after computing block k-2.
-    const int rounds = (it.nblk + NPF - 1) / NPF;
-    for (int rr = 0; rr < rounds; ++rr) {
+    int mk = col_keys[0];
 #pragma unroll
-      for (int u = 0; u < NPF; ++u) {
-        const int k = rr * NPF + u;
-        const bool live = k < it.nblk;  // uniform over the workgroup
-        if (live) stage_to_lds(stg[u], buf);
-        issue(it, k + NPF, stg[u]);      // unconditional: the wait counts stay static
-        if (live) {
-          __syncthreads();
-          const int t0 = (it.b_begin + k) * kBlockTokens;
-          compute(buf, t0, min(kBlockTokens, it.ctx - t0));
-          buf ^= 1;
-        }
-      }
-    }
-
+    for (int c = 1; c < CT; ++c) mk = min(mk, col_keys[c]);
 #pragma unroll
-    for (int c = 0; c < kTiles; ++c) {
-      const float lt = sum_over_rows(l[c]);
+    for (int o = 1; o < 32; o <<= 1) mk = min(mk, __shfl_xor(mk, o, kWave));
+    min_keys = __builtin_amdgcn_readfirstlane(mk);
+  };
+
+  auto finish_item = [&](const Item& it) {
+#pragma unroll
+    for (int c = 0; c < CT; ++c) {
+      const float lt = sum_over_halves(l[c]);
       const int r = wave * RPW + c * R + n / G;
       const int keys = max(0, it.key0 + r);
       const int nparts = max(1, (keys + kPartTokens - 1) / kPartTokens);
@@ -297,49 +365,138 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void prefill_mfma_kernel(DecodeP
       if (r < it.nrows && it.part < nparts) {
         const int64_t orow = (int64_t)(it.qrow0 + r) * Hq + it.g * G + n % G;
         const float inv = lt > 0.f ? 1.f / lt : 0.f;
+        // register i holds dims NT*(8*(i/4) + 4*hh + i%4) + e, e < NT: one
+        // vector store of NT consecutive dims per register index
         if (nparts == 1) {
-          uint16_t* o = reinterpret_cast<uint16_t*>(p.out) + orow * D;
+          char* o = reinterpret_cast<char*>(p.out) + orow * D * 2;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-#pragma unroll
-            for (int e = 0; e < EPL; ++e) o[EPL * (4 * j + i) + e] = f32_to_bf16(acc[c][e][i] * inv);
+          for (int i = 0; i < 16; ++i) {
+            const int d0 = NT * (8 * (i / 4) + 4 * hh + (i % 4));
+            if constexpr (NT == 4) {
+              *reinterpret_cast<uint2*>(o + d0 * 2) =
+                  make_uint2(pack_bf16x2(acc[c][0][i] * inv, acc[c][1][i] * inv),
+                             pack_bf16x2(acc[c][2][i] * inv, acc[c][3][i] * inv));
+            } else {
+              *reinterpret_cast<uint32_t*>(o + d0 * 2) = pack_bf16x2(acc[c][0][i] * inv, acc[c][1][i] * inv);
+            }
           }
         } else {
           const int64_t pr = orow * p.max_parts + it.part;
           float* o = p.part_o + pr * D;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-#pragma unroll
-            for (int e = 0; e < EPL; ++e) o[EPL * (4 * j + i) + e] = acc[c][e][i] * inv;
+          for (int i = 0; i < 16; ++i) {
+            const int d0 = NT * (8 * (i / 4) + 4 * hh + (i % 4));
+            if constexpr (NT == 4) {
+              *reinterpret_cast<float4*>(o + d0) =
+                  make_float4(acc[c][0][i] * inv, acc[c][1][i] * inv, acc[c][2][i] * inv, acc[c][3][i] * inv);
+            } else {
+              *reinterpret_cast<float2*>(o + d0) = make_float2(acc[c][0][i] * inv, acc[c][1][i] * inv);
+            }
           }
-          if (j == 0) {
+          if (hh == 0) {
             p.part_m[pr] = m[c];
             p.part_l[pr] = lt;
           }
         }
       }
     }
-    if (tid == 0) s_ticket[parity] = next_tk;
-    __syncthreads();
-    tk = __builtin_amdgcn_readfirstlane(s_ticket[parity]);
+  };
+
+  // The item queue: cur (being computed) and n1 (record known, q loaded into
+  // qn); the ticket after n1 is fetched while cur runs.  The loads run NS steps
+  // ahead of the staging, NS + 2 ahead of the computation: into n1 near the
+  // end of cur, never past it.
+  Item cur, n1;
+  make_item(blockIdx.x, cur);
+  if (!cur.valid) return;
+  make_item(blockIdx.x + grid, n1);
+  load_q(cur, qf);
+  load_q(n1, qn);
+
+  // The stream position `ahead` <= NS + 2 steps after step q of cur, chosen by
+  // selects so that every path issues the same loads in the same order; an
+  // invalid item has no blocks (zero-sized loads).
+  auto issue_ahead = [&](int q, int ahead, Stage& st) {
+    const int r0 = q + ahead;
+    const bool in_cur = r0 < cur.nsteps;
+    const int s = in_cur ? cur.s : n1.s;
+    const int g = in_cur ? cur.g : n1.g;
+    const int b_begin = in_cur ? cur.b_begin : n1.b_begin;
+    const int nblk = in_cur ? cur.nblk : n1.nblk;
+    issue_step(s, g, b_begin, nblk, in_cur ? r0 : r0 - cur.nsteps, st);
+  };
+
+  // Step q is staged into LDS at iteration q - 2 (from the registers its loads
+  // landed in, NS steps after they were issued), its scores are computed at
+  // iteration q - 1 while step q - 1's softmax and values run, and its own
+  // softmax and values at iteration q: one barrier per iteration.
+  Stage stg[NS];
+#pragma unroll
+  for (int u = 0; u < NS; ++u) issue_ahead(0, u, stg[u]);
+#pragma unroll
+  for (int u = 0; u < NS; ++u) {
+    stage_to_lds(stg[u], u);
+    issue_ahead(u, NS, stg[u]);
+  }
+  __syncthreads();
+  int buf = 0, tpar = 0;  // LDS buffer of step 0 of cur
+  f32x16 sc_cur[CT], sc_next[CT];
+  for (;;) {  // one item per iteration
+    int fetched;  // thread 0: the ticket after n1, written to LDS at cur's last step
+    if (tid == 0) fetched = atomicAdd(&p.sched[2], 1);  // offset added where it is read
+    begin_item(cur);
+    if (cur.nblk > 0) scores(buf, sc_next);
+    for (int q0 = 0; q0 < cur.nsteps; q0 += NS) {
+#pragma unroll
+      for (int u = 0; u < NS; ++u) {
+        const int q = q0 + u;
+        const int b1 = buf == 2 ? 0 : buf + 1, b2 = b1 == 2 ? 0 : b1 + 1;
+        // step q + 2 (stream order, possibly n1's) sits in stg[u]: stage it
+        // into buffer b2 (read last at iteration q - 1, before the last
+        // barrier) and refill the slot with step q + 2 + NS
+        stage_to_lds(stg[u], b2);
+        issue_ahead(q + 2, NS, stg[u]);
+        if (q + 1 == cur.nsteps && tid == 0) s_ticket[tpar] = fetched;
+#pragma unroll
+        for (int c = 0; c < CT; ++c) sc_cur[c] = sc_next[c];
+        if (2 * (q + 1) < cur.nblk) scores(b1, sc_next);  // overlaps the softmax below
+        if (2 * q < cur.nblk) {
+          const int t0 = (cur.b_begin + 2 * q) * kBlockTokens;
+          softmax_values(sc_cur, buf, t0, min(kStepTokens, cur.ctx - t0));
+        }
+        __syncthreads();
+        buf = b1;
+      }
+    }
+    // Switch to n1.  Its q was loaded at the start of this item; the empty asm
+    // makes the wait for those loads happen here, once, before the output
+    // stores are in flight (left to the compiler, it lands before the score
+    // products inside the step loop, every other step).
+#pragma unroll
+    for (int c = 0; c < CT; ++c) {
+#pragma unroll
+      for (int kc = 0; kc < NKC; ++kc) {
+        qf[c][kc] = qn[c][kc];
+        asm volatile("" : "+v"(qf[c][kc]));
+      }
+    }
+    finish_item(cur);
+    const int tk = 2 * grid + __builtin_amdgcn_readfirstlane(s_ticket[tpar]);
+    tpar ^= 1;
+    cur = n1;
+    if (!cur.valid) break;
+    make_item(tk, n1);
+    load_q(n1, qn);
   }
 }
 
 template <int D, int G>
 int launch_prefill_t(const DecodeArgs& a, hipStream_t st) {
   const DecodeParams p = make_params(a);
-  static int per_cu = 0;
-  if (per_cu == 0) {
-    int nb = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, prefill_mfma_kernel<D, G>, kDecodeThreads, 0) !=
-            hipSuccess || nb < 1)
-      nb = 1;
-    per_cu = nb;
-  }
   const int64_t items = (int64_t)a.pre_cap * a.num_kv_heads;  // upper bound
-  const int64_t grid = std::min<int64_t>(items, (int64_t)a.num_cus * per_cu);
+  const int64_t grid = std::min<int64_t>(items, (int64_t)a.num_cus);
   hipLaunchKernelGGL((prefill_mfma_kernel<D, G>), dim3((unsigned)std::max<int64_t>(grid, 1)),
-                     dim3(kDecodeThreads), 0, st, p);
+                     dim3(kPrefillThreads), 0, st, p);
   return (int)hipGetLastError();
 }
 
