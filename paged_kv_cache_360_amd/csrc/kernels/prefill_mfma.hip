@@ -200,19 +200,27 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void prefill_mfma_kernel(Decode
     kk = buffer_load_piece<PT>(kr, off, 0);
     vv = buffer_load_piece<PT>(vr, off, 0);
   };
-  // This thread's rows of step `step` of an item.  Block ids are scalar loads
-  // from the table (written before this launch, read-only here): they never
-  // wait for the vector loads in flight.
-  auto issue_step = [&](int s, int g, int b_begin, int nblk, int step, Stage& st) {
+  // Block ids of this wave's rows of step `step` of an item: scalar loads from
+  // the table (written before this launch, read-only here), which never wait
+  // for the vector loads in flight; -1 past the item's blocks.
+  struct Ids {
+    int v[RPT];
+  };
+  auto step_ids = [&](int s, int b_begin, int nblk, int step) {
     const __attribute__((address_space(4))) int* trow =
         (const __attribute__((address_space(4))) int*)(const void*)(p.tables + (int64_t)s * p.MB + b_begin);
+    Ids ids;
 #pragma unroll
     for (int j = 0; j < RPT; ++j) {
       const int row = st_row + j * kRowStride;                 // wave-uniform block
       const int k = 2 * step + __builtin_amdgcn_readfirstlane(row / kBlockTokens);
-      const int id = k < nblk ? trow[k] : -1;
-      issue_row(g, id, row, st.k[j], st.v[j]);
+      ids.v[j] = k < nblk ? trow[k] : -1;
     }
+    return ids;
+  };
+  auto issue_step = [&](int g, const Ids& ids, Stage& st) {
+#pragma unroll
+    for (int j = 0; j < RPT; ++j) issue_row(g, ids.v[j], st_row + j * kRowStride, st.k[j], st.v[j]);
   };
   auto stage_to_lds = [&](const Stage& st, int buf) {
 #pragma unroll
@@ -416,14 +424,23 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void prefill_mfma_kernel(Decode
   // The stream position `ahead` <= NS + 2 steps after step q of cur, chosen by
   // selects so that every path issues the same loads in the same order; an
   // invalid item has no blocks (zero-sized loads).
-  auto issue_ahead = [&](int q, int ahead, Stage& st) {
+  // The ids of each position are loaded one issue ahead (pf_ids, valid when
+  // pf_ok), so the issue does not wait for the scalar load; a position past n1
+  // is not known yet and is loaded at its issue instead.
+  Ids pf_ids;
+  bool pf_ok = false;
+  auto known = [&](int q, int ahead) { return q + ahead < cur.nsteps + n1.nsteps; };
+  auto position_ids = [&](int q, int ahead) {
     const int r0 = q + ahead;
     const bool in_cur = r0 < cur.nsteps;
-    const int s = in_cur ? cur.s : n1.s;
-    const int g = in_cur ? cur.g : n1.g;
-    const int b_begin = in_cur ? cur.b_begin : n1.b_begin;
-    const int nblk = in_cur ? cur.nblk : n1.nblk;
-    issue_step(s, g, b_begin, nblk, in_cur ? r0 : r0 - cur.nsteps, st);
+    return step_ids(in_cur ? cur.s : n1.s, in_cur ? cur.b_begin : n1.b_begin, in_cur ? cur.nblk : n1.nblk,
+                    in_cur ? r0 : r0 - cur.nsteps);
+  };
+  auto issue_ahead = [&](int q, int ahead, Stage& st) {
+    const Ids ids = pf_ok ? pf_ids : position_ids(q, ahead);  // always within n1 here
+    issue_step(q + ahead < cur.nsteps ? cur.g : n1.g, ids, st);
+    pf_ok = known(q, ahead + 1);
+    if (pf_ok) pf_ids = position_ids(q, ahead + 1);
   };
 
   // Step q is staged into LDS at iteration q - 2 (from the registers its loads
