@@ -69,6 +69,13 @@ VARLEN_CASES = {
     "mha_d64": (8, 8, 64, [1, 70, 2, 65], [90, 800, 513, 65]),
     "gqa8_d128": (16, 2, 128, [9, 1, 33, 8], [1024, 517, 600, 8]),
     "gqa2_d64": (8, 4, 64, [31, 1, 12], [700, 1000, 12]),
+    # one tile row group per 256 / G rows: chunks at, one past and one short of
+    # that size, with last rows that cross a 512-key partition boundary
+    "mha_d128": (16, 16, 128, [64, 1, 257, 5], [64, 900, 1030, 520]),
+    "gqa2_d128": (16, 8, 128, [128, 129, 2], [128, 1000, 2]),
+    "gqa8_d64": (32, 4, 64, [33, 32, 1], [33, 600, 3000]),
+    # prefill rows only (no decode work), row groups of 64 at partition edges
+    "gqa4_d128_item_edges": (32, 8, 128, [64, 65, 128, 63], [64, 577, 640, 1087]),
 }
 
 
@@ -79,6 +86,22 @@ def test_varlen_matches_oracle(name):
     inp = mixed_case(zlib.crc32(name.encode()) % 1000, hq, hkv, d, qlens, ctxs)
     got = host_f64(gpu_varlen(inp))
     assert_close(got, oracle_varlen(inp), "bf16", name)
+
+
+def test_varlen_many_short_chunks():
+    """Many chunks of 2 .. 12 rows over short contexts, so that a persistent
+    workgroup runs several one- and two-block items in a row (the key stream
+    prefetched across item boundaries), interleaved with decode rows."""
+    rng = np.random.default_rng(53)
+    n = 150
+    qlens = rng.integers(2, 13, n)
+    qlens[rng.random(n) < 0.2] = 1
+    ctxs = np.maximum(qlens, rng.integers(1, 260, n))
+    ctxs[::7] = qlens[::7]                      # chunks that are the whole context
+    say(f"varlen many short chunks: {n} seqs, {int(qlens.sum())} rows")
+    inp = mixed_case(53, 32, 8, 128, qlens, ctxs)
+    got = host_f64(gpu_varlen(inp))
+    assert_close(got, oracle_varlen(inp), "bf16", "short chunks")
 
 
 def test_varlen_unit_scale_zero_query():
