@@ -410,8 +410,10 @@ def mixed_main(args, spec):
     Sequence 0 holds a context of spec.chunk_ctx tokens whose last spec.chunk_rows
     are the chunk's query rows (written every step into the same slots, so each
     step has the same shape); sequences 1..S append one decode token per step.
-    One step = host allocation + metadata H2D + pkv_write of all new rows +
-    pkv_attention_varlen (plan, decode partitions, prefill tiles, merge).
+    One step = host allocation into pinned staging + one H2D copy on a side
+    stream + pkv_write of all new rows + pkv_attention_varlen (plan, decode
+    partitions, prefill tiles, merge).  The write and attention launches of
+    every EV_EVERY-th timed step are bracketed by events.
     """
     import numpy as np
     import torch
@@ -454,30 +456,63 @@ def mixed_main(args, spec):
     ws = pkv.varlen_workspace(S + 1, T, Hq, Hkv, D, C, max_ctx)
     scale = float(np.float32(1.0 / math.sqrt(D)))
     qsl = torch.from_numpy(np.concatenate([[0], C + np.arange(S + 1)]).astype(np.int32)).cuda()
-    slots_h = np.empty(T, np.int32)
-    slots_h[:C] = chunk_slots
+
+    # pinned staging, two sets: [slots T | lens S+1 | tables (S+1)*MB] int32
+    meta_len = T + (S + 1) + (S + 1) * MB
+    stage = [torch.empty(meta_len, dtype=torch.int32, pin_memory=True) for _ in range(2)]
+    dmeta = [torch.empty(meta_len, dtype=torch.int32, device="cuda") for _ in range(2)]
+    views = []
+    for b in range(2):
+        h = stage[b].numpy()
+        h[:C] = chunk_slots                               # the chunk rewrites the same slots each step
+        views.append((h[:T], h[T:T + S + 1], h[T + S + 1:].reshape(S + 1, MB)))
+    ones = np.ones(S, np.int32)
     main = torch.cuda.current_stream()
+    side = torch.cuda.Stream()                            # default priority
+    h2d_done = [torch.cuda.Event() for _ in range(2)]
+    kern_done = [torch.cuda.Event() for _ in range(2)]
     events, lens_log = [], []
 
+    # direct C-ABI calls with precomputed pointers (as in the decode step)
+    L = pkv.lib()
+    check = pkv.check
+    q_stride, kv_stride = T * Hq * D * 2, T * Hkv * D * 2
+    q0, knew0, vnew0, out_p = qs.data_ptr(), knew.data_ptr(), vnew.data_ptr(), out.data_ptr()
+    kc_p = [t.data_ptr() for t in kcs]
+    vc_p = [t.data_ptr() for t in vcs]
+    dptr = [m.data_ptr() for m in dmeta]
+    qsl_p, ws_p, ws_n, main_h = qsl.data_ptr(), ws.data_ptr(), ws.numel(), main.cuda_stream
+
     def step(i, timed):
-        _, pairs = alloc.append_batch(ids[1:], np.ones(S, np.int32), slots_out=slots_h[C:])
-        tables, lens = alloc.block_tables(ids, MB)
-        d_slots = torch.from_numpy(slots_h).cuda(non_blocking=False)
-        d_tables = torch.from_numpy(tables).cuda()
-        d_lens = torch.from_numpy(lens).cuda()
+        b = i % 2
+        slots_h, lens_h, tables_h = views[b]
+        h2d_done[b].synchronize()                         # staging set b is free (copy of step i-2 done)
+        _, pairs = alloc.append_batch(ids[1:], ones, slots_out=slots_h[C:])
+        alloc.block_tables(ids, MB, fill=-1, tables_out=tables_h, lens_out=lens_h)
         r = i % R
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)] if timed else None
+        with torch.cuda.stream(side):
+            side.wait_event(kern_done[b])                 # device set b no longer read by step i-2
+            dmeta[b].copy_(stage[b], non_blocking=True)
+            h2d_done[b].record(side)
+        main.wait_event(h2d_done[b])
+        bracket = timed and (i - W) % EV_EVERY == 0
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)] if bracket else None
         if timed:
-            lens_log.append(lens.copy())
+            lens_log.append(lens_h.copy())
+        if bracket:
             ev[0].record(main)
-        pkv.pkv_write(kcs[r], vcs[r], knew[i], vnew[i], d_slots)
-        if timed:
+        d = dptr[b]
+        check("pkv_write", L.pkv_write(kc_p[r], vc_p[r], knew0 + i * kv_stride, vnew0 + i * kv_stride, d, T, nb,
+                                       16, Hkv, D, pkv.PKV_BF16, main_h))
+        if bracket:
             ev[1].record(main)
-        pkv.pkv_attention_varlen(out, qs[i], kcs[r], vcs[r], d_tables, d_lens, qsl, scale, C, max_ctx,
-                                 workspace=ws)
-        if timed:
+        check("pkv_attention_varlen", L.pkv_attention_varlen(
+            out_p, q0 + i * q_stride, kc_p[r], vc_p[r], d + 4 * (T + S + 1), d + 4 * T, qsl_p, T, C, scale, 16,
+            Hq, Hkv, D, S + 1, MB, nb, max_ctx, pkv.PKV_BF16, ws_p, ws_n, main_h))
+        if bracket:
             ev[2].record(main)
             events.append(ev)
+        kern_done[b].record(main)
 
     for i in range(W):
         step(i, False)

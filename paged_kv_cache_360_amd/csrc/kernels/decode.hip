@@ -253,10 +253,13 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_partition_kernel(Decode
 // are skipped); otherwise from num_parts[row].
 // Latency is one round trip per kMergeUnroll partitions: the first group's
 // partial outputs are loaded before the maxima are reduced, and the maxima and
-// sums are read lane-parallel (64 partitions per load).
+// sums are read lane-parallel (64 partitions per load).  LIVE_LOADS: a partial
+// output is loaded only where its sum is positive (one more round trip; for
+// batches whose prefill items span two partitions, where every other slot of
+// such a row is empty).
 constexpr int kMergeUnroll = 8;
 
-template <bool BF16, int D, bool FROM_KEYS>
+template <bool BF16, int D, bool FROM_KEYS, bool LIVE_LOADS = false>
 __global__ __launch_bounds__(kWave) void lse_merge_kernel(
     void* __restrict__ out, const float* __restrict__ pm, const float* __restrict__ pl,
     const float* __restrict__ po, const int32_t* __restrict__ counts, int32_t Hq,
@@ -277,11 +280,16 @@ __global__ __launch_bounds__(kWave) void lse_merge_kernel(
   const float* rl = pl + row * max_parts;
   const float* ro = po + row * max_parts * D;
 
+  auto wanted = [&](int i) {  // i < n
+    if constexpr (LIVE_LOADS) return rl[i] > 0.f;
+    return true;
+  };
   float ov[U][PER];  // first group of partial outputs, in flight during the reductions
 #pragma unroll
   for (int u = 0; u < U; ++u) {
+    const bool w = u < n && wanted(u);
 #pragma unroll
-    for (int k = 0; k < PER; ++k) ov[u][k] = u < n ? ro[(int64_t)u * D + lane + k * kWave] : 0.f;
+    for (int k = 0; k < PER; ++k) ov[u][k] = w ? ro[(int64_t)u * D + lane + k * kWave] : 0.f;
   }
 
   // live partial: l > 0 and a finite max; the rest weigh 0
@@ -313,9 +321,9 @@ __global__ __launch_bounds__(kWave) void lse_merge_kernel(
     for (int base = U; base < n; base += U) {
 #pragma unroll
       for (int u = 0; u < U; ++u) {
+        const bool w = base + u < n && wanted(base + u);
 #pragma unroll
-        for (int k = 0; k < PER; ++k)
-          ov[u][k] = base + u < n ? ro[(int64_t)(base + u) * D + lane + k * kWave] : 0.f;
+        for (int k = 0; k < PER; ++k) ov[u][k] = w ? ro[(int64_t)(base + u) * D + lane + k * kWave] : 0.f;
       }
 #pragma unroll
       for (int u = 0; u < U; ++u) {
@@ -349,8 +357,13 @@ int launch_partitions_g(const DecodeParams& p, const DecodeArgs& a, hipStream_t 
 
 template <bool BF16, int D>
 void launch_merge_t(const DecodeArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL((lse_merge_kernel<BF16, D, true>), dim3(a.num_tokens * a.num_q_heads), dim3(kWave),
-                     0, st, a.out, a.part_m, a.part_l, a.part_o, a.row_keys, a.num_q_heads, a.max_parts);
+  const dim3 grid(a.num_tokens * a.num_q_heads), block(kWave);
+  if (a.qsl)  // variable-length batch: prefill rows may have empty slots
+    hipLaunchKernelGGL((lse_merge_kernel<BF16, D, true, true>), grid, block, 0, st, a.out, a.part_m, a.part_l,
+                       a.part_o, a.row_keys, a.num_q_heads, a.max_parts);
+  else
+    hipLaunchKernelGGL((lse_merge_kernel<BF16, D, true>), grid, block, 0, st, a.out, a.part_m, a.part_l,
+                       a.part_o, a.row_keys, a.num_q_heads, a.max_parts);
 }
 
 }  // namespace

@@ -15,10 +15,13 @@
 //    full, kItemBlocks blocks) first, then each sequence's last item in
 //    decreasing block count (a counting sort over the kItemBlocks + 1 possible
 //    counts), so the persistent run ends on its shortest items;
-//  * prefill records, two int4 each: {sequence, partition, context, first query
-//    row} and {rows, ctx - q + r0 + 1, 0, 0} (row i of the group sees max(0, that
-//    + i) keys; negative when the chunk is longer than the context); one per (group of
-//    rows_per_item consecutive rows, partition the group's last row reaches);
+//  * prefill records, two int4 each: {sequence, first partition, context, first
+//    query row} and {rows, ctx - q + r0 + 1, span, 0} (row i of the group sees
+//    max(0, that + i) keys; negative when the chunk is longer than the context);
+//    one per (group of rows_per_item consecutive rows, run of `span` partitions
+//    up to the one the group's last row reaches).  The span is 2 when halving
+//    the item count still leaves every compute unit the same number of rounds
+//    of items (then each row writes half the partial results), else 1;
 //  * row_keys[T]: the keys each query row sees (its partition count for the
 //    merge);
 //  * sched: both ticket counters reset, and each list's ticket count (records
@@ -37,11 +40,12 @@ namespace {
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(
     const int32_t* __restrict__ ctx, const int32_t* __restrict__ qsl, int32_t S, int32_t T,
     int32_t ctx_cap, int32_t Hkv, int32_t rows_per_item, int32_t dec_cap, int32_t pre_cap,
-    int32_t* __restrict__ sched, int4* __restrict__ dec, int4* __restrict__ pre,
+    int32_t num_cus, int32_t* __restrict__ sched, int4* __restrict__ dec, int4* __restrict__ pre,
     int32_t* __restrict__ row_keys) {
   constexpr int NBK = kItemBlocks + 1;  // buckets: last-item block count kItemBlocks .. 0
   __shared__ int32_t s_full[kPlanThreads];
-  __shared__ int32_t s_pre[kPlanThreads];
+  __shared__ int32_t s_pre[kPlanThreads];   // prefill records at span 1
+  __shared__ int32_t s_pre2[kPlanThreads];  // and at span 2
   __shared__ int32_t s_bucket[NBK];
   const int t = threadIdx.x;
   const int per = (S + kPlanThreads - 1) / kPlanThreads;
@@ -62,7 +66,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(
   if (t < NBK) s_bucket[t] = 0;
   for (int r = t; r < T; r += kPlanThreads) row_keys[r] = 0;  // rows no sequence owns see nothing
   __syncthreads();
-  int full = 0, npre = 0;
+  int full = 0, npre = 0, npre2 = 0;
   int own_c = 0, own_q = 0, own_row0 = 0;  // this thread's (last) sequence, for the write loop
   for (int s = s0; s < s1; ++s) {
     const int c = ctx_of(s);
@@ -75,23 +79,35 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(
       full += items_of(n) - 1;
       atomicAdd(&s_bucket[last_bucket(c, n)], 1);
     } else if (q > 1) {
-      for (int r0 = 0; r0 < q; r0 += rows_per_item)
-        npre += parts_of(row_keys_of(c, q, min(q, r0 + rows_per_item) - 1));
+      for (int r0 = 0; r0 < q; r0 += rows_per_item) {
+        const int n = parts_of(row_keys_of(c, q, min(q, r0 + rows_per_item) - 1));
+        npre += n;
+        npre2 += (n + 1) / 2;
+      }
     }
   }
   s_full[t] = full;
   s_pre[t] = npre;
+  s_pre2[t] = npre2;
   __syncthreads();
   for (int off = 1; off < kPlanThreads; off <<= 1) {  // inclusive scans (Hillis-Steele)
     const int vf = t >= off ? s_full[t - off] : 0;
     const int vp = t >= off ? s_pre[t - off] : 0;
+    const int vp2 = t >= off ? s_pre2[t - off] : 0;
     __syncthreads();
     s_full[t] += vf;
     s_pre[t] += vp;
+    s_pre2[t] += vp2;
     __syncthreads();
   }
   const int num_full = s_full[kPlanThreads - 1];
-  const int num_pre = s_pre[kPlanThreads - 1];
+  // Prefill span: rounds of items per compute unit (one workgroup each) at
+  // span 1 and 2; span 2 when its rounds, each twice as long, take no longer.
+  const int64_t cus = max(1, num_cus);
+  const int64_t rounds1 = ((int64_t)s_pre[kPlanThreads - 1] * Hkv + cus - 1) / cus;
+  const int64_t rounds2 = ((int64_t)s_pre2[kPlanThreads - 1] * Hkv + cus - 1) / cus;
+  const int span = (rounds1 > 1 && 2 * rounds2 <= rounds1) ? 2 : 1;
+  const int num_pre = span == 2 ? s_pre2[kPlanThreads - 1] : s_pre[kPlanThreads - 1];
   if (t == 0) {  // bucket start offsets in the decode tail region
     int acc = num_full;
     for (int k = 0; k < NBK; ++k) {
@@ -125,7 +141,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(
       if ((per == 1 ? own_q : rows_of(s)) > 1) return s;
     return s1;
   };
-  int op = s_pre[t] - npre;
+  int op = span == 2 ? s_pre2[t] - npre2 : s_pre[t] - npre;
   int ps = next_prefill(s0);
   for (;;) {
     const unsigned long long pending = __ballot(ps < s1);
@@ -138,12 +154,12 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(
     const int row0 = first_row(s);
     for (int r0 = 0; r0 < q; r0 += rows_per_item) {
       const int nr = min(q, r0 + rows_per_item) - r0;
-      const int n = parts_of(row_keys_of(c, q, r0 + nr - 1));
+      const int n = (parts_of(row_keys_of(c, q, r0 + nr - 1)) + span - 1) / span;
       for (int k = lane; k < n; k += kWave) {
         if (cop + k < pre_cap) {
-          pre[2 * (cop + k)] = make_int4(s, k, c, row0 + r0);
+          pre[2 * (cop + k)] = make_int4(s, k * span, c, row0 + r0);
           // unclamped: row i of the group sees max(0, this + i) keys
-          pre[2 * (cop + k) + 1] = make_int4(nr, c - q + r0 + 1, 0, 0);
+          pre[2 * (cop + k) + 1] = make_int4(nr, c - q + r0 + 1, span, 0);
         }
       }
       cop += n;
@@ -172,7 +188,7 @@ int launch_plan(const DecodeArgs& a, void* stream) {
   const int32_t G = a.num_q_heads / a.num_kv_heads;
   hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, (hipStream_t)stream, a.ctx, a.qsl,
                      a.num_seqs, a.num_tokens, p.ctx_cap, a.num_kv_heads, prefill_rows_per_item(G),
-                     a.dec_cap, a.pre_cap, a.sched, reinterpret_cast<int4*>(a.dec_recs),
+                     a.dec_cap, a.pre_cap, a.num_cus, a.sched, reinterpret_cast<int4*>(a.dec_recs),
                      reinterpret_cast<int4*>(a.pre_recs), a.row_keys);
   return (int)hipGetLastError();
 }

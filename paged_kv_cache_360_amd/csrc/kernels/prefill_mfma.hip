@@ -10,8 +10,10 @@
 //
 // Unlike a decode row, a chunk's rows make a dense tile, so this kernel runs on
 // the 32x32x16 matrix instructions (the fastest bf16 shape here).  A workgroup
-// item is 256/G consecutive rows x the G q heads of one KV head over one
-// partition of keys; each of the eight waves owns one 32-column tile (column n
+// item is 256/G consecutive rows x the G q heads of one KV head over one or two
+// partitions of keys (the plan's span: two when the batch has enough items to
+// keep every compute unit busy, which halves the partial results written and
+// merged); each of the eight waves owns one 32-column tile (column n
 // = row n/G of the wave's 32/G rows, head n%G).
 // Keys go in steps of 32 tokens (two blocks):
 //  * scores S^T[t][n] = sum_d K[t][d] q[n][d]: v_mfma_f32_32x32x16_bf16, D/16
@@ -22,16 +24,19 @@
 //  * values O^T[d][n] += sum_t V^T[d][t] P^T[t][n]: two 16-token k-steps of
 //    D/32 MFMAs per tile.  B = P^T is the score registers i = 8s .. 8s+7 of
 //    k-step s, rounded to bf16: element e <-> token 16s + 8*(e/4) + 4h + e%4.
-//    A = V^T takes the same tokens for the same elements: each lane reads
-//    those 8 token rows at dims NT*m .. NT*m + NT-1 (m = lane%32, NT = D/32)
-//    and regroups 16-bit halves, so tile e holds dim NT*m + e in row slot m.
-//    C: lane (n, h), register i <-> dim NT*(8*(i/4) + 4h + i%4) + e.
+//    A = V^T takes the same tokens for the same elements, dim 32E + lane%32
+//    for output tile E: two transposing LDS reads (ds_read_b64_tr_b16) per
+//    tile and k-step gather them from the token-major V rows in LDS.
+//    C: lane (n, h), register i of tile E <-> dim 32E + 8*(i/4) + 4h + i%4.
 // Each column keeps its own causal mask (token < the keys its row sees), so the
 // diagonal block needs no special case.
 //
 // K and V of each step are loaded once per workgroup (one D/8-byte piece of K
 // and of V per thread and step row), staged through a three-buffer LDS slab
-// with rows padded to D*2 + 16 bytes, and read by every wave.  Each wave
+// (K rows padded to D*2 + 16 bytes, V rows to D*2 + 64, which keeps both read
+// patterns free of bank conflicts), and read by every wave.  Rows past the
+// context read as zeros (the block's buffer resource ends at the context), so
+// a V row there never meets a zero weight as 0 * NaN.  Each wave
 // computes the scores of step q + 1 while it runs step q's softmax and value
 // products, so the matrix cores work during the vector code.  The load stream
 // runs four steps ahead of the computation across item boundaries: the
@@ -41,7 +46,9 @@
 // Workgroups take items from the prefill tickets: the first two are static
 // (blockIdx.x and blockIdx.x + gridDim.x), the rest come from the counter.  A row whose
 // keys fit one partition gets its output written directly; other rows'
-// partials go to the workspace for the merge.
+// partials go to the workspace for the merge, in the slot of the item's first
+// partition, with the second partition's slot of a two-partition item marked
+// empty (zero sum).
 
 #include <hip/hip_runtime.h>
 
@@ -77,15 +84,17 @@ constexpr int kPrefillSteps = PKV_PREFILL_STEPS;  // steps of K/V in flight
 template <int D> struct KVPiece;
 template <> struct KVPiece<128> { using T = uint4; };
 template <> struct KVPiece<64> { using T = uint2; };
-// One lane's dims of a V row for the V^T operand: D / 32 bf16 values.
-template <int D> struct VDims;
-template <> struct VDims<128> { using T = uint2; };
-template <> struct VDims<64> { using T = uint32_t; };
 
-// 16-bit halves of two words, one byte permute each: (low(a), low(b)) and
-// (high(a), high(b)).
-__device__ __forceinline__ uint32_t pair_lo(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x05040100u); }
-__device__ __forceinline__ uint32_t pair_hi(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x07060302u); }
+// Transposing LDS read of 16-bit data (gfx950): each lane names 8 bytes (four
+// 16-bit values); within each group of 16 lanes, lane i receives value i%4 of
+// lanes 4j + i/4, j = 0..3, as its values j.  With lane 4j + a of a group
+// pointing at four consecutive dims 4a .. 4a+3 of token row j, lane i gets dim
+// i of the four token rows.
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint2 lds_read_tr16(const char* p) {
+  const i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(p));
+  return __builtin_bit_cast(uint2, r);
+}
 // Sum of a packed bf16 pair, added to acc (one dot-product instruction).
 __device__ __forceinline__ float add_bf16_pair(uint32_t w, float acc) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), __builtin_bit_cast(bf16x2, 0x3F803F80u), acc,
@@ -95,8 +104,6 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   const bf16x2 v = {(__bf16)a, (__bf16)b};
   return __builtin_bit_cast(uint32_t, v);
 }
-__device__ __forceinline__ uint32_t word(uint2 v, int k) { return k == 0 ? v.x : v.y; }
-__device__ __forceinline__ uint32_t word(uint32_t v, int) { return v; }
 
 template <int D, int G>
 __global__ __launch_bounds__(kPrefillThreads, 1) void prefill_mfma_kernel(DecodeParams p) {
@@ -105,11 +112,11 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void prefill_mfma_kernel(Decode
   constexpr int CT = kColTiles;
   constexpr int R = 32 / G;                // rows per column tile
   constexpr int RPW = CT * R;              // rows per wave
-  constexpr int RS = D * 2 + 16;           // LDS row stride in bytes (16-byte pad)
+  constexpr int RSK = D * 2 + 16;          // LDS row strides in bytes: K (16-byte pad)
+  constexpr int RSV = D * 2 + 64;          // and V (64-byte pad)
   constexpr int PS = D / 8;                // bytes per thread and block row
   constexpr int NS = kPrefillSteps;
   using PT = typename KVPiece<D>::T;
-  using VD = typename VDims<D>::T;
   static_assert(G >= 1 && G <= 32 && 32 % G == 0, "a tile holds whole rows of G heads");
   constexpr int RPT = kStepTokens * 16 / kPrefillThreads;  // step rows each thread stages
   static_assert(RPT >= 1 && kStepTokens * 16 % kPrefillThreads == 0, "16 threads per token row");
@@ -125,13 +132,14 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void prefill_mfma_kernel(Decode
   const int total = min(p.sched[3], p.pre_cap * p.Hkv);
   const int grid = (int)gridDim.x;
 
-  // [buffer][K, V][32 rows x RS bytes]: three buffers, step q in q % 3 (the
+  // [buffer][32 rows x row stride]: three buffers, step q in q % 3 (the
   // scores of step q + 1 are computed while step q's values are)
-  __shared__ __attribute__((aligned(16))) char s_kv[3][2][kStepTokens * RS];
+  __shared__ __attribute__((aligned(16))) char s_k[3][kStepTokens * RSK];
+  __shared__ __attribute__((aligned(16))) char s_v[3][kStepTokens * RSV];
   __shared__ int s_ticket[2];
 
   struct Item {
-    int s, part, g, ctx, qrow0, nrows, key0, b_begin, nblk, nsteps;
+    int s, part, span, g, ctx, qrow0, nrows, key0, b_begin, nblk, nsteps;
     bool valid;
   };
   // Records are written by the plan launch and read-only here: read through the
@@ -149,9 +157,10 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void prefill_mfma_kernel(Decode
     it.qrow0 = r[3];
     it.nrows = r[4];
     it.key0 = r[5];                                       // row i sees max(0, key0 + i) keys
+    it.span = r[6];                                       // partitions covered: 1 or 2
     const int key_last = max(0, it.key0 + it.nrows - 1);  // keys the item's last row sees
     const int k_begin = it.part * kPartTokens;
-    const int k_end = min(k_begin + kPartTokens, key_last);
+    const int k_end = min(k_begin + it.span * kPartTokens, key_last);
     it.b_begin = it.part * kPartBlocks;
     it.nblk = it.valid ? max(0, (k_end - k_begin + kBlockTokens - 1) / kBlockTokens) : 0;
     // steps of two blocks, padded to a multiple of NS so that every item starts
@@ -184,14 +193,13 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void prefill_mfma_kernel(Decode
   struct Stage {
     PT k[RPT], v[RPT];
   };
-  // Block k of a partition (block id pb; -1 past the partition): the loads go
-  // through resources sized to the block, empty for an id outside the pool.
-  // Row `row` (block row row % 16) of block id pb (-1 past the partition): the
-  // loads go through resources sized to the block, empty for an id outside the pool.
-  auto issue_row = [&](int g, int pb, int row, PT& kk, PT& vv) {
+  // Row `row` (block row row % 16) of block id pb (-1 past the partition),
+  // whose first `lim` rows are in the context: the loads go through resources
+  // that end there (rows past it read zeros), empty for an id outside the pool.
+  auto issue_row = [&](int g, int pb, int lim, int row, PT& kk, PT& vv) {
     const bool ok = (unsigned)pb < (unsigned)p.NB;
     const int64_t base = (int64_t)(ok ? pb : 0) * blk_bytes;
-    const int nrec = ok ? (int)blk_bytes : 0;
+    const int nrec = ok ? lim * (int)tok_bytes : 0;
     const __amdgpu_buffer_rsrc_t kr =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(p.kc + base), (short)0, nrec, kRawBufferWord3);
     const __amdgpu_buffer_rsrc_t vr =
@@ -202,11 +210,12 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void prefill_mfma_kernel(Decode
   };
   // Block ids of this wave's rows of step `step` of an item: scalar loads from
   // the table (written before this launch, read-only here), which never wait
-  // for the vector loads in flight; -1 past the item's blocks.
+  // for the vector loads in flight; -1 past the item's blocks.  With each id,
+  // the number of the block's rows inside the context.
   struct Ids {
-    int v[RPT];
+    int v[RPT], lim[RPT];
   };
-  auto step_ids = [&](int s, int b_begin, int nblk, int step) {
+  auto step_ids = [&](int s, int b_begin, int nblk, int ctx, int step) {
     const __attribute__((address_space(4))) int* trow =
         (const __attribute__((address_space(4))) int*)(const void*)(p.tables + (int64_t)s * p.MB + b_begin);
     Ids ids;
@@ -215,19 +224,20 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void prefill_mfma_kernel(Decode
       const int row = st_row + j * kRowStride;                 // wave-uniform block
       const int k = 2 * step + __builtin_amdgcn_readfirstlane(row / kBlockTokens);
       ids.v[j] = k < nblk ? trow[k] : -1;
+      ids.lim[j] = min(kBlockTokens, ctx - (b_begin + k) * kBlockTokens);
     }
     return ids;
   };
   auto issue_step = [&](int g, const Ids& ids, Stage& st) {
 #pragma unroll
-    for (int j = 0; j < RPT; ++j) issue_row(g, ids.v[j], st_row + j * kRowStride, st.k[j], st.v[j]);
+    for (int j = 0; j < RPT; ++j) issue_row(g, ids.v[j], ids.lim[j], st_row + j * kRowStride, st.k[j], st.v[j]);
   };
   auto stage_to_lds = [&](const Stage& st, int buf) {
 #pragma unroll
     for (int j = 0; j < RPT; ++j) {
       const int row = st_row + j * kRowStride;
-      *reinterpret_cast<PT*>(&s_kv[buf][0][row * RS + st_col]) = st.k[j];
-      *reinterpret_cast<PT*>(&s_kv[buf][1][row * RS + st_col]) = st.v[j];
+      *reinterpret_cast<PT*>(&s_k[buf][row * RSK + st_col]) = st.k[j];
+      *reinterpret_cast<PT*>(&s_v[buf][row * RSV + st_col]) = st.v[j];
     }
   };
 
@@ -239,45 +249,47 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void prefill_mfma_kernel(Decode
 
   // Scores of the step in LDS buffer buf (the matrix products only).
   auto scores = [&](int buf, f32x16 (&sc)[CT]) {
-    const char* kb = s_kv[buf][0];
+    const char* kb = s_k[buf];
 #pragma unroll
     for (int c = 0; c < CT; ++c) sc[c] = f32x16{};
 #pragma unroll
     for (int kc = 0; kc < NKC; ++kc) {
-      const bf16x8 kf = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(kb + n * RS + 32 * kc + 16 * hh));
+      const bf16x8 kf = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(kb + n * RSK + 32 * kc + 16 * hh));
 #pragma unroll
       for (int c = 0; c < CT; ++c) sc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[c][kc], sc[c], 0, 0, 0);
     }
   };
+  // This lane's address in a V buffer for the transposing reads: lane
+  // 16g + 4j + a names token row 4*(g/2) + j (of the 8-row group read), dims
+  // 16*(g%2) + 4a .. +3 of the output tile, so that lane 16g + i receives dim
+  // 16*(g%2) + i = lane%32 of token rows 4*(g/2) + 0..3 = 4*hh + 0..3.
+  const int v_lane = (4 * hh + ((lane >> 2) & 3)) * RSV + (16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2;
+
   // Softmax and value products of a step from its scores and LDS buffer buf:
-  // tokens t0 .. t0+31, of which `valid` are in the context (V rows past it
-  // are zeroed: 0 * NaN).
-  auto softmax_values = [&](f32x16 (&sc)[CT], int buf, int t0, int valid) {
-    const char* vb = s_kv[buf][1];
+  // tokens t0 .. t0+31 (V rows past the context hold zeros).
+  auto softmax_values = [&](f32x16 (&sc)[CT], int buf, int t0) {
+    const char* vb = s_v[buf] + v_lane;
     // softmax per column in base 2: register i holds token 8*(i/4) + 4*hh + i%4.
     // Only steps that reach past some column's keys (the causal edge, the end
-    // of the context) need the per-element mask; the others take the scale into
-    // the exponent's fused multiply-add.
+    // of the context) need the per-element mask, which sets the raw score to
+    // -inf; every step then takes the scale into the exponent's fused
+    // multiply-add (-inf stays -inf: the scale is positive).
     const bool masked = t0 + kStepTokens > min_keys;  // uniform over the wave
     float ms[CT], mref[CT];
     bool grew = false;
 #pragma unroll
     for (int c = 0; c < CT; ++c) {
-      float mx;
       if (masked) {
-        mx = -INFINITY;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int t = t0 + 8 * (i / 4) + 4 * hh + (i % 4);
-          sc[c][i] = t < col_keys[c] ? sc[c][i] * p.scale_log2 : -INFINITY;
-          mx = fmaxf(mx, sc[c][i]);
+          sc[c][i] = t < col_keys[c] ? sc[c][i] : -INFINITY;
         }
-      } else {
-        float r = sc[c][0];
-#pragma unroll
-        for (int i = 1; i < 16; ++i) r = fmaxf(r, sc[c][i]);
-        mx = r * p.scale_log2;  // the scale is positive: the max commutes with it
       }
+      float r = sc[c][0];
+#pragma unroll
+      for (int i = 1; i < 16; ++i) r = fmaxf(r, sc[c][i]);
+      const float mx = r * p.scale_log2;  // the scale is positive: the max commutes with it
       const float mb = max_over_halves(mx);
       const bool up = mb > m[c] + kRescaleLog2;  // -inf + 8 = -inf: the first live step moves it
       const float mn = up ? mb : m[c];
@@ -295,10 +307,7 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void prefill_mfma_kernel(Decode
         for (int e = 0; e < NT; ++e) acc[c][e] *= alpha;
       }
     }
-    auto weight = [&](int c, int i) {
-      return masked ? exp2_fast(sc[c][i] - mref[c]) : exp2_fast(fmaf(sc[c][i], p.scale_log2, -mref[c]));
-    };
-    const bool ragged = valid < kStepTokens;  // uniform: V rows past the context are zeroed
+    auto weight = [&](int c, int i) { return exp2_fast(fmaf(sc[c][i], p.scale_log2, -mref[c])); };
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       // P^T operand of k-step s (rounded weights summed into l)
@@ -313,30 +322,13 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void prefill_mfma_kernel(Decode
         }
         pt[c] = __builtin_bit_cast(bf16x8, make_uint4(w[0], w[1], w[2], w[3]));
       }
-      // V^T operand: element e <-> token 16s + 8*(e/4) + 4*hh + e%4, dims NT*n ..
-      VD raw[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int tr = 16 * s + 8 * (e / 4) + 4 * hh + (e % 4);
-        raw[e] = *reinterpret_cast<const VD*>(vb + tr * RS + NT * 2 * n);
-      }
-      if (ragged) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int tr = 16 * s + 8 * (e / 4) + 4 * hh + (e % 4);
-          if (tr >= valid) raw[e] = VD{};
-        }
-      }
+      // V^T operand of tile e: element j <-> token 16s + 8*(j/4) + 4*hh + j%4,
+      // dim 32e + lane%32 (token rows 16s + 4*hh + 0..3, then 8 rows on)
 #pragma unroll
       for (int e = 0; e < NT; ++e) {
-        // tile e: dim NT*n + e, i.e. 16-bit half (e & 1) of word (e >> 1)
-        uint32_t w[4];
-#pragma unroll
-        for (int d = 0; d < 4; ++d) {
-          const uint32_t a = word(raw[2 * d], e >> 1), b = word(raw[2 * d + 1], e >> 1);
-          w[d] = (e & 1) ? pair_hi(a, b) : pair_lo(a, b);
-        }
-        const bf16x8 av = __builtin_bit_cast(bf16x8, make_uint4(w[0], w[1], w[2], w[3]));
+        const uint2 lo = lds_read_tr16(vb + 16 * s * RSV + 64 * e);
+        const uint2 hi = lds_read_tr16(vb + (16 * s + 8) * RSV + 64 * e);
+        const bf16x8 av = __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
 #pragma unroll
         for (int c = 0; c < CT; ++c) acc[c][e] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pt[c], acc[c][e], 0, 0, 0);
       }
@@ -373,37 +365,39 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void prefill_mfma_kernel(Decode
       if (r < it.nrows && it.part < nparts) {
         const int64_t orow = (int64_t)(it.qrow0 + r) * Hq + it.g * G + n % G;
         const float inv = lt > 0.f ? 1.f / lt : 0.f;
-        // register i holds dims NT*(8*(i/4) + 4*hh + i%4) + e, e < NT: one
-        // vector store of NT consecutive dims per register index
+        // registers 4k .. 4k+3 of tile e hold dims 32e + 8k + 4*hh + 0..3: one
+        // vector store of four consecutive dims each
         if (nparts == 1) {
           char* o = reinterpret_cast<char*>(p.out) + orow * D * 2;
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int d0 = NT * (8 * (i / 4) + 4 * hh + (i % 4));
-            if constexpr (NT == 4) {
-              *reinterpret_cast<uint2*>(o + d0 * 2) =
-                  make_uint2(pack_bf16x2(acc[c][0][i] * inv, acc[c][1][i] * inv),
-                             pack_bf16x2(acc[c][2][i] * inv, acc[c][3][i] * inv));
-            } else {
-              *reinterpret_cast<uint32_t*>(o + d0 * 2) = pack_bf16x2(acc[c][0][i] * inv, acc[c][1][i] * inv);
+          for (int e = 0; e < NT; ++e) {
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+              const f32x16& a = acc[c][e];
+              *reinterpret_cast<uint2*>(o + (32 * e + 8 * k + 4 * hh) * 2) =
+                  make_uint2(pack_bf16x2(a[4 * k] * inv, a[4 * k + 1] * inv),
+                             pack_bf16x2(a[4 * k + 2] * inv, a[4 * k + 3] * inv));
             }
           }
         } else {
           const int64_t pr = orow * p.max_parts + it.part;
           float* o = p.part_o + pr * D;
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int d0 = NT * (8 * (i / 4) + 4 * hh + (i % 4));
-            if constexpr (NT == 4) {
-              *reinterpret_cast<float4*>(o + d0) =
-                  make_float4(acc[c][0][i] * inv, acc[c][1][i] * inv, acc[c][2][i] * inv, acc[c][3][i] * inv);
-            } else {
-              *reinterpret_cast<float2*>(o + d0) = make_float2(acc[c][0][i] * inv, acc[c][1][i] * inv);
+          for (int e = 0; e < NT; ++e) {
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+              const f32x16& a = acc[c][e];
+              *reinterpret_cast<float4*>(o + 32 * e + 8 * k + 4 * hh) =
+                  make_float4(a[4 * k] * inv, a[4 * k + 1] * inv, a[4 * k + 2] * inv, a[4 * k + 3] * inv);
             }
           }
           if (hh == 0) {
             p.part_m[pr] = m[c];
             p.part_l[pr] = lt;
+            if (it.span == 2 && it.part + 1 < nparts) {  // the second partition's slot: empty
+              p.part_m[pr + 1] = -INFINITY;
+              p.part_l[pr + 1] = 0.f;
+            }
           }
         }
       }
@@ -434,6 +428,7 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void prefill_mfma_kernel(Decode
     const int r0 = q + ahead;
     const bool in_cur = r0 < cur.nsteps;
     return step_ids(in_cur ? cur.s : n1.s, in_cur ? cur.b_begin : n1.b_begin, in_cur ? cur.nblk : n1.nblk,
+                    in_cur ? cur.ctx : n1.ctx,
                     in_cur ? r0 : r0 - cur.nsteps);
   };
   auto issue_ahead = [&](int q, int ahead, Stage& st) {
@@ -479,7 +474,7 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void prefill_mfma_kernel(Decode
         if (2 * (q + 1) < cur.nblk) scores(b1, sc_next);  // overlaps the softmax below
         if (2 * q < cur.nblk) {
           const int t0 = (cur.b_begin + 2 * q) * kBlockTokens;
-          softmax_values(sc_cur, buf, t0, min(kStepTokens, cur.ctx - t0));
+          softmax_values(sc_cur, buf, t0);
         }
         __syncthreads();
         buf = b1;

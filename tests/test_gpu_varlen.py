@@ -104,6 +104,40 @@ def test_varlen_many_short_chunks():
     assert_close(got, oracle_varlen(inp), "bf16", "short chunks")
 
 
+def prefill_span(qlens, ctxs, G, Hkv, cus):
+    """The plan's span rule restated: prefill items cover two partitions when the
+    rounds of items per compute unit at span 2 are at most half those at span 1."""
+    rpi = 256 // G
+    n1 = n2 = 0
+    for q, c in zip(qlens, ctxs):
+        if q <= 1:
+            continue
+        for r0 in range(0, q, rpi):
+            keys = max(0, c - q + min(q, r0 + rpi))
+            n = max(1, -(-keys // 512))
+            n1, n2 = n1 + n, n2 + (n + 1) // 2
+    r1, r2 = -(-n1 * Hkv // cus), -(-n2 * Hkv // cus)
+    return 2 if r1 > 1 and 2 * r2 <= r1 else 1
+
+
+SPAN2_CASES = {
+    # rows with 1, 2, 4 and 5 partitions; two-partition items whose second
+    # partition is empty, partly used, or absent (odd partition counts)
+    "mha_d64": (32, 32, 64, [256, 256, 100, 1], [2300, 1000, 560, 3000]),
+    "gqa4_d128": (32, 8, 128, [256, 256, 1], [2500, 2600, 777]),
+}
+
+
+@pytest.mark.parametrize("name", sorted(SPAN2_CASES))
+def test_varlen_two_partition_prefill_items(name):
+    hq, hkv, d, qlens, ctxs = SPAN2_CASES[name]
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    say(f"varlen span-2 {name}: cus={cus} span={prefill_span(qlens, ctxs, hq // hkv, hkv, cus)}")
+    inp = mixed_case(zlib.crc32(name.encode()) % 1000 + 7, hq, hkv, d, qlens, ctxs)
+    got = host_f64(gpu_varlen(inp))
+    assert_close(got, oracle_varlen(inp), "bf16", name)
+
+
 def test_varlen_unit_scale_zero_query():
     """q = 0: row r's output is the mean of V over its visible keys (|out| ~ 1)."""
     say("varlen zero-query unit scale")
