@@ -127,8 +127,8 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void prefill_mfma_kernel(Decode
   const int n = lane & 31;                 // column of a tile; token / dim slot of operands
   const int hh = lane >> 5;                // lane half
   const int Hq = p.Hkv * G;
-  const int64_t tok_bytes = (int64_t)p.Hkv * D * 2;
-  const int64_t blk_bytes = tok_bytes * kBlockTokens;
+  const uint32_t tok_bytes = (uint32_t)p.Hkv * D * 2;
+  const uint32_t blk_bytes = tok_bytes * kBlockTokens;
   const int total = min(p.sched[3], p.pre_cap * p.Hkv);
   const int grid = (int)gridDim.x;
 
@@ -138,8 +138,10 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void prefill_mfma_kernel(Decode
   __shared__ __attribute__((aligned(16))) char s_v[3][kStepTokens * RSV];
   __shared__ int s_ticket[2];
 
+  using TablePtr = const __attribute__((address_space(4))) int*;
   struct Item {
     int s, part, span, g, ctx, qrow0, nrows, key0, b_begin, nblk, nsteps;
+    TablePtr trow;  // the sequence's block table from the item's first block
     bool valid;
   };
   // Records are written by the plan launch and read-only here: read through the
@@ -168,6 +170,7 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void prefill_mfma_kernel(Decode
     // steps ahead of the computation) never runs past the next item; padding
     // steps load nothing and compute nothing
     it.nsteps = max(2 * NS, (max(1, (it.nblk + 1) / 2) + NS - 1) / NS * NS);
+    it.trow = (TablePtr)(const void*)(p.tables + (int64_t)it.s * p.MB + it.b_begin);
   };
   // q operands (B of the scores) of this wave's columns; rows past the item read
   // zeros through the resource bound.
@@ -186,19 +189,23 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void prefill_mfma_kernel(Decode
 
   // Cooperative loads: thread t holds the same piece of K and of V of step rows
   // t / 16 + j * (threads / 16), j < RPT, bytes (t % 16) * PS .. + PS of KV head
-  // g's slice.  A wave's rows lie in one block, so its loads use one resource.
+  // g's slice.  A wave's rows lie in one block (wblk[j] of the step's two), so
+  // its loads use one resource.
   const int st_row = tid / 16;
   const int st_col = (tid % 16) * PS;
   constexpr int kRowStride = kPrefillThreads / 16;
+  int wblk[RPT];
+#pragma unroll
+  for (int j = 0; j < RPT; ++j) wblk[j] = __builtin_amdgcn_readfirstlane((st_row + j * kRowStride) / kBlockTokens);
   struct Stage {
     PT k[RPT], v[RPT];
   };
-  // Row `row` (block row row % 16) of block id pb (-1 past the partition),
+  // Row `row` (block row row % 16) of block id pb (-1 past the item's blocks),
   // whose first `lim` rows are in the context: the loads go through resources
   // that end there (rows past it read zeros), empty for an id outside the pool.
   auto issue_row = [&](int g, int pb, int lim, int row, PT& kk, PT& vv) {
     const bool ok = (unsigned)pb < (unsigned)p.NB;
-    const int64_t base = (int64_t)(ok ? pb : 0) * blk_bytes;
+    const uint64_t base = (uint64_t)(uint32_t)(ok ? pb : 0) * blk_bytes;
     const int nrec = ok ? lim * (int)tok_bytes : 0;
     const __amdgpu_buffer_rsrc_t kr =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(p.kc + base), (short)0, nrec, kRawBufferWord3);
@@ -208,23 +215,34 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void prefill_mfma_kernel(Decode
     kk = buffer_load_piece<PT>(kr, off, 0);
     vv = buffer_load_piece<PT>(vr, off, 0);
   };
-  // Block ids of this wave's rows of step `step` of an item: scalar loads from
-  // the table (written before this launch, read-only here), which never wait
-  // for the vector loads in flight; -1 past the item's blocks.  With each id,
-  // the number of the block's rows inside the context.
+  // The load stream's position: an item (copied) and a step of it.  Block ids
+  // are scalar loads from the table (written before this launch, read-only
+  // here), which never wait for the vector loads in flight; with each id, the
+  // number of the block's rows inside the context.
+  struct Cursor {
+    TablePtr trow;
+    int nblk, ctx_rel, g, step, nsteps;
+  };
   struct Ids {
     int v[RPT], lim[RPT];
   };
-  auto step_ids = [&](int s, int b_begin, int nblk, int ctx, int step) {
-    const __attribute__((address_space(4))) int* trow =
-        (const __attribute__((address_space(4))) int*)(const void*)(p.tables + (int64_t)s * p.MB + b_begin);
+  auto cursor_of = [&](const Item& it) {
+    Cursor c;
+    c.trow = it.trow;
+    c.nblk = it.nblk;
+    c.ctx_rel = it.ctx - it.b_begin * kBlockTokens;  // context tokens from the item's first block
+    c.g = it.g;
+    c.step = 0;
+    c.nsteps = it.nsteps;
+    return c;
+  };
+  auto ids_at = [&](const Cursor& c) {
     Ids ids;
 #pragma unroll
     for (int j = 0; j < RPT; ++j) {
-      const int row = st_row + j * kRowStride;                 // wave-uniform block
-      const int k = 2 * step + __builtin_amdgcn_readfirstlane(row / kBlockTokens);
-      ids.v[j] = k < nblk ? trow[k] : -1;
-      ids.lim[j] = min(kBlockTokens, ctx - (b_begin + k) * kBlockTokens);
+      const int k = 2 * c.step + wblk[j];
+      ids.v[j] = k < c.nblk ? c.trow[k] : -1;
+      ids.lim[j] = min(kBlockTokens, c.ctx_rel - k * kBlockTokens);
     }
     return ids;
   };
@@ -415,49 +433,53 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void prefill_mfma_kernel(Decode
   load_q(cur, qf);
   load_q(n1, qn);
 
-  // The stream position `ahead` <= NS + 2 steps after step q of cur, chosen by
-  // selects so that every path issues the same loads in the same order; an
-  // invalid item has no blocks (zero-sized loads).
-  // The ids of each position are loaded one issue ahead (pf_ids, valid when
-  // pf_ok), so the issue does not wait for the scalar load; a position past n1
-  // is not known yet and is loaded at its issue instead.
+  // The load stream runs NS + 2 steps ahead of the computation: in cur, then
+  // in n1 (cs_n1).  Stepping past the end of n1 (only when n1 has the minimum
+  // 2*NS steps) leaves it pending (cs_wait) until the item switch makes the
+  // next n1; that happens before the next issue.  An invalid item has no
+  // blocks (zero-sized loads).  The ids of each position are loaded one issue
+  // ahead (pf_ids, valid when pf_ok), so the issue does not wait for the
+  // scalar loads.
+  Cursor cs = cursor_of(cur);
+  bool cs_n1 = false, cs_wait = false;
   Ids pf_ids;
   bool pf_ok = false;
-  auto known = [&](int q, int ahead) { return q + ahead < cur.nsteps + n1.nsteps; };
-  auto position_ids = [&](int q, int ahead) {
-    const int r0 = q + ahead;
-    const bool in_cur = r0 < cur.nsteps;
-    return step_ids(in_cur ? cur.s : n1.s, in_cur ? cur.b_begin : n1.b_begin, in_cur ? cur.nblk : n1.nblk,
-                    in_cur ? cur.ctx : n1.ctx,
-                    in_cur ? r0 : r0 - cur.nsteps);
-  };
-  auto issue_ahead = [&](int q, int ahead, Stage& st) {
-    const Ids ids = pf_ok ? pf_ids : position_ids(q, ahead);  // always within n1 here
-    issue_step(q + ahead < cur.nsteps ? cur.g : n1.g, ids, st);
-    pf_ok = known(q, ahead + 1);
-    if (pf_ok) pf_ids = position_ids(q, ahead + 1);
+  auto issue_next = [&](Stage& st) {
+    const Ids ids = pf_ok ? pf_ids : ids_at(cs);
+    issue_step(cs.g, ids, st);
+    if (++cs.step == cs.nsteps) {
+      if (cs_n1) {
+        cs_wait = true;
+      } else {
+        cs = cursor_of(n1);
+        cs_n1 = true;
+      }
+    }
+    pf_ok = !cs_wait;
+    if (pf_ok) pf_ids = ids_at(cs);
   };
 
   // Step q is staged into LDS at iteration q - 2 (from the registers its loads
   // landed in, NS steps after they were issued), its scores are computed at
   // iteration q - 1 while step q - 1's softmax and values run, and its own
   // softmax and values at iteration q: one barrier per iteration.
+  static_assert(NS % 2 == 0, "step q's scores sit in sc[q % 2]: the unrolled loop keeps the parity");
   Stage stg[NS];
 #pragma unroll
-  for (int u = 0; u < NS; ++u) issue_ahead(0, u, stg[u]);
+  for (int u = 0; u < NS; ++u) issue_next(stg[u]);
 #pragma unroll
   for (int u = 0; u < NS; ++u) {
     stage_to_lds(stg[u], u);
-    issue_ahead(u, NS, stg[u]);
+    issue_next(stg[u]);
   }
   __syncthreads();
   int buf = 0, tpar = 0;  // LDS buffer of step 0 of cur
-  f32x16 sc_cur[CT], sc_next[CT];
+  f32x16 sc[2][CT];       // scores of steps of either parity
   for (;;) {  // one item per iteration
     int fetched;  // thread 0: the ticket after n1, written to LDS at cur's last step
     if (tid == 0) fetched = atomicAdd(&p.sched[2], 1);  // offset added where it is read
     begin_item(cur);
-    if (cur.nblk > 0) scores(buf, sc_next);
+    if (cur.nblk > 0) scores(buf, sc[0]);
     for (int q0 = 0; q0 < cur.nsteps; q0 += NS) {
 #pragma unroll
       for (int u = 0; u < NS; ++u) {
@@ -467,14 +489,12 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void prefill_mfma_kernel(Decode
         // into buffer b2 (read last at iteration q - 1, before the last
         // barrier) and refill the slot with step q + 2 + NS
         stage_to_lds(stg[u], b2);
-        issue_ahead(q + 2, NS, stg[u]);
+        issue_next(stg[u]);
         if (q + 1 == cur.nsteps && tid == 0) s_ticket[tpar] = fetched;
-#pragma unroll
-        for (int c = 0; c < CT; ++c) sc_cur[c] = sc_next[c];
-        if (2 * (q + 1) < cur.nblk) scores(b1, sc_next);  // overlaps the softmax below
+        if (2 * (q + 1) < cur.nblk) scores(b1, sc[(u + 1) % 2]);  // overlaps the softmax below
         if (2 * q < cur.nblk) {
           const int t0 = (cur.b_begin + 2 * q) * kBlockTokens;
-          softmax_values(sc_cur, buf, t0);
+          softmax_values(sc[u % 2], buf, t0);
         }
         __syncthreads();
         buf = b1;
@@ -499,6 +519,12 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void prefill_mfma_kernel(Decode
     if (!cur.valid) break;
     make_item(tk, n1);
     load_q(n1, qn);
+    if (cs_wait) {  // the stream stepped past the old n1: it continues in the new one
+      cs = cursor_of(n1);
+      cs_wait = false;
+    } else {
+      cs_n1 = false;  // the stream's item (the old n1) is now cur
+    }
   }
 }
 
