@@ -284,9 +284,12 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void prefill_mfma_kernel(Decode
   const int v_lane = (4 * hh + ((lane >> 2) & 3)) * RSV + (16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2;
 
   // Softmax and value products of a step from its scores and LDS buffer buf:
-  // tokens t0 .. t0+31 (V rows past the context hold zeros).
-  auto softmax_values = [&](f32x16 (&sc)[CT], int buf, int t0) {
+  // tokens t0 .. t0+31 (V rows past the context hold zeros); with them, in
+  // the same straight-line code, the score products of the next step (K in
+  // LDS buffer kbuf, into sn), so that the matrix and vector work interleave.
+  auto softmax_values = [&](f32x16 (&sc)[CT], int buf, int t0, int kbuf, f32x16 (&sn)[CT]) {
     const char* vb = s_v[buf] + v_lane;
+    const char* kb = s_k[kbuf];
     // softmax per column in base 2: register i holds token 8*(i/4) + 4*hh + i%4.
     // Only steps that reach past some column's keys (the causal edge, the end
     // of the context) need the per-element mask, which sets the raw score to
@@ -327,6 +330,8 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void prefill_mfma_kernel(Decode
     }
     auto weight = [&](int c, int i) { return exp2_fast(fmaf(sc[c][i], p.scale_log2, -mref[c])); };
 #pragma unroll
+    for (int c = 0; c < CT; ++c) sn[c] = f32x16{};
+#pragma unroll
     for (int s = 0; s < 2; ++s) {
       // P^T operand of k-step s (rounded weights summed into l)
       bf16x8 pt[CT];
@@ -339,6 +344,13 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void prefill_mfma_kernel(Decode
           l[c] = add_bf16_pair(w[d], l[c]);
         }
         pt[c] = __builtin_bit_cast(bf16x8, make_uint4(w[0], w[1], w[2], w[3]));
+      }
+      // half of the next step's score products
+#pragma unroll
+      for (int kc = s * NKC / 2; kc < (s + 1) * NKC / 2; ++kc) {
+        const bf16x8 kf = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(kb + n * RSK + 32 * kc + 16 * hh));
+#pragma unroll
+        for (int c = 0; c < CT; ++c) sn[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[c][kc], sn[c], 0, 0, 0);
       }
       // V^T operand of tile e: element j <-> token 16s + 8*(j/4) + 4*hh + j%4,
       // dim 32e + lane%32 (token rows 16s + 4*hh + 0..3, then 8 rows on)
@@ -491,10 +503,11 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void prefill_mfma_kernel(Decode
         stage_to_lds(stg[u], b2);
         issue_next(stg[u]);
         if (q + 1 == cur.nsteps && tid == 0) s_ticket[tpar] = fetched;
-        if (2 * (q + 1) < cur.nblk) scores(b1, sc[(u + 1) % 2]);  // overlaps the softmax below
+        // step q's softmax and values with step q + 1's scores (computed
+        // also past the item's blocks, where they are never used)
         if (2 * q < cur.nblk) {
           const int t0 = (cur.b_begin + 2 * q) * kBlockTokens;
-          softmax_values(sc[u % 2], buf, t0);
+          softmax_values(sc[u % 2], buf, t0, b1, sc[(u + 1) % 2]);
         }
         __syncthreads();
         buf = b1;
