@@ -56,8 +56,8 @@ struct DecodeArgs {
   const void* vnew;
 };
 
-// Rows of one prefill work item (one workgroup of four wavefronts, each with
-// four 16-column MFMA tiles of 16/G rows x G heads).
+// Rows of one prefill work item (one workgroup of eight wavefronts, each with
+// one 32-column MFMA tile of 32/G rows x G heads).
 inline int32_t prefill_rows_per_item(int32_t G) { return 256 / G; }
 
 // Work-list plan: decode records, prefill records and per-row key counts.
