@@ -162,8 +162,7 @@ def main():
     spec = SPECS[args.workload]
     if spec.chunk_rows:
         return mixed_main(args, spec)
-    if spec.ctx_kind == "prefix":
-        raise SystemExit(f"workload {spec.name} is not a plain decode batch")
+    prefix = spec.ctx_kind == "prefix"                  # sequences forked from one shared prefix
     S, Hq, Hkv, D = spec.num_seqs, spec.num_q_heads, spec.num_kv_heads, spec.head_dim
     es = 2 if spec.dtype == "bf16" else 4
     tdt = torch.bfloat16 if spec.dtype == "bf16" else torch.float32
@@ -178,15 +177,33 @@ def main():
     final_ctx = ctx0.astype(np.int64) + n_steps - 1
     MB = int(-(-final_ctx.max() // 16))
     max_ctx_bound = int(final_ctx.max())
-    nb = pool_blocks_for(spec, final_ctx)
-    alloc = pkv.BlockAllocator(nb, 16, shuffle_seed=args.seed)
     ids = np.arange(S, dtype=np.int64)
-    for s in range(S):
-        alloc.add_seq(int(s))
-    alloc.append_batch(ids, ctx0 - 1)                   # prefilled tokens; the pool holds their K/V
+    cow_pairs = np.zeros((0, 2), np.int32)
+    if prefix:
+        # the prefix's full blocks are shared by every sequence; each sequence's
+        # copy of the partial prefix block (copy-on-write) and its tail are its own
+        Pn = spec.prefix_len
+        shared_tokens = Pn // 16 * 16
+        nb = int(math.ceil(1.25 * (Pn // 16 + int(np.sum(-(-final_ctx // 16) - Pn // 16)))))
+        alloc = pkv.BlockAllocator(nb, 16, shuffle_seed=args.seed)
+        alloc.add_seq(0)
+        alloc.append(0, Pn)
+        for s in range(1, S):
+            alloc.fork(0, s)
+        _, cow_pairs = alloc.append_batch(ids, ctx0 - 1 - Pn)   # tails written before the first step
+    else:
+        shared_tokens = 0
+        nb = pool_blocks_for(spec, final_ctx)
+        alloc = pkv.BlockAllocator(nb, 16, shuffle_seed=args.seed)
+        for s in range(S):
+            alloc.add_seq(int(s))
+        alloc.append_batch(ids, ctx0 - 1)               # prefilled tokens; the pool holds their K/V
 
     pool_host_k = normal_values_parallel(args.seed * 10 + 1, (nb, 16, Hkv, D), spec.dtype)
     pool_host_v = normal_values_parallel(args.seed * 10 + 2, (nb, 16, Hkv, D), spec.dtype)
+    for src, dst in np.asarray(cow_pairs).reshape(-1, 2):  # the host copy (oracle baseline) mirrors the device one
+        pool_host_k[dst] = pool_host_k[src]
+        pool_host_v[dst] = pool_host_v[src]
 
     def up(a):
         a = np.ascontiguousarray(a)
@@ -194,6 +211,9 @@ def main():
         return t.view(tdt) if a.dtype == np.uint16 else t
 
     kcs, vcs = [up(pool_host_k)], [up(pool_host_v)]
+    if len(cow_pairs):                                  # copy-on-write of the shared partial block (setup)
+        pkv.pkv_copy_blocks(kcs[0], vcs[0], torch.from_numpy(np.ascontiguousarray(cow_pairs, np.int32)).cuda())
+        torch.cuda.synchronize()
     for _ in range(R - 1):
         kcs.append(kcs[0].clone())
         vcs.append(vcs[0].clone())
@@ -317,11 +337,13 @@ def main():
     # write (fp32) or nothing (bf16: fused), plus any wait for the plan on the side stream
     t_write = [e[0].elapsed_time(e[1]) * 1e-3 for e in events[K:]]
     t_merge = [e[2].elapsed_time(e[3]) * 1e-3 for e in events[K:]]
-    kv_b, part_b, merge_b = [], [], []
+    kv_b, part_b, merge_b, logical_b = [], [], [], []
     for lens in step_lens:
         lens = lens.astype(np.int64)
         nparts = -(-lens // 512)
-        kv = int(lens.sum()) * 2 * Hkv * D * es
+        # K/V bytes the launch must bring in: a shared prefix block counts once
+        kv = (int(lens.sum()) - (S - 1) * shared_tokens) * 2 * Hkv * D * es
+        logical_b.append(int(lens.sum()) * 2 * Hkv * D * es)
         q_out = S * Hq * D * es + int((nparts == 1).sum()) * Hq * D * es
         meta = int((4 * -(-lens // 16)).sum()) + 4 * S
         partials = int(nparts[nparts > 1].sum()) * Hq * (D + 2) * 4
@@ -386,6 +408,8 @@ def main():
             "pool_blocks": nb, "pool_copies": R, "seed": args.seed,
         },
         "kv_read_GBps": round(kv_gbps, 1),
+        **({"kv_logical_read_GBps": round(sum(logical_b[k] for k in timed_ev) / sum_tp / 1e9, 1),
+            "prefix_len": spec.prefix_len, "cow_pairs": int(len(cow_pairs))} if prefix else {}),
         "kv_read_frac_of_peak": round(kv_gbps / HBM_PEAK_GBPS, 4),
         "kernels_us": {
             ("plan_wait" if fused else "write"): round(float(np.mean(t_write)) * 1e6, 2),
