@@ -31,10 +31,10 @@ constexpr size_t kSchedBytes = 256;  // decode workspace header: ticket counters
 constexpr size_t kDecRecBytes = 4 * sizeof(int32_t);  // {sequence, partition, context, query row}
 constexpr size_t kPreRecBytes = 8 * sizeof(int32_t);  // two int4 (see plan.hip)
 
-// Workspace of one attention call: header, the two work lists, per-row key
+// Workspace of one attention call: header, the two work lists, per-row slot
 // counts and (when a row can span several partitions) the partials.
 struct WsLayout {
-  size_t dec, pre, keys, pm, pl, po, total;
+  size_t dec, pre, slots, pm, pl, po, total;
   int64_t P, dec_cap, pre_cap;
 };
 WsLayout workspace_layout(int64_t S, int64_t T, int64_t Hq, int64_t G, int64_t D, int64_t max_qlen,
@@ -47,7 +47,7 @@ WsLayout workspace_layout(int64_t S, int64_t T, int64_t Hq, int64_t G, int64_t D
   size_t off = kSchedBytes;
   w.dec = off; off += align256((size_t)w.dec_cap * kDecRecBytes);
   w.pre = off; off += align256((size_t)w.pre_cap * kPreRecBytes);
-  w.keys = off; off += align256((size_t)T * sizeof(int32_t));
+  w.slots = off; off += align256((size_t)T * sizeof(int32_t));
   if (w.P > 1) {
     const size_t rows = (size_t)T * Hq;
     w.pm = off; off += align256(rows * w.P * sizeof(float));
@@ -221,7 +221,7 @@ int prepare_attention(const char* who, pkv::DecodeArgs& a, void* out, const void
   a.sched = reinterpret_cast<int32_t*>(ws);
   a.dec_recs = reinterpret_cast<int32_t*>(ws + w.dec);
   a.pre_recs = reinterpret_cast<int32_t*>(ws + w.pre);
-  a.row_keys = reinterpret_cast<int32_t*>(ws + w.keys);
+  a.row_slots = reinterpret_cast<int32_t*>(ws + w.slots);
   a.dec_cap = (int32_t)w.dec_cap;
   a.pre_cap = (int32_t)w.pre_cap;
   if (w.P > 1) {

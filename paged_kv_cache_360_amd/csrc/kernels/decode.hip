@@ -247,19 +247,16 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_partition_kernel(Decode
   }
 }
 
-// One wave per output row (query row x q head).  FROM_KEYS: the partition count
-// comes from the keys the query row sees (counts = the plan's row_keys; rows
-// with a single partition were already written by the partition kernels and
-// are skipped); otherwise from num_parts[row].
+// One wave per output row (query row x q head).  PER_TOKEN: the slot count is
+// that of the row's query token (counts = the plan's row_slots; rows with one
+// slot were already written by the partition or prefill kernels and are
+// skipped); otherwise num_parts[row].
 // Latency is one round trip per kMergeUnroll partitions: the first group's
 // partial outputs are loaded before the maxima are reduced, and the maxima and
-// sums are read lane-parallel (64 partitions per load).  LIVE_LOADS: a partial
-// output is loaded only where its sum is positive (one more round trip; for
-// batches whose prefill items span two partitions, where every other slot of
-// such a row is empty).
+// sums are read lane-parallel (64 partitions per load).
 constexpr int kMergeUnroll = 8;
 
-template <bool BF16, int D, bool FROM_KEYS, bool LIVE_LOADS = false>
+template <bool BF16, int D, bool PER_TOKEN>
 __global__ __launch_bounds__(kWave) void lse_merge_kernel(
     void* __restrict__ out, const float* __restrict__ pm, const float* __restrict__ pl,
     const float* __restrict__ po, const int32_t* __restrict__ counts, int32_t Hq,
@@ -268,9 +265,8 @@ __global__ __launch_bounds__(kWave) void lse_merge_kernel(
   constexpr int U = kMergeUnroll;
   const int64_t row = blockIdx.x;
   int n;
-  if constexpr (FROM_KEYS) {
-    const int keys = max(0, counts[row / Hq]);
-    n = min((keys + kPartTokens - 1) / kPartTokens, max_parts);
+  if constexpr (PER_TOKEN) {
+    n = min(counts[row / Hq], max_parts);
     if (n <= 1) return;
   } else {
     n = max(0, min(counts[row], max_parts));
@@ -280,16 +276,11 @@ __global__ __launch_bounds__(kWave) void lse_merge_kernel(
   const float* rl = pl + row * max_parts;
   const float* ro = po + row * max_parts * D;
 
-  auto wanted = [&](int i) {  // i < n
-    if constexpr (LIVE_LOADS) return rl[i] > 0.f;
-    return true;
-  };
   float ov[U][PER];  // first group of partial outputs, in flight during the reductions
 #pragma unroll
   for (int u = 0; u < U; ++u) {
-    const bool w = u < n && wanted(u);
 #pragma unroll
-    for (int k = 0; k < PER; ++k) ov[u][k] = w ? ro[(int64_t)u * D + lane + k * kWave] : 0.f;
+    for (int k = 0; k < PER; ++k) ov[u][k] = u < n ? ro[(int64_t)u * D + lane + k * kWave] : 0.f;
   }
 
   // live partial: l > 0 and a finite max; the rest weigh 0
@@ -321,9 +312,9 @@ __global__ __launch_bounds__(kWave) void lse_merge_kernel(
     for (int base = U; base < n; base += U) {
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const bool w = base + u < n && wanted(base + u);
 #pragma unroll
-        for (int k = 0; k < PER; ++k) ov[u][k] = w ? ro[(int64_t)(base + u) * D + lane + k * kWave] : 0.f;
+        for (int k = 0; k < PER; ++k)
+          ov[u][k] = base + u < n ? ro[(int64_t)(base + u) * D + lane + k * kWave] : 0.f;
       }
 #pragma unroll
       for (int u = 0; u < U; ++u) {
@@ -357,13 +348,8 @@ int launch_partitions_g(const DecodeParams& p, const DecodeArgs& a, hipStream_t 
 
 template <bool BF16, int D>
 void launch_merge_t(const DecodeArgs& a, hipStream_t st) {
-  const dim3 grid(a.num_tokens * a.num_q_heads), block(kWave);
-  if (a.qsl)  // variable-length batch: prefill rows may have empty slots
-    hipLaunchKernelGGL((lse_merge_kernel<BF16, D, true, true>), grid, block, 0, st, a.out, a.part_m, a.part_l,
-                       a.part_o, a.row_keys, a.num_q_heads, a.max_parts);
-  else
-    hipLaunchKernelGGL((lse_merge_kernel<BF16, D, true>), grid, block, 0, st, a.out, a.part_m, a.part_l,
-                       a.part_o, a.row_keys, a.num_q_heads, a.max_parts);
+  hipLaunchKernelGGL((lse_merge_kernel<BF16, D, true>), dim3(a.num_tokens * a.num_q_heads), dim3(kWave),
+                     0, st, a.out, a.part_m, a.part_l, a.part_o, a.row_slots, a.num_q_heads, a.max_parts);
 }
 
 }  // namespace
@@ -388,7 +374,7 @@ DecodeParams make_params(const DecodeArgs& a) {
   p.sched = a.sched;
   p.dec_recs = reinterpret_cast<const int4*>(a.dec_recs);
   p.pre_recs = reinterpret_cast<const int4*>(a.pre_recs);
-  p.row_keys = a.row_keys;
+  p.row_slots = a.row_slots;
   p.dec_cap = a.dec_cap;
   p.pre_cap = a.pre_cap;
   p.part_m = a.part_m;

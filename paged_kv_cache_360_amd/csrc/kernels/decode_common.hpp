@@ -42,7 +42,7 @@ struct DecodeParams {
   int32_t* sched;        // [0] decode tickets taken from the counter, [1] decode tickets; [2], [3] prefill
   const int4* dec_recs;  // decode records {sequence, partition, context, query row}
   const int4* pre_recs;  // prefill records, two int4 each (see plan.hip)
-  const int32_t* row_keys;
+  const int32_t* row_slots;
   int32_t dec_cap, pre_cap;
   float* part_m;
   float* part_l;

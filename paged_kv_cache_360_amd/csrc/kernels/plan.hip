@@ -22,8 +22,10 @@
 //    up to the one the group's last row reaches).  The span is 2 when halving
 //    the item count still leaves every compute unit the same number of rounds
 //    of items (then each row writes half the partial results), else 1;
-//  * row_keys[T]: the keys each query row sees (its partition count for the
-//    merge);
+//  * row_slots[T]: the partial results each query row's merge combines: its
+//    partition count for a decode row, its item count (partitions / span,
+//    rounded up) for a prefill row; 1 for a row written directly (or with no
+//    keys), 0 for rows no sequence owns;
 //  * sched: both ticket counters reset, and each list's ticket count (records
 //    times KV heads: ticket t is record t / Hkv, KV head t % Hkv).
 // One workgroup; sequence chunks are scanned in LDS.
@@ -41,7 +43,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(
     const int32_t* __restrict__ ctx, const int32_t* __restrict__ qsl, int32_t S, int32_t T,
     int32_t ctx_cap, int32_t Hkv, int32_t rows_per_item, int32_t dec_cap, int32_t pre_cap,
     int32_t num_cus, int32_t* __restrict__ sched, int4* __restrict__ dec, int4* __restrict__ pre,
-    int32_t* __restrict__ row_keys) {
+    int32_t* __restrict__ row_slots) {
   constexpr int NBK = kItemBlocks + 1;  // buckets: last-item block count kItemBlocks .. 0
   __shared__ int32_t s_full[kPlanThreads];
   __shared__ int32_t s_pre[kPlanThreads];   // prefill records at span 1
@@ -64,7 +66,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(
   auto row_keys_of = [&](int c, int q, int r) { return max(0, c - q + r + 1); };
 
   if (t < NBK) s_bucket[t] = 0;
-  for (int r = t; r < T; r += kPlanThreads) row_keys[r] = 0;  // rows no sequence owns see nothing
+  for (int r = t; r < T; r += kPlanThreads) row_slots[r] = 0;  // rows no sequence owns: nothing to merge
   __syncthreads();
   int full = 0, npre = 0, npre2 = 0;
   int own_c = 0, own_q = 0, own_row0 = 0;  // this thread's (last) sequence, for the write loop
@@ -134,7 +136,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(
       if (od < dec_cap) dec[od] = make_int4(s, k * kItemParts, c, row0);
     const int at = atomicAdd(&s_bucket[last_bucket(c, n)], 1);
     if (at < dec_cap) dec[at] = make_int4(s, (ni - 1) * kItemParts, c, row0);
-    row_keys[row0] = c;
+    row_slots[row0] = parts_of(c);
   }
   auto next_prefill = [&](int from) {
     for (int s = from; s < s1; ++s)
@@ -164,7 +166,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(
       }
       cop += n;
     }
-    for (int r = lane; r < q; r += kWave) row_keys[row0 + r] = row_keys_of(c, q, r);
+    for (int r = lane; r < q; r += kWave) row_slots[row0 + r] = (parts_of(row_keys_of(c, q, r)) + span - 1) / span;
     if (lane == src) {
       op = cop;
       ps = next_prefill(ps + 1);
@@ -189,7 +191,7 @@ int launch_plan(const DecodeArgs& a, void* stream) {
   hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, (hipStream_t)stream, a.ctx, a.qsl,
                      a.num_seqs, a.num_tokens, p.ctx_cap, a.num_kv_heads, prefill_rows_per_item(G),
                      a.dec_cap, a.pre_cap, a.num_cus, a.sched, reinterpret_cast<int4*>(a.dec_recs),
-                     reinterpret_cast<int4*>(a.pre_recs), a.row_keys);
+                     reinterpret_cast<int4*>(a.pre_recs), a.row_slots);
   return (int)hipGetLastError();
 }
 

@@ -45,10 +45,8 @@
 //
 // Workgroups take items from the prefill tickets: the first two are static
 // (blockIdx.x and blockIdx.x + gridDim.x), the rest come from the counter.  A row whose
-// keys fit one partition gets its output written directly; other rows'
-// partials go to the workspace for the merge, in the slot of the item's first
-// partition, with the second partition's slot of a two-partition item marked
-// empty (zero sum).
+// keys one item covers gets its output written directly; other rows' partials
+// go to the workspace for the merge, one slot per item (slot part / span).
 
 #include <hip/hip_runtime.h>
 
@@ -390,14 +388,16 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void prefill_mfma_kernel(Decode
       const int r = wave * RPW + c * R + n / G;
       const int keys = max(0, it.key0 + r);
       const int nparts = max(1, (keys + kPartTokens - 1) / kPartTokens);
+      const int nslots = (nparts + it.span - 1) / it.span;  // this row's items, one partial each
       // a row that ends before this partition has nothing here (its own items
-      // cover its partitions); only partition 0 of a one-partition row is output
+      // cover its partitions); a row one item covers gets its output directly,
+      // the others a partial in slot part / span
       if (r < it.nrows && it.part < nparts) {
         const int64_t orow = (int64_t)(it.qrow0 + r) * Hq + it.g * G + n % G;
         const float inv = lt > 0.f ? 1.f / lt : 0.f;
         // registers 4k .. 4k+3 of tile e hold dims 32e + 8k + 4*hh + 0..3: one
         // vector store of four consecutive dims each
-        if (nparts == 1) {
+        if (nslots == 1) {
           char* o = reinterpret_cast<char*>(p.out) + orow * D * 2;
 #pragma unroll
           for (int e = 0; e < NT; ++e) {
@@ -410,7 +410,7 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void prefill_mfma_kernel(Decode
             }
           }
         } else {
-          const int64_t pr = orow * p.max_parts + it.part;
+          const int64_t pr = orow * p.max_parts + it.part / it.span;
           float* o = p.part_o + pr * D;
 #pragma unroll
           for (int e = 0; e < NT; ++e) {
@@ -424,10 +424,6 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void prefill_mfma_kernel(Decode
           if (hh == 0) {
             p.part_m[pr] = m[c];
             p.part_l[pr] = lt;
-            if (it.span == 2 && it.part + 1 < nparts) {  // the second partition's slot: empty
-              p.part_m[pr + 1] = -INFINITY;
-              p.part_l[pr + 1] = 0.f;
-            }
           }
         }
       }

@@ -44,7 +44,7 @@ struct DecodeArgs {
   int32_t* sched;        // [0], [1]: decode ticket counter, tickets; [2], [3]: prefill
   int32_t* dec_recs;     // decode work list, dec_cap records of 4 int32
   int32_t* pre_recs;     // prefill work list, pre_cap records of 8 int32
-  int32_t* row_keys;     // [T] keys each query row sees (written by the plan)
+  int32_t* row_slots;    // [T] partial results each query row's merge combines (plan)
   int32_t dec_cap, pre_cap;
   float* part_m;         // [T*Hq, max_parts]
   float* part_l;         // [T*Hq, max_parts]
@@ -60,7 +60,7 @@ struct DecodeArgs {
 // one 32-column MFMA tile of 32/G rows x G heads).
 inline int32_t prefill_rows_per_item(int32_t G) { return 256 / G; }
 
-// Work-list plan: decode records, prefill records and per-row key counts.
+// Work-list plan: decode records, prefill records and per-row merge slot counts.
 int launch_plan(const DecodeArgs& a, void* stream);
 // Chunked-prefill rows (sequences with more than one query row), bf16 only.
 int launch_prefill(const DecodeArgs& a, void* stream);
