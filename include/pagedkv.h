@@ -205,9 +205,11 @@ int pkv_attention_decode_partitions_append(void* out, const void* q, const void*
  * A long prompt split into chunks and batched with decode steps is the pages'
  * chunked prefill ("How vLLM Works?", section 04; "vLLM and PagedAttention",
  * key engineering optimizations); a sequence with one row is a decode step.
- * One-row sequences run the decode kernels; longer ones run 64/G-row tiles on
- * the matrix cores.  Both split keys into 512-token partitions merged by
- * log-sum-exp.  A row that sees no key (q_s > ctx_s) gets zeros.
+ * One-row sequences run the decode kernels; longer ones run work items of
+ * 256/G rows x the G q heads of one KV head on the matrix cores, over one or
+ * two 512-token partitions each.  Keys are split into 512-token partitions
+ * whose partial results are merged by log-sum-exp.  A row that sees no key
+ * (q_s > ctx_s) gets zeros.
  *
  *   out, q            device [num_tokens, num_q_heads, head_dim] bf16
  *   query_start_loc   device int32 [num_seqs + 1], non-decreasing, values in
