@@ -129,12 +129,19 @@ def copy_probe(torch, pkv):
     vc = torch.zeros_like(kc)
     half = nb // 2
     pairs = torch.stack([torch.arange(half), torch.arange(half) + half], 1).to(torch.int32).cuda()
-    for _ in range(3):
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    for i in range(3):
+        ev[i].record()
         pkv.pkv_copy_blocks(kc, vc, pairs)
+    ev[3].record()
     torch.cuda.synchronize()
     moved = 2 * half * 16 * hkv * d * 2
+    us = [ev[i].elapsed_time(ev[i + 1]) * 1e3 for i in range(1, 3)]   # the first launch warms up
+    t = sum(us) / len(us) * 1e-6
     print(json.dumps({"probe": "pkv_copy_blocks", "bytes_read_per_launch": moved,
-                      "bytes_written_per_launch": moved, "launches": 3}))
+                      "bytes_written_per_launch": moved, "launches": 3,
+                      "avg_launch_us": round(t * 1e6, 1), "read_plus_write_GBps": round(2 * moved / t / 1e9, 1),
+                      "frac_of_hbm_peak": round(2 * moved / t / 1e9 / HBM_PEAK_GBPS, 4)}))
 
 
 def main():
