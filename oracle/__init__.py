@@ -24,7 +24,8 @@ Modules:
 * ``attention``  gather through the block table, fp64 softmax attention (decode
   and causal chunk), log-sum-exp merge of partial softmaxes.
 * ``cache_ops``  the slot scatter write and the copy-on-write block copy.
-* ``allocator``  a Python model of the block allocator (refcounts, fork, CoW).
+* ``allocator``  a Python model of the block allocator (refcounts, fork, CoW) and
+  of its automatic prefix caching.
 
 Every function here is pinned by tests under ``tests/`` against something other
 than itself (closed forms, a library attention routine on contiguous K/V,
@@ -40,4 +41,4 @@ from .attention import (  # noqa: F401
     split_decode_partials,
 )
 from .cache_ops import write_kv, copy_blocks  # noqa: F401
-from .allocator import BlockAllocatorModel, slot_for_position  # noqa: F401
+from .allocator import BlockAllocatorModel, PrefixCachingAllocatorModel, slot_for_position  # noqa: F401
