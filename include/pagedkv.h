@@ -301,7 +301,8 @@ int pkv_alloc_add_seq(pkv_allocator* a, int64_t seq_id);
 int pkv_alloc_fork(pkv_allocator* a, int64_t parent, int64_t child);
 /* Reserve n_tokens slots at the end of seq_id.  slots_out[n_tokens] receives each
  * new token's slot; cow_pairs_out (capacity 2 ints) receives at most one (src, dst)
- * pair, *num_cow_out its count (0 or 1). */
+ * pair, *num_cow_out its count (0 or 1).  The token ids are not known, so a
+ * sequence made with pkv_alloc_add_seq_tokens stops caching its blocks here. */
 int pkv_alloc_append(pkv_allocator* a, int64_t seq_id, int32_t n_tokens, int32_t* slots_out,
                      int32_t* cow_pairs_out, int32_t* num_cow_out);
 /* Batched append, all-or-nothing over the batch.  seq_ids must be distinct.
@@ -310,7 +311,8 @@ int pkv_alloc_append(pkv_allocator* a, int64_t seq_id, int32_t n_tokens, int32_t
 int pkv_alloc_append_batch(pkv_allocator* a, const int64_t* seq_ids, const int32_t* n_tokens,
                            int32_t num_seqs, int32_t* slots_out, int64_t slots_cap,
                            int32_t* cow_pairs_out, int32_t cow_cap, int32_t* num_cow_out);
-/* Drop a sequence; blocks whose count reaches 0 return to the free list. */
+/* Drop a sequence; blocks whose count reaches 0 return to the free list, or, if
+ * cached, to the released list (below). */
 int pkv_alloc_free_seq(pkv_allocator* a, int64_t seq_id);
 /* Copy seq_id's table into out (capacity cap); *len_out = its block count. */
 int pkv_alloc_block_table(const pkv_allocator* a, int64_t seq_id, int32_t* out, int32_t cap,
@@ -321,10 +323,38 @@ int pkv_alloc_block_tables(const pkv_allocator* a, const int64_t* seq_ids, int32
                            int32_t* context_lens_out);
 /* Tokens held by seq_id, or PKV_ENOSEQ. */
 int64_t pkv_alloc_seq_len(const pkv_allocator* a, int64_t seq_id);
+/* Blocks an allocation can take: free blocks plus released cached ones. */
 int32_t pkv_alloc_num_free(const pkv_allocator* a);
 int32_t pkv_alloc_num_blocks(const pkv_allocator* a);
 /* Reference count of a block (number of table entries holding it); -1 if out of range. */
 int32_t pkv_alloc_refcount(const pkv_allocator* a, int32_t block_id);
+
+/* Automatic prefix caching ("How vLLM Works?", section 05; "vLLM and
+ * PagedAttention", section 4; "vLLM — PagedAttention and Continuous Batching",
+ * §5).  A sequence made with its token ids keys every full block by (the key of
+ * the block before it, a salt, the block's 16 token ids); a full block whose key
+ * is new is cached.  A block that is not full is never cached.  A cached block
+ * whose last user is freed goes on a released list: a later hit revives it, and
+ * when no free block is left an allocation takes over the least recently
+ * released one (a freed sequence's cached blocks join that list from its last
+ * block to its first).  Different salts never share blocks (tenant isolation).
+ *
+ * pkv_alloc_add_seq_tokens: new sequence seq_id holding tokens[n_tokens].  Its
+ * longest prefix of whole cached blocks (looked up block by block from the
+ * start, stopping at the first key not found) is taken from the cache: those
+ * *num_cached_out tokens get slot -1 in slots_out[n_tokens] (their K/V is in the
+ * pool already; pkv_write skips negative slots), the others get new slots.
+ * PKV_EINVAL (bad arguments, id exists), PKV_ENOMEM (all-or-nothing: the blocks
+ * a hit revives are counted out of the released list first). */
+int pkv_alloc_add_seq_tokens(pkv_allocator* a, int64_t seq_id, const int32_t* tokens, int32_t n_tokens,
+                             uint64_t salt, int32_t* slots_out, int32_t* num_cached_out);
+/* pkv_alloc_append with the new tokens' ids, for a sequence made by
+ * pkv_alloc_add_seq_tokens (or forked from one): blocks that become full are
+ * keyed and cached.  PKV_EINVAL for a sequence without token ids. */
+int pkv_alloc_append_tokens(pkv_allocator* a, int64_t seq_id, const int32_t* tokens, int32_t n_tokens,
+                            int32_t* slots_out, int32_t* cow_pairs_out, int32_t* num_cow_out);
+/* Released cached blocks (count 0, reusable by a hit; included in num_free). */
+int32_t pkv_alloc_num_cached(const pkv_allocator* a);
 
 #ifdef __cplusplus
 }

@@ -146,8 +146,10 @@ class PrefixCachingAllocatorModel(BlockAllocatorModel):
 
     Readings where the pages are silent: a block's key here is the exact tuple
     (parent key, salt, tokens), so equal keys mean equal contents; a released
-    sequence hands its blocks back from its last to its first, so a prefix's
-    later blocks are taken over before its earlier ones; a block that becomes
+    sequence hands its uncached blocks back to the free list in table order (as
+    the plain allocator does) and its cached ones to the released list from its
+    last to its first, so a prefix's later blocks are taken over before its
+    earlier ones; a block that becomes
     full while an equal block is already cached is not cached a second time;
     a plain ``append`` (token ids unknown) ends caching for that sequence.
     """
@@ -284,10 +286,10 @@ class PrefixCachingAllocatorModel(BlockAllocatorModel):
         del self._lens[seq]
         for m in (self._toks, self._salt, self._keys):
             m.pop(seq, None)
-        for b in reversed(tbl):
+        for b in tbl:
             self._ref[b] -= 1
-            if self._ref[b] == 0:
-                if b in self._key_of:
-                    self._evictable[b] = True
-                else:
-                    self._free.append(b)
+            if self._ref[b] == 0 and b not in self._key_of:
+                self._free.append(b)
+        for b in reversed(tbl):
+            if self._ref[b] == 0 and b in self._key_of:
+                self._evictable[b] = True

@@ -67,6 +67,9 @@ SIGNATURES = {
     "pkv_alloc_num_free": (_i32, [_p]),
     "pkv_alloc_num_blocks": (_i32, [_p]),
     "pkv_alloc_refcount": (_i32, [_p, _i32]),
+    "pkv_alloc_add_seq_tokens": (ctypes.c_int, [_p, _i64, _p, _i32, _u64, _p, _p]),
+    "pkv_alloc_append_tokens": (ctypes.c_int, [_p, _i64, _p, _i32, _p, _p, _p]),
+    "pkv_alloc_num_cached": (_i32, [_p]),
 }
 
 _lib = None

@@ -119,3 +119,36 @@ class BlockAllocator:
 
     def refcount(self, block):
         return int(lib().pkv_alloc_refcount(self._h, int(block)))
+
+    # --- automatic prefix caching -------------------------------------------
+    def add_seq_tokens(self, seq, tokens, salt=0):
+        """New sequence holding ``tokens``; returns ``(slots, n_cached)``.
+
+        The first ``n_cached`` tokens (whole cached blocks) get slot -1: their K/V
+        is in the pool already and ``pkv_write`` skips them.
+        """
+        toks = np.ascontiguousarray(tokens, dtype=np.int32)
+        n = toks.size
+        slots = np.empty(max(1, n), dtype=np.int32)
+        nc = ctypes.c_int32(0)
+        self._check("pkv_alloc_add_seq_tokens", lib().pkv_alloc_add_seq_tokens(
+            self._h, int(seq), toks.ctypes.data if n else None, n, int(salt) & (2**64 - 1),
+            slots.ctypes.data, ctypes.addressof(nc)))
+        return slots[:n].tolist(), int(nc.value)
+
+    def append_tokens(self, seq, tokens):
+        """``append`` with the new tokens' ids: blocks that become full are cached."""
+        toks = np.ascontiguousarray(tokens, dtype=np.int32)
+        n = toks.size
+        slots = np.empty(max(1, n), dtype=np.int32)
+        pairs = np.empty(2, dtype=np.int32)
+        ncow = ctypes.c_int32(0)
+        self._check("pkv_alloc_append_tokens", lib().pkv_alloc_append_tokens(
+            self._h, int(seq), toks.ctypes.data if n else None, n, slots.ctypes.data, pairs.ctypes.data,
+            ctypes.addressof(ncow)))
+        cow = [(int(pairs[0]), int(pairs[1]))] if ncow.value else []
+        return slots[:n].tolist(), cow
+
+    def num_cached(self):
+        """Released cached blocks (count 0, reusable by a prefix hit)."""
+        return int(lib().pkv_alloc_num_cached(self._h))

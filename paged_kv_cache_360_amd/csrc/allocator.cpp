@@ -9,12 +9,27 @@
 // PagedAttention and Continuous Batching", §2.3).  Only a partly filled last block
 // is ever written, so that is the only block copy-on-write ever copies.
 //
+// Automatic prefix caching ("How vLLM Works?", section 05; "vLLM and
+// PagedAttention", section 4; "vLLM — PagedAttention and Continuous Batching",
+// §5): sequences made with their token ids key every full block by its tokens,
+// the key of the block before it and a per-sequence salt (which keeps tenants
+// apart), and a full block whose key is new is cached.  A later sequence whose
+// prompt starts with cached blocks takes them instead of new ones, block by
+// block from the start until the first key not found; only full blocks are ever
+// cached.  A cached block whose last user is released is kept on a released
+// list and revived by a later hit; when no free block is left, allocation takes
+// over the least recently released one (a sequence's blocks go on that list
+// from its last to its first).  Keys are looked up by a 64-bit hash and
+// compared in full (parent key hash, salt, tokens).
+//
 // The allocator touches no device memory.  It hands (src, dst) copy pairs back to
 // the caller, who runs them with pkv_copy_blocks before writing the new tokens.
 
 #include <algorithm>
+#include <array>
 #include <cstdint>
 #include <cstring>
+#include <list>
 #include <new>
 #include <unordered_map>
 #include <unordered_set>
@@ -28,7 +43,37 @@ namespace {
 struct Seq {
   std::vector<int32_t> table;  // logical block index -> physical block id
   int64_t len = 0;             // tokens held
+  // prefix caching: only for sequences whose token ids are known
+  bool tracked = false;
+  uint64_t salt = 0;
+  std::vector<int32_t> tokens;  // all len token ids
+  std::vector<uint64_t> keys;   // key hash of each full block
 };
+
+// A cached full block: its key, compared in full on lookup.
+struct CacheEntry {
+  int32_t block;
+  uint64_t parent;  // key hash of the block before it (0 for a first block)
+  uint64_t salt;
+  std::array<int32_t, PKV_BLOCK_SIZE> tokens;
+  bool same(uint64_t p, uint64_t s, const int32_t* t) const {
+    return parent == p && salt == s && std::equal(tokens.begin(), tokens.end(), t);
+  }
+};
+
+// 64-bit key hash of a full block: the splitmix64 output function applied
+// after each of parent, salt and the tokens is folded in.
+inline uint64_t mix64(uint64_t z) {
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+inline uint64_t block_key(uint64_t parent, uint64_t salt, const int32_t* tokens) {
+  uint64_t h = mix64(parent + 0x9E3779B97F4A7C15ull);
+  h = mix64(h ^ salt);
+  for (int i = 0; i < PKV_BLOCK_SIZE; ++i) h = mix64(h + (uint32_t)tokens[i] + 0x9E3779B97F4A7C15ull);
+  return h;
+}
 
 // splitmix64 (Steele, Lea and Flood, "Fast splittable pseudorandom number
 // generators", OOPSLA 2014): a Weyl sequence passed through a 64-bit mixer.
@@ -57,6 +102,55 @@ struct pkv_allocator {
   std::vector<int32_t> free_stack;  // back() is handed out next
   std::vector<int32_t> ref;
   std::unordered_map<int64_t, Seq> seqs;
+  // prefix cache: key hash -> entry; per block: its key hash when cached; the
+  // released cached blocks (count 0), least recently released first
+  std::unordered_map<uint64_t, CacheEntry> cache;
+  std::vector<uint64_t> key_of;
+  std::vector<char> cached;
+  std::list<int32_t> released;
+  std::vector<std::list<int32_t>::iterator> released_at;
+  std::vector<char> is_released;
+
+  // Blocks an allocation can take: free ones and released cached ones.
+  int64_t available() const { return (int64_t)free_stack.size() + (int64_t)released.size(); }
+
+  // A block for new data: a free one, else the least recently released cached
+  // one (dropped from the cache).  Callers check available() first.
+  int32_t take() {
+    if (!free_stack.empty()) {
+      const int32_t b = free_stack.back();
+      free_stack.pop_back();
+      return b;
+    }
+    const int32_t b = released.front();
+    released.pop_front();
+    is_released[b] = 0;
+    cache.erase(key_of[b]);
+    cached[b] = 0;
+    return b;
+  }
+
+  // Block idx of s just became full: record its key; cache it if the key is new.
+  void register_full(Seq& s, int64_t idx) {
+    const uint64_t parent = idx > 0 ? s.keys[idx - 1] : 0;
+    const int32_t* t = s.tokens.data() + idx * block_size;
+    const uint64_t h = block_key(parent, s.salt, t);
+    s.keys.push_back(h);
+    const int32_t b = s.table[idx];
+    if (cached[b] || cache.count(h)) return;
+    CacheEntry e{b, parent, s.salt, {}};
+    std::copy(t, t + block_size, e.tokens.begin());
+    cache.emplace(h, e);
+    key_of[b] = h;
+    cached[b] = 1;
+  }
+
+  void untrack(Seq& s) {
+    s.tracked = false;
+    s.tokens.clear();
+    s.tokens.shrink_to_fit();
+    s.keys.clear();
+  }
 
   // Blocks and CoW copies that appending n tokens to s needs, given pending
   // refcount decrements from earlier members of the same batch.
@@ -84,8 +178,7 @@ struct pkv_allocator {
     const int32_t bs = block_size;
     if ((s.len % bs) != 0 && ref[s.table.back()] > 1) {
       const int32_t src = s.table.back();
-      const int32_t dst = free_stack.back();
-      free_stack.pop_back();
+      const int32_t dst = take();
       ref[src] -= 1;
       ref[dst] = 1;
       s.table.back() = dst;
@@ -96,14 +189,38 @@ struct pkv_allocator {
     for (int32_t i = 0; i < n; ++i) {
       const int64_t pos = s.len + i;
       if (pos % bs == 0) {
-        const int32_t b = free_stack.back();
-        free_stack.pop_back();
+        const int32_t b = take();
         ref[b] = 1;
         s.table.push_back(b);
       }
       slots[i] = s.table[pos / bs] * bs + (int32_t)(pos % bs);
     }
     s.len += n;
+  }
+
+  // append_fitting for a tracked sequence: the ids are kept and blocks that
+  // become full are keyed (and cached when their key is new).
+  void append_tokens_fitting(Seq& s, const int32_t* toks, int32_t n, int32_t* slots, int32_t* pair,
+                             int32_t* ncow) {
+    const int64_t before = s.len;
+    append_fitting(s, n, slots, pair, ncow);
+    s.tokens.insert(s.tokens.end(), toks, toks + n);
+    for (int64_t idx = before / block_size; idx < s.len / block_size; ++idx) register_full(s, idx);
+  }
+
+  // A released sequence's blocks: uncached ones back to the free list in table
+  // order, cached ones to the released list from the last to the first.
+  void release(const Seq& s) {
+    for (int32_t b : s.table)
+      if (--ref[b] == 0 && !cached[b]) free_stack.push_back(b);
+    for (auto it = s.table.rbegin(); it != s.table.rend(); ++it) {
+      const int32_t b = *it;
+      if (ref[b] == 0 && cached[b] && !is_released[b]) {
+        released.push_back(b);
+        released_at[b] = std::prev(released.end());
+        is_released[b] = 1;
+      }
+    }
   }
 };
 
@@ -120,6 +237,10 @@ pkv_allocator* pkv_alloc_create(int32_t num_blocks, int32_t block_size, uint64_t
     a->num_blocks = num_blocks;
     a->block_size = block_size;
     a->ref.assign(num_blocks, 0);
+    a->key_of.assign(num_blocks, 0);
+    a->cached.assign(num_blocks, 0);
+    a->released_at.assign(num_blocks, a->released.end());
+    a->is_released.assign(num_blocks, 0);
     std::vector<int32_t> order(num_blocks);
     for (int32_t i = 0; i < num_blocks; ++i) order[i] = i;
     if (shuffle_seed != 0) {
@@ -167,11 +288,11 @@ int pkv_alloc_append(pkv_allocator* a, int64_t seq_id, int32_t n_tokens, int32_t
   std::unordered_map<int32_t, int32_t> pending;
   int64_t blocks = 0, cows = 0;
   a->need_for(it->second, n_tokens, pending, blocks, cows);
-  if (blocks > (int64_t)a->free_stack.size())
-    return pkv::fail(PKV_ENOMEM, "pkv_alloc_append: block pool exhausted");
+  if (blocks > a->available()) return pkv::fail(PKV_ENOMEM, "pkv_alloc_append: block pool exhausted");
   if (it->second.len + n_tokens > (int64_t)INT32_MAX)
     return pkv::fail(PKV_EINVAL, "pkv_alloc_append: sequence too long");
   a->append_fitting(it->second, n_tokens, slots_out, cow_pairs_out, num_cow_out);
+  if (n_tokens > 0) a->untrack(it->second);  // ids unknown from here on
   return PKV_OK;
 }
 
@@ -200,13 +321,14 @@ int pkv_alloc_append_batch(pkv_allocator* a, const int64_t* seq_ids, const int32
     return pkv::fail(PKV_EINVAL, "pkv_alloc_append_batch: slots_out too small");
   if (cows > cow_cap || (cows > 0 && !cow_pairs_out))
     return pkv::fail(PKV_EINVAL, "pkv_alloc_append_batch: cow_pairs_out too small");
-  if (blocks > (int64_t)a->free_stack.size())
+  if (blocks > a->available())
     return pkv::fail(PKV_ENOMEM, "pkv_alloc_append_batch: block pool exhausted");
   int64_t off = 0;
   int32_t ncow_total = 0;
   for (int32_t i = 0; i < num_seqs; ++i) {
     int32_t pair[2], ncow = 0;
     a->append_fitting(*rows[i], n_tokens[i], slots_out + off, pair, &ncow);
+    if (n_tokens[i] > 0) a->untrack(*rows[i]);
     off += n_tokens[i];
     if (ncow) {
       cow_pairs_out[2 * ncow_total] = pair[0];
@@ -222,9 +344,7 @@ int pkv_alloc_free_seq(pkv_allocator* a, int64_t seq_id) {
   if (!a) return pkv::fail(PKV_EINVAL, "pkv_alloc_free_seq: null allocator");
   auto it = a->seqs.find(seq_id);
   if (it == a->seqs.end()) return pkv::fail(PKV_ENOSEQ, "pkv_alloc_free_seq: unknown sequence");
-  for (int32_t b : it->second.table) {
-    if (--a->ref[b] == 0) a->free_stack.push_back(b);
-  }
+  a->release(it->second);
   a->seqs.erase(it);
   return PKV_OK;
 }
@@ -272,8 +392,72 @@ int64_t pkv_alloc_seq_len(const pkv_allocator* a, int64_t seq_id) {
   return it->second.len;
 }
 
-int32_t pkv_alloc_num_free(const pkv_allocator* a) {
-  return a ? (int32_t)a->free_stack.size() : PKV_EINVAL;
+int32_t pkv_alloc_num_free(const pkv_allocator* a) { return a ? (int32_t)a->available() : PKV_EINVAL; }
+
+int32_t pkv_alloc_num_cached(const pkv_allocator* a) { return a ? (int32_t)a->released.size() : PKV_EINVAL; }
+
+int pkv_alloc_add_seq_tokens(pkv_allocator* a, int64_t seq_id, const int32_t* tokens, int32_t n_tokens,
+                             uint64_t salt, int32_t* slots_out, int32_t* num_cached_out) {
+  if (!a || n_tokens < 0 || (n_tokens > 0 && (!tokens || !slots_out)) || !num_cached_out)
+    return pkv::fail(PKV_EINVAL, "pkv_alloc_add_seq_tokens: bad arguments");
+  if (a->seqs.count(seq_id)) return pkv::fail(PKV_EINVAL, "pkv_alloc_add_seq_tokens: sequence exists");
+  const int32_t bs = a->block_size;
+  // cached full blocks from the start, up to the first key not found
+  std::vector<std::pair<int32_t, uint64_t>> hits;
+  uint64_t parent = 0;
+  int64_t revived = 0;
+  for (int32_t i = 0; i + 1 <= n_tokens / bs; ++i) {
+    const int32_t* t = tokens + (int64_t)i * bs;
+    const uint64_t h = block_key(parent, salt, t);
+    auto it = a->cache.find(h);
+    if (it == a->cache.end() || !it->second.same(parent, salt, t)) break;
+    hits.emplace_back(it->second.block, h);
+    if (a->ref[it->second.block] == 0) ++revived;
+    parent = h;
+  }
+  const int64_t need = blocks_for(n_tokens, bs) - (int64_t)hits.size();
+  if (need > a->available() - revived)
+    return pkv::fail(PKV_ENOMEM, "pkv_alloc_add_seq_tokens: block pool exhausted");
+  Seq s;
+  s.tracked = true;
+  s.salt = salt;
+  for (const auto& hk : hits) {
+    const int32_t b = hk.first;
+    if (a->is_released[b]) {
+      a->released.erase(a->released_at[b]);
+      a->is_released[b] = 0;
+    }
+    a->ref[b] += 1;
+    s.table.push_back(b);
+    s.keys.push_back(hk.second);
+  }
+  const int32_t n_cached = (int32_t)hits.size() * bs;
+  s.tokens.assign(tokens, tokens + n_cached);
+  s.len = n_cached;
+  for (int32_t i = 0; i < n_cached; ++i) slots_out[i] = -1;
+  int32_t pair[2], ncow = 0;  // a sequence of whole cached blocks has no partial block to copy
+  a->append_tokens_fitting(s, tokens + n_cached, n_tokens - n_cached, slots_out + n_cached, pair, &ncow);
+  a->seqs.emplace(seq_id, std::move(s));
+  *num_cached_out = n_cached;
+  return PKV_OK;
+}
+
+int pkv_alloc_append_tokens(pkv_allocator* a, int64_t seq_id, const int32_t* tokens, int32_t n_tokens,
+                            int32_t* slots_out, int32_t* cow_pairs_out, int32_t* num_cow_out) {
+  if (!a || n_tokens < 0 || (n_tokens > 0 && (!tokens || !slots_out)) || !cow_pairs_out || !num_cow_out)
+    return pkv::fail(PKV_EINVAL, "pkv_alloc_append_tokens: bad arguments");
+  auto it = a->seqs.find(seq_id);
+  if (it == a->seqs.end()) return pkv::fail(PKV_ENOSEQ, "pkv_alloc_append_tokens: unknown sequence");
+  if (!it->second.tracked)
+    return pkv::fail(PKV_EINVAL, "pkv_alloc_append_tokens: sequence was not made with token ids");
+  std::unordered_map<int32_t, int32_t> pending;
+  int64_t blocks = 0, cows = 0;
+  a->need_for(it->second, n_tokens, pending, blocks, cows);
+  if (blocks > a->available()) return pkv::fail(PKV_ENOMEM, "pkv_alloc_append_tokens: block pool exhausted");
+  if (it->second.len + n_tokens > (int64_t)INT32_MAX)
+    return pkv::fail(PKV_EINVAL, "pkv_alloc_append_tokens: sequence too long");
+  a->append_tokens_fitting(it->second, tokens, n_tokens, slots_out, cow_pairs_out, num_cow_out);
+  return PKV_OK;
 }
 
 int32_t pkv_alloc_num_blocks(const pkv_allocator* a) { return a ? a->num_blocks : PKV_EINVAL; }
