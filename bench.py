@@ -61,6 +61,9 @@ def parse_args():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain block copy of known size (counter calibration)")
+    ap.add_argument("--prefix-cache-probe", action="store_true",
+                    help="only time the host allocator admitting requests through the prefix cache "
+                         "(a shared 1500-token system prompt; no GPU work)")
     ap.add_argument("--json-out", default=None)
     ap.add_argument("--traffic-from", nargs=4, metavar="CSV", default=None,
                     help="rocprofv3 counter_collection CSVs: FETCH_SIZE and WRITE_SIZE of a "
@@ -144,10 +147,51 @@ def copy_probe(torch, pkv):
                       "frac_of_hbm_peak": round(2 * moved / t / 1e9 / HBM_PEAK_GBPS, 4)}))
 
 
+def prefix_cache_probe(np, pkv, seed):
+    """Host allocator with automatic prefix caching: requests made of a shared
+    1500-token system prompt and a user part of 8..512 tokens (the shared-prefix
+    batch's lengths) are admitted with add_seq_tokens, decoded for 16 tokens with
+    append_tokens and released, 256 at a time in flight, on a pool that holds
+    them.  Reports how many prompt tokens the cache served and the host time per
+    admission."""
+    rng = np.random.default_rng(seed)
+    system = np.arange(1500, dtype=np.int32)
+    n_req, in_flight = 4096, 256
+    alloc = pkv.BlockAllocator(in_flight * 64 + 256, 16, shuffle_seed=seed)
+    prompt_tokens = cached_tokens = 0
+    t_admit = t_decode = 0.0
+    live = []
+    for r in range(n_req):
+        user = 100_000 + rng.integers(0, 50_000, size=int(rng.integers(8, 513)), dtype=np.int32)
+        toks = np.concatenate([system, user])
+        t0 = time.perf_counter()
+        _, c = alloc.add_seq_tokens(r, toks)
+        t_admit += time.perf_counter() - t0
+        prompt_tokens += toks.size
+        cached_tokens += c
+        t0 = time.perf_counter()
+        alloc.append_tokens(r, rng.integers(0, 50_000, size=16, dtype=np.int32))
+        t_decode += time.perf_counter() - t0
+        live.append(r)
+        if len(live) == in_flight:
+            alloc.free_seq(live.pop(0))
+    print(json.dumps({"probe": "prefix_cache_host_allocator", "requests": n_req, "in_flight": in_flight,
+                      "system_prompt_tokens": 1500, "user_tokens": "uniform [8, 512]",
+                      "prompt_tokens": int(prompt_tokens), "served_from_cache": int(cached_tokens),
+                      "served_fraction": round(cached_tokens / prompt_tokens, 4),
+                      "admit_us_per_request": round(t_admit / n_req * 1e6, 2),
+                      "append16_us_per_request": round(t_decode / n_req * 1e6, 2)}))
+
+
 def main():
     args = parse_args()
     if args.traffic_from:
         return traffic_from_counters(args.traffic_from, args.workload, args.warmup, args.steps)
+    if args.prefix_cache_probe:
+        import numpy as np
+
+        import paged_kv_cache_360_amd as pkv
+        return prefix_cache_probe(np, pkv, args.seed)
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU only: --gpus {args.gpus} (WORLD_SIZE={world}) is not "
