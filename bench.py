@@ -64,6 +64,9 @@ def parse_args():
     ap.add_argument("--prefix-cache-probe", action="store_true",
                     help="only time the host allocator admitting requests through the prefix cache "
                          "(a shared 1500-token system prompt; no GPU work)")
+    ap.add_argument("--capacity-sim", action="store_true",
+                    help="only run the host capacity simulator: static reservation against paged "
+                         "blocks under continuous batching (no GPU work)")
     ap.add_argument("--json-out", default=None)
     ap.add_argument("--traffic-from", nargs=4, metavar="CSV", default=None,
                     help="rocprofv3 counter_collection CSVs: FETCH_SIZE and WRITE_SIZE of a "
@@ -192,6 +195,18 @@ def main():
 
         import paged_kv_cache_360_amd as pkv
         return prefix_cache_probe(np, pkv, args.seed)
+    if args.capacity_sim:
+        import numpy as np
+
+        from paged_kv_cache_360_amd import capacity
+        reqs = capacity.draw_requests(np.random.default_rng(args.seed), 1500, 64, 512, 200, 1536)
+        res = {p: capacity.simulate(reqs, 65536, 1536, p) for p in ("static", "paged")}
+        print(json.dumps({"probe": "capacity_sim", "requests": 1500, "prompt": "uniform [64, 512]",
+                          "output": "geometric mean 200, capped at 1536", "memory_slots": 65536,
+                          "static": res["static"], "paged": res["paged"],
+                          "running_ratio": round(res["paged"]["mean_running"] / res["static"]["mean_running"], 2),
+                          "iterations_ratio": round(res["static"]["iterations"] / res["paged"]["iterations"], 2)}))
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU only: --gpus {args.gpus} (WORLD_SIZE={world}) is not "
