@@ -23,7 +23,8 @@ Modules:
 
 * ``attention``  gather through the block table, fp64 softmax attention (decode
   and causal chunk), log-sum-exp merge of partial softmaxes.
-* ``cache_ops``  the slot scatter write and the copy-on-write block copy.
+* ``cache_ops``  the slot scatter write, the copy-on-write block copy and the
+  block copy between the device pool and a host pool (swapping).
 * ``allocator``  a Python model of the block allocator (refcounts, fork, CoW) and
   of its automatic prefix caching.
 
@@ -40,5 +41,5 @@ from .attention import (  # noqa: F401
     merge_partials,
     split_decode_partials,
 )
-from .cache_ops import write_kv, copy_blocks  # noqa: F401
+from .cache_ops import write_kv, copy_blocks, swap_blocks  # noqa: F401
 from .allocator import BlockAllocatorModel, PrefixCachingAllocatorModel, slot_for_position  # noqa: F401

@@ -18,6 +18,19 @@ sequences) that hold it; it returns to the free list when the count reaches 0.
 Only a partly filled last block is ever written, so only that block is ever
 copied; full shared blocks stay shared.
 
+Preemption by swapping ("vLLM and PagedAttention", §3 continuous batching, on
+the scheduler's preemption: under memory pressure the KV of some requests moves
+to CPU memory and comes back once memory frees up; "How vLLM Works?", section
+04 on preemption, recompute being the other mode): a second pool of host blocks; a
+swap-out moves whole sequences there, a swap-in brings them back.  Readings
+where the pages are silent: a block held several times within one swap-out
+group gets one host block (and one device block on the way back), so sharing
+inside the group survives the round trip; a device block also held by a
+sequence that stays on the device is copied and stays where it is; host blocks
+are handed out lowest id first and reused last-freed first; a swapped sequence
+can only be swapped in or freed.  Recompute mode needs no new operation: the
+sequence is freed and later added again with its tokens.
+
 Operations are all-or-nothing: when the pool cannot supply every block an
 operation needs, ``MemoryError`` is raised and no state changes.
 """
@@ -47,10 +60,27 @@ class BlockAllocatorModel:
         self._ref = [0] * num_blocks
         self._tables = {}
         self._lens = {}
+        self._hfree = []                  # host blocks, pop() hands out the lowest first
+        self._href = []
+        self._swapped = {}                # seq -> table of host block ids
 
     # --- queries -----------------------------------------------------------
     def num_free(self):
         return len(self._free)
+
+    def num_free_host(self):
+        return len(self._hfree)
+
+    def host_refcount(self, hblock):
+        return self._href[hblock]
+
+    def host_table(self, seq):
+        return list(self._swapped[seq])
+
+    def is_swapped(self, seq):
+        if seq not in self._tables and seq not in self._swapped:
+            raise KeyError(f"unknown sequence {seq}")
+        return seq in self._swapped
 
     def refcount(self, block):
         return self._ref[block]
@@ -65,15 +95,18 @@ class BlockAllocatorModel:
         return list(self._tables)
 
     # --- operations --------------------------------------------------------
+    def _exists(self, seq):
+        return seq in self._tables or seq in self._swapped
+
     def add_seq(self, seq):
-        if seq in self._tables:
+        if self._exists(seq):
             raise KeyError(f"sequence {seq} exists")
         self._tables[seq] = []
         self._lens[seq] = 0
 
     def fork(self, parent, child):
         """Child shares every block of the parent (counts +1); same length."""
-        if child in self._tables:
+        if self._exists(child):
             raise KeyError(f"sequence {child} exists")
         tbl = list(self._tables[parent])
         for b in tbl:
@@ -101,7 +134,7 @@ class BlockAllocatorModel:
         pairs = []
         if cow:
             src = tbl[-1]
-            dst = self._free.pop()
+            dst = self._take()
             self._ref[src] -= 1
             self._ref[dst] = 1
             tbl[-1] = dst
@@ -109,7 +142,7 @@ class BlockAllocatorModel:
         slots = []
         for pos in range(L, L + n_tokens):
             if pos % bs == 0:
-                b = self._free.pop()
+                b = self._take()
                 self._ref[b] = 1
                 tbl.append(b)
             slots.append(slot_for_position(tbl, pos, bs))
@@ -117,13 +150,95 @@ class BlockAllocatorModel:
         return slots, pairs
 
     def free_seq(self, seq):
-        """Drop a sequence; blocks whose count reaches 0 return to the free list."""
+        """Drop a sequence; blocks whose count reaches 0 return to the free list
+        (host blocks to the host free list for a swapped sequence)."""
+        if seq in self._swapped:
+            self._drop_host(self._swapped.pop(seq))
+            del self._lens[seq]
+            return
         tbl = self._tables.pop(seq)
         del self._lens[seq]
+        self._release(tbl)
+
+    # --- swapping to a host pool ---------------------------------------------
+    def set_host_pool(self, num_host_blocks):
+        """A host pool of ``num_host_blocks`` blocks (no sequence may be swapped out)."""
+        if num_host_blocks < 0:
+            raise ValueError("num_host_blocks must be >= 0")
+        if self._swapped:
+            raise ValueError("sequences are swapped out")
+        self._hfree = list(range(num_host_blocks))[::-1]
+        self._href = [0] * num_host_blocks
+
+    def swap_out(self, seqs):
+        """Move the sequences ``seqs`` (distinct, on the device) to host blocks.
+
+        Returns the ``(device block, host block)`` copies, one per distinct device
+        block in order of first appearance (sequences in the given order, each
+        table in order).  The caller copies them before the device blocks are
+        reused.
+        """
+        seqs = self._group(seqs, swapped=False)
+        distinct = list(dict.fromkeys(b for q in seqs for b in self._tables[q]))
+        if len(distinct) > len(self._hfree):
+            raise MemoryError("host pool exhausted")
+        to_host = {b: self._hfree.pop() for b in distinct}
+        for q in seqs:
+            tbl = self._tables.pop(q)
+            htbl = [to_host[b] for b in tbl]
+            for h in htbl:
+                self._href[h] += 1
+            self._swapped[q] = htbl
+            self._release(tbl)
+        return [(b, to_host[b]) for b in distinct]
+
+    def swap_in(self, seqs):
+        """Bring swapped sequences back to new device blocks.
+
+        Returns the ``(host block, device block)`` copies, one per distinct host
+        block in order of first appearance.
+        """
+        seqs = self._group(seqs, swapped=True)
+        distinct = list(dict.fromkeys(h for q in seqs for h in self._swapped[q]))
+        if len(distinct) > self.num_free():
+            raise MemoryError("block pool exhausted")
+        to_dev = {h: self._take() for h in distinct}
+        for q in seqs:
+            htbl = self._swapped.pop(q)
+            tbl = [to_dev[h] for h in htbl]
+            for b in tbl:
+                self._ref[b] += 1
+            self._tables[q] = tbl
+            self._drop_host(htbl)
+        return [(h, to_dev[h]) for h in distinct]
+
+    # --- internals -----------------------------------------------------------
+    def _take(self):
+        return self._free.pop()
+
+    def _release(self, tbl):
+        """Drop one reference per table entry; blocks at 0 return to the free list."""
         for b in tbl:
             self._ref[b] -= 1
             if self._ref[b] == 0:
                 self._free.append(b)
+
+    def _drop_host(self, htbl):
+        for h in htbl:
+            self._href[h] -= 1
+            if self._href[h] == 0:
+                self._hfree.append(h)
+
+    def _group(self, seqs, swapped):
+        seqs = list(seqs)
+        if len(set(seqs)) != len(seqs):
+            raise ValueError("sequence ids must be distinct")
+        for q in seqs:
+            if q not in self._tables and q not in self._swapped:
+                raise KeyError(f"unknown sequence {q}")
+            if (q in self._swapped) != swapped:
+                raise ValueError(f"sequence {q} is {'not ' if swapped else ''}swapped out")
+        return seqs
 
 
 class PrefixCachingAllocatorModel(BlockAllocatorModel):
@@ -197,7 +312,7 @@ class PrefixCachingAllocatorModel(BlockAllocatorModel):
         first ``n_cached`` tokens (whole blocks) come from cached blocks and get
         slot -1 (nothing to write); the others get the slot to write their K/V to.
         """
-        if seq in self._tables:
+        if self._exists(seq):
             raise KeyError(f"sequence {seq} exists")
         bs = self.block_size
         tokens = [int(t) for t in tokens]
@@ -282,10 +397,13 @@ class PrefixCachingAllocatorModel(BlockAllocatorModel):
             self._keys[child] = list(self._keys[parent])
 
     def free_seq(self, seq):
-        tbl = self._tables.pop(seq)
-        del self._lens[seq]
+        super().free_seq(seq)
         for m in (self._toks, self._salt, self._keys):
             m.pop(seq, None)
+
+    def _release(self, tbl):
+        """Uncached blocks at count 0 go back to the free list in table order,
+        cached ones to the released list from the last to the first."""
         for b in tbl:
             self._ref[b] -= 1
             if self._ref[b] == 0 and b not in self._key_of:

@@ -45,3 +45,23 @@ def copy_blocks(key_cache, value_cache, pairs):
         kc[dst] = key_cache[src]
         vc[dst] = value_cache[src]
     return kc, vc
+
+
+def swap_blocks(dst_key, dst_value, src_key, src_value, pairs):
+    """Block copies between two pools of the same block shape: for each
+    ``(src, dst)``, block ``dst`` of the destination := block ``src`` of the source.
+
+    Swapping a preempted request's KV out to CPU memory and back ("vLLM and
+    PagedAttention", §3 continuous batching, on preemption) moves whole
+    blocks between the device pool and a host pool; each block is one contiguous
+    ``[block_size, Hkv, D]`` slab in both.  Pairs whose ids fall outside either
+    pool are skipped.  Returns new destination arrays.
+    """
+    kd = np.array(dst_key, copy=True)
+    vd = np.array(dst_value, copy=True)
+    ns, nd = src_key.shape[0], dst_key.shape[0]
+    for src, dst in np.asarray(pairs, dtype=np.int64).reshape(-1, 2).tolist():
+        if 0 <= src < ns and 0 <= dst < nd:
+            kd[dst] = src_key[src]
+            vd[dst] = src_value[src]
+    return kd, vd
