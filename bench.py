@@ -67,6 +67,10 @@ def parse_args():
     ap.add_argument("--capacity-sim", action="store_true",
                     help="only run the host capacity simulator: static reservation against paged "
                          "blocks under continuous batching (no GPU work)")
+    ap.add_argument("--swap-probe", action="store_true",
+                    help="only time pkv_swap_blocks between the device pool and a pinned host pool "
+                         "(8192 scattered 32 KiB blocks per cache each way) against one contiguous "
+                         "copy of the same bytes")
     ap.add_argument("--json-out", default=None)
     ap.add_argument("--traffic-from", nargs=4, metavar="CSV", default=None,
                     help="rocprofv3 counter_collection CSVs: FETCH_SIZE and WRITE_SIZE of a "
@@ -150,6 +154,52 @@ def copy_probe(torch, pkv):
                       "frac_of_hbm_peak": round(2 * moved / t / 1e9 / HBM_PEAK_GBPS, 4)}))
 
 
+def swap_probe(torch, pkv, seed):
+    """pkv_swap_blocks moving 8192 scattered 32 KiB blocks per cache (512 MiB in all)
+    from the device pool to a pinned host pool and back, next to one contiguous
+    copy of the same bytes each way (the host link's rate for a plain copy)."""
+    n, hkv, d = 8192, 8, 128
+    nb = 2 * n                                          # device pool twice the moved blocks
+    kc = torch.randn((nb, 16, hkv, d), device="cuda").to(torch.bfloat16)
+    vc = torch.randn((nb, 16, hkv, d), device="cuda").to(torch.bfloat16)
+    hk = torch.empty((n, 16, hkv, d), dtype=torch.bfloat16, pin_memory=True)
+    hv = torch.empty_like(hk, pin_memory=True)
+    g = torch.Generator().manual_seed(seed)
+    dev_ids = torch.randperm(nb, generator=g)[:n]
+    host_ids = torch.randperm(n, generator=g)
+    out_pairs = torch.stack([dev_ids, host_ids], 1).to(torch.int32).cuda()
+    in_pairs = torch.stack([host_ids, dev_ids], 1).to(torch.int32).cuda()
+    moved = 2 * n * 16 * hkv * d * 2
+    reps = 3
+
+    def timed(fn):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 2)]
+        ev[0].record()
+        fn()                                            # warm-up launch
+        for i in range(reps):
+            ev[i + 1].record()
+            fn()
+        ev[reps + 1].record()
+        torch.cuda.synchronize()
+        us = [ev[i].elapsed_time(ev[i + 1]) * 1e3 for i in range(1, reps + 1)]
+        return sum(us) / len(us)
+
+    res = {}
+    res["swap_out_us"] = timed(lambda: pkv.pkv_swap_blocks(hk, hv, kc, vc, out_pairs))
+    res["swap_in_us"] = timed(lambda: pkv.pkv_swap_blocks(kc, vc, hk, hv, in_pairs))
+    dk = kc[:n]
+    dv = vc[:n]
+    res["contiguous_d2h_us"] = timed(lambda: (hk.copy_(dk, non_blocking=True), hv.copy_(dv, non_blocking=True)))
+    res["contiguous_h2d_us"] = timed(lambda: (dk.copy_(hk, non_blocking=True), dv.copy_(hv, non_blocking=True)))
+    line = {"probe": "pkv_swap_blocks", "blocks_per_cache": n, "block_bytes": 16 * hkv * d * 2,
+            "bytes_per_direction": moved, "launches": reps}
+    for k, us in res.items():
+        line[k] = round(us, 1)
+        line[k.replace("_us", "_GBps")] = round(moved / (us * 1e-6) / 1e9, 1)
+    torch.cuda.synchronize()
+    print(json.dumps(line))
+
+
 def prefix_cache_probe(np, pkv, seed):
     """Host allocator with automatic prefix caching: requests made of a shared
     1500-token system prompt and a user part of 8..512 tokens (the shared-prefix
@@ -223,6 +273,9 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     if args.copy_probe:
         copy_probe(torch, pkv)
+        return
+    if args.swap_probe:
+        swap_probe(torch, pkv, args.seed)
         return
 
     spec = SPECS[args.workload]

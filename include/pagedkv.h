@@ -52,7 +52,8 @@ enum {
   PKV_ENOMEM = -3,       /* allocator: not enough free blocks (state unchanged) */
   PKV_ELAUNCH = -4,      /* the HIP runtime rejected a launch */
   PKV_ENOSEQ = -5,       /* allocator: unknown sequence id */
-  PKV_EWORKSPACE = -6    /* workspace missing or smaller than the query says */
+  PKV_EWORKSPACE = -6,   /* workspace missing or smaller than the query says */
+  PKV_ESWAPPED = -7      /* allocator: the sequence is swapped out (or, for a swap-in, is not) */
 };
 
 #define PKV_BLOCK_SIZE 16        /* tokens per block; the only size built */
@@ -265,6 +266,32 @@ int pkv_copy_blocks(void* key_cache, void* value_cache, const int32_t* pairs,
                     int32_t num_kv_heads, int32_t head_dim, pkv_dtype dt, void* stream);
 
 /* ------------------------------------------------------------------------ */
+/* Block copies between two pools of the same block shape, for preemption by
+ * swapping ("vLLM and PagedAttention", §3 continuous batching: under memory
+ * pressure the scheduler moves some requests' KV to CPU memory and brings it
+ * back once memory frees up).  For each pair (src, dst), block dst of the
+ * destination pool (both caches) becomes a byte copy of block src of the source
+ * pool.  One launch moves every pair; run the pairs of pkv_alloc_swap_out
+ * (device pool -> host pool) or pkv_alloc_swap_in (host pool -> device pool).
+ *
+ *   dst_*_cache, src_*_cache  [num_blocks, 16, num_kv_heads, head_dim] of dtype dt,
+ *              each either device memory or page-locked host memory allocated
+ *              mapped for the device (hipHostMalloc; torch pin_memory), which the
+ *              kernel reads or writes across the host link.  The library checks
+ *              each pointer with the HIP runtime: pageable memory, or a buffer
+ *              shorter than its num_blocks blocks, is PKV_EINVAL.
+ *   pairs      device int32 [num_pairs, 2] of (src block, dst block); pairs whose
+ *              ids fall outside [0, src_num_blocks) x [0, dst_num_blocks) are
+ *              skipped.  Two pairs with one dst race (caller error).
+ * Enqueued on stream; the caller keeps a host pool alive and unread until the
+ * stream passes the copy.  num_pairs == 0 launches nothing.
+ * Errors: PKV_EINVAL, PKV_EUNSUPPORTED, PKV_ELAUNCH. */
+int pkv_swap_blocks(void* dst_key_cache, void* dst_value_cache, const void* src_key_cache,
+                    const void* src_value_cache, const int32_t* pairs, int32_t num_pairs,
+                    int32_t src_num_blocks, int32_t dst_num_blocks, int32_t block_size,
+                    int32_t num_kv_heads, int32_t head_dim, pkv_dtype dt, void* stream);
+
+/* ------------------------------------------------------------------------ */
 /* Host-side debug checks (no device access).
  * pkv_check_tables: every entry a sequence uses (the first ceil(context_lens[s]/16)
  * of its row) lies in [0, num_blocks), and context_lens are in [0, max_blocks*16].
@@ -274,6 +301,12 @@ int pkv_check_tables(const int32_t* host_block_tables, const int32_t* host_conte
                      int32_t num_seqs, int32_t max_blocks_per_seq, int32_t num_blocks);
 int pkv_check_slots(const int32_t* host_slot_mapping, int32_t num_tokens, int32_t num_blocks,
                     int32_t block_size);
+/* The check pkv_swap_blocks makes of each pool, on its own (asks the HIP runtime,
+ * launches nothing): PKV_OK if [pool, pool + bytes) is device memory or
+ * page-locked host memory mapped for the device, within one allocation;
+ * PKV_EINVAL otherwise (pageable memory, unknown addresses, a range running past
+ * its allocation). */
+int pkv_check_pool(const void* pool, size_t bytes);
 
 /* ------------------------------------------------------------------------ */
 /* Host block allocator (no device memory; not thread-safe; one pool per object).
@@ -355,6 +388,47 @@ int pkv_alloc_append_tokens(pkv_allocator* a, int64_t seq_id, const int32_t* tok
                             int32_t* slots_out, int32_t* cow_pairs_out, int32_t* num_cow_out);
 /* Released cached blocks (count 0, reusable by a hit; included in num_free). */
 int32_t pkv_alloc_num_cached(const pkv_allocator* a);
+
+/* Preemption by swapping ("vLLM and PagedAttention", §3 continuous batching, on
+ * the scheduler's preemption; "How vLLM Works?", section 04, where recompute is
+ * the other mode: pkv_alloc_free_seq now, pkv_alloc_add_seq_tokens again later).
+ *
+ * pkv_alloc_set_host_pool: a pool of num_host_blocks host block ids (the caller
+ * owns the memory: a page-locked [num_host_blocks, 16, Hkv, D] pair of caches).
+ * Ids are handed out lowest first; freed ids are reused last-freed first.
+ * PKV_ESWAPPED while any sequence is swapped out.
+ *
+ * pkv_alloc_swap_out: moves the distinct sequences seq_ids[num_seqs] (all on the
+ * device) to host blocks.  pairs_out (capacity pairs_cap pairs of 2 ints)
+ * receives one (device block, host block) pair per distinct device block of the
+ * group, in order of first appearance (sequences in the given order, each table
+ * in order); *num_pairs_out their count.  A block held several times inside the
+ * group gets one host block, so sharing inside the group survives.  The group's
+ * device references are dropped as pkv_alloc_free_seq drops them; a block still
+ * held by a sequence outside the group stays where it is.  Run the pairs with
+ * pkv_swap_blocks before anything is written into the released blocks.
+ *
+ * pkv_alloc_swap_in: brings swapped sequences back to new device blocks; pairs
+ * are (host block, device block), one per distinct host block of the group.
+ *
+ * A swapped sequence can only be swapped in, freed (its host blocks return) or
+ * queried for its length and host table: append, fork and the table calls
+ * return PKV_ESWAPPED.  Both calls are all-or-nothing: PKV_ENOMEM when the
+ * target pool is short of blocks, PKV_EINVAL when pairs_out is too small,
+ * PKV_ENOSEQ / PKV_EINVAL (duplicate id) / PKV_ESWAPPED (wrong pool) for a bad
+ * group; nothing changes on an error. */
+int pkv_alloc_set_host_pool(pkv_allocator* a, int32_t num_host_blocks);
+int pkv_alloc_swap_out(pkv_allocator* a, const int64_t* seq_ids, int32_t num_seqs, int32_t* pairs_out,
+                       int32_t pairs_cap, int32_t* num_pairs_out);
+int pkv_alloc_swap_in(pkv_allocator* a, const int64_t* seq_ids, int32_t num_seqs, int32_t* pairs_out,
+                      int32_t pairs_cap, int32_t* num_pairs_out);
+/* 1 if seq_id is swapped out, 0 if on the device; PKV_ENOSEQ if unknown. */
+int pkv_alloc_is_swapped(const pkv_allocator* a, int64_t seq_id);
+/* A swapped sequence's table of host block ids (as pkv_alloc_block_table). */
+int pkv_alloc_host_table(const pkv_allocator* a, int64_t seq_id, int32_t* out, int32_t cap, int32_t* len_out);
+int32_t pkv_alloc_num_free_host(const pkv_allocator* a);
+/* Host table entries holding a host block; -1 if out of range. */
+int32_t pkv_alloc_host_refcount(const pkv_allocator* a, int32_t host_block);
 
 #ifdef __cplusplus
 }

@@ -1,7 +1,8 @@
 """MI355X-native paged KV-cache attention: a thin binding over ``libpagedkv.so``.
 
 The hot path (slot write, copy-on-write block copy, split-context decode
-attention, chunked-prefill attention, log-sum-exp merge) runs in hand-written HIP kernels for gfx950 behind
+attention, chunked-prefill attention, log-sum-exp merge, and the block copies
+that swap preempted sequences to a pinned host pool and back) runs in hand-written HIP kernels for gfx950 behind
 the C ABI declared in ``include/pagedkv.h``; the block allocator is C++ in the
 same library.  This package only marshals arguments.  Importing it loads the
 library and raises if it has not been built.
@@ -25,6 +26,7 @@ from .ops import (  # noqa: F401
     varlen_workspace,
     pkv_lse_merge,
     pkv_copy_blocks,
+    pkv_swap_blocks,
     pkv_check_tables,
     pkv_check_slots,
 )

@@ -22,6 +22,7 @@ PKV_ENOMEM = -3
 PKV_ELAUNCH = -4
 PKV_ENOSEQ = -5
 PKV_EWORKSPACE = -6
+PKV_ESWAPPED = -7
 BLOCK_SIZE = 16
 PARTITION_TOKENS = 512
 
@@ -52,8 +53,11 @@ SIGNATURES = {
                                             _i32, _i32, _i32, _i32, _i32, ctypes.c_int, _p, _sz, _p]),
     "pkv_lse_merge": (ctypes.c_int, [_p, _p, _p, _p, _p, _i32, _i32, _i32, ctypes.c_int, _p]),
     "pkv_copy_blocks": (ctypes.c_int, [_p, _p, _p, _i32, _i32, _i32, _i32, _i32, ctypes.c_int, _p]),
+    "pkv_swap_blocks": (ctypes.c_int, [_p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32, ctypes.c_int,
+                                       _p]),
     "pkv_check_tables": (ctypes.c_int, [_p, _p, _i32, _i32, _i32]),
     "pkv_check_slots": (ctypes.c_int, [_p, _i32, _i32, _i32]),
+    "pkv_check_pool": (ctypes.c_int, [_p, _sz]),
     "pkv_alloc_create": (_p, [_i32, _i32, _u64]),
     "pkv_alloc_destroy": (None, [_p]),
     "pkv_alloc_add_seq": (ctypes.c_int, [_p, _i64]),
@@ -70,6 +74,13 @@ SIGNATURES = {
     "pkv_alloc_add_seq_tokens": (ctypes.c_int, [_p, _i64, _p, _i32, _u64, _p, _p]),
     "pkv_alloc_append_tokens": (ctypes.c_int, [_p, _i64, _p, _i32, _p, _p, _p]),
     "pkv_alloc_num_cached": (_i32, [_p]),
+    "pkv_alloc_set_host_pool": (ctypes.c_int, [_p, _i32]),
+    "pkv_alloc_swap_out": (ctypes.c_int, [_p, _p, _i32, _p, _i32, _p]),
+    "pkv_alloc_swap_in": (ctypes.c_int, [_p, _p, _i32, _p, _i32, _p]),
+    "pkv_alloc_is_swapped": (ctypes.c_int, [_p, _i64]),
+    "pkv_alloc_host_table": (ctypes.c_int, [_p, _i64, _p, _i32, _p]),
+    "pkv_alloc_num_free_host": (_i32, [_p]),
+    "pkv_alloc_host_refcount": (_i32, [_p, _i32]),
 }
 
 _lib = None

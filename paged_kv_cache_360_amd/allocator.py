@@ -152,3 +152,59 @@ class BlockAllocator:
     def num_cached(self):
         """Released cached blocks (count 0, reusable by a prefix hit)."""
         return int(lib().pkv_alloc_num_cached(self._h))
+
+    # --- preemption by swapping to a host pool ----------------------------------
+    def set_host_pool(self, num_host_blocks):
+        self._check("pkv_alloc_set_host_pool", lib().pkv_alloc_set_host_pool(self._h, int(num_host_blocks)))
+        self.num_host_blocks = int(num_host_blocks)
+
+    def _swap(self, cname, seqs):
+        ids = np.ascontiguousarray(list(seqs), dtype=np.int64)
+        cap = 0
+        for q in ids.tolist():          # an upper bound on the distinct blocks of the group
+            cap += self._table_len(q)
+        pairs = np.empty((max(1, cap), 2), dtype=np.int32)
+        n = ctypes.c_int32(0)
+        self._check(cname, getattr(lib(), cname)(
+            self._h, ids.ctypes.data if ids.size else None, ids.size, pairs.ctypes.data, pairs.shape[0],
+            ctypes.addressof(n)))
+        return [(int(a), int(b)) for a, b in pairs[:n.value].tolist()]
+
+    def _table_len(self, seq):
+        n = ctypes.c_int32(0)
+        swapped = lib().pkv_alloc_is_swapped(self._h, int(seq))
+        fn = lib().pkv_alloc_host_table if swapped == 1 else lib().pkv_alloc_block_table
+        code = fn(self._h, int(seq), None, 0, ctypes.addressof(n))
+        if code not in (0, -1):
+            return 0                    # unknown id: the swap call itself reports it
+        return n.value
+
+    def swap_out(self, seqs):
+        """Move the sequences to host blocks; returns the (device, host) block copies."""
+        return self._swap("pkv_alloc_swap_out", seqs)
+
+    def swap_in(self, seqs):
+        """Bring swapped sequences back; returns the (host, device) block copies."""
+        return self._swap("pkv_alloc_swap_in", seqs)
+
+    def is_swapped(self, seq):
+        v = lib().pkv_alloc_is_swapped(self._h, int(seq))
+        if v < 0:
+            self._check("pkv_alloc_is_swapped", int(v))
+        return bool(v)
+
+    def host_table(self, seq):
+        n = ctypes.c_int32(0)
+        code = lib().pkv_alloc_host_table(self._h, int(seq), None, 0, ctypes.addressof(n))
+        if code not in (0, -1):
+            self._check("pkv_alloc_host_table", code)
+        out = np.empty(max(1, n.value), dtype=np.int32)
+        self._check("pkv_alloc_host_table", lib().pkv_alloc_host_table(
+            self._h, int(seq), out.ctypes.data, out.shape[0], ctypes.addressof(n)))
+        return out[:n.value].tolist()
+
+    def num_free_host(self):
+        return int(lib().pkv_alloc_num_free_host(self._h))
+
+    def host_refcount(self, hblock):
+        return int(lib().pkv_alloc_host_refcount(self._h, int(hblock)))

@@ -22,8 +22,17 @@
 // from its last to its first).  Keys are looked up by a 64-bit hash and
 // compared in full (parent key hash, salt, tokens).
 //
+// Preemption by swapping ("vLLM and PagedAttention", §3 continuous batching, on
+// the scheduler's preemption; "How vLLM Works?", section 04): a second pool of
+// host block ids.  A swap-out moves a group of sequences to host blocks and
+// drops their device references; a swap-in gives them new device blocks.  A
+// block held several times inside one group is copied once, so sharing inside
+// the group survives the round trip.  A swapped sequence can only be swapped in
+// or freed.
+//
 // The allocator touches no device memory.  It hands (src, dst) copy pairs back to
-// the caller, who runs them with pkv_copy_blocks before writing the new tokens.
+// the caller, who runs them with pkv_copy_blocks before writing the new tokens
+// (or pkv_swap_blocks between the device pool and the host pool).
 
 #include <algorithm>
 #include <array>
@@ -43,6 +52,7 @@ namespace {
 struct Seq {
   std::vector<int32_t> table;  // logical block index -> physical block id
   int64_t len = 0;             // tokens held
+  bool swapped = false;        // table holds host block ids
   // prefix caching: only for sequences whose token ids are known
   bool tracked = false;
   uint64_t salt = 0;
@@ -94,6 +104,8 @@ struct SplitMix64 {
 
 inline int64_t blocks_for(int64_t tokens, int32_t bs) { return (tokens + bs - 1) / bs; }
 
+inline int swapped_error(const char* msg) { return pkv::fail(PKV_ESWAPPED, msg); }
+
 }  // namespace
 
 struct pkv_allocator {
@@ -110,6 +122,9 @@ struct pkv_allocator {
   std::list<int32_t> released;
   std::vector<std::list<int32_t>::iterator> released_at;
   std::vector<char> is_released;
+  // host pool for swapped sequences: free stack (back() handed out next) and counts
+  std::vector<int32_t> hfree;
+  std::vector<int32_t> href;
 
   // Blocks an allocation can take: free ones and released cached ones.
   int64_t available() const { return (int64_t)free_stack.size() + (int64_t)released.size(); }
@@ -211,6 +226,11 @@ struct pkv_allocator {
   // A released sequence's blocks: uncached ones back to the free list in table
   // order, cached ones to the released list from the last to the first.
   void release(const Seq& s) {
+    if (s.swapped) {
+      for (int32_t h : s.table)
+        if (--href[h] == 0) hfree.push_back(h);
+      return;
+    }
     for (int32_t b : s.table)
       if (--ref[b] == 0 && !cached[b]) free_stack.push_back(b);
     for (auto it = s.table.rbegin(); it != s.table.rend(); ++it) {
@@ -272,6 +292,7 @@ int pkv_alloc_fork(pkv_allocator* a, int64_t parent, int64_t child) {
   auto it = a->seqs.find(parent);
   if (it == a->seqs.end()) return pkv::fail(PKV_ENOSEQ, "pkv_alloc_fork: unknown parent");
   if (a->seqs.count(child)) return pkv::fail(PKV_EINVAL, "pkv_alloc_fork: child exists");
+  if (it->second.swapped) return swapped_error("pkv_alloc_fork: parent is swapped out");
   Seq c = it->second;  // copy before emplace: emplace may rehash
   for (int32_t b : c.table) a->ref[b] += 1;
   a->seqs.emplace(child, std::move(c));
@@ -285,6 +306,7 @@ int pkv_alloc_append(pkv_allocator* a, int64_t seq_id, int32_t n_tokens, int32_t
     return pkv::fail(PKV_EINVAL, "pkv_alloc_append: bad arguments");
   auto it = a->seqs.find(seq_id);
   if (it == a->seqs.end()) return pkv::fail(PKV_ENOSEQ, "pkv_alloc_append: unknown sequence");
+  if (it->second.swapped) return swapped_error("pkv_alloc_append: sequence is swapped out");
   std::unordered_map<int32_t, int32_t> pending;
   int64_t blocks = 0, cows = 0;
   a->need_for(it->second, n_tokens, pending, blocks, cows);
@@ -311,6 +333,7 @@ int pkv_alloc_append_batch(pkv_allocator* a, const int64_t* seq_ids, const int32
       return pkv::fail(PKV_EINVAL, "pkv_alloc_append_batch: duplicate sequence id");
     auto it = a->seqs.find(seq_ids[i]);
     if (it == a->seqs.end()) return pkv::fail(PKV_ENOSEQ, "pkv_alloc_append_batch: unknown sequence");
+    if (it->second.swapped) return swapped_error("pkv_alloc_append_batch: sequence is swapped out");
     if (it->second.len + n_tokens[i] > (int64_t)INT32_MAX)
       return pkv::fail(PKV_EINVAL, "pkv_alloc_append_batch: sequence too long");
     rows[i] = &it->second;
@@ -354,6 +377,7 @@ int pkv_alloc_block_table(const pkv_allocator* a, int64_t seq_id, int32_t* out, 
   if (!a || !len_out) return pkv::fail(PKV_EINVAL, "pkv_alloc_block_table: bad arguments");
   auto it = a->seqs.find(seq_id);
   if (it == a->seqs.end()) return pkv::fail(PKV_ENOSEQ, "pkv_alloc_block_table: unknown sequence");
+  if (it->second.swapped) return swapped_error("pkv_alloc_block_table: sequence is swapped out");
   const auto& t = it->second.table;
   *len_out = (int32_t)t.size();
   if ((int64_t)t.size() > cap || (!t.empty() && !out))
@@ -371,6 +395,7 @@ int pkv_alloc_block_tables(const pkv_allocator* a, const int64_t* seq_ids, int32
   for (int32_t i = 0; i < num_seqs; ++i) {
     auto it = a->seqs.find(seq_ids[i]);
     if (it == a->seqs.end()) return pkv::fail(PKV_ENOSEQ, "pkv_alloc_block_tables: unknown sequence");
+    if (it->second.swapped) return swapped_error("pkv_alloc_block_tables: sequence is swapped out");
     if ((int64_t)it->second.table.size() > max_blocks || it->second.len > INT32_MAX)
       return pkv::fail(PKV_EINVAL, "pkv_alloc_block_tables: table wider than max_blocks");
   }
@@ -448,6 +473,7 @@ int pkv_alloc_append_tokens(pkv_allocator* a, int64_t seq_id, const int32_t* tok
     return pkv::fail(PKV_EINVAL, "pkv_alloc_append_tokens: bad arguments");
   auto it = a->seqs.find(seq_id);
   if (it == a->seqs.end()) return pkv::fail(PKV_ENOSEQ, "pkv_alloc_append_tokens: unknown sequence");
+  if (it->second.swapped) return swapped_error("pkv_alloc_append_tokens: sequence is swapped out");
   if (!it->second.tracked)
     return pkv::fail(PKV_EINVAL, "pkv_alloc_append_tokens: sequence was not made with token ids");
   std::unordered_map<int32_t, int32_t> pending;
@@ -465,6 +491,139 @@ int32_t pkv_alloc_num_blocks(const pkv_allocator* a) { return a ? a->num_blocks 
 int32_t pkv_alloc_refcount(const pkv_allocator* a, int32_t block_id) {
   if (!a || block_id < 0 || block_id >= a->num_blocks) return -1;
   return a->ref[block_id];
+}
+
+int pkv_alloc_set_host_pool(pkv_allocator* a, int32_t num_host_blocks) {
+  if (!a || num_host_blocks < 0) return pkv::fail(PKV_EINVAL, "pkv_alloc_set_host_pool: bad arguments");
+  for (const auto& kv : a->seqs)
+    if (kv.second.swapped) return swapped_error("pkv_alloc_set_host_pool: sequences are swapped out");
+  try {
+    std::vector<int32_t> hfree((size_t)num_host_blocks);
+    for (int32_t i = 0; i < num_host_blocks; ++i) hfree[(size_t)i] = num_host_blocks - 1 - i;
+    a->href.assign((size_t)num_host_blocks, 0);
+    a->hfree.swap(hfree);
+  } catch (...) {
+    return pkv::fail(PKV_ENOMEM, "pkv_alloc_set_host_pool: out of host memory");
+  }
+  return PKV_OK;
+}
+
+namespace {
+
+// Validates a swap group: known, distinct ids, all with swapped == want.
+int swap_group(pkv_allocator* a, const int64_t* ids, int32_t n, bool want, const char* who,
+               std::vector<Seq*>& rows) {
+  std::unordered_set<int64_t> seen;
+  rows.resize((size_t)n);
+  for (int32_t i = 0; i < n; ++i) {
+    if (!seen.insert(ids[i]).second) return pkv::fail(PKV_EINVAL, who);
+    auto it = a->seqs.find(ids[i]);
+    if (it == a->seqs.end()) return pkv::fail(PKV_ENOSEQ, who);
+    if (it->second.swapped != want) return swapped_error(who);
+    rows[(size_t)i] = &it->second;
+  }
+  return PKV_OK;
+}
+
+// Distinct block ids over the group's tables, in order of first appearance.
+std::vector<int32_t> distinct_blocks(const std::vector<Seq*>& rows) {
+  std::vector<int32_t> out;
+  std::unordered_set<int32_t> seen;
+  for (const Seq* s : rows)
+    for (int32_t b : s->table)
+      if (seen.insert(b).second) out.push_back(b);
+  return out;
+}
+
+}  // namespace
+
+int pkv_alloc_swap_out(pkv_allocator* a, const int64_t* seq_ids, int32_t num_seqs, int32_t* pairs_out,
+                       int32_t pairs_cap, int32_t* num_pairs_out) {
+  if (!a || num_seqs < 0 || (num_seqs > 0 && !seq_ids) || !num_pairs_out || pairs_cap < 0)
+    return pkv::fail(PKV_EINVAL, "pkv_alloc_swap_out: bad arguments");
+  std::vector<Seq*> rows;
+  const int rc = swap_group(a, seq_ids, num_seqs, false, "pkv_alloc_swap_out: bad sequence in the group", rows);
+  if (rc != PKV_OK) return rc;
+  const std::vector<int32_t> blocks = distinct_blocks(rows);
+  if ((int64_t)blocks.size() > pairs_cap || (!blocks.empty() && !pairs_out))
+    return pkv::fail(PKV_EINVAL, "pkv_alloc_swap_out: pairs_out too small");
+  if (blocks.size() > a->hfree.size()) return pkv::fail(PKV_ENOMEM, "pkv_alloc_swap_out: host pool exhausted");
+  std::unordered_map<int32_t, int32_t> to_host;
+  for (size_t i = 0; i < blocks.size(); ++i) {
+    const int32_t h = a->hfree.back();
+    a->hfree.pop_back();
+    to_host[blocks[i]] = h;
+    pairs_out[2 * i] = blocks[i];
+    pairs_out[2 * i + 1] = h;
+  }
+  for (Seq* s : rows) {
+    a->release(*s);  // device references of the group dropped
+    for (int32_t& b : s->table) {
+      b = to_host[b];
+      a->href[b] += 1;
+    }
+    s->swapped = true;
+  }
+  *num_pairs_out = (int32_t)blocks.size();
+  return PKV_OK;
+}
+
+int pkv_alloc_swap_in(pkv_allocator* a, const int64_t* seq_ids, int32_t num_seqs, int32_t* pairs_out,
+                      int32_t pairs_cap, int32_t* num_pairs_out) {
+  if (!a || num_seqs < 0 || (num_seqs > 0 && !seq_ids) || !num_pairs_out || pairs_cap < 0)
+    return pkv::fail(PKV_EINVAL, "pkv_alloc_swap_in: bad arguments");
+  std::vector<Seq*> rows;
+  const int rc = swap_group(a, seq_ids, num_seqs, true, "pkv_alloc_swap_in: bad sequence in the group", rows);
+  if (rc != PKV_OK) return rc;
+  const std::vector<int32_t> hblocks = distinct_blocks(rows);
+  if ((int64_t)hblocks.size() > pairs_cap || (!hblocks.empty() && !pairs_out))
+    return pkv::fail(PKV_EINVAL, "pkv_alloc_swap_in: pairs_out too small");
+  if ((int64_t)hblocks.size() > a->available())
+    return pkv::fail(PKV_ENOMEM, "pkv_alloc_swap_in: block pool exhausted");
+  std::unordered_map<int32_t, int32_t> to_dev;
+  for (size_t i = 0; i < hblocks.size(); ++i) {
+    const int32_t b = a->take();
+    to_dev[hblocks[i]] = b;
+    pairs_out[2 * i] = hblocks[i];
+    pairs_out[2 * i + 1] = b;
+  }
+  for (Seq* s : rows) {
+    a->release(*s);  // host references dropped (s is still marked swapped)
+    for (int32_t& h : s->table) {
+      h = to_dev[h];
+      a->ref[h] += 1;
+    }
+    s->swapped = false;
+  }
+  *num_pairs_out = (int32_t)hblocks.size();
+  return PKV_OK;
+}
+
+int pkv_alloc_is_swapped(const pkv_allocator* a, int64_t seq_id) {
+  if (!a) return pkv::fail(PKV_EINVAL, "pkv_alloc_is_swapped: null allocator");
+  auto it = a->seqs.find(seq_id);
+  if (it == a->seqs.end()) return pkv::fail(PKV_ENOSEQ, "pkv_alloc_is_swapped: unknown sequence");
+  return it->second.swapped ? 1 : 0;
+}
+
+int pkv_alloc_host_table(const pkv_allocator* a, int64_t seq_id, int32_t* out, int32_t cap, int32_t* len_out) {
+  if (!a || !len_out) return pkv::fail(PKV_EINVAL, "pkv_alloc_host_table: bad arguments");
+  auto it = a->seqs.find(seq_id);
+  if (it == a->seqs.end()) return pkv::fail(PKV_ENOSEQ, "pkv_alloc_host_table: unknown sequence");
+  if (!it->second.swapped) return swapped_error("pkv_alloc_host_table: sequence is not swapped out");
+  const auto& t = it->second.table;
+  *len_out = (int32_t)t.size();
+  if ((int64_t)t.size() > cap || (!t.empty() && !out))
+    return pkv::fail(PKV_EINVAL, "pkv_alloc_host_table: output too small");
+  if (!t.empty()) std::memcpy(out, t.data(), t.size() * sizeof(int32_t));
+  return PKV_OK;
+}
+
+int32_t pkv_alloc_num_free_host(const pkv_allocator* a) { return a ? (int32_t)a->hfree.size() : PKV_EINVAL; }
+
+int32_t pkv_alloc_host_refcount(const pkv_allocator* a, int32_t host_block) {
+  if (!a || host_block < 0 || host_block >= (int32_t)a->href.size()) return -1;
+  return a->href[(size_t)host_block];
 }
 
 }  // extern "C"

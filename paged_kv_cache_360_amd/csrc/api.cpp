@@ -72,6 +72,32 @@ int32_t device_cus() {
 }
 
 
+// Device address of a buffer of `bytes` bytes at p: device memory as is,
+// page-locked host memory through its device mapping.  False for pageable or
+// unknown memory, or when the first and last byte do not lie in one mapping.
+bool device_span(const void* p, int64_t bytes, void** dev_out) {
+  if (!p || bytes <= 0) return false;
+  hipPointerAttribute_t a0{}, a1{};
+  const char* last = static_cast<const char*>(p) + (bytes - 1);
+  if (hipPointerGetAttributes(&a0, p) != hipSuccess) { (void)hipGetLastError(); return false; }
+  if (hipPointerGetAttributes(&a1, last) != hipSuccess) { (void)hipGetLastError(); return false; }
+  if (a0.type != a1.type || !a0.devicePointer || !a1.devicePointer) return false;
+  if (a0.type != hipMemoryTypeDevice && a0.type != hipMemoryTypeHost) return false;
+  const char* d0 = static_cast<const char*>(a0.devicePointer);
+  const char* d1 = static_cast<const char*>(a1.devicePointer);
+  if (d1 - d0 != bytes - 1) return false;
+  *dev_out = a0.devicePointer;
+  return true;
+}
+
+// A small table the kernel reads (pairs): device memory only.
+bool device_readable(const void* p, int64_t bytes) {
+  void* d = nullptr;
+  if (!device_span(p, bytes, &d)) return false;
+  hipPointerAttribute_t a{};
+  return hipPointerGetAttributes(&a, p) == hipSuccess && a.type == hipMemoryTypeDevice && d == p;
+}
+
 int launched(int hip_status, const char* who) {
   if (hip_status == 0) return PKV_OK;
   char buf[256];
@@ -104,6 +130,7 @@ const char* pkv_strerror(int code) {
     case PKV_ELAUNCH: return "PKV_ELAUNCH";
     case PKV_ENOSEQ: return "PKV_ENOSEQ";
     case PKV_EWORKSPACE: return "PKV_EWORKSPACE";
+    case PKV_ESWAPPED: return "PKV_ESWAPPED";
     default: return "PKV_UNKNOWN";
   }
 }
@@ -401,6 +428,48 @@ int pkv_copy_blocks(void* key_cache, void* value_cache, const int32_t* pairs,
   return pkv::launched(pkv::launch_copy_blocks(key_cache, value_cache, pairs, num_pairs, num_blocks,
                                                block_bytes, stream),
                        "pkv_copy_blocks");
+}
+
+int pkv_swap_blocks(void* dst_key_cache, void* dst_value_cache, const void* src_key_cache,
+                    const void* src_value_cache, const int32_t* pairs, int32_t num_pairs,
+                    int32_t src_num_blocks, int32_t dst_num_blocks, int32_t block_size,
+                    int32_t num_kv_heads, int32_t head_dim, pkv_dtype dt, void* stream) {
+  if (!pkv::dtype_ok(dt)) return fail(PKV_EUNSUPPORTED, "pkv_swap_blocks: unsupported dtype");
+  if (block_size != PKV_BLOCK_SIZE)
+    return fail(PKV_EUNSUPPORTED, "pkv_swap_blocks: block_size must be 16");
+  if (num_pairs < 0 || src_num_blocks <= 0 || dst_num_blocks <= 0 || num_kv_heads <= 0 || head_dim <= 0)
+    return fail(PKV_EINVAL, "pkv_swap_blocks: bad sizes");
+  const int64_t block_bytes = (int64_t)block_size * num_kv_heads * head_dim * pkv::elem_size(dt);
+  if (block_bytes % 16 != 0)
+    return fail(PKV_EUNSUPPORTED, "pkv_swap_blocks: block bytes must be a multiple of 16");
+  if (num_pairs == 0) return PKV_OK;
+  if (!dst_key_cache || !dst_value_cache || !src_key_cache || !src_value_cache || !pairs)
+    return fail(PKV_EINVAL, "pkv_swap_blocks: null pointer");
+  if (num_pairs > 2147483647 / 2 || num_pairs > 65535 * 1024)
+    return fail(PKV_EINVAL, "pkv_swap_blocks: too many pairs");
+  void* dk = nullptr; void* dv = nullptr; void* sk = nullptr; void* sv = nullptr;
+  const int64_t dst_bytes = (int64_t)dst_num_blocks * block_bytes;
+  const int64_t src_bytes = (int64_t)src_num_blocks * block_bytes;
+  if (!pkv::device_span(dst_key_cache, dst_bytes, &dk) || !pkv::device_span(dst_value_cache, dst_bytes, &dv) ||
+      !pkv::device_span(src_key_cache, src_bytes, &sk) || !pkv::device_span(src_value_cache, src_bytes, &sv))
+    return fail(PKV_EINVAL,
+                "pkv_swap_blocks: each pool must be device memory or page-locked host memory mapped for "
+                "the device, covering num_blocks blocks");
+  if (!pkv::device_readable(pairs, (int64_t)num_pairs * 2 * sizeof(int32_t)))
+    return fail(PKV_EINVAL, "pkv_swap_blocks: pairs must be device memory");
+  if (!pkv::aligned16(dk) || !pkv::aligned16(dv) || !pkv::aligned16(sk) || !pkv::aligned16(sv))
+    return fail(PKV_EINVAL, "pkv_swap_blocks: pools must be 16-byte aligned");
+  return pkv::launched(pkv::launch_swap_blocks(dk, dv, sk, sv, pairs, num_pairs, src_num_blocks,
+                                               dst_num_blocks, block_bytes, stream),
+                       "pkv_swap_blocks");
+}
+
+int pkv_check_pool(const void* pool, size_t bytes) {
+  void* d = nullptr;
+  if (!pool || bytes == 0 || bytes > (size_t)INT64_MAX) return fail(PKV_EINVAL, "pkv_check_pool: bad arguments");
+  if (!pkv::device_span(pool, (int64_t)bytes, &d))
+    return fail(PKV_EINVAL, "pkv_check_pool: not device memory or mapped page-locked host memory of that size");
+  return PKV_OK;
 }
 
 int pkv_check_tables(const int32_t* host_block_tables, const int32_t* host_context_lens,

@@ -1,5 +1,6 @@
-// Cache writes on gfx950: the slot scatter of new tokens' K/V rows and the
-// copy-on-write block copy.  Both are byte copies in 16-byte vectors; a token row
+// Cache writes on gfx950: the slot scatter of new tokens' K/V rows, the
+// copy-on-write block copy and the block copy between two pools (swapping
+// between the device pool and a page-locked host pool).  Both are byte copies in 16-byte vectors; a token row
 // (num_kv_heads * head_dim elements) and a block (16 rows) are contiguous in the
 // [num_blocks, 16, num_kv_heads, head_dim] layout, so each workgroup streams one
 // contiguous span with fully coalesced dwordx4 loads and stores.
@@ -48,6 +49,38 @@ __global__ __launch_bounds__(kCopyThreads) void copy_blocks_kernel(
   }
 }
 
+// Loads in flight per thread in the pool-to-pool copy: a read across the host
+// link takes microseconds, so each thread issues a whole batch before storing.
+constexpr int kSwapBatch = 8;
+
+// One workgroup per (pair, cache): block dst of the destination pool := block
+// src of the source pool.  Either pool may be page-locked host memory reached
+// through its device mapping.
+__global__ __launch_bounds__(kCopyThreads) void swap_blocks_kernel(
+    char* __restrict__ dk, char* __restrict__ dv, const char* __restrict__ sk,
+    const char* __restrict__ sv, const int32_t* __restrict__ pairs, int32_t src_blocks,
+    int32_t dst_blocks, int64_t block_bytes) {
+  const int32_t src = pairs[2 * blockIdx.x];
+  const int32_t dst = pairs[2 * blockIdx.x + 1];
+  if (src < 0 || src >= src_blocks || dst < 0 || dst >= dst_blocks) return;
+  const char* s = (blockIdx.y == 0 ? sk : sv) + (int64_t)src * block_bytes;
+  char* d = (blockIdx.y == 0 ? dk : dv) + (int64_t)dst * block_bytes;
+  constexpr int64_t kStride = (int64_t)kCopyThreads * 16;
+  for (int64_t base = threadIdx.x * 16; base < block_bytes; base += kStride * kSwapBatch) {
+    uint4 r[kSwapBatch];
+#pragma unroll
+    for (int u = 0; u < kSwapBatch; ++u) {
+      const int64_t off = base + u * kStride;
+      if (off < block_bytes) r[u] = load16(s + off);
+    }
+#pragma unroll
+    for (int u = 0; u < kSwapBatch; ++u) {
+      const int64_t off = base + u * kStride;
+      if (off < block_bytes) *reinterpret_cast<uint4*>(d + off) = r[u];
+    }
+  }
+}
+
 }  // namespace
 
 int launch_kv_write(void* kc, void* vc, const void* k, const void* v, const int32_t* slots,
@@ -62,6 +95,15 @@ int launch_copy_blocks(void* kc, void* vc, const int32_t* pairs, int32_t num_pai
                        int32_t num_blocks, int64_t block_bytes, void* stream) {
   hipLaunchKernelGGL(copy_blocks_kernel, dim3(num_pairs, 2), dim3(kCopyThreads), 0,
                      (hipStream_t)stream, (char*)kc, (char*)vc, pairs, num_blocks, block_bytes);
+  return (int)hipGetLastError();
+}
+
+int launch_swap_blocks(void* dk, void* dv, const void* sk, const void* sv, const int32_t* pairs,
+                       int32_t num_pairs, int32_t src_blocks, int32_t dst_blocks, int64_t block_bytes,
+                       void* stream) {
+  hipLaunchKernelGGL(swap_blocks_kernel, dim3(num_pairs, 2), dim3(kCopyThreads), 0,
+                     (hipStream_t)stream, (char*)dk, (char*)dv, (const char*)sk, (const char*)sv, pairs,
+                     src_blocks, dst_blocks, block_bytes);
   return (int)hipGetLastError();
 }
 

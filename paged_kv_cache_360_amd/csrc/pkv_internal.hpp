@@ -24,6 +24,12 @@ int launch_kv_write(void* kc, void* vc, const void* k, const void* v, const int3
 int launch_copy_blocks(void* kc, void* vc, const int32_t* pairs, int32_t num_pairs,
                        int32_t num_blocks, int64_t block_bytes, void* stream);
 
+// Pool-to-pool block copy; the pool pointers are device addresses (a host pool's
+// device mapping).
+int launch_swap_blocks(void* dk, void* dv, const void* sk, const void* sv, const int32_t* pairs,
+                       int32_t num_pairs, int32_t src_blocks, int32_t dst_blocks, int64_t block_bytes,
+                       void* stream);
+
 struct DecodeArgs {
   void* out;             // [T, Hq, D]
   const void* q;         // [T, Hq, D]

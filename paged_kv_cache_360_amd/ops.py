@@ -228,6 +228,38 @@ def pkv_copy_blocks(key_cache, value_cache, pairs, stream=None):
         n, nb, bs, hkv, d, _dt(key_cache), _stream(stream)))
 
 
+def _pool_ptr(t, name):
+    """Address of a pool: a device tensor, or a page-locked host tensor (the
+    library maps it for the device and rejects anything else)."""
+    if not isinstance(t, torch.Tensor) or not (t.is_cuda or t.is_pinned()):
+        raise TypeError(f"{name} must be a device tensor or a pinned host tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def pkv_swap_blocks(dst_key_cache, dst_value_cache, src_key_cache, src_value_cache, pairs, stream=None):
+    """Block copies between two pools (device and pinned host, either way round);
+    ``pairs`` is a device int32 [n, 2] of (src block, dst block)."""
+    snb, bs, hkv, d = src_key_cache.shape
+    dnb = dst_key_cache.shape[0]
+    for name, t, nb in (("dst_key_cache", dst_key_cache, dnb), ("dst_value_cache", dst_value_cache, dnb),
+                        ("src_value_cache", src_value_cache, snb)):
+        if tuple(t.shape) != (nb, bs, hkv, d):
+            raise ValueError(f"{name} must be [{nb}, {bs}, {hkv}, {d}]")
+        if t.dtype != src_key_cache.dtype:
+            raise TypeError("all four pools must share one dtype")
+    n = pairs.shape[0] if pairs.numel() else 0
+    if n and tuple(pairs.shape) != (n, 2):
+        raise ValueError("pairs must be [n, 2]")
+    if n == 0:
+        return
+    check("pkv_swap_blocks", lib().pkv_swap_blocks(
+        _pool_ptr(dst_key_cache, "dst_key_cache"), _pool_ptr(dst_value_cache, "dst_value_cache"),
+        _pool_ptr(src_key_cache, "src_key_cache"), _pool_ptr(src_value_cache, "src_value_cache"),
+        _dev(pairs, "pairs", torch.int32), n, snb, dnb, bs, hkv, d, _dt(src_key_cache), _stream(stream)))
+
+
 def pkv_check_tables(block_tables, context_lens, num_blocks):
     """Host-side table validation (numpy int32 arrays).  Raises PagedKVError on a bad entry."""
     import numpy as np
