@@ -71,6 +71,9 @@ def parse_args():
                     help="only time pkv_swap_blocks between the device pool and a pinned host pool "
                          "(8192 scattered 32 KiB blocks per cache each way) against one contiguous "
                          "copy of the same bytes")
+    ap.add_argument("--graph-probe", action="store_true",
+                    help="only time one decode step replayed as a HIP graph against the same launches "
+                         "made one by one (4-sequence fp32 MHA batch and the default GQA batch)")
     ap.add_argument("--json-out", default=None)
     ap.add_argument("--traffic-from", nargs=4, metavar="CSV", default=None,
                     help="rocprofv3 counter_collection CSVs: FETCH_SIZE and WRITE_SIZE of a "
@@ -200,6 +203,96 @@ def swap_probe(torch, pkv, seed):
     print(json.dumps(line))
 
 
+def graph_probe(torch, np, pkv, seed):
+    """One decode step (write + plan + partitions + merge; the append form for
+    bf16) made with direct C-ABI calls, one launch at a time, against the same
+    step replayed as a HIP graph (``pkv_decode_graph_launch``).  Inputs are
+    resident and unchanged between steps, so the difference is launch cost."""
+    import ctypes
+
+    from paged_kv_cache_360_amd._lib import lib
+    from workloads import SPECS, draw_context_lens
+
+    L = lib()
+    rng = np.random.default_rng(seed)
+    lines = []
+    for name, steps in (("tiny_f32_mha_s4_h8_d64", 400), (DEFAULT_WORKLOAD, 60)):
+        spec = SPECS[name]
+        S, Hq, Hkv, D = spec.num_seqs, spec.num_q_heads, spec.num_kv_heads, spec.head_dim
+        bf16 = spec.dtype == "bf16"
+        tdt = torch.bfloat16 if bf16 else torch.float32
+        ctx = np.asarray(draw_context_lens(rng, spec), np.int64)
+        nblk = -(-ctx // 16)
+        nb = int(math.ceil(1.25 * nblk.sum())) if bf16 else 64
+        mb = int(nblk.max())
+        perm = rng.permutation(nb).astype(np.int32)
+        tables = np.zeros((S, mb), np.int32)
+        off = 0
+        for i in range(S):
+            tables[i, :nblk[i]] = perm[off:off + nblk[i]]
+            off += int(nblk[i])
+        slots = np.array([tables[i, (ctx[i] - 1) // 16] * 16 + (ctx[i] - 1) % 16 for i in range(S)], np.int32)
+        kc = torch.randn((nb, 16, Hkv, D), device="cuda").to(tdt)
+        vc = torch.randn((nb, 16, Hkv, D), device="cuda").to(tdt)
+        q = torch.randn((S, Hq, D), device="cuda").to(tdt)
+        kn = torch.randn((S, Hkv, D), device="cuda").to(tdt)
+        vn = torch.randn((S, Hkv, D), device="cuda").to(tdt)
+        out = torch.empty_like(q)
+        t_d = torch.from_numpy(tables).cuda()
+        c_d = torch.from_numpy(ctx.astype(np.int32)).cuda()
+        s_d = torch.from_numpy(slots).cuda()
+        max_ctx = int(ctx.max())
+        ws = pkv.decode_workspace(S, Hq, D, max_ctx)
+        ws_p, ws_n = (ws.data_ptr(), ws.numel()) if ws is not None else (0, 0)
+        scale = 1.0 / math.sqrt(D)
+        dt = 1 if bf16 else 0
+        stream = torch.cuda.current_stream().cuda_stream
+        p = lambda t: t.data_ptr()
+        if bf16:
+            a_app = (p(out), p(q), p(kn), p(vn), p(kc), p(vc), p(t_d), p(c_d), ctypes.c_float(scale), 16, Hq, Hkv,
+                     D, S, mb, nb, max_ctx, dt, ws_p, ws_n, stream)
+
+            def eager():
+                L.pkv_attention_decode_append(*a_app)
+        else:
+            a_w = (p(kc), p(vc), p(kn), p(vn), p(s_d), S, nb, 16, Hkv, D, dt, stream)
+            a_d = (p(out), p(q), p(kc), p(vc), p(t_d), p(c_d), ctypes.c_float(scale), 16, Hq, Hkv, D, S, mb, nb,
+                   max_ctx, dt, ws_p, ws_n, stream)
+
+            def eager():
+                L.pkv_write(*a_w)
+                L.pkv_attention_decode(*a_d)
+        g = pkv.DecodeGraph(out, q, kn, vn, kc, vc, t_d, c_d, scale, max_ctx,
+                            slot_mapping=None if bf16 else s_d, workspace=ws)
+
+        def run(fn):
+            """(device µs per step between events, host µs per step to issue)."""
+            for _ in range(20):
+                fn()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            t0 = time.perf_counter()
+            for _ in range(steps):
+                fn()
+            t1 = time.perf_counter()
+            e1.record()
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) * 1e3 / steps, (t1 - t0) * 1e6 / steps
+
+        us_e, host_e = run(eager)
+        us_g, host_g = run(lambda: L.pkv_decode_graph_launch(g._h, stream))
+        g.close()
+        parts = -(-max_ctx // 512)
+        lines.append({"workload": name, "steps": steps,
+                      "kernels_per_step": (2 if bf16 else 3) + (1 if parts > 1 else 0),
+                      "eager_us_per_step": round(us_e, 2), "graph_us_per_step": round(us_g, 2),
+                      "eager_host_issue_us_per_step": round(host_e, 2),
+                      "graph_host_issue_us_per_step": round(host_g, 2),
+                      "speedup": round(us_e / us_g, 3)})
+    print(json.dumps({"probe": "decode_graph", "results": lines}))
+
+
 def prefix_cache_probe(np, pkv, seed):
     """Host allocator with automatic prefix caching: requests made of a shared
     1500-token system prompt and a user part of 8..512 tokens (the shared-prefix
@@ -276,6 +369,9 @@ def main():
         return
     if args.swap_probe:
         swap_probe(torch, pkv, args.seed)
+        return
+    if args.graph_probe:
+        graph_probe(torch, np, pkv, args.seed)
         return
 
     spec = SPECS[args.workload]
@@ -715,28 +811,32 @@ def mixed_main(args, spec):
 
 
 def cpu_baseline(np, spec, q_last, pool_k, pool_v, alloc, ids, MB, scale, budget_s):
-    """The fp64 oracle on the host, sequence by sequence, for about ``budget_s`` seconds."""
+    """The fp64 oracle on the host, sequence by sequence, for about ``budget_s``
+    seconds: passes over the last timed step's batch, repeated until the time is
+    spent (the last pass may stop part way)."""
     import oracle
     from threadpoolctl import threadpool_limits
 
     tables, lens = alloc.block_tables(ids, MB)
-    done, t0 = 0, time.perf_counter()
+    n = len(ids)
+    done, kv_tokens, t0 = 0, 0, time.perf_counter()
     with threadpool_limits(limits=1):
-        for s in range(len(ids)):
+        while True:
+            s = done % n
             oracle.decode_attention(q_last[s:s + 1], pool_k, pool_v, tables[s:s + 1], lens[s:s + 1], scale)
             done += 1
+            kv_tokens += int(lens[s])
             if time.perf_counter() - t0 >= budget_s:
                 break
     el = time.perf_counter() - t0
-    kv = int(lens[:done].astype(np.int64).sum()) * 2 * spec.num_kv_heads * spec.head_dim * (
-        2 if spec.dtype == "bf16" else 4)
+    kv = kv_tokens * 2 * spec.num_kv_heads * spec.head_dim * (2 if spec.dtype == "bf16" else 4)
     return {
         "value": round(done / el, 3),
         "unit": "tokens/s",
         "cores": 1,
         "kind": "oracle",
-        "sample": f"first {done} of {len(ids)} sequences of the last timed step's batch "
-                  f"(mean context {float(lens[:done].mean()):.0f}), fp64 NumPy, 1 BLAS thread, "
+        "sample": f"{done} sequence decodes ({done / n:.2f} passes over the {n} sequences of the last timed "
+                  f"step's batch, mean context {float(lens.mean()):.0f}), fp64 NumPy, 1 BLAS thread, "
                   f"{el:.1f} s; host {os.cpu_count()} logical CPUs",
         "kv_GBps": round(kv / el / 1e9, 4),
     }

@@ -292,6 +292,40 @@ int pkv_swap_blocks(void* dst_key_cache, void* dst_value_cache, const void* src_
                     int32_t num_kv_heads, int32_t head_dim, pkv_dtype dt, void* stream);
 
 /* ------------------------------------------------------------------------ */
+/* One decode step as a HIP graph ("vLLM and PagedAttention", §6 version
+ * evolution, key engineering optimizations: a generation step's kernel
+ * sequence is recorded into a graph and launched as one instead of one launch
+ * per kernel).  pkv_decode_graph_create records the launches of one step on a
+ * private stream of the current device and instantiates them:
+ *
+ *   slot_mapping != NULL: pkv_write(k_new, v_new, slot_mapping, num_new_tokens)
+ *                         (skipped when num_new_tokens == 0), then
+ *                         pkv_attention_decode (plan, partitions, merge);
+ *   slot_mapping == NULL: pkv_attention_decode_append (bf16 only; k_new, v_new
+ *                         are [num_seqs, Hkv, D], one new row per sequence).
+ *
+ * Every pointer and every size is fixed into the graph; device data (q, the new
+ * K/V rows, slots, tables, context lengths) is read when the graph runs, so the
+ * caller updates those buffers in place between launches (on the stream it
+ * launches on, or with the ordering it needs).  max_context_len is the bound the
+ * graph was made for: every later context must stay at or below it.  The
+ * workspace is the graph's own: two graphs (or a graph and a direct call) that
+ * run at the same time need separate workspaces.  Argument errors as for the
+ * captured calls; nothing runs at creation.  pkv_decode_graph_launch enqueues the
+ * whole step with one call on stream (NULL = the default stream).
+ * No node of the graph is a memset (the plan kernel clears its own counters). */
+typedef struct pkv_graph pkv_graph;
+int pkv_decode_graph_create(pkv_graph** graph_out, void* out, const void* q, const void* k_new,
+                            const void* v_new, const int32_t* slot_mapping, int32_t num_new_tokens,
+                            void* key_cache, void* value_cache, const int32_t* block_tables,
+                            const int32_t* context_lens, float scale, int32_t block_size,
+                            int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t num_seqs,
+                            int32_t max_blocks_per_seq, int32_t num_blocks, int32_t max_context_len,
+                            pkv_dtype dt, void* workspace, size_t workspace_bytes);
+int pkv_decode_graph_launch(pkv_graph* graph, void* stream);
+void pkv_decode_graph_destroy(pkv_graph* graph);
+
+/* ------------------------------------------------------------------------ */
 /* Host-side debug checks (no device access).
  * pkv_check_tables: every entry a sequence uses (the first ceil(context_lens[s]/16)
  * of its row) lies in [0, num_blocks), and context_lens are in [0, max_blocks*16].

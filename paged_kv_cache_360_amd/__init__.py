@@ -27,6 +27,7 @@ from .ops import (  # noqa: F401
     pkv_lse_merge,
     pkv_copy_blocks,
     pkv_swap_blocks,
+    DecodeGraph,
     pkv_check_tables,
     pkv_check_slots,
 )

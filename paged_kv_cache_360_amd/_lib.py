@@ -55,6 +55,10 @@ SIGNATURES = {
     "pkv_copy_blocks": (ctypes.c_int, [_p, _p, _p, _i32, _i32, _i32, _i32, _i32, ctypes.c_int, _p]),
     "pkv_swap_blocks": (ctypes.c_int, [_p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32, ctypes.c_int,
                                        _p]),
+    "pkv_decode_graph_create": (ctypes.c_int, [_p, _p, _p, _p, _p, _p, _i32, _p, _p, _p, _p, _f32, _i32, _i32,
+                                               _i32, _i32, _i32, _i32, _i32, _i32, ctypes.c_int, _p, _sz]),
+    "pkv_decode_graph_launch": (ctypes.c_int, [_p, _p]),
+    "pkv_decode_graph_destroy": (None, [_p]),
     "pkv_check_tables": (ctypes.c_int, [_p, _p, _i32, _i32, _i32]),
     "pkv_check_slots": (ctypes.c_int, [_p, _i32, _i32, _i32]),
     "pkv_check_pool": (ctypes.c_int, [_p, _sz]),

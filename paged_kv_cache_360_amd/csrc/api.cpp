@@ -11,6 +11,7 @@
 #include <cstdio>
 #include <cstdint>
 #include <cstring>
+#include <new>
 #include <vector>
 
 #include "../../include/pagedkv.h"
@@ -506,6 +507,100 @@ int pkv_check_slots(const int32_t* host_slot_mapping, int32_t num_tokens, int32_
     seen[(size_t)s] = 1;
   }
   return PKV_OK;
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// One decode step captured into a HIP graph: the launches of pkv_write +
+// pkv_attention_decode (or of pkv_attention_decode_append) recorded once on a
+// private stream and replayed with one hipGraphLaunch.
+
+struct pkv_graph {
+  hipGraph_t graph = nullptr;
+  hipGraphExec_t exec = nullptr;
+};
+
+extern "C" {
+
+int pkv_decode_graph_create(pkv_graph** graph_out, void* out, const void* q, const void* k_new,
+                            const void* v_new, const int32_t* slot_mapping, int32_t num_new_tokens,
+                            void* key_cache, void* value_cache, const int32_t* block_tables,
+                            const int32_t* context_lens, float scale, int32_t block_size,
+                            int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t num_seqs,
+                            int32_t max_blocks_per_seq, int32_t num_blocks, int32_t max_context_len,
+                            pkv_dtype dt, void* workspace, size_t workspace_bytes) {
+  const char* who = "pkv_decode_graph_create";
+  if (!graph_out) return fail(PKV_EINVAL, "pkv_decode_graph_create: null graph_out");
+  *graph_out = nullptr;
+  if (num_seqs <= 0) return fail(PKV_EINVAL, "pkv_decode_graph_create: num_seqs must be > 0");
+  const bool append_form = slot_mapping == nullptr;
+  if (append_form && dt != PKV_BF16)
+    return fail(PKV_EUNSUPPORTED, "pkv_decode_graph_create: the append form (no slot_mapping) is bf16 only");
+  if (!append_form && num_new_tokens < 0) return fail(PKV_EINVAL, "pkv_decode_graph_create: bad num_new_tokens");
+  // Validate everything with a dry run of the same checks the launches make.
+  {
+    pkv::DecodeArgs a{};
+    const int rc = prepare_attention(who, a, out, q, key_cache, value_cache, block_tables, context_lens,
+                                     nullptr, num_seqs, 1, scale, block_size, num_q_heads, num_kv_heads,
+                                     head_dim, num_seqs, max_blocks_per_seq, num_blocks, max_context_len, dt,
+                                     workspace, workspace_bytes);
+    if (rc != PKV_OK) return rc;
+    if (append_form && (!k_new || !v_new || !pkv::aligned16(k_new) || !pkv::aligned16(v_new)))
+      return fail(PKV_EINVAL, "pkv_decode_graph_create: k_new / v_new null or misaligned");
+  }
+  pkv_graph* g = new (std::nothrow) pkv_graph();
+  if (!g) return fail(PKV_ENOMEM, "pkv_decode_graph_create: out of host memory");
+  hipStream_t s = nullptr;
+  if (hipStreamCreateWithFlags(&s, hipStreamNonBlocking) != hipSuccess) {
+    delete g;
+    return fail(PKV_ELAUNCH, "pkv_decode_graph_create: hipStreamCreateWithFlags failed");
+  }
+  int rc = PKV_OK;
+  if (hipStreamBeginCapture(s, hipStreamCaptureModeThreadLocal) != hipSuccess) {
+    rc = fail(PKV_ELAUNCH, "pkv_decode_graph_create: hipStreamBeginCapture failed");
+  } else {
+    if (append_form) {
+      rc = pkv_attention_decode_append(out, q, k_new, v_new, key_cache, value_cache, block_tables, context_lens,
+                                       scale, block_size, num_q_heads, num_kv_heads, head_dim, num_seqs,
+                                       max_blocks_per_seq, num_blocks, max_context_len, dt, workspace,
+                                       workspace_bytes, s);
+    } else {
+      if (num_new_tokens > 0)
+        rc = pkv_write(key_cache, value_cache, k_new, v_new, slot_mapping, num_new_tokens, num_blocks,
+                       block_size, num_kv_heads, head_dim, dt, s);
+      if (rc == PKV_OK)
+        rc = pkv_attention_decode(out, q, key_cache, value_cache, block_tables, context_lens, scale, block_size,
+                                  num_q_heads, num_kv_heads, head_dim, num_seqs, max_blocks_per_seq, num_blocks,
+                                  max_context_len, dt, workspace, workspace_bytes, s);
+    }
+    const hipError_t end = hipStreamEndCapture(s, &g->graph);
+    if (rc == PKV_OK && end != hipSuccess)
+      rc = fail(PKV_ELAUNCH, "pkv_decode_graph_create: hipStreamEndCapture failed");
+  }
+  if (rc == PKV_OK && hipGraphInstantiateWithFlags(&g->exec, g->graph, 0) != hipSuccess)
+    rc = fail(PKV_ELAUNCH, "pkv_decode_graph_create: hipGraphInstantiate failed");
+  (void)hipStreamDestroy(s);
+  if (rc != PKV_OK) {
+    pkv_decode_graph_destroy(g);
+    return rc;
+  }
+  *graph_out = g;
+  return PKV_OK;
+}
+
+int pkv_decode_graph_launch(pkv_graph* g, void* stream) {
+  if (!g || !g->exec) return fail(PKV_EINVAL, "pkv_decode_graph_launch: null graph");
+  const hipError_t e = hipGraphLaunch(g->exec, (hipStream_t)stream);
+  if (e != hipSuccess) return pkv::launched((int)e, "pkv_decode_graph_launch");
+  return PKV_OK;
+}
+
+void pkv_decode_graph_destroy(pkv_graph* g) {
+  if (!g) return;
+  if (g->exec) (void)hipGraphExecDestroy(g->exec);
+  if (g->graph) (void)hipGraphDestroy(g->graph);
+  delete g;
 }
 
 }  // extern "C"

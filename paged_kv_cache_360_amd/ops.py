@@ -158,6 +158,70 @@ def pkv_attention_decode_partitions_append(out, q, k_new, v_new, key_cache, valu
                         value_cache, block_tables, context_lens, scale, max_context_len, workspace, stream)
 
 
+class DecodeGraph:
+    """One decode step as a HIP graph (``pkv_decode_graph_create`` / ``_launch`` /
+    ``_destroy``).
+
+    With ``slot_mapping`` the step is ``pkv_write(k_new, v_new, slot_mapping)`` +
+    ``pkv_attention_decode``; without it, the bf16 append form (``k_new``/``v_new``
+    are [S, Hkv, D], one new row per sequence).  Every tensor's address is fixed
+    into the graph, so this object keeps them alive: update their contents in
+    place between launches.  ``max_context_len`` bounds every later context.
+    """
+
+    def __init__(self, out, q, k_new, v_new, key_cache, value_cache, block_tables, context_lens, scale,
+                 max_context_len, slot_mapping=None, workspace=None):
+        import ctypes
+        s, hq, d = q.shape
+        nb, bs, hkv, dk = key_cache.shape
+        if out.shape != q.shape or dk != d or value_cache.shape != key_cache.shape:
+            raise ValueError("shape mismatch")
+        for t in (out, k_new, v_new, key_cache, value_cache):
+            if t.dtype != q.dtype:
+                raise TypeError("q, k_new, v_new, caches and out must share one dtype")
+        if block_tables.dim() != 2 or block_tables.shape[0] != s or context_lens.shape != (s,):
+            raise ValueError("block_tables must be [S, MB] and context_lens [S]")
+        if slot_mapping is None:
+            if k_new.shape != (s, hkv, d) or v_new.shape != (s, hkv, d):
+                raise ValueError("k_new / v_new must be [num_seqs, num_kv_heads, head_dim]")
+            slots_ptr, t = None, 0
+        else:
+            t = k_new.shape[0]
+            if k_new.shape != v_new.shape or k_new.shape[1:] != (hkv, d) or slot_mapping.shape != (t,):
+                raise ValueError("k_new / v_new must be [T, Hkv, D] and slot_mapping [T]")
+            slots_ptr = _dev(slot_mapping, "slot_mapping", torch.int32)
+        if workspace is None:
+            workspace = decode_workspace(s, hq, d, max_context_len, q.device)
+        ws_ptr = 0 if workspace is None else _dev(workspace, "workspace")
+        ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+        self._keep = (out, q, k_new, v_new, key_cache, value_cache, block_tables, context_lens, slot_mapping,
+                      workspace)
+        h = ctypes.c_void_p(0)
+        check("pkv_decode_graph_create", lib().pkv_decode_graph_create(
+            ctypes.addressof(h), _dev(out, "out"), _dev(q, "q"), _dev(k_new, "k_new"), _dev(v_new, "v_new"),
+            slots_ptr, t, _dev(key_cache, "key_cache"), _dev(value_cache, "value_cache"),
+            _dev(block_tables, "block_tables", torch.int32), _dev(context_lens, "context_lens", torch.int32),
+            float(scale), bs, hq, hkv, d, s, block_tables.shape[1], nb, int(max_context_len), _dt(q), ws_ptr,
+            ws_bytes))
+        self._h = h.value
+
+    def launch(self, stream=None):
+        if not self._h:
+            raise RuntimeError("graph destroyed")
+        check("pkv_decode_graph_launch", lib().pkv_decode_graph_launch(self._h, _stream(stream)))
+
+    def close(self):
+        if getattr(self, "_h", None):
+            lib().pkv_decode_graph_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
 def pkv_varlen_workspace_bytes(num_seqs, num_tokens, num_q_heads, num_kv_heads, head_dim,
                                max_query_len, max_context_len):
     return int(lib().pkv_varlen_workspace_bytes(num_seqs, num_tokens, num_q_heads, num_kv_heads,
