@@ -285,7 +285,10 @@ def graph_probe(torch, np, pkv, seed):
         g.close()
         parts = -(-max_ctx // 512)
         lines.append({"workload": name, "steps": steps,
-                      "kernels_per_step": (2 if bf16 else 3) + (1 if parts > 1 else 0),
+                      # bf16: plan, partitions (append form); fp32: write, partitions, and the
+                      # plan only when a context spans partitions; a merge when one does
+                      "kernels_per_step": 2 + (0 if bf16 else 1) - (0 if bf16 or parts > 1 else 1)
+                      + (1 if parts > 1 else 0),
                       "eager_us_per_step": round(us_e, 2), "graph_us_per_step": round(us_g, 2),
                       "eager_host_issue_us_per_step": round(host_e, 2),
                       "graph_host_issue_us_per_step": round(host_g, 2),

@@ -127,7 +127,9 @@ int pkv_attention_decode(void* out, const void* q, const void* key_cache,
  * same arguments (so each can be timed or overlapped on its own).
  * _plan: builds the work list in the workspace from context_lens (reads nothing
  * else, writes only the workspace), so it may run on another stream -- e.g.
- * beside pkv_write -- if the caller orders it before _partitions.
+ * beside pkv_write -- if the caller orders it before _partitions.  It launches
+ * nothing for fp32 when max_context_len <= PKV_PARTITION_TOKENS (the fp32
+ * kernel reads no work list, and there is nothing to merge).
  * _partitions: computes every (sequence, KV head, 512-token partition) of the
  * planned work list; writes `out` for sequences with a single partition and the
  * partials (max, sum, normalized output) of the others to the workspace.

@@ -186,6 +186,11 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(
 }  // namespace
 
 int launch_plan(const DecodeArgs& a, void* stream) {
+  // The fp32 decode kernel runs on a grid of (KV head, partition, sequence) and
+  // reads no work list; the plan's only other output, the per-row partial
+  // counts, feeds the merge, which has nothing to do when every row fits one
+  // partition.
+  if (!a.bf16 && a.qsl == nullptr && a.max_parts <= 1) return 0;
   const DecodeParams p = make_params(a);
   const int32_t G = a.num_q_heads / a.num_kv_heads;
   hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, (hipStream_t)stream, a.ctx, a.qsl,
