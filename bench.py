@@ -6,14 +6,17 @@ path included:
   1. host block allocator: one new token per sequence (a new block when the last
      one is full), slot of each new token, refreshed block tables and lengths,
      written into a pinned staging buffer (C++ allocator behind the C ABI);
-  2. one H2D copy of that metadata on a side stream (default priority), then
-     pkv_attention_decode_plan (work list from the lengths) on the same side
-     stream, joined to the compute stream by events, so the plan overlaps 3-4;
+  2. pkv_attention_decode_plan_upload on the compute stream: one launch builds
+     the work list from the pinned lengths while its other workgroups copy the
+     pinned metadata to the device (no copy engine, no second stream: a
+     cross-stream wait costs the stream ~11 us, a copy-engine transfer more),
+     and others merge the previous step's partials (step 5 of that step);
   3. pkv_copy_blocks for any copy-on-write pairs (none for unshared batches);
   4. bf16: pkv_attention_decode_partitions_append (split-context decode, the
      dominant kernel, which also stores each sequence's new K/V row in the cache);
      fp32: pkv_write of the new tokens' K/V, then pkv_attention_decode_partitions;
-  5. pkv_attention_decode_merge (log-sum-exp merge of multi-partition sequences).
+  5. the log-sum-exp merge of multi-partition sequences: inside the next step's
+     launch of 2, or pkv_attention_decode_merge after the last step of a run.
 Contexts grow by one token per step, as in real decoding.  Inputs (pool, q, new
 K/V rows) are resident in HBM before timing starts.  R copies of the KV pool are
 rotated step to step so each step's KV reads come from HBM, not the 256 MiB
@@ -38,7 +41,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
-EV_EVERY = 4                                            # timed steps per event-bracketed launch
+EV_EVERY = 10                                           # timed steps per event-bracketed launch
 METRIC = "decode tokens/s + KV-read HBM GB/s (% of MI355X peak), bf16 GQA ctx 2k–8k"
 HBM_PEAK_GBPS = 8000.0
 DEFAULT_WORKLOAD = "gqa32x8_bf16_s128_ctx512_8192"
@@ -440,8 +443,7 @@ def main():
     knew = up(normal_values_parallel(args.seed * 10 + 4, (n_steps, S, Hkv, D), spec.dtype))
     vnew = up(normal_values_parallel(args.seed * 10 + 5, (n_steps, S, Hkv, D), spec.dtype))
     out = torch.empty((S, Hq, D), dtype=tdt, device="cuda")
-    # one workspace per staging set: step i's plan (side stream) may run while
-    # step i-1's partitions and merge still read the other one
+    # one workspace per staging set: consecutive steps alternate between them
     wss = [pkv.decode_workspace(S, Hq, D, max_ctx_bound) for _ in range(2)]
     scale = float(np.float32(1.0 / math.sqrt(D)))
 
@@ -455,10 +457,7 @@ def main():
         views.append((h[:S], h[S:2 * S], h[2 * S:].reshape(S, MB)))
     ones = np.ones(S, dtype=np.int32)
     main = torch.cuda.current_stream()
-    side = torch.cuda.Stream()                          # default priority
-    h2d_done = [torch.cuda.Event() for _ in range(2)]
-    plan_done = [torch.cuda.Event() for _ in range(2)]
-    kern_done = [torch.cuda.Event() for _ in range(2)]
+    h2d_done = [torch.cuda.Event() for _ in range(2)]   # the upload of staging set b has run
     log(f"[bench] setup {time.time() - t0:.1f}s: {spec.name} S={S} Hq={Hq} Hkv={Hkv} D={D} "
         f"pool={nb} blocks x{R} MB={MB}")
 
@@ -473,8 +472,10 @@ def main():
     q_stride = S * Hq * D * es
     kv_stride = S * Hkv * D * es
     q0, knew0, vnew0, out_p = qs.data_ptr(), knew.data_ptr(), vnew.data_ptr(), out.data_ptr()
-    side_h, main_h = side.cuda_stream, main.cuda_stream
+    main_h = main.cuda_stream
     dptr = [m.data_ptr() for m in dmeta]
+    sptr = [st.data_ptr() for st in stage]
+    meta_bytes = meta_len * 4
     ws_arg = [(w.data_ptr(), w.numel()) for w in wss]
     kc_p = [t.data_ptr() for t in kcs]
     vc_p = [t.data_ptr() for t in vcs]
@@ -488,10 +489,22 @@ def main():
         return (out_p, q0 + i * q_stride, kc_p[r], vc_p[r], d + 8 * S, d + 4 * S, scale, 16, Hq, Hkv,
                 D, S, MB, nb, max_ctx_bound, dt, ws_arg[b][0], ws_arg[b][1], stream)
 
+    # The merge of step i runs inside step i+1's upload + plan launch (the two
+    # are latency-bound and overlap); `pending` is the step whose merge is still
+    # due, flushed with a plain merge launch at the end of each phase.  The
+    # detail steps after the timed region keep the launches apart to time them.
+    pending = [None]
+
+    def flush():
+        if pending[0] is not None:
+            pi, pb, pr = pending[0]
+            check("pkv_attention_decode_merge", L.pkv_attention_decode_merge(*attn_args(pi, pb, pr, main_h)))
+            pending[0] = None
+
     def step(i, timed, detail=False):
         b = i % 2
         slots_h, lens_h, tables_h = views[b]
-        h2d_done[b].synchronize()                       # staging set b is free again (copy of step i-2 done)
+        h2d_done[b].synchronize()                       # staging set b is free again (step i-2's upload ran)
         ta = time.perf_counter()
         _, pairs = alloc.append_batch(ids, ones, slots_out=slots_h)
         alloc.block_tables(ids, MB, fill=-1, tables_out=tables_h, lens_out=lens_h)
@@ -499,25 +512,26 @@ def main():
         if timed:
             step_lens.append(lens_h.copy())
         r = i % R
-        with torch.cuda.stream(side):
-            side.wait_event(kern_done[b])               # device set b no longer read by step i-2
-            dmeta[b].copy_(stage[b], non_blocking=True)
-            h2d_done[b].record(side)
-        # the work list needs only the lengths: it runs beside the write
-        check("pkv_attention_decode_plan", L.pkv_attention_decode_plan(*attn_args(i, b, r, side_h)))
-        plan_done[b].record(side)
-        # (plan_done follows the copy on the side stream, so it orders both)
         bracket = detail or (timed and (i - W) % EV_EVERY == 0)
         ev = events[i - W] if bracket else None
         if detail:
+            flush()
             ev[0].record(main)
+        merge_out, merge_ws = None, None
+        if pending[0] is not None:                      # the previous step's merge rides along
+            merge_out, merge_ws = out_p, ws_arg[pending[0][1]][0]
+            pending[0] = None
+        # metadata upload + work list (+ that merge), one launch on the compute
+        # stream; the lengths it plans from are the staging's, at offset S
+        check("pkv_attention_decode_plan_upload", L.pkv_attention_decode_plan_upload(
+            *attn_args(i, b, r, None)[:-1], sptr[b] + 4 * S, sptr[b], dptr[b], meta_bytes, merge_out, merge_ws,
+            main_h))
+        h2d_done[b].record(main)
         if len(pairs):
             pkv.pkv_copy_blocks(kcs[r], vcs[r], torch.from_numpy(pairs).cuda())
         if not fused:
-            main.wait_event(h2d_done[b])                # the write reads the slots
             check("pkv_write", L.pkv_write(kc_p[r], vc_p[r], knew0 + i * kv_stride, vnew0 + i * kv_stride,
                                            dptr[b], S, nb, 16, Hkv, D, dt, main_h))
-        main.wait_event(plan_done[b])
         if bracket:
             ev[1].record(main)
         args_m = attn_args(i, b, r, main_h)
@@ -529,19 +543,22 @@ def main():
             check("pkv_attention_decode_partitions", L.pkv_attention_decode_partitions(*args_m))
         if bracket:
             ev[2].record(main)
-        check("pkv_attention_decode_merge", L.pkv_attention_decode_merge(*args_m))
         if detail:
+            check("pkv_attention_decode_merge", L.pkv_attention_decode_merge(*args_m))
             ev[3].record(main)
-        kern_done[b].record(main)
+        else:
+            pending[0] = (i, b, r)
         host_step_s.append(time.perf_counter() - ta)
 
     for i in range(W):
         step(i, False)
+    flush()
     torch.cuda.synchronize()
     log(f"[bench] warmup {W} steps done")
     t_start = time.perf_counter()
     for i in range(W, W + K):
         step(i, True)
+    flush()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
     log(f"[bench] timed {K} steps: {wall * 1e3:.2f} ms")
@@ -552,7 +569,8 @@ def main():
     # ---- per-kernel durations and algorithmic bytes --------------------------
     timed_ev = list(range(0, K, EV_EVERY))             # timed steps whose launch was bracketed
     t_part = [events[k][1].elapsed_time(events[k][2]) * 1e-3 for k in timed_ev]
-    # write (fp32) or nothing (bf16: fused), plus any wait for the plan on the side stream
+    # detail steps: the upload + plan launch (no merge rides along there), plus the
+    # write for fp32 (bf16: fused into the partitions); the merge on its own
     t_write = [e[0].elapsed_time(e[1]) * 1e-3 for e in events[K:]]
     t_merge = [e[2].elapsed_time(e[3]) * 1e-3 for e in events[K:]]
     kv_b, part_b, merge_b, logical_b = [], [], [], []
@@ -630,7 +648,7 @@ def main():
             "prefix_len": spec.prefix_len, "cow_pairs": int(len(cow_pairs))} if prefix else {}),
         "kv_read_frac_of_peak": round(kv_gbps / HBM_PEAK_GBPS, 4),
         "kernels_us": {
-            ("plan_wait" if fused else "write"): round(float(np.mean(t_write)) * 1e6, 2),
+            ("upload_plan" if fused else "upload_plan_write"): round(float(np.mean(t_write)) * 1e6, 2),
             "decode_partitions": round(float(np.mean(t_part)) * 1e6, 2),
             "merge": round(float(np.mean(t_merge)) * 1e6, 2),
         },

@@ -144,6 +144,35 @@ int pkv_attention_decode_plan(void* out, const void* q, const void* key_cache,
                               int32_t num_seqs, int32_t max_blocks_per_seq, int32_t num_blocks,
                               int32_t max_context_len, pkv_dtype dt, void* workspace,
                               size_t workspace_bytes, void* stream);
+/* _plan_upload: the plan of a step whose metadata the host has just written to
+ * page-locked memory, fused with the copy of that metadata to the device, in
+ * one launch on `stream` (no copy engine, no second stream).  Workgroup 0 builds
+ * the work list from host_context_lens (page-locked, mapped for the device;
+ * num_seqs values); the others copy upload_bytes (a multiple of 16) from
+ * upload_src (page-locked) to upload_dst (device), typically the step's slots,
+ * context lengths and tables, so that context_lens / block_tables of the later
+ * launches point into upload_dst.  The work list equals _plan's for the same
+ * lengths.  Decode (one query row per sequence) only; num_seqs > 0.  The host
+ * must not rewrite the page-locked buffers until the stream has passed this
+ * launch.  Pointers are checked with the HIP runtime: PKV_EINVAL for pageable
+ * or device memory where page-locked host memory is required, and the other
+ * way round.  Other errors as pkv_attention_decode.
+ * merge_out, merge_workspace (both NULL, or both given): the same launch also
+ * runs _merge for the previous step -- one whose _partitions wrote its partials
+ * to merge_workspace with the same shapes, max_context_len and workspace size,
+ * and whose output is merge_out -- so a decode loop is
+ *   _plan_upload(step i, merging step i-1) ; _partitions(step i)
+ * with a plain _merge after the last step.  merge_workspace must not be
+ * `workspace` (PKV_EINVAL): step i's plan writes its own workspace while step
+ * i-1's partials are read. */
+int pkv_attention_decode_plan_upload(void* out, const void* q, const void* key_cache, const void* value_cache,
+                                     const int32_t* block_tables, const int32_t* context_lens, float scale,
+                                     int32_t block_size, int32_t num_q_heads, int32_t num_kv_heads,
+                                     int32_t head_dim, int32_t num_seqs, int32_t max_blocks_per_seq,
+                                     int32_t num_blocks, int32_t max_context_len, pkv_dtype dt, void* workspace,
+                                     size_t workspace_bytes, const int32_t* host_context_lens,
+                                     const void* upload_src, void* upload_dst, size_t upload_bytes,
+                                     void* merge_out, const void* merge_workspace, void* stream);
 int pkv_attention_decode_partitions(void* out, const void* q, const void* key_cache,
                                     const void* value_cache, const int32_t* block_tables,
                                     const int32_t* context_lens, float scale, int32_t block_size,

@@ -15,6 +15,7 @@ from .ops import (  # noqa: F401
     pkv_write,
     pkv_attention_decode,
     pkv_attention_decode_plan,
+    pkv_attention_decode_plan_upload,
     pkv_attention_decode_partitions,
     pkv_attention_decode_merge,
     pkv_attention_decode_append,

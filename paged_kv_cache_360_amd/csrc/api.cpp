@@ -91,6 +91,13 @@ bool device_span(const void* p, int64_t bytes, void** dev_out) {
   return true;
 }
 
+// Page-locked host memory mapped for the device: its device address.
+bool host_mapped(const void* p, int64_t bytes, void** dev_out) {
+  if (!device_span(p, bytes, dev_out)) return false;
+  hipPointerAttribute_t a{};
+  return hipPointerGetAttributes(&a, p) == hipSuccess && a.type == hipMemoryTypeHost;
+}
+
 // A small table the kernel reads (pairs): device memory only.
 bool device_readable(const void* p, int64_t bytes) {
   void* d = nullptr;
@@ -281,6 +288,53 @@ int pkv_attention_decode_plan(PKV_DECODE_ARGS) {
   int rc = prepare_attention(who, a, PKV_DECODE_FWD);
   if (rc != PKV_OK || num_seqs == 0) return rc;
   return pkv::launched(pkv::launch_plan(a, stream), who);
+}
+
+int pkv_attention_decode_plan_upload(void* out, const void* q, const void* key_cache, const void* value_cache,
+                                     const int32_t* block_tables, const int32_t* context_lens, float scale,
+                                     int32_t block_size, int32_t num_q_heads, int32_t num_kv_heads,
+                                     int32_t head_dim, int32_t num_seqs, int32_t max_blocks_per_seq,
+                                     int32_t num_blocks, int32_t max_context_len, pkv_dtype dt, void* workspace,
+                                     size_t workspace_bytes, const int32_t* host_context_lens,
+                                     const void* upload_src, void* upload_dst, size_t upload_bytes,
+                                     void* merge_out, const void* merge_workspace, void* stream) {
+  pkv::DecodeArgs a{};
+  const char* who = "pkv_attention_decode_plan_upload";
+  if (num_seqs <= 0) return fail(PKV_EINVAL, "pkv_attention_decode_plan_upload: num_seqs must be > 0");
+  int rc = prepare_attention(who, a, PKV_DECODE_FWD);
+  if (rc != PKV_OK) return rc;
+  if (upload_bytes % 16 != 0 || upload_bytes > (size_t)INT64_MAX)
+    return fail(PKV_EINVAL, "pkv_attention_decode_plan_upload: upload_bytes must be a multiple of 16");
+  void* hctx = nullptr;
+  if (!pkv::host_mapped(host_context_lens, (int64_t)num_seqs * 4, &hctx))
+    return fail(PKV_EINVAL, "pkv_attention_decode_plan_upload: host_context_lens must be page-locked host memory");
+  void* src = nullptr;
+  void* dst = nullptr;
+  if (upload_bytes > 0) {
+    if (!pkv::host_mapped(upload_src, (int64_t)upload_bytes, &src))
+      return fail(PKV_EINVAL, "pkv_attention_decode_plan_upload: upload_src must be page-locked host memory");
+    if (!pkv::device_readable(upload_dst, (int64_t)upload_bytes))
+      return fail(PKV_EINVAL, "pkv_attention_decode_plan_upload: upload_dst must be device memory");
+    dst = upload_dst;
+    if (!pkv::aligned16(src) || !pkv::aligned16(dst))
+      return fail(PKV_EINVAL, "pkv_attention_decode_plan_upload: upload buffers must be 16-byte aligned");
+  }
+  pkv::DecodeArgs prev{};
+  const pkv::DecodeArgs* prev_p = nullptr;
+  if (merge_out != nullptr || merge_workspace != nullptr) {
+    if (merge_workspace == workspace)
+      return fail(PKV_EINVAL, "pkv_attention_decode_plan_upload: merge_workspace must differ from workspace");
+    // the previous step: same shapes and bound, its own output and workspace
+    rc = prepare_attention(who, prev, merge_out, q, key_cache, value_cache, block_tables, context_lens, nullptr,
+                           num_seqs, 1, scale, block_size, num_q_heads, num_kv_heads, head_dim, num_seqs,
+                           max_blocks_per_seq, num_blocks, max_context_len, dt, const_cast<void*>(merge_workspace),
+                           workspace_bytes);
+    if (rc != PKV_OK) return rc;
+    prev_p = &prev;
+  }
+  return pkv::launched(pkv::launch_upload_plan(a, static_cast<const int32_t*>(hctx), src, dst,
+                                               (int64_t)upload_bytes, prev_p, stream),
+                       who);
 }
 
 int pkv_attention_decode_partitions(PKV_DECODE_ARGS) {

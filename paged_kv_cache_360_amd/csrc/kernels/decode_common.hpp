@@ -73,4 +73,83 @@ struct DecodeArgs;
 DecodeParams make_params(const DecodeArgs& a);
 // bf16 partition kernel on the matrix cores (decode_mfma.hip).
 int launch_decode_partitions_bf16(const DecodeParams& p, const DecodeArgs& a, void* stream);
+// The merge of one output row (query row x q head) by one wave (lane = its lane).  PER_TOKEN: the slot count is
+// that of the row's query token (counts = the plan's row_slots; rows with one
+// slot were already written by the partition or prefill kernels and are
+// skipped); otherwise num_parts[row].
+// Latency is one round trip per kMergeUnroll partitions: the first group's
+// partial outputs are loaded before the maxima are reduced, and the maxima and
+// sums are read lane-parallel (64 partitions per load).
+constexpr int kMergeUnroll = 8;
+
+template <bool BF16, int D, bool PER_TOKEN>
+__device__ __forceinline__ void merge_row(
+    int64_t row, int lane, void* __restrict__ out, const float* __restrict__ pm, const float* __restrict__ pl,
+    const float* __restrict__ po, const int32_t* __restrict__ counts, int32_t Hq, int32_t max_parts) {
+  constexpr int PER = D / kWave;
+  constexpr int U = kMergeUnroll;
+  int n;
+  if constexpr (PER_TOKEN) {
+    n = min(counts[row / Hq], max_parts);
+    if (n <= 1) return;
+  } else {
+    n = max(0, min(counts[row], max_parts));
+  }
+  const float* rm = pm + row * max_parts;
+  const float* rl = pl + row * max_parts;
+  const float* ro = po + row * max_parts * D;
+
+  float ov[U][PER];  // first group of partial outputs, in flight during the reductions
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+#pragma unroll
+    for (int k = 0; k < PER; ++k) ov[u][k] = u < n ? ro[(int64_t)u * D + lane + k * kWave] : 0.f;
+  }
+
+  // live partial: l > 0 and a finite max; the rest weigh 0
+  float M = -INFINITY;
+  for (int base = 0; base < n; base += kWave) {
+    const int i = base + lane;
+    if (i < n && rl[i] > 0.f) M = fmaxf(M, rm[i]);
+  }
+  M = xor_max<1, kWave>(M);
+  float o[PER];
+#pragma unroll
+  for (int k = 0; k < PER; ++k) o[k] = 0.f;
+  float L = 0.f;
+  if (M != -INFINITY) {
+    // a dead partial is skipped, not weighted by 0: its output may hold NaN
+    auto add = [&](int i, const float (&v)[PER]) {
+      const float mi = rm[i], li = rl[i];
+      if (li > 0.f && mi != -INFINITY) {
+        const float w = li * exp2_fast(mi - M);
+        L += w;
+#pragma unroll
+        for (int k = 0; k < PER; ++k) o[k] = fmaf(w, v[k], o[k]);
+      }
+    };
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (u < n) add(u, ov[u]);
+    }
+    for (int base = U; base < n; base += U) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+#pragma unroll
+        for (int k = 0; k < PER; ++k)
+          ov[u][k] = base + u < n ? ro[(int64_t)(base + u) * D + lane + k * kWave] : 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (base + u < n) add(base + u, ov[u]);
+      }
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    store_out<BF16>(out, row * D + lane + k * kWave, L > 0.f ? o[k] / L : 0.f);
+  }
+}
+
+
 }  // namespace pkv

@@ -32,6 +32,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+
 #include "../pkv_internal.hpp"
 #include "decode_common.hpp"
 
@@ -39,7 +41,7 @@ namespace pkv {
 
 namespace {
 
-__global__ __launch_bounds__(kPlanThreads) void plan_kernel(
+__device__ __forceinline__ void plan_body(
     const int32_t* __restrict__ ctx, const int32_t* __restrict__ qsl, int32_t S, int32_t T,
     int32_t ctx_cap, int32_t Hkv, int32_t rows_per_item, int32_t dec_cap, int32_t pre_cap,
     int32_t num_cus, int32_t* __restrict__ sched, int4* __restrict__ dec, int4* __restrict__ pre,
@@ -183,6 +185,59 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(
   }
 }
 
+__global__ __launch_bounds__(kPlanThreads) void plan_kernel(
+    const int32_t* __restrict__ ctx, const int32_t* __restrict__ qsl, int32_t S, int32_t T,
+    int32_t ctx_cap, int32_t Hkv, int32_t rows_per_item, int32_t dec_cap, int32_t pre_cap,
+    int32_t num_cus, int32_t* __restrict__ sched, int4* __restrict__ dec, int4* __restrict__ pre,
+    int32_t* __restrict__ row_slots) {
+  plan_body(ctx, qsl, S, T, ctx_cap, Hkv, rows_per_item, dec_cap, pre_cap, num_cus, sched, dec, pre, row_slots);
+}
+
+// Loads in flight per thread in the staging copy (reads cross the host link).
+constexpr int kUploadBatch = 4;
+constexpr int kMergeRowsPerBlock = kPlanThreads / kWave;
+
+// The plan of a step whose metadata is still in page-locked host memory, fused
+// with the copy of that metadata to the device and, optionally, with the
+// log-sum-exp merge of the previous step's partials.  Workgroup 0 builds the
+// work list from the host copy of the context lengths (read through its device
+// mapping); workgroups 1 .. n_up copy n16 16-byte words from src (host) to dst
+// (device); the rest merge one row per wave.  One launch on the compute stream
+// replaces a copy-engine transfer, a cross-stream wait and the merge launch:
+// the three parts are latency-bound and overlap.  The previous step's partials
+// and row counts live in another workspace than the one planned here.
+template <bool BF16, int D>
+__global__ __launch_bounds__(kPlanThreads) void upload_plan_kernel(
+    const int32_t* __restrict__ host_ctx, int32_t S, int32_t ctx_cap, int32_t Hkv, int32_t dec_cap,
+    int32_t num_cus, int32_t* __restrict__ sched, int4* __restrict__ dec, int32_t* __restrict__ row_slots,
+    const uint4* __restrict__ src, uint4* __restrict__ dst, int64_t n16, int32_t n_up,
+    void* __restrict__ m_out, const float* __restrict__ m_pm, const float* __restrict__ m_pl,
+    const float* __restrict__ m_po, const int32_t* __restrict__ m_counts, int32_t Hq, int32_t m_max_parts,
+    int64_t m_rows) {
+  if (blockIdx.x == 0) {
+    plan_body(host_ctx, nullptr, S, S, ctx_cap, Hkv, /*rows_per_item, unused without prefill rows*/ 1, dec_cap, 0,
+              num_cus, sched, dec, nullptr, row_slots);
+    return;
+  }
+  if ((int)blockIdx.x <= n_up) {
+    const int64_t stride = (int64_t)n_up * kPlanThreads;
+    for (int64_t base = (int64_t)(blockIdx.x - 1) * kPlanThreads + threadIdx.x; base < n16;
+         base += stride * kUploadBatch) {
+      uint4 r[kUploadBatch];
+#pragma unroll
+      for (int u = 0; u < kUploadBatch; ++u)
+        if (base + u * stride < n16) r[u] = src[base + u * stride];
+#pragma unroll
+      for (int u = 0; u < kUploadBatch; ++u)
+        if (base + u * stride < n16) dst[base + u * stride] = r[u];
+    }
+    return;
+  }
+  const int64_t row = (int64_t)(blockIdx.x - 1 - n_up) * kMergeRowsPerBlock + threadIdx.x / kWave;
+  if (row < m_rows)
+    merge_row<BF16, D, true>(row, threadIdx.x & (kWave - 1), m_out, m_pm, m_pl, m_po, m_counts, Hq, m_max_parts);
+}
+
 }  // namespace
 
 int launch_plan(const DecodeArgs& a, void* stream) {
@@ -197,6 +252,36 @@ int launch_plan(const DecodeArgs& a, void* stream) {
                      a.num_seqs, a.num_tokens, p.ctx_cap, a.num_kv_heads, prefill_rows_per_item(G),
                      a.dec_cap, a.pre_cap, a.num_cus, a.sched, reinterpret_cast<int4*>(a.dec_recs),
                      reinterpret_cast<int4*>(a.pre_recs), a.row_slots);
+  return (int)hipGetLastError();
+}
+
+int launch_upload_plan(const DecodeArgs& a, const int32_t* host_ctx, const void* src, void* dst,
+                       int64_t bytes, const DecodeArgs* prev, void* stream) {
+  const DecodeParams p = make_params(a);
+  const int64_t n16 = bytes / 16;
+  // copy workgroups: enough 16-byte loads in flight to cover the host link's latency
+  const int64_t per_wg = (int64_t)kPlanThreads * kUploadBatch;
+  const int n_up = n16 > 0 ? (int)std::min<int64_t>((n16 + per_wg - 1) / per_wg, 256) : 0;
+  // merge of the previous step: only rows spanning several partitions need it
+  const bool merge = prev != nullptr && prev->max_parts > 1;
+  const int64_t m_rows = merge ? (int64_t)prev->num_tokens * prev->num_q_heads : 0;
+  const int64_t n_mg = (m_rows + kMergeRowsPerBlock - 1) / kMergeRowsPerBlock;
+  const DecodeArgs& m = merge ? *prev : a;
+  const dim3 grid((unsigned)(1 + n_up + n_mg));
+  const bool bf16 = merge ? prev->bf16 : a.bf16;
+  const int D = merge ? prev->head_dim : a.head_dim;
+#define PKV_UPLOAD_PLAN_LAUNCH(B, DD)                                                                   \
+  hipLaunchKernelGGL((upload_plan_kernel<B, DD>), grid, dim3(kPlanThreads), 0, (hipStream_t)stream, host_ctx, \
+                     a.num_seqs, p.ctx_cap, a.num_kv_heads, a.dec_cap, a.num_cus, a.sched,              \
+                     reinterpret_cast<int4*>(a.dec_recs), a.row_slots, reinterpret_cast<const uint4*>(src), \
+                     reinterpret_cast<uint4*>(dst), n16, n_up, m.out, m.part_m, m.part_l, m.part_o,       \
+                     m.row_slots, m.num_q_heads, m.max_parts, m_rows)
+  if (bf16) {
+    if (D == 64) PKV_UPLOAD_PLAN_LAUNCH(true, 64); else PKV_UPLOAD_PLAN_LAUNCH(true, 128);
+  } else {
+    if (D == 64) PKV_UPLOAD_PLAN_LAUNCH(false, 64); else PKV_UPLOAD_PLAN_LAUNCH(false, 128);
+  }
+#undef PKV_UPLOAD_PLAN_LAUNCH
   return (int)hipGetLastError();
 }
 

@@ -101,6 +101,45 @@ def pkv_attention_decode_plan(out, q, key_cache, value_cache, block_tables, cont
                         block_tables, context_lens, scale, max_context_len, workspace, stream)
 
 
+def pkv_attention_decode_plan_upload(out, q, key_cache, value_cache, block_tables, context_lens, scale,
+                                     max_context_len, host_context_lens, upload_src, upload_dst,
+                                     workspace=None, merge_out=None, merge_workspace=None, stream=None):
+    """``_plan`` from a pinned host copy of the lengths, fused with the copy of the
+    pinned ``upload_src`` into the device tensor ``upload_dst`` (same byte size),
+    in one launch.  ``block_tables`` / ``context_lens`` are the device tensors the
+    later launches read (usually views of ``upload_dst``).  With ``merge_out`` and
+    ``merge_workspace``, the launch also merges the previous step's partials
+    (same shapes, another workspace) into ``merge_out``."""
+    if (merge_out is None) != (merge_workspace is None):
+        raise ValueError("give both merge_out and merge_workspace, or neither")
+    for name, t in (("host_context_lens", host_context_lens), ("upload_src", upload_src)):
+        if not isinstance(t, torch.Tensor) or t.is_cuda or not t.is_pinned() or not t.is_contiguous():
+            raise TypeError(f"{name} must be a contiguous pinned host tensor")
+    if host_context_lens.dtype != torch.int32 or host_context_lens.shape != (q.shape[0],):
+        raise ValueError("host_context_lens must be int32 [num_seqs]")
+    nbytes = upload_src.numel() * upload_src.element_size()
+    if upload_dst.numel() * upload_dst.element_size() != nbytes:
+        raise ValueError("upload_src and upload_dst must have the same byte size")
+    s, hq, d = q.shape
+    nb, bs, hkv, dk = key_cache.shape
+    if out.shape != q.shape or dk != d or value_cache.shape != key_cache.shape:
+        raise ValueError("shape mismatch")
+    if block_tables.dim() != 2 or block_tables.shape[0] != s or context_lens.shape != (s,):
+        raise ValueError("block_tables must be [S, MB] and context_lens [S]")
+    if workspace is None:
+        workspace = decode_workspace(s, hq, d, max_context_len, q.device)
+    ws_ptr = 0 if workspace is None else _dev(workspace, "workspace")
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    check("pkv_attention_decode_plan_upload", lib().pkv_attention_decode_plan_upload(
+        _dev(out, "out"), _dev(q, "q"), _dev(key_cache, "key_cache"), _dev(value_cache, "value_cache"),
+        _dev(block_tables, "block_tables", torch.int32), _dev(context_lens, "context_lens", torch.int32),
+        float(scale), bs, hq, hkv, d, s, block_tables.shape[1], nb, int(max_context_len), _dt(q), ws_ptr,
+        ws_bytes, host_context_lens.data_ptr(), upload_src.data_ptr(), _dev(upload_dst, "upload_dst"), nbytes,
+        None if merge_out is None else _dev(merge_out, "merge_out"),
+        None if merge_workspace is None else _dev(merge_workspace, "merge_workspace"), _stream(stream)))
+    return out
+
+
 def pkv_attention_decode_partitions(out, q, key_cache, value_cache, block_tables, context_lens,
                                     scale, max_context_len, workspace=None, stream=None):
     """Second launch of ``pkv_attention_decode`` alone (partition kernel; needs the plan)."""
