@@ -301,10 +301,10 @@ int pkv_attention_decode_plan_upload(void* out, const void* q, const void* key_c
   pkv::DecodeArgs a{};
   const char* who = "pkv_attention_decode_plan_upload";
   if (num_seqs <= 0) return fail(PKV_EINVAL, "pkv_attention_decode_plan_upload: num_seqs must be > 0");
-  int rc = prepare_attention(who, a, PKV_DECODE_FWD);
-  if (rc != PKV_OK) return rc;
   if (upload_bytes % 16 != 0 || upload_bytes > (size_t)INT64_MAX)
     return fail(PKV_EINVAL, "pkv_attention_decode_plan_upload: upload_bytes must be a multiple of 16");
+  int rc = prepare_attention(who, a, PKV_DECODE_FWD);
+  if (rc != PKV_OK) return rc;
   void* hctx = nullptr;
   if (!pkv::host_mapped(host_context_lens, (int64_t)num_seqs * 4, &hctx))
     return fail(PKV_EINVAL, "pkv_attention_decode_plan_upload: host_context_lens must be page-locked host memory");

@@ -168,6 +168,41 @@ def test_write_and_copy_argument_errors():
     assert m(FAKE, 0, FAKE, FAKE, FAKE, 3, 4, 128, PKV_F32, None) == PKV_EINVAL
 
 
+def test_graph_and_plan_upload_argument_errors():
+    """Rejected before any HIP call: nothing is captured, uploaded or launched."""
+    import ctypes
+    L = lib()
+    g = ctypes.c_void_p(0)
+    ws = 1 << 20
+    # (out, q, k_new, v_new, slots, n_new, kc, vc, tables, lens, scale, bs, Hq, Hkv, D, S, MB, NB, max_ctx, dt, ws, ws_bytes)
+    ok = [FAKE, FAKE, FAKE, FAKE, FAKE, 4, FAKE, FAKE, FAKE, FAKE, 0.125, 16, 8, 8, 64, 4, 8, 64, 100, PKV_F32,
+          0x100000, ws]
+
+    def create(**kw):
+        a = list(ok)
+        for i, v in kw.items():
+            a[int(i[1:])] = v
+        return L.pkv_decode_graph_create(ctypes.addressof(g), *a)
+
+    assert L.pkv_decode_graph_create(None, *ok) == PKV_EINVAL              # no handle to fill
+    assert create(a15=0) == PKV_EINVAL                                    # no sequences
+    assert create(a4=None) == PKV_EUNSUPPORTED                            # append form is bf16 only
+    assert create(a5=-1) == PKV_EINVAL                                    # negative token count
+    assert create(a11=32) == PKV_EUNSUPPORTED                             # block size
+    assert create(a18=200) == PKV_EINVAL                                  # bound wider than the tables
+    assert create(a20=0x100010) == PKV_EWORKSPACE                          # workspace misaligned
+    assert g.value in (None, 0)
+    assert L.pkv_decode_graph_launch(None, None) == PKV_EINVAL
+    L.pkv_decode_graph_destroy(None)
+    # plan_upload: (decode args without stream) + host lens, src, dst, bytes, merge out, merge ws, stream
+    d = [FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0.125, 16, 8, 8, 64, 4, 8, 64, 100, PKV_F32, 0x100000, ws]
+    pu = L.pkv_attention_decode_plan_upload
+    assert pu(*d[:11], 0, *d[12:], FAKE, FAKE, FAKE, 64, None, None, None) == PKV_EINVAL        # no sequences
+    assert pu(*d, FAKE, FAKE, FAKE, 60, None, None, None) == PKV_EINVAL                         # not 16-byte words
+    assert pu(*d[:7], 32, *d[8:], FAKE, FAKE, FAKE, 64, None, None, None) == PKV_EUNSUPPORTED   # block size
+    assert L.pkv_check_pool(None, 64) == PKV_EINVAL and L.pkv_check_pool(FAKE, 0) == PKV_EINVAL
+
+
 def test_host_table_and_slot_checks():
     tables = np.array([[3, 1, -1], [0, 7, 2]], np.int32)
     pkv.pkv_check_tables(tables, [20, 40], 8)
