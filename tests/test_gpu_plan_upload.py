@@ -135,3 +135,71 @@ def test_plan_upload_rejects_wrong_memory_kinds():
                                               64, *nm, None) != 0
     assert L.pkv_attention_decode_plan_upload(*base, pinned.data_ptr(), pinned.data_ptr(), dst.data_ptr(), 60,
                                               *nm, None) != 0
+
+
+def test_bench_launch_sequence_full_size():
+    """The decode loop bench.py times, at its full size (128 sequences, GQA 32/8,
+    head_dim 128, contexts log-uniform in [512, 8192], 4 steps of growth by one
+    token, tables from the C++ allocator with a shuffled pool): per step,
+    _plan_upload (pinned staging, merging the previous step, alternating
+    workspaces) then _partitions_append; a plain _merge after the last step.
+    Every step's output and the final cache equal the one-call append form run
+    step by step on a copy of the pool, byte for byte; sampled rows of the last
+    step match the oracle."""
+    from workloads import SPECS, draw_context_lens, pool_blocks_for
+    spec = SPECS["gqa32x8_bf16_s128_ctx512_8192"]
+    S, Hq, Hkv, D = spec.num_seqs, spec.num_q_heads, spec.num_kv_heads, spec.head_dim
+    steps = 4
+    rng = np.random.default_rng(1002)
+    ctx0 = np.asarray(draw_context_lens(rng, spec), np.int64)
+    nb = pool_blocks_for(spec, ctx0 + steps)
+    MB = -(-(int(ctx0.max()) + steps) // 16)
+    bound = 16 * MB
+    say(f"bench launch sequence S={S} nb={nb} MB={MB}")
+    alloc = pkv.BlockAllocator(nb, 16, shuffle_seed=7)
+    ids = np.arange(S, dtype=np.int64)
+    for s in range(S):
+        alloc.add_seq(s)
+        alloc.append(s, int(ctx0[s]) - 1)
+    kc = dev(normal_values_parallel(11, (nb, 16, Hkv, D), "bf16"))
+    vc = dev(normal_values_parallel(12, (nb, 16, Hkv, D), "bf16"))
+    kc_ref, vc_ref = kc.clone(), vc.clone()
+    scale = float(np.float32(1.0 / math.sqrt(D)))
+    meta_len = 2 * S + S * MB
+    meta_len += -meta_len % 4
+    stage = [torch.zeros(meta_len, dtype=torch.int32, pin_memory=True) for _ in range(2)]
+    dmeta = [torch.zeros(meta_len, dtype=torch.int32, device="cuda") for _ in range(2)]
+    wss = [pkv.decode_workspace(S, Hq, D, bound) for _ in range(2)]
+    out = [torch.zeros((S, Hq, D), dtype=torch.bfloat16, device="cuda") for _ in range(steps)]
+    refs, qs, last = [], [], None
+    for i in range(steps):
+        b = i % 2
+        h = stage[b].numpy()
+        alloc.append_batch(ids, np.ones(S, np.int32), slots_out=h[:S])
+        tables, lens = alloc.block_tables(ids, MB, fill=-1, tables_out=h[2 * S:2 * S + S * MB].reshape(S, MB),
+                                          lens_out=h[S:2 * S])
+        q = dev(normal_values_parallel(100 + i, (S, Hq, D), "bf16"))
+        kn = dev(normal_values_parallel(200 + i, (S, Hkv, D), "bf16"))
+        vn = dev(normal_values_parallel(300 + i, (S, Hkv, D), "bf16"))
+        d_lens, d_tab = dmeta[b][S:2 * S], dmeta[b][2 * S:2 * S + S * MB].view(S, MB)
+        merge_kw = dict(merge_out=out[i - 1], merge_workspace=wss[1 - b]) if i > 0 else {}
+        pkv.pkv_attention_decode_plan_upload(out[i], q, kc, vc, d_tab, d_lens, scale, bound, stage[b][S:2 * S],
+                                             stage[b], dmeta[b], workspace=wss[b], **merge_kw)
+        pkv.pkv_attention_decode_partitions_append(out[i], q, kn, vn, kc, vc, d_tab, d_lens, scale, bound,
+                                                   workspace=wss[b])
+        ref = torch.zeros_like(out[i])
+        pkv.pkv_attention_decode_append(ref, q, kn, vn, kc_ref, vc_ref, dev(tables), dev(lens), scale, bound)
+        refs.append(ref)
+        qs.append(q)
+        last = (tables.copy(), lens.copy())
+        torch.cuda.synchronize()                     # the staging set is rewritten two steps later
+    pkv.pkv_attention_decode_merge(out[-1], qs[-1], kc, vc, dmeta[(steps - 1) % 2][2 * S:2 * S + S * MB].view(S, MB),
+                                   dmeta[(steps - 1) % 2][S:2 * S], scale, bound, workspace=wss[(steps - 1) % 2])
+    torch.cuda.synchronize()
+    for i in range(steps):
+        assert host(out[i]).tobytes() == host(refs[i]).tobytes(), f"step {i} differs"
+    assert host(kc).tobytes() == host(kc_ref).tobytes() and host(vc).tobytes() == host(vc_ref).tobytes()
+    tables, lens = last
+    idx = np.unique(np.concatenate([np.argsort(lens)[:2], np.argsort(lens)[-2:], rng.choice(S, 6, replace=False)]))
+    ref = oracle.decode_attention(host(qs[-1])[idx], host(kc), host(vc), tables[idx], lens[idx], np.float32(scale))
+    assert_close(host_f64(out[-1])[idx], ref, "bf16", "bench launch sequence, last step")
