@@ -28,7 +28,8 @@
 //    keys), 0 for rows no sequence owns;
 //  * sched: both ticket counters reset, and each list's ticket count (records
 //    times KV heads: ticket t is record t / Hkv, KV head t % Hkv).
-// One workgroup; sequence chunks are scanned in LDS.
+// One workgroup; per-thread counts are scanned with lane shuffles and one
+// exchange of wave totals in LDS.
 
 #include <hip/hip_runtime.h>
 
@@ -47,9 +48,7 @@ __device__ __forceinline__ void plan_body(
     int32_t num_cus, int32_t* __restrict__ sched, int4* __restrict__ dec, int4* __restrict__ pre,
     int32_t* __restrict__ row_slots) {
   constexpr int NBK = kItemBlocks + 1;  // buckets: last-item block count kItemBlocks .. 0
-  __shared__ int32_t s_full[kPlanThreads];
-  __shared__ int32_t s_pre[kPlanThreads];   // prefill records at span 1
-  __shared__ int32_t s_pre2[kPlanThreads];  // and at span 2
+  __shared__ int32_t s_wsum[kPlanThreads / kWave][3];  // per wave: full items, prefill records at span 1, 2
   __shared__ int32_t s_bucket[NBK];
   const int t = threadIdx.x;
   const int per = (S + kPlanThreads - 1) / kPlanThreads;
@@ -90,43 +89,65 @@ __device__ __forceinline__ void plan_body(
       }
     }
   }
-  s_full[t] = full;
-  s_pre[t] = npre;
-  s_pre2[t] = npre2;
-  __syncthreads();
-  for (int off = 1; off < kPlanThreads; off <<= 1) {  // inclusive scans (Hillis-Steele)
-    const int vf = t >= off ? s_full[t - off] : 0;
-    const int vp = t >= off ? s_pre[t - off] : 0;
-    const int vp2 = t >= off ? s_pre2[t - off] : 0;
-    __syncthreads();
-    s_full[t] += vf;
-    s_pre[t] += vp;
-    s_pre2[t] += vp2;
-    __syncthreads();
+  // Inclusive scans of (full, npre, npre2) over the workgroup: within each
+  // wave by lane shuffles, then across the waves' totals in LDS (one barrier).
+  constexpr int NWV = kPlanThreads / kWave;
+  const int lane = t & (kWave - 1);
+  const int wv = t / kWave;
+  int inc_f = full, inc_p = npre, inc_p2 = npre2;
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int vf = __shfl_up(inc_f, off, kWave);
+    const int vp = __shfl_up(inc_p, off, kWave);
+    const int vp2 = __shfl_up(inc_p2, off, kWave);
+    if (lane >= off) {
+      inc_f += vf;
+      inc_p += vp;
+      inc_p2 += vp2;
+    }
   }
-  const int num_full = s_full[kPlanThreads - 1];
+  if (lane == kWave - 1) {
+    s_wsum[wv][0] = inc_f;
+    s_wsum[wv][1] = inc_p;
+    s_wsum[wv][2] = inc_p2;
+  }
+  __syncthreads();  // (also orders the bucket counts of the loop above)
+  int tot_f = 0, tot_p = 0, tot_p2 = 0;
+  for (int w = 0; w < NWV; ++w) {
+    const int a = s_wsum[w][0], b = s_wsum[w][1], c = s_wsum[w][2];
+    if (w < wv) {
+      inc_f += a;
+      inc_p += b;
+      inc_p2 += c;
+    }
+    tot_f += a;
+    tot_p += b;
+    tot_p2 += c;
+  }
+  const int num_full = tot_f;
   // Prefill span: rounds of items per compute unit (one workgroup each) at
   // span 1 and 2; span 2 when its rounds, each twice as long, take no longer.
   const int64_t cus = max(1, num_cus);
-  const int64_t rounds1 = ((int64_t)s_pre[kPlanThreads - 1] * Hkv + cus - 1) / cus;
-  const int64_t rounds2 = ((int64_t)s_pre2[kPlanThreads - 1] * Hkv + cus - 1) / cus;
+  const int64_t rounds1 = ((int64_t)tot_p * Hkv + cus - 1) / cus;
+  const int64_t rounds2 = ((int64_t)tot_p2 * Hkv + cus - 1) / cus;
   const int span = (rounds1 > 1 && 2 * rounds2 <= rounds1) ? 2 : 1;
-  const int num_pre = span == 2 ? s_pre2[kPlanThreads - 1] : s_pre[kPlanThreads - 1];
-  if (t == 0) {  // bucket start offsets in the decode tail region
-    int acc = num_full;
-    for (int k = 0; k < NBK; ++k) {
-      const int c = s_bucket[k];
-      s_bucket[k] = acc;
-      acc += c;
+  const int num_pre = span == 2 ? tot_p2 : tot_p;
+  if (wv == 0) {  // bucket start offsets in the decode tail region: a lane-parallel scan
+    static_assert(NBK == kWave + 1, "one bucket per lane plus the empty-item bucket");
+    const int c = s_bucket[lane];
+    int inc = c;
+    for (int off = 1; off < kWave; off <<= 1) {
+      const int v = __shfl_up(inc, off, kWave);
+      if (lane >= off) inc += v;
     }
+    s_bucket[lane] = num_full + inc - c;
+    if (lane == kWave - 1) s_bucket[kWave] = num_full + inc;
   }
   __syncthreads();
 
   // Writes.  Decode sequences (at most a few records each): every thread writes
   // its own.  Prefill sequences (hundreds of rows and records each): the wave
   // takes them one at a time, in each owner's order, and all 64 lanes write.
-  const int lane = t & (kWave - 1);
-  int od = s_full[t] - full;
+  int od = inc_f - full;
   for (int s = s0; s < s1; ++s) {
     const int c = per == 1 ? own_c : ctx_of(s);
     const int q = per == 1 ? own_q : rows_of(s);
@@ -145,7 +166,7 @@ __device__ __forceinline__ void plan_body(
       if ((per == 1 ? own_q : rows_of(s)) > 1) return s;
     return s1;
   };
-  int op = span == 2 ? s_pre2[t] - npre2 : s_pre[t] - npre;
+  int op = span == 2 ? inc_p2 - npre2 : inc_p - npre;
   int ps = next_prefill(s0);
   for (;;) {
     const unsigned long long pending = __ballot(ps < s1);
