@@ -8,7 +8,8 @@ path included:
      written into a pinned staging buffer (C++ allocator behind the C ABI);
   2. pkv_attention_decode_plan_upload on the compute stream: one launch builds
      the work list from the pinned lengths while its other workgroups copy the
-     pinned metadata to the device (no copy engine, no second stream: a
+     pinned slots and lengths, and the used entries of each table row, to the
+     device (no copy engine, no second stream: a
      cross-stream wait costs the stream ~11 us, a copy-engine transfer more),
      and others merge the previous step's partials (step 5 of that step);
   3. pkv_copy_blocks for any copy-on-write pairs (none for unshared batches);
@@ -447,14 +448,17 @@ def main():
     wss = [pkv.decode_workspace(S, Hq, D, max_ctx_bound) for _ in range(2)]
     scale = float(np.float32(1.0 / math.sqrt(D)))
 
-    # pinned staging: [slots S | lens S | tables S*MB] int32, two sets
-    meta_len = 2 * S + S * MB
+    # pinned staging: [slots S | lens S | pad to 16 bytes | tables S*MB] int32, two
+    # sets; the slots and lengths go up as bytes, the tables row by row (only
+    # the entries each context uses)
+    head = 2 * S + (-2 * S) % 4
+    meta_len = head + S * MB
     stage = [torch.empty(meta_len, dtype=torch.int32, pin_memory=True) for _ in range(2)]
     dmeta = [torch.empty(meta_len, dtype=torch.int32, device="cuda") for _ in range(2)]
     views = []
     for b in range(2):
         h = stage[b].numpy()
-        views.append((h[:S], h[S:2 * S], h[2 * S:].reshape(S, MB)))
+        views.append((h[:S], h[S:2 * S], h[head:].reshape(S, MB)))
     ones = np.ones(S, dtype=np.int32)
     main = torch.cuda.current_stream()
     h2d_done = [torch.cuda.Event() for _ in range(2)]   # the upload of staging set b has run
@@ -475,7 +479,7 @@ def main():
     main_h = main.cuda_stream
     dptr = [m.data_ptr() for m in dmeta]
     sptr = [st.data_ptr() for st in stage]
-    meta_bytes = meta_len * 4
+    head_bytes = head * 4
     ws_arg = [(w.data_ptr(), w.numel()) for w in wss]
     kc_p = [t.data_ptr() for t in kcs]
     vc_p = [t.data_ptr() for t in vcs]
@@ -486,7 +490,7 @@ def main():
 
     def attn_args(i, b, r, stream):
         d = dptr[b]
-        return (out_p, q0 + i * q_stride, kc_p[r], vc_p[r], d + 8 * S, d + 4 * S, scale, 16, Hq, Hkv,
+        return (out_p, q0 + i * q_stride, kc_p[r], vc_p[r], d + 4 * head, d + 4 * S, scale, 16, Hq, Hkv,
                 D, S, MB, nb, max_ctx_bound, dt, ws_arg[b][0], ws_arg[b][1], stream)
 
     # The merge of step i runs inside step i+1's upload + plan launch (the two
@@ -524,8 +528,8 @@ def main():
         # metadata upload + work list (+ that merge), one launch on the compute
         # stream; the lengths it plans from are the staging's, at offset S
         check("pkv_attention_decode_plan_upload", L.pkv_attention_decode_plan_upload(
-            *attn_args(i, b, r, None)[:-1], sptr[b] + 4 * S, sptr[b], dptr[b], meta_bytes, merge_out, merge_ws,
-            main_h))
+            *attn_args(i, b, r, None)[:-1], sptr[b] + 4 * S, sptr[b], dptr[b], head_bytes, sptr[b] + 4 * head,
+            merge_out, merge_ws, main_h))
         h2d_done[b].record(main)
         if len(pairs):
             pkv.pkv_copy_blocks(kcs[r], vcs[r], torch.from_numpy(pairs).cuda())

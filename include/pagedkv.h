@@ -157,6 +157,11 @@ int pkv_attention_decode_plan(void* out, const void* q, const void* key_cache,
  * launch.  Pointers are checked with the HIP runtime: PKV_EINVAL for pageable
  * or device memory where page-locked host memory is required, and the other
  * way round.  Other errors as pkv_attention_decode.
+ * host_block_tables (NULL, or page-locked [num_seqs, max_blocks_per_seq]): the
+ * launch also copies, for each sequence s, the first
+ * ceil(min(host_context_lens[s], max_context_len) / 16) entries of row s into
+ * block_tables (device); the entries after them are not sent (no launch reads
+ * them), so the upload region then only needs the rest of the metadata.
  * merge_out, merge_workspace (both NULL, or both given): the same launch also
  * runs _merge for the previous step -- one whose _partitions wrote its partials
  * to merge_workspace with the same shapes, max_context_len and workspace size,
@@ -172,7 +177,8 @@ int pkv_attention_decode_plan_upload(void* out, const void* q, const void* key_c
                                      int32_t num_blocks, int32_t max_context_len, pkv_dtype dt, void* workspace,
                                      size_t workspace_bytes, const int32_t* host_context_lens,
                                      const void* upload_src, void* upload_dst, size_t upload_bytes,
-                                     void* merge_out, const void* merge_workspace, void* stream);
+                                     const int32_t* host_block_tables, void* merge_out,
+                                     const void* merge_workspace, void* stream);
 int pkv_attention_decode_partitions(void* out, const void* q, const void* key_cache,
                                     const void* value_cache, const int32_t* block_tables,
                                     const int32_t* context_lens, float scale, int32_t block_size,

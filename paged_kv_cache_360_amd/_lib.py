@@ -41,7 +41,7 @@ SIGNATURES = {
                                                  _i32, _i32, _i32, _i32, ctypes.c_int, _p, _sz, _p]),
     "pkv_attention_decode_plan_upload": (ctypes.c_int, [_p, _p, _p, _p, _p, _p, _f32, _i32, _i32, _i32, _i32,
                                                         _i32, _i32, _i32, _i32, ctypes.c_int, _p, _sz, _p, _p,
-                                                        _p, _sz, _p, _p, _p]),
+                                                        _p, _sz, _p, _p, _p, _p]),
     "pkv_attention_decode_partitions": (ctypes.c_int, [_p, _p, _p, _p, _p, _p, _f32, _i32, _i32, _i32, _i32,
                                                        _i32, _i32, _i32, _i32, ctypes.c_int, _p, _sz, _p]),
     "pkv_attention_decode_merge": (ctypes.c_int, [_p, _p, _p, _p, _p, _p, _f32, _i32, _i32, _i32, _i32,

@@ -297,7 +297,8 @@ int pkv_attention_decode_plan_upload(void* out, const void* q, const void* key_c
                                      int32_t num_blocks, int32_t max_context_len, pkv_dtype dt, void* workspace,
                                      size_t workspace_bytes, const int32_t* host_context_lens,
                                      const void* upload_src, void* upload_dst, size_t upload_bytes,
-                                     void* merge_out, const void* merge_workspace, void* stream) {
+                                     const int32_t* host_block_tables, void* merge_out,
+                                     const void* merge_workspace, void* stream) {
   pkv::DecodeArgs a{};
   const char* who = "pkv_attention_decode_plan_upload";
   if (num_seqs <= 0) return fail(PKV_EINVAL, "pkv_attention_decode_plan_upload: num_seqs must be > 0");
@@ -319,6 +320,14 @@ int pkv_attention_decode_plan_upload(void* out, const void* q, const void* key_c
     if (!pkv::aligned16(src) || !pkv::aligned16(dst))
       return fail(PKV_EINVAL, "pkv_attention_decode_plan_upload: upload buffers must be 16-byte aligned");
   }
+  void* htab = nullptr;
+  if (host_block_tables != nullptr) {
+    const int64_t tab_bytes = (int64_t)num_seqs * max_blocks_per_seq * 4;
+    if (!pkv::host_mapped(host_block_tables, tab_bytes, &htab))
+      return fail(PKV_EINVAL, "pkv_attention_decode_plan_upload: host_block_tables must be page-locked host memory");
+    if (!pkv::device_readable(block_tables, tab_bytes))
+      return fail(PKV_EINVAL, "pkv_attention_decode_plan_upload: block_tables must be device memory");
+  }
   pkv::DecodeArgs prev{};
   const pkv::DecodeArgs* prev_p = nullptr;
   if (merge_out != nullptr || merge_workspace != nullptr) {
@@ -333,7 +342,8 @@ int pkv_attention_decode_plan_upload(void* out, const void* q, const void* key_c
     prev_p = &prev;
   }
   return pkv::launched(pkv::launch_upload_plan(a, static_cast<const int32_t*>(hctx), src, dst,
-                                               (int64_t)upload_bytes, prev_p, stream),
+                                               (int64_t)upload_bytes, static_cast<const int32_t*>(htab), prev_p,
+                                               stream),
                        who);
 }
 

@@ -223,7 +223,10 @@ constexpr int kMergeRowsPerBlock = kPlanThreads / kWave;
 // log-sum-exp merge of the previous step's partials.  Workgroup 0 builds the
 // work list from the host copy of the context lengths (read through its device
 // mapping); workgroups 1 .. n_up copy n16 16-byte words from src (host) to dst
-// (device); the rest merge one row per wave.  One launch on the compute stream
+// (device); the next ones copy, one table row per wave, the entries of each
+// sequence's block-table row that its (clamped) context uses, from a host table
+// to the device one (entries past them are never read, so they are not sent);
+// the rest merge one row per wave.  One launch on the compute stream
 // replaces a copy-engine transfer, a cross-stream wait and the merge launch:
 // the three parts are latency-bound and overlap.  The previous step's partials
 // and row counts live in another workspace than the one planned here.
@@ -232,6 +235,7 @@ __global__ __launch_bounds__(kPlanThreads) void upload_plan_kernel(
     const int32_t* __restrict__ host_ctx, int32_t S, int32_t ctx_cap, int32_t Hkv, int32_t dec_cap,
     int32_t num_cus, int32_t* __restrict__ sched, int4* __restrict__ dec, int32_t* __restrict__ row_slots,
     const uint4* __restrict__ src, uint4* __restrict__ dst, int64_t n16, int32_t n_up,
+    const int32_t* __restrict__ host_tables, int32_t* __restrict__ tables, int32_t MB, int32_t n_tab,
     void* __restrict__ m_out, const float* __restrict__ m_pm, const float* __restrict__ m_pl,
     const float* __restrict__ m_po, const int32_t* __restrict__ m_counts, int32_t Hq, int32_t m_max_parts,
     int64_t m_rows) {
@@ -254,7 +258,26 @@ __global__ __launch_bounds__(kPlanThreads) void upload_plan_kernel(
     }
     return;
   }
-  const int64_t row = (int64_t)(blockIdx.x - 1 - n_up) * kMergeRowsPerBlock + threadIdx.x / kWave;
+  if ((int)blockIdx.x <= n_up + n_tab) {
+    const int s = ((int)blockIdx.x - 1 - n_up) * kMergeRowsPerBlock + (int)threadIdx.x / kWave;
+    if (s >= S) return;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int c = max(0, min(host_ctx[s], ctx_cap));
+    const int n = min((c + kBlockTokens - 1) / kBlockTokens, MB);
+    const int32_t* from = host_tables + (int64_t)s * MB;
+    int32_t* to = tables + (int64_t)s * MB;
+    for (int base = lane; base < n; base += kWave * kUploadBatch) {
+      int32_t r[kUploadBatch];
+#pragma unroll
+      for (int u = 0; u < kUploadBatch; ++u)
+        if (base + u * kWave < n) r[u] = from[base + u * kWave];
+#pragma unroll
+      for (int u = 0; u < kUploadBatch; ++u)
+        if (base + u * kWave < n) to[base + u * kWave] = r[u];
+    }
+    return;
+  }
+  const int64_t row = (int64_t)(blockIdx.x - 1 - n_up - n_tab) * kMergeRowsPerBlock + threadIdx.x / kWave;
   if (row < m_rows)
     merge_row<BF16, D, true>(row, threadIdx.x & (kWave - 1), m_out, m_pm, m_pl, m_po, m_counts, Hq, m_max_parts);
 }
@@ -277,7 +300,7 @@ int launch_plan(const DecodeArgs& a, void* stream) {
 }
 
 int launch_upload_plan(const DecodeArgs& a, const int32_t* host_ctx, const void* src, void* dst,
-                       int64_t bytes, const DecodeArgs* prev, void* stream) {
+                       int64_t bytes, const int32_t* host_tables, const DecodeArgs* prev, void* stream) {
   const DecodeParams p = make_params(a);
   const int64_t n16 = bytes / 16;
   // copy workgroups: enough 16-byte loads in flight to cover the host link's latency
@@ -288,14 +311,17 @@ int launch_upload_plan(const DecodeArgs& a, const int32_t* host_ctx, const void*
   const int64_t m_rows = merge ? (int64_t)prev->num_tokens * prev->num_q_heads : 0;
   const int64_t n_mg = (m_rows + kMergeRowsPerBlock - 1) / kMergeRowsPerBlock;
   const DecodeArgs& m = merge ? *prev : a;
-  const dim3 grid((unsigned)(1 + n_up + n_mg));
+  // table rows, one per wave
+  const int n_tab = host_tables ? (a.num_seqs + kMergeRowsPerBlock - 1) / kMergeRowsPerBlock : 0;
+  const dim3 grid((unsigned)(1 + n_up + n_tab + n_mg));
   const bool bf16 = merge ? prev->bf16 : a.bf16;
   const int D = merge ? prev->head_dim : a.head_dim;
 #define PKV_UPLOAD_PLAN_LAUNCH(B, DD)                                                                   \
   hipLaunchKernelGGL((upload_plan_kernel<B, DD>), grid, dim3(kPlanThreads), 0, (hipStream_t)stream, host_ctx, \
                      a.num_seqs, p.ctx_cap, a.num_kv_heads, a.dec_cap, a.num_cus, a.sched,              \
                      reinterpret_cast<int4*>(a.dec_recs), a.row_slots, reinterpret_cast<const uint4*>(src), \
-                     reinterpret_cast<uint4*>(dst), n16, n_up, m.out, m.part_m, m.part_l, m.part_o,       \
+                     reinterpret_cast<uint4*>(dst), n16, n_up, host_tables, const_cast<int32_t*>(a.tables), \
+                     a.max_blocks, n_tab, m.out, m.part_m, m.part_l, m.part_o,                            \
                      m.row_slots, m.num_q_heads, m.max_parts, m_rows)
   if (bf16) {
     if (D == 64) PKV_UPLOAD_PLAN_LAUNCH(true, 64); else PKV_UPLOAD_PLAN_LAUNCH(true, 128);

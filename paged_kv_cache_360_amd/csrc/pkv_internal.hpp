@@ -70,11 +70,13 @@ inline int32_t prefill_rows_per_item(int32_t G) { return 256 / G; }
 int launch_plan(const DecodeArgs& a, void* stream);
 // Decode plan from a page-locked host copy of the context lengths (host_ctx,
 // its device address), fused with a copy of `bytes` (a multiple of 16) from
-// page-locked host memory src to device memory dst (device addresses) and, when
-// prev is given, with the merge of the partials in prev's workspace into
-// prev->out (a previous step of the same shapes, another workspace).
+// page-locked host memory src to device memory dst (device addresses), with
+// the copy of the used entries of each row of the page-locked host_tables
+// (device address; null: none) into a.tables, and, when prev is given, with the
+// merge of the partials in prev's workspace into prev->out (a previous step of
+// the same shapes, another workspace).
 int launch_upload_plan(const DecodeArgs& a, const int32_t* host_ctx, const void* src, void* dst,
-                       int64_t bytes, const DecodeArgs* prev, void* stream);
+                       int64_t bytes, const int32_t* host_tables, const DecodeArgs* prev, void* stream);
 // Chunked-prefill rows (sequences with more than one query row), bf16 only.
 int launch_prefill(const DecodeArgs& a, void* stream);
 

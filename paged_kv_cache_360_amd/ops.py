@@ -103,13 +103,21 @@ def pkv_attention_decode_plan(out, q, key_cache, value_cache, block_tables, cont
 
 def pkv_attention_decode_plan_upload(out, q, key_cache, value_cache, block_tables, context_lens, scale,
                                      max_context_len, host_context_lens, upload_src, upload_dst,
-                                     workspace=None, merge_out=None, merge_workspace=None, stream=None):
+                                     workspace=None, merge_out=None, merge_workspace=None,
+                                     host_block_tables=None, stream=None):
     """``_plan`` from a pinned host copy of the lengths, fused with the copy of the
     pinned ``upload_src`` into the device tensor ``upload_dst`` (same byte size),
     in one launch.  ``block_tables`` / ``context_lens`` are the device tensors the
     later launches read (usually views of ``upload_dst``).  With ``merge_out`` and
     ``merge_workspace``, the launch also merges the previous step's partials
-    (same shapes, another workspace) into ``merge_out``."""
+    (same shapes, another workspace) into ``merge_out``.  With
+    ``host_block_tables`` (pinned, [S, MB]), it also copies each row's used
+    entries into ``block_tables``."""
+    if host_block_tables is not None:
+        if host_block_tables.is_cuda or not host_block_tables.is_pinned() or not host_block_tables.is_contiguous():
+            raise TypeError("host_block_tables must be a contiguous pinned host tensor")
+        if host_block_tables.dtype != torch.int32 or tuple(host_block_tables.shape) != tuple(block_tables.shape):
+            raise ValueError("host_block_tables must be int32 of block_tables' shape")
     if (merge_out is None) != (merge_workspace is None):
         raise ValueError("give both merge_out and merge_workspace, or neither")
     for name, t in (("host_context_lens", host_context_lens), ("upload_src", upload_src)):
@@ -135,6 +143,7 @@ def pkv_attention_decode_plan_upload(out, q, key_cache, value_cache, block_table
         _dev(block_tables, "block_tables", torch.int32), _dev(context_lens, "context_lens", torch.int32),
         float(scale), bs, hq, hkv, d, s, block_tables.shape[1], nb, int(max_context_len), _dt(q), ws_ptr,
         ws_bytes, host_context_lens.data_ptr(), upload_src.data_ptr(), _dev(upload_dst, "upload_dst"), nbytes,
+        None if host_block_tables is None else host_block_tables.data_ptr(),
         None if merge_out is None else _dev(merge_out, "merge_out"),
         None if merge_workspace is None else _dev(merge_workspace, "merge_workspace"), _stream(stream)))
     return out

@@ -194,12 +194,13 @@ def test_graph_and_plan_upload_argument_errors():
     assert g.value in (None, 0)
     assert L.pkv_decode_graph_launch(None, None) == PKV_EINVAL
     L.pkv_decode_graph_destroy(None)
-    # plan_upload: (decode args without stream) + host lens, src, dst, bytes, merge out, merge ws, stream
+    # plan_upload: (decode args without stream) + host lens, src, dst, bytes, host tables, merge out, merge ws,
+    # stream
     d = [FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0.125, 16, 8, 8, 64, 4, 8, 64, 100, PKV_F32, 0x100000, ws]
     pu = L.pkv_attention_decode_plan_upload
-    assert pu(*d[:11], 0, *d[12:], FAKE, FAKE, FAKE, 64, None, None, None) == PKV_EINVAL        # no sequences
-    assert pu(*d, FAKE, FAKE, FAKE, 60, None, None, None) == PKV_EINVAL                         # not 16-byte words
-    assert pu(*d[:7], 32, *d[8:], FAKE, FAKE, FAKE, 64, None, None, None) == PKV_EUNSUPPORTED   # block size
+    assert pu(*d[:11], 0, *d[12:], FAKE, FAKE, FAKE, 64, None, None, None, None) == PKV_EINVAL        # no sequences
+    assert pu(*d, FAKE, FAKE, FAKE, 60, None, None, None, None) == PKV_EINVAL                         # not 16-byte words
+    assert pu(*d[:7], 32, *d[8:], FAKE, FAKE, FAKE, 64, None, None, None, None) == PKV_EUNSUPPORTED   # block size
     assert L.pkv_check_pool(None, 64) == PKV_EINVAL and L.pkv_check_pool(FAKE, 0) == PKV_EINVAL
 
 

@@ -27,15 +27,19 @@ pkv = pytest.importorskip("paged_kv_cache_360_amd") if torch.cuda.is_available()
 
 @pytest.mark.parametrize("append", [False, True])
 @pytest.mark.parametrize("fuse_merge", [False, True])
-def test_plan_upload_equals_copy_then_plan(append, fuse_merge):
+@pytest.mark.parametrize("ragged", [False, True])
+def test_plan_upload_equals_copy_then_plan(append, fuse_merge, ragged):
     """Two decode steps through _plan_upload + _partitions (+ _merge): with
     fuse_merge, step 1's upload launch also merges step 0's partials (the
-    workspaces alternate), and step 1 is merged by a plain _merge afterwards."""
+    workspaces alternate), and step 1 is merged by a plain _merge afterwards.
+    With ragged, the tables go up row by row (only the entries each context
+    uses; the rest of the device table stays poisoned) and the byte upload
+    carries the slots and lengths only."""
     S, Hq, Hkv, D = 40, 32, 8, 128
     rng = np.random.default_rng(17)
     MB = 200
     nb = 40 * 200 + 16
-    say(f"plan_upload append={append} fuse_merge={fuse_merge} S={S} MB={MB}")
+    say(f"plan_upload append={append} fuse_merge={fuse_merge} ragged={ragged} S={S} MB={MB}")
     kc = dev(normal_values_parallel(5, (nb, 16, Hkv, D), "bf16"))
     vc = dev(normal_values_parallel(6, (nb, 16, Hkv, D), "bf16"))
     scale = np.float32(1.0 / math.sqrt(D))
@@ -72,8 +76,13 @@ def test_plan_upload_equals_copy_then_plan(append, fuse_merge):
         merge_kw = {}
         if fuse_merge and step > 0:
             merge_kw = dict(merge_out=outs[-1], merge_workspace=wss[(step - 1) % 2])
-        pkv.pkv_attention_decode_plan_upload(out, q, kc1, vc1, d_tab, d_lens, float(scale), bound, host_lens,
-                                             stage, dmeta, workspace=ws, **merge_kw)
+        if ragged:
+            merge_kw["host_block_tables"] = stage[2 * S:].view(S, MB)
+            pkv.pkv_attention_decode_plan_upload(out, q, kc1, vc1, d_tab, d_lens, float(scale), bound, host_lens,
+                                                 stage[:2 * S], dmeta[:2 * S], workspace=ws, **merge_kw)
+        else:
+            pkv.pkv_attention_decode_plan_upload(out, q, kc1, vc1, d_tab, d_lens, float(scale), bound, host_lens,
+                                                 stage, dmeta, workspace=ws, **merge_kw)
         if append:
             pkv.pkv_attention_decode_partitions_append(out, q, kn, vn, kc1, vc1, d_tab, d_lens, float(scale),
                                                        bound, workspace=ws)
@@ -96,7 +105,15 @@ def test_plan_upload_equals_copy_then_plan(append, fuse_merge):
     torch.cuda.synchronize()
     for step in range(2):
         dmeta, stage, q, tables, ctx = metas[step]
-        assert host(dmeta).tobytes() == stage.numpy().tobytes(), f"step {step}: device metadata differs"
+        got, want = host(dmeta), stage.numpy()
+        if ragged:                                   # slots, lengths, and the used part of each table row
+            assert got[:2 * S].tobytes() == want[:2 * S].tobytes(), f"step {step}: slots / lengths differ"
+            gt, wt = got[2 * S:].reshape(S, MB), want[2 * S:].reshape(S, MB)
+            for s in range(S):
+                n = -(-int(ctx[s]) // 16)
+                assert np.array_equal(gt[s, :n], wt[s, :n]) and np.all(gt[s, n:] == -7), (step, s)
+        else:
+            assert got.tobytes() == want.tobytes(), f"step {step}: device metadata differs"
         assert host(outs[step]).tobytes() == host(refs[step]).tobytes(), f"step {step}: output differs"
         idx = np.unique(np.concatenate([[0], np.argsort(ctx)[-2:], rng.choice(S, 4, replace=False)]))
         ref = oracle.decode_attention(host(q)[idx], snaps[step][0], snaps[step][1], tables[idx], ctx[idx], scale)
@@ -118,7 +135,7 @@ def test_plan_upload_rejects_wrong_memory_kinds():
     base = (z(S, Hq, D).data_ptr(), z(S, Hq, D).data_ptr(), kc.data_ptr(), kc.data_ptr(), tab.data_ptr(),
             lens.data_ptr(), 0.125, 16, Hq, Hkv, D, S, 4, 8, 64, 0, ws.data_ptr(), ws.numel())
     dst = z(16, dt=torch.int32)
-    nm = (None, None)                              # no merge of a previous step
+    nm = (None, None, None)                        # no host tables, no merge of a previous step
     # host lengths in pageable memory, then in device memory
     assert L.pkv_attention_decode_plan_upload(*base, pageable.ctypes.data, pinned.data_ptr(), dst.data_ptr(), 64,
                                               *nm, None) != 0
@@ -127,7 +144,15 @@ def test_plan_upload_rejects_wrong_memory_kinds():
     # merging into the workspace being planned
     out_m = z(S, Hq, D)
     assert L.pkv_attention_decode_plan_upload(*base, pinned.data_ptr(), pinned.data_ptr(), dst.data_ptr(), 64,
-                                              out_m.data_ptr(), ws.data_ptr(), None) != 0
+                                              None, out_m.data_ptr(), ws.data_ptr(), None) != 0
+    # host tables in pageable memory, and device tables that are not device memory
+    big = torch.zeros(S * 4, dtype=torch.int32, pin_memory=True)
+    assert L.pkv_attention_decode_plan_upload(*base, pinned.data_ptr(), pinned.data_ptr(), dst.data_ptr(), 64,
+                                              np.zeros(S * 4, np.int32).ctypes.data, None, None, None) != 0
+    base_h = list(base)
+    base_h[4] = big.data_ptr()
+    assert L.pkv_attention_decode_plan_upload(*base_h, pinned.data_ptr(), pinned.data_ptr(), dst.data_ptr(), 64,
+                                              big.data_ptr(), None, None, None) != 0
     # source pageable; destination pinned instead of device; size not a multiple of 16
     assert L.pkv_attention_decode_plan_upload(*base, pinned.data_ptr(), pageable.ctypes.data, dst.data_ptr(),
                                               64, *nm, None) != 0
@@ -141,7 +166,8 @@ def test_bench_launch_sequence_full_size():
     """The decode loop bench.py times, at its full size (128 sequences, GQA 32/8,
     head_dim 128, contexts log-uniform in [512, 8192], 4 steps of growth by one
     token, tables from the C++ allocator with a shuffled pool): per step,
-    _plan_upload (pinned staging, merging the previous step, alternating
+    _plan_upload (pinned staging: slots and lengths as bytes, the used entries
+    of each table row by rows; merging the previous step; alternating
     workspaces) then _partitions_append; a plain _merge after the last step.
     Every step's output and the final cache equal the one-call append form run
     step by step on a copy of the pool, byte for byte; sampled rows of the last
@@ -184,7 +210,8 @@ def test_bench_launch_sequence_full_size():
         d_lens, d_tab = dmeta[b][S:2 * S], dmeta[b][2 * S:2 * S + S * MB].view(S, MB)
         merge_kw = dict(merge_out=out[i - 1], merge_workspace=wss[1 - b]) if i > 0 else {}
         pkv.pkv_attention_decode_plan_upload(out[i], q, kc, vc, d_tab, d_lens, scale, bound, stage[b][S:2 * S],
-                                             stage[b], dmeta[b], workspace=wss[b], **merge_kw)
+                                             stage[b][:2 * S], dmeta[b][:2 * S], workspace=wss[b],
+                                             host_block_tables=stage[b][2 * S:2 * S + S * MB].view(S, MB), **merge_kw)
         pkv.pkv_attention_decode_partitions_append(out[i], q, kn, vn, kc, vc, d_tab, d_lens, scale, bound,
                                                    workspace=wss[b])
         ref = torch.zeros_like(out[i])
