@@ -309,3 +309,40 @@ def test_three_call_form_equals_one_call():
     pkv.pkv_attention_decode_merge(out, q, kc, vc, tables, ctx, float(inp["scale"]), mx, workspace=ws)
     torch.cuda.synchronize()
     assert host(out).tobytes() == ref.tobytes()
+
+
+def test_decode_more_sequences_than_plan_threads():
+    """2500 sequences (more than the plan workgroup's 1024 threads, so each
+    thread plans several), contexts 1..1200: sampled rows against the oracle,
+    and the fused upload + plan launch (row-wise tables from pinned memory)
+    gives the same bytes as the one-call decode."""
+    rng = np.random.default_rng(77)
+    S, Hq, Hkv, D = 2500, 8, 2, 64
+    ctx = rng.integers(1, 1201, size=S).astype(np.int32)
+    say(f"decode S={S} ctx 1..1200 (plan threads handle several sequences)")
+    inp = explicit_case(78, "bf16", Hq, Hkv, D, ctx)
+    got_t = gpu_decode(inp)
+    got = host_f64(got_t)
+    idx = np.unique(np.concatenate([np.argsort(ctx)[:3], np.argsort(ctx)[-3:], rng.choice(S, 34, replace=False)]))
+    assert_close(got[idx], oracle_decode(inp, idx), "bf16", "decode S=2500")
+    # the same step through the fused upload + plan launch
+    tables = inp["block_tables"]
+    MB = tables.shape[1]
+    bound = int(ctx.max())
+    stage_t = torch.from_numpy(np.ascontiguousarray(tables)).pin_memory()
+    lens_h = torch.from_numpy(ctx.copy()).pin_memory()
+    dummy = torch.zeros(4, dtype=torch.int32).pin_memory()
+    d_tab = torch.full((S, MB), -5, dtype=torch.int32, device="cuda")
+    d_lens = torch.zeros(S, dtype=torch.int32, device="cuda")
+    d_dummy = torch.zeros(4, dtype=torch.int32, device="cuda")
+    q, kc, vc = dev(inp["q"]), dev(inp["key_cache"]), dev(inp["value_cache"])
+    out = torch.empty_like(q)
+    ws = pkv.decode_workspace(S, Hq, D, bound)
+    scale = float(inp["scale"])
+    d_lens.copy_(dev(ctx))
+    pkv.pkv_attention_decode_plan_upload(out, q, kc, vc, d_tab, d_lens, scale, bound, lens_h, dummy, d_dummy,
+                                         workspace=ws, host_block_tables=stage_t)
+    pkv.pkv_attention_decode_partitions(out, q, kc, vc, d_tab, d_lens, scale, bound, workspace=ws)
+    pkv.pkv_attention_decode_merge(out, q, kc, vc, d_tab, d_lens, scale, bound, workspace=ws)
+    torch.cuda.synchronize()
+    assert host(out).tobytes() == host(got_t).tobytes()
