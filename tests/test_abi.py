@@ -31,6 +31,22 @@ def declared_functions():
     return sorted(names)
 
 
+def test_header_is_plain_c():
+    """include/*.h compiles as C99 and as C++17 on its own: no C++ or torch types cross the ABI."""
+    import shutil
+    import subprocess
+    for fn in sorted(os.listdir(os.path.join(ROOT, "include"))):
+        if not fn.endswith(".h"):
+            continue
+        path = os.path.join(ROOT, "include", fn)
+        for cc, std, lang in (("gcc", "-std=c99", "c"), ("g++", "-std=c++17", "c++")):
+            if shutil.which(cc) is None:
+                pytest.skip(f"{cc} not available")
+            r = subprocess.run([cc, std, "-Wall", "-Wextra", "-Werror", "-fsyntax-only", "-x", lang, path],
+                               capture_output=True, text=True)
+            assert r.returncode == 0, f"{fn} as {lang}: {r.stderr}"
+
+
 def test_library_exports_every_declared_symbol():
     names = declared_functions()
     assert len(names) >= 20
