@@ -25,21 +25,25 @@ pytestmark = pytest.mark.gpu
 pkv = pytest.importorskip("paged_kv_cache_360_amd") if torch.cuda.is_available() else None
 
 
-def test_prefix_shared_equals_duplicated():
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_prefix_shared_equals_duplicated(dtype):
+    """The prefix-shared batch at full size; f32 is the tight structural
+    variant of the same shapes (the vector-ALU kernel, 1e-5 row-relative)."""
     spec = SPECS["prefix1500_gqa32x8_bf16_s256_tail8_512"]
     S, Hq, Hkv, D, P = spec.num_seqs, spec.num_q_heads, spec.num_kv_heads, spec.head_dim, spec.prefix_len
-    say(f"prefix-shared decode S={S} prefix={P}")
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    say(f"prefix-shared decode S={S} prefix={P} {dtype}")
     rng = np.random.default_rng(1003)
     tails = rng.integers(spec.ctx_lo, spec.ctx_hi + 1, size=S).astype(np.int32)
     total = P + tails
     mb = spec.max_blocks_per_seq
     need_shared = 93 + int(np.sum(-(-total // 16) - 93))
     nb = int(math.ceil(1.25 * need_shared))
-    k_pre = normal_values_parallel(31, (P, Hkv, D), "bf16")
-    v_pre = normal_values_parallel(32, (P, Hkv, D), "bf16")
-    k_tail = normal_values_parallel(33, (int(tails.sum()), Hkv, D), "bf16")
-    v_tail = normal_values_parallel(34, (int(tails.sum()), Hkv, D), "bf16")
-    q = normal_values_parallel(35, (S, Hq, D), "bf16")
+    k_pre = normal_values_parallel(31, (P, Hkv, D), dtype)
+    v_pre = normal_values_parallel(32, (P, Hkv, D), dtype)
+    k_tail = normal_values_parallel(33, (int(tails.sum()), Hkv, D), dtype)
+    v_tail = normal_values_parallel(34, (int(tails.sum()), Hkv, D), dtype)
+    q = normal_values_parallel(35, (S, Hq, D), dtype)
     scale = np.float32(1.0 / math.sqrt(D))
     ids = np.arange(S, dtype=np.int64)
 
@@ -53,7 +57,7 @@ def test_prefix_shared_equals_duplicated():
     shared_blocks = alloc.block_table(0)
     assert len(shared_blocks) == 94
     assert all(alloc.refcount(b) == S for b in shared_blocks)
-    kc = torch.zeros((nb, 16, Hkv, D), dtype=torch.bfloat16, device="cuda")
+    kc = torch.zeros((nb, 16, Hkv, D), dtype=tdt, device="cuda")
     vc = torch.zeros_like(kc)
     pkv.pkv_write(kc, vc, dev(k_pre), dev(v_pre), dev(np.array(pre_slots, np.int32)))
     slots, pairs = alloc.append_batch(ids, tails)
@@ -63,14 +67,14 @@ def test_prefix_shared_equals_duplicated():
     pkv.pkv_write(kc, vc, dev(k_tail), dev(v_tail), dev(slots))
     tables, lens = alloc.block_tables(ids, mb)
     assert np.array_equal(lens, total)
-    out_shared = torch.empty((S, Hq, D), dtype=torch.bfloat16, device="cuda")
+    out_shared = torch.empty((S, Hq, D), dtype=tdt, device="cuda")
     pkv.pkv_attention_decode(out_shared, dev(q), kc, vc, dev(tables), dev(lens), float(scale),
                              int(lens.max()))
 
     # ---- duplicated pool: every sequence writes its own copy of the prefix
     nb2 = int(np.sum(-(-total // 16))) + 8
     alloc2 = pkv.BlockAllocator(nb2, 16, shuffle_seed=78)
-    kc2 = torch.zeros((nb2, 16, Hkv, D), dtype=torch.bfloat16, device="cuda")
+    kc2 = torch.zeros((nb2, 16, Hkv, D), dtype=tdt, device="cuda")
     vc2 = torch.zeros_like(kc2)
     all_slots, k_log, v_log = [], [], []
     off = 0
@@ -96,7 +100,7 @@ def test_prefix_shared_equals_duplicated():
                                     rng.choice(S, 6, replace=False)]))
     kh, vh = host(kc), host(vc)
     ref = oracle.decode_attention(q[idx], kh, vh, tables[idx], lens[idx], scale)
-    assert_close(host_f64(out_shared)[idx], ref, "bf16", "prefix-shared")
+    assert_close(host_f64(out_shared)[idx], ref, dtype, f"prefix-shared {dtype}")
     # the logical K/V the shared pool holds equals what was written
     for s in idx[:3]:
         Kl, Vl = oracle.gather_kv(kh, vh, tables[s], int(lens[s]))
