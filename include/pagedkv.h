@@ -16,11 +16,15 @@
  *    per-block results ("vLLM and PagedAttention", §2 "Reworking the Attention
  *    Computation"; "vLLM — PagedAttention and Continuous Batching", §2.4).
  *  - Copy-on-write sharing of prefix blocks ("vLLM and PagedAttention", §2 bullets;
- *    "How vLLM Works?", section 03).
+ *    "How vLLM Works?", section 03), automatic prefix caching ("How vLLM
+ *    Works?", section 05), chunked prefill batched with decode ("How vLLM
+ *    Works?", section 04), preemption by swapping blocks to host memory ("vLLM
+ *    and PagedAttention", §3), and a decode step captured as one graph ("vLLM
+ *    and PagedAttention", §6).
  *
  * Conventions for every call below:
  *  - Device buffers are allocated and owned by the caller; the library keeps no
- *    device memory.  Pointers named "device" must be device-accessible, 16-byte
+ *    device memory (a graph handle holds only the HIP runtime's graph objects).  Pointers named "device" must be device-accessible, 16-byte
  *    aligned and contiguous in the stated layout.
  *  - Calls only enqueue work on `stream` (a hipStream_t; NULL = the null stream)
  *    and never synchronize.
