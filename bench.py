@@ -50,6 +50,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_partitions_traffic.json")
 KERNEL_SOURCES = ["paged_kv_cache_360_amd/csrc/kernels/decode_mfma.hip",
                   "paged_kv_cache_360_amd/csrc/kernels/decode_common.hpp",
                   "paged_kv_cache_360_amd/csrc/kernels/device_common.hpp"]
+MFMA_BF16_PEAK_TFLOPS = 2500.0          # MI355X dense bf16 matrix peak
 COPY_PROBE_BYTES = 512 * 1024 * 1024   # pkv_copy_blocks in --copy-probe: read and written per launch
 
 
@@ -804,6 +805,28 @@ def mixed_main(args, spec):
         b += 2 * (int(nparts[nparts > 1].sum()) + int(pc[pc > 1].sum())) * Hq * (D + 2) * 4
         att_b.append(b)
     ta = float(np.mean(t_attn))
+
+    # The chunk alone (after the timed region): the same varlen call over
+    # sequence 0's 512 rows only, so its time is the prefill tiles' (plus the
+    # plan and merge launches around them), against the dense bf16 peak.
+    tab0, len0 = alloc.block_tables(ids[:1], MB)
+    t0_d = torch.from_numpy(tab0).cuda()
+    c0_d = torch.tensor([CC], dtype=torch.int32, device="cuda")
+    qsl0 = torch.tensor([0, C], dtype=torch.int32, device="cuda")
+    q0_d = qs[n_steps - 1, :C].contiguous()
+    out0 = torch.empty((C, Hq, D), dtype=tdt, device="cuda")
+    ws0 = pkv.varlen_workspace(1, C, Hq, Hkv, D, C, CC)
+    chunk_call = lambda: pkv.pkv_attention_varlen(out0, q0_d, kcs[0], vcs[0], t0_d, c0_d, qsl0, scale, C, CC,
+                                                  workspace=ws0)
+    for _ in range(3):
+        chunk_call()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(10):
+        chunk_call()
+    e1.record()
+    torch.cuda.synchronize()
+    t_chunk = e0.elapsed_time(e1) * 1e-3 / 10
     res = {
         "metric": "mixed chunked-prefill step: query rows/s (prefill chunk + decode rows), bf16 GQA",
         "value": round(T * K / wall, 1),
@@ -825,6 +848,12 @@ def mixed_main(args, spec):
             "peak": HBM_PEAK_GBPS, "unit": "GB/s",
             "frac": round(float(np.mean(att_b)) / ta / 1e9 / HBM_PEAK_GBPS, 4), "traffic": None,
             "algorithmic_bytes_per_launch": int(np.mean(att_b)), "avg_launch_us": round(ta * 1e6, 2),
+        },
+        "roofline_prefill": {
+            "kernel": "pkv_attention_varlen over the chunk alone (plan + prefill tiles + merge; 10 calls)",
+            "bound": "mfma", "achieved": round(flops_prefill / t_chunk / 1e12, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s", "frac": round(flops_prefill / t_chunk / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+            "flops_per_launch": int(flops_prefill), "avg_launch_us": round(t_chunk * 1e6, 2),
         },
         "cpu_baseline": None,
     }
