@@ -77,6 +77,14 @@ constexpr int kColTiles = 8 / kPrefillWaves;   // 32-column tiles per wave
 #define PKV_PREFILL_STEPS 2
 #endif
 constexpr int kPrefillSteps = PKV_PREFILL_STEPS;  // steps of K/V in flight
+// Barrier interval: two steps (five LDS buffers; steps q .. q+2 are read
+// while q+3 and q+4 are staged), or one step (three buffers).  Two let the
+// waves of a SIMD drift apart within the interval (~1% faster).
+#ifndef PKV_PREFILL_PAIRS
+#define PKV_PREFILL_PAIRS 1
+#endif
+constexpr bool kPrefillPairs = PKV_PREFILL_PAIRS != 0;
+constexpr int kPrefillBufs = kPrefillPairs ? 5 : 3;
 
 // One thread's piece of a block row: D / 8 bytes.
 template <int D> struct KVPiece;
@@ -130,10 +138,10 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void prefill_mfma_kernel(Decode
   const int total = min(p.sched[3], p.pre_cap * p.Hkv);
   const int grid = (int)gridDim.x;
 
-  // [buffer][32 rows x row stride]: three buffers, step q in q % 3 (the
+  // [buffer][32 rows x row stride]: step q in buffer q % kPrefillBufs (the
   // scores of step q + 1 are computed while step q's values are)
-  __shared__ __attribute__((aligned(16))) char s_k[3][kStepTokens * RSK];
-  __shared__ __attribute__((aligned(16))) char s_v[3][kStepTokens * RSV];
+  __shared__ __attribute__((aligned(16))) char s_k[kPrefillBufs][kStepTokens * RSK];
+  __shared__ __attribute__((aligned(16))) char s_v[kPrefillBufs][kStepTokens * RSV];
   __shared__ int s_ticket[2];
 
   using TablePtr = const __attribute__((address_space(4))) int*;
@@ -167,7 +175,9 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void prefill_mfma_kernel(Decode
     // on stage slot 0, and to at least 2*NS so that the load stream (NS + 2
     // steps ahead of the computation) never runs past the next item; padding
     // steps load nothing and compute nothing
-    it.nsteps = max(2 * NS, (max(1, (it.nblk + 1) / 2) + NS - 1) / NS * NS);
+    // (with two steps per barrier the stream runs up to 6 steps ahead of the
+    // pair being computed, so an item has at least 6)
+    it.nsteps = max(kPrefillPairs ? 6 : 2 * NS, (max(1, (it.nblk + 1) / 2) + NS - 1) / NS * NS);
     it.trow = (TablePtr)(const void*)(p.tables + (int64_t)it.s * p.MB + it.b_begin);
   };
   // q operands (B of the scores) of this wave's columns; rows past the item read
@@ -467,11 +477,13 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void prefill_mfma_kernel(Decode
     if (pf_ok) pf_ids = ids_at(cs);
   };
 
-  // Step q is staged into LDS at iteration q - 2 (from the registers its loads
-  // landed in, NS steps after they were issued), its scores are computed at
-  // iteration q - 1 while step q - 1's softmax and values run, and its own
-  // softmax and values at iteration q: one barrier per iteration.
+  // One step per barrier: step q is staged into LDS at iteration q - 2 (from
+  // the registers its loads landed in, NS steps after they were issued), its
+  // scores are computed at iteration q - 1 while step q - 1's softmax and
+  // values run, and its own softmax and values at iteration q.  Two steps per
+  // barrier: steps q + 3 and q + 4 are staged while the pair q, q + 1 runs.
   static_assert(NS % 2 == 0, "step q's scores sit in sc[q % 2]: the unrolled loop keeps the parity");
+  static_assert(!kPrefillPairs || NS == 2, "two steps per barrier: step s's loads sit in stg[s % 2]");
   Stage stg[NS];
 #pragma unroll
   for (int u = 0; u < NS; ++u) issue_next(stg[u]);
@@ -479,6 +491,10 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void prefill_mfma_kernel(Decode
   for (int u = 0; u < NS; ++u) {
     stage_to_lds(stg[u], u);
     issue_next(stg[u]);
+  }
+  if (kPrefillPairs) {  // steps 0 .. 2 in LDS, 3 and 4 in flight
+    stage_to_lds(stg[0], 2);
+    issue_next(stg[0]);
   }
   __syncthreads();
   int buf = 0, tpar = 0;  // LDS buffer of step 0 of cur
@@ -488,6 +504,26 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void prefill_mfma_kernel(Decode
     if (tid == 0) fetched = atomicAdd(&p.sched[2], 1);  // offset added where it is read
     begin_item(cur);
     if (cur.nblk > 0) scores(buf, sc[0]);
+#if PKV_PREFILL_PAIRS
+    // Two steps per barrier: buffers rotate over five; step q in (buf + q) % 5
+    // relative to the pair.  Steps q + 1 and q + 2 were staged in the previous
+    // interval; q + 3 and q + 4 go into the buffers of q - 2 and q - 1, read
+    // last before the previous barrier.
+    auto rot = [](int b, int k) { return b + k >= kPrefillBufs ? b + k - kPrefillBufs : b + k; };
+    for (int q = 0; q < cur.nsteps; q += 2) {
+      const int b1 = rot(buf, 1), b2 = rot(buf, 2);
+      stage_to_lds(stg[1], rot(buf, 3));  // step q + 3 (odd)
+      issue_next(stg[1]);                 // step q + 5
+      stage_to_lds(stg[0], rot(buf, 4));  // step q + 4
+      issue_next(stg[0]);                 // step q + 6
+      if (q + 2 == cur.nsteps && tid == 0) s_ticket[tpar] = fetched;
+      const int t0 = (cur.b_begin + 2 * q) * kBlockTokens;
+      if (2 * q < cur.nblk) softmax_values(sc[0], buf, t0, b1, sc[1]);
+      if (2 * q + 2 < cur.nblk) softmax_values(sc[1], b1, t0 + kStepTokens, b2, sc[0]);
+      __syncthreads();
+      buf = b2;
+    }
+#else
     for (int q0 = 0; q0 < cur.nsteps; q0 += NS) {
 #pragma unroll
       for (int u = 0; u < NS; ++u) {
@@ -509,6 +545,7 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void prefill_mfma_kernel(Decode
         buf = b1;
       }
     }
+#endif
     // Switch to n1.  Its q was loaded at the start of this item; the empty asm
     // makes the wait for those loads happen here, once, before the output
     // stores are in flight (left to the compiler, it lands before the score
