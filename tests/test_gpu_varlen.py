@@ -104,6 +104,22 @@ def test_varlen_many_short_chunks():
     assert_close(got, oracle_varlen(inp), "bf16", "short chunks")
 
 
+def test_varlen_runs_of_padded_items():
+    """Chunks over contexts of 150 .. 600 keys: prefill items of about 5 to 19
+    two-block steps (padded to an even count of at least six), several
+    per persistent workgroup, so that the key stream runs from one short item into
+    the next again and again; some rows cross the 512-key partition edge."""
+    rng = np.random.default_rng(71)
+    n = 200
+    qlens = rng.integers(2, 41, n)
+    qlens[rng.random(n) < 0.15] = 1
+    ctxs = np.maximum(qlens, rng.integers(150, 601, n))
+    say(f"varlen runs of padded items: {n} seqs, {int(qlens.sum())} rows")
+    inp = mixed_case(71, 32, 8, 128, qlens, ctxs)
+    got = host_f64(gpu_varlen(inp))
+    assert_close(got, oracle_varlen(inp), "bf16", "padded items")
+
+
 def prefill_span(qlens, ctxs, G, Hkv, cus):
     """The plan's span rule restated: prefill items cover two partitions when the
     rounds of items per compute unit at span 2 are at most half those at span 1."""
