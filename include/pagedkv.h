@@ -108,6 +108,8 @@ int pkv_write(void* key_cache, void* value_cache, const void* k, const void* v,
  *                        (larger values are clamped, never faulted on)
  *   max_context_len      host-known bound on context_lens (no device sync);
  *                        must be <= max_blocks_per_seq * 16
+ *   scale                softmax scale (e.g. 1/sqrt(head_dim)); finite and > 0,
+ *                        else PKV_EINVAL (every attention call below checks this)
  *   workspace            device, >= pkv_decode_workspace_bytes(...) bytes, 256-byte
  *                        aligned.  Scratch only: a work list the call builds on the
  *                        device from context_lens, and the partition partials.

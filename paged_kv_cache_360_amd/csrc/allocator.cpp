@@ -19,8 +19,10 @@
 // cached.  A cached block whose last user is released is kept on a released
 // list and revived by a later hit; when no free block is left, allocation takes
 // over the least recently released one (a sequence's blocks go on that list
-// from its last to its first).  Keys are looked up by a 64-bit hash and
-// compared in full (parent key hash, salt, tokens).
+// from its last to its first).  Keys are looked up by a 64-bit hash and then
+// compared field by field: the salt and the 16 token ids exactly, the block
+// before it by that block's 64-bit key hash (so the chain of earlier blocks is
+// compared through hashes, not token by token).
 //
 // Preemption by swapping ("vLLM and PagedAttention", §3 continuous batching, on
 // the scheduler's preemption; "How vLLM Works?", section 04): a second pool of
@@ -60,7 +62,8 @@ struct Seq {
   std::vector<uint64_t> keys;   // key hash of each full block
 };
 
-// A cached full block: its key, compared in full on lookup.
+// A cached full block: its key (salt and ids compared exactly on lookup, the
+// parent by its 64-bit key hash).
 struct CacheEntry {
   int32_t block;
   uint64_t parent;  // key hash of the block before it (0 for a first block)

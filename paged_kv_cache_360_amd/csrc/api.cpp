@@ -215,7 +215,9 @@ int prepare_attention(const char* who, pkv::DecodeArgs& a, void* out, const void
     return bad(PKV_EINVAL, "bad sizes");
   if ((int64_t)max_context_len > (int64_t)max_blocks_per_seq * PKV_BLOCK_SIZE)
     return bad(PKV_EINVAL, "max_context_len exceeds the table width");
-  if (!std::isfinite(scale)) return bad(PKV_EINVAL, "scale must be finite");
+  // The kernels take the row max of raw scores and mask with -inf before the
+  // scale is applied, which is right only for a positive scale.
+  if (!std::isfinite(scale) || !(scale > 0.f)) return bad(PKV_EINVAL, "scale must be finite and positive");
   if (num_tokens < 0 || max_query_len < 1) return bad(PKV_EINVAL, "bad query sizes");
   if (num_seqs == 0 || num_tokens == 0) return PKV_OK;
   if (!out || !q || !key_cache || !value_cache || !block_tables || !context_lens)

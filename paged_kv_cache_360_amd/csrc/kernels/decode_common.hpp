@@ -13,14 +13,10 @@ namespace pkv {
 constexpr int kDecodeThreads = 256;                 // 4 wavefronts per workgroup
 constexpr int kDecodeWaves = kDecodeThreads / kWave;
 constexpr int kPlanThreads = 1024;                  // work-list builder: one workgroup
-// A decode work item covers up to PKV_ITEM_PARTS consecutive 512-token
-// partitions of one (sequence, KV head): the waves keep one state per partition
-// and meet once per item, while each partition still yields its own partial for
-// the merge.
-#ifndef PKV_ITEM_PARTS
-#define PKV_ITEM_PARTS 2
-#endif
-constexpr int kItemParts = PKV_ITEM_PARTS;
+// A decode work item covers up to two consecutive 512-token partitions of one
+// (sequence, KV head): the waves keep one state per partition and meet once per
+// item, while each partition still yields its own partial for the merge.
+constexpr int kItemParts = 2;
 constexpr int kItemBlocks = kItemParts * kPartBlocks;
 
 struct DecodeParams {

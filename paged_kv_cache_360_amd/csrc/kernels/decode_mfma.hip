@@ -13,9 +13,12 @@
 // reductions cost more issue slots than the HBM stream leaves; as MFMA operands
 // bf16 is consumed as stored and no cross-lane reduction remains.
 //
-// Work decomposition: grid = (KV head g, partition p, sequence s), 4 wavefronts;
-// partition p is tokens [512p, 512p + 512).  Wave w takes blocks p*32 + w, + 4,
-// ... and keeps its own online-softmax state; the four waves merge through LDS.
+// Work decomposition: one persistent 4-wave workgroup per compute unit takes
+// work items from the plan's list (ticket t = record t / Hkv, KV head t % Hkv);
+// an item is one (sequence, KV head) over one or two consecutive 512-token
+// partitions (partition p is tokens [512p, 512p + 512)).  Wave w takes the
+// item's blocks w, w + 4, ... and keeps one online-softmax state per partition;
+// the four waves' states merge through LDS into one partial per partition.
 //
 // Per 16-token block, one wave (lane = 16 j + h, h = lane & 15, j = lane >> 4):
 //  scores  S[t][n] = sum_d K[t][d] q[n][d]  (v_mfma_f32_16x16x32_bf16, D/32 of
@@ -38,8 +41,9 @@
 // accumulator), so NaN/Inf in unused slots never reaches the output.  Block ids
 // outside [0, num_blocks) are not dereferenced; such a block counts as masked.
 //
-// Memory-level parallelism: each wave double-buffers two blocks (K and V, 8 KiB
-// at head_dim 128) in registers, issuing block i+1's loads before computing i.
+// Memory-level parallelism: each wave double-buffers two blocks (its KV head's
+// K and V slices, 8 KiB at head_dim 128) in registers, issuing block i+1's
+// loads before computing i.
 // Loads go through per-block buffer resources (base = the block, range = its
 // size): the lane offsets are 32-bit, and a block that must not be read gets a
 // zero range, so the prefetch needs no branch.
@@ -50,19 +54,6 @@
 
 #include "../pkv_internal.hpp"
 #include "decode_common.hpp"
-
-#ifndef PKV_MFMA_NBUF
-#define PKV_MFMA_NBUF 2
-#endif
-#ifndef PKV_MFMA_WG_PER_CU
-#define PKV_MFMA_WG_PER_CU 1
-#endif
-#ifndef PKV_MFMA_WAVES
-#define PKV_MFMA_WAVES 2
-#endif
-#ifndef PKV_MFMA_THREADS
-#define PKV_MFMA_THREADS 256
-#endif
 
 namespace pkv {
 
@@ -75,14 +66,14 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 // Blocks each wave keeps in flight, and the occupancy the register budget is
 // sized for (waves per SIMD).
-constexpr int kMfmaPipelineDepth = PKV_MFMA_NBUF;
-constexpr int kMfmaWavesPerSimd = PKV_MFMA_WAVES;
+constexpr int kMfmaPipelineDepth = 2;
+constexpr int kMfmaWavesPerSimd = 2;
 // Persistent workgroups per compute unit (capped by what fits).  Fewer, deeper
 // pipelined workgroups keep the same bytes in flight and finish each item
 // sooner, which shortens the end-of-run tail of the ticket schedule.
-constexpr int kMfmaWgPerCu = PKV_MFMA_WG_PER_CU;
+constexpr int kMfmaWgPerCu = 1;
 // Threads per workgroup: the waves of a workgroup split each item's blocks.
-constexpr int kMfmaThreads = PKV_MFMA_THREADS;
+constexpr int kMfmaThreads = 256;
 
 // One lane's share of a V row load: head_dim / 16 bf16 values.
 template <int D> struct VPiece;

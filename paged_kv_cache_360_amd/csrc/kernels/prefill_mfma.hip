@@ -32,16 +32,18 @@
 // diagonal block needs no special case.
 //
 // K and V of each step are loaded once per workgroup (one D/8-byte piece of K
-// and of V per thread and step row), staged through a three-buffer LDS slab
-// (K rows padded to D*2 + 16 bytes, V rows to D*2 + 64, which keeps both read
-// patterns free of bank conflicts), and read by every wave.  Rows past the
-// context read as zeros (the block's buffer resource ends at the context), so
-// a V row there never meets a zero weight as 0 * NaN.  Each wave
-// computes the scores of step q + 1 while it runs step q's softmax and value
-// products, so the matrix cores work during the vector code.  The load stream
-// runs four steps ahead of the computation across item boundaries: the
-// workgroup keeps the record and the q operand of the next item, so a new item
-// starts with its first steps and q already loaded.
+// and of V per thread and step row), staged through five LDS buffers (K rows
+// padded to D*2 + 16 bytes, V rows to D*2 + 64, which keeps both read patterns
+// free of bank conflicts), and read by every wave.  Rows past the context read
+// as zeros (the block's buffer resource ends at the context), so a V row there
+// never meets a zero weight as 0 * NaN.  Each wave computes the scores of step
+// q + 1 while it runs step q's softmax and value products, so the matrix cores
+// work during the vector code.  There is one barrier per two steps: while the
+// pair q, q + 1 runs, steps q + 3 and q + 4 are staged into the buffers of
+// steps q - 2 and q - 1, and the loads of q + 5 and q + 6 are issued, so the
+// load stream runs up to six steps ahead of the computation, across item
+// boundaries: the workgroup keeps the record and the q operand of the next
+// item, so a new item starts with its first steps and q already loaded.
 //
 // Workgroups take items from the prefill tickets: the first two are static
 // (blockIdx.x and blockIdx.x + gridDim.x), the rest come from the counter.  A row whose
@@ -67,24 +69,14 @@ constexpr int kStepTokens = 2 * kBlockTokens;  // tokens per step (two blocks)
 // Waves per workgroup; the item's 256 columns are split among them in 32-column
 // tiles.  Eight waves (two per SIMD) let one wave's softmax and LDS reads
 // overlap another's matrix products.
-#ifndef PKV_PREFILL_WAVES
-#define PKV_PREFILL_WAVES 8
-#endif
-constexpr int kPrefillWaves = PKV_PREFILL_WAVES;
+constexpr int kPrefillWaves = 8;
 constexpr int kPrefillThreads = kPrefillWaves * kWave;
 constexpr int kColTiles = 8 / kPrefillWaves;   // 32-column tiles per wave
-#ifndef PKV_PREFILL_STEPS
-#define PKV_PREFILL_STEPS 2
-#endif
-constexpr int kPrefillSteps = PKV_PREFILL_STEPS;  // steps of K/V in flight
-// Barrier interval: two steps (five LDS buffers; steps q .. q+2 are read
-// while q+3 and q+4 are staged), or one step (three buffers).  Two let the
-// waves of a SIMD drift apart within the interval (~1% faster).
-#ifndef PKV_PREFILL_PAIRS
-#define PKV_PREFILL_PAIRS 1
-#endif
-constexpr bool kPrefillPairs = PKV_PREFILL_PAIRS != 0;
-constexpr int kPrefillBufs = kPrefillPairs ? 5 : 3;
+constexpr int kPrefillSteps = 2;               // steps of K/V in flight in registers
+// Barrier interval: two steps, over five LDS buffers (steps q .. q+2 are read
+// while q+3 and q+4 are staged), which lets the waves of a SIMD drift apart
+// within the interval.
+constexpr int kPrefillBufs = 5;
 
 // One thread's piece of a block row: D / 8 bytes.
 template <int D> struct KVPiece;
@@ -172,12 +164,10 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void prefill_mfma_kernel(Decode
     it.b_begin = it.part * kPartBlocks;
     it.nblk = it.valid ? max(0, (k_end - k_begin + kBlockTokens - 1) / kBlockTokens) : 0;
     // steps of two blocks, padded to a multiple of NS so that every item starts
-    // on stage slot 0, and to at least 2*NS so that the load stream (NS + 2
-    // steps ahead of the computation) never runs past the next item; padding
-    // steps load nothing and compute nothing
-    // (with two steps per barrier the stream runs up to 6 steps ahead of the
-    // pair being computed, so an item has at least 6)
-    it.nsteps = max(kPrefillPairs ? 6 : 2 * NS, (max(1, (it.nblk + 1) / 2) + NS - 1) / NS * NS);
+    // on stage slot 0, and to at least 6: the load stream runs up to six steps
+    // ahead of the pair being computed and must never run past the next item;
+    // padding steps load nothing and compute nothing
+    it.nsteps = max(6, (max(1, (it.nblk + 1) / 2) + NS - 1) / NS * NS);
     it.trow = (TablePtr)(const void*)(p.tables + (int64_t)it.s * p.MB + it.b_begin);
   };
   // q operands (B of the scores) of this wave's columns; rows past the item read
@@ -441,9 +431,9 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void prefill_mfma_kernel(Decode
   };
 
   // The item queue: cur (being computed) and n1 (record known, q loaded into
-  // qn); the ticket after n1 is fetched while cur runs.  The loads run NS steps
-  // ahead of the staging, NS + 2 ahead of the computation: into n1 near the
-  // end of cur, never past it.
+  // qn); the ticket after n1 is fetched while cur runs.  The loads run up to
+  // six steps ahead of the pair being computed: into n1 near the end of cur,
+  // never past it.
   Item cur, n1;
   make_item(blockIdx.x, cur);
   if (!cur.valid) return;
@@ -451,10 +441,10 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void prefill_mfma_kernel(Decode
   load_q(cur, qf);
   load_q(n1, qn);
 
-  // The load stream runs NS + 2 steps ahead of the computation: in cur, then
-  // in n1 (cs_n1).  Stepping past the end of n1 (only when n1 has the minimum
-  // 2*NS steps) leaves it pending (cs_wait) until the item switch makes the
-  // next n1; that happens before the next issue.  An invalid item has no
+  // The load stream runs ahead of the computation: in cur, then in n1
+  // (cs_n1).  Stepping past the end of n1 (only when n1 has the minimum six
+  // steps) leaves it pending (cs_wait) until the item switch makes the next
+  // n1; that happens before the next issue.  An invalid item has no
   // blocks (zero-sized loads).  The ids of each position are loaded one issue
   // ahead (pf_ids, valid when pf_ok), so the issue does not wait for the
   // scalar loads.
@@ -477,13 +467,12 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void prefill_mfma_kernel(Decode
     if (pf_ok) pf_ids = ids_at(cs);
   };
 
-  // One step per barrier: step q is staged into LDS at iteration q - 2 (from
-  // the registers its loads landed in, NS steps after they were issued), its
-  // scores are computed at iteration q - 1 while step q - 1's softmax and
-  // values run, and its own softmax and values at iteration q.  Two steps per
-  // barrier: steps q + 3 and q + 4 are staged while the pair q, q + 1 runs.
-  static_assert(NS % 2 == 0, "step q's scores sit in sc[q % 2]: the unrolled loop keeps the parity");
-  static_assert(!kPrefillPairs || NS == 2, "two steps per barrier: step s's loads sit in stg[s % 2]");
+  // Two steps per barrier: while the pair q, q + 1 runs (reading the LDS
+  // buffers of steps q .. q + 2; step q + 1's scores are computed during step
+  // q's softmax and values, step q + 2's during q + 1's), steps q + 3 and q + 4
+  // are staged from the registers their loads landed in, and the loads of
+  // steps q + 5 and q + 6 are issued.
+  static_assert(NS == 2, "two steps per barrier: step s's loads sit in stg[s % 2]");
   Stage stg[NS];
 #pragma unroll
   for (int u = 0; u < NS; ++u) issue_next(stg[u]);
@@ -492,10 +481,8 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void prefill_mfma_kernel(Decode
     stage_to_lds(stg[u], u);
     issue_next(stg[u]);
   }
-  if (kPrefillPairs) {  // steps 0 .. 2 in LDS, 3 and 4 in flight
-    stage_to_lds(stg[0], 2);
-    issue_next(stg[0]);
-  }
+  stage_to_lds(stg[0], 2);  // steps 0 .. 2 in LDS, 3 and 4 in flight
+  issue_next(stg[0]);
   __syncthreads();
   int buf = 0, tpar = 0;  // LDS buffer of step 0 of cur
   f32x16 sc[2][CT];       // scores of steps of either parity
@@ -504,7 +491,6 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void prefill_mfma_kernel(Decode
     if (tid == 0) fetched = atomicAdd(&p.sched[2], 1);  // offset added where it is read
     begin_item(cur);
     if (cur.nblk > 0) scores(buf, sc[0]);
-#if PKV_PREFILL_PAIRS
     // Two steps per barrier: buffers rotate over five; step q in (buf + q) % 5
     // relative to the pair.  Steps q + 1 and q + 2 were staged in the previous
     // interval; q + 3 and q + 4 go into the buffers of q - 2 and q - 1, read
@@ -523,29 +509,6 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void prefill_mfma_kernel(Decode
       __syncthreads();
       buf = b2;
     }
-#else
-    for (int q0 = 0; q0 < cur.nsteps; q0 += NS) {
-#pragma unroll
-      for (int u = 0; u < NS; ++u) {
-        const int q = q0 + u;
-        const int b1 = buf == 2 ? 0 : buf + 1, b2 = b1 == 2 ? 0 : b1 + 1;
-        // step q + 2 (stream order, possibly n1's) sits in stg[u]: stage it
-        // into buffer b2 (read last at iteration q - 1, before the last
-        // barrier) and refill the slot with step q + 2 + NS
-        stage_to_lds(stg[u], b2);
-        issue_next(stg[u]);
-        if (q + 1 == cur.nsteps && tid == 0) s_ticket[tpar] = fetched;
-        // step q's softmax and values with step q + 1's scores (computed
-        // also past the item's blocks, where they are never used)
-        if (2 * q < cur.nblk) {
-          const int t0 = (cur.b_begin + 2 * q) * kBlockTokens;
-          softmax_values(sc[u % 2], buf, t0, b1, sc[(u + 1) % 2]);
-        }
-        __syncthreads();
-        buf = b1;
-      }
-    }
-#endif
     // Switch to n1.  Its q was loaded at the start of this item; the empty asm
     // makes the wait for those loads happen here, once, before the output
     // stores are in flight (left to the compiler, it lands before the score

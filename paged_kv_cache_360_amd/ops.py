@@ -35,6 +35,25 @@ def _stream(stream):
     return getattr(stream, "cuda_stream", stream)
 
 
+def _temp_workspace(nbytes_fn, device, stream):
+    """A workspace owned by one call (None if 0 bytes).  When the call runs on
+    a stream other than torch's current one, the buffer is marked as used there,
+    so torch's caching allocator does not hand it out again before that
+    stream's work has run."""
+    ws = nbytes_fn(device)
+    if ws is not None and stream is not None:
+        st = stream if isinstance(stream, torch.cuda.Stream) else torch.cuda.ExternalStream(_stream(stream))
+        ws.record_stream(st)
+    return ws
+
+
+def _need_workspace(workspace, cname):
+    """The split forms share the plan's work list through the workspace: a fresh
+    buffer would hold no plan, so it must be the caller's."""
+    if workspace is None:
+        raise ValueError(f"{cname}: workspace is required (the one the plan launch filled)")
+
+
 def pkv_write(key_cache, value_cache, k, v, slot_mapping, stream=None):
     """Scatter new tokens' K/V rows ``[T, Hkv, D]`` into their slots (bit copy)."""
     nb, bs, hkv, d = key_cache.shape
@@ -65,7 +84,9 @@ def decode_workspace(num_seqs, num_q_heads, head_dim, max_context_len, device="c
 
 
 def _decode_call(cname, out, q, key_cache, value_cache, block_tables, context_lens, scale,
-                 max_context_len, workspace, stream):
+                 max_context_len, workspace, stream, own_workspace=False):
+    if not own_workspace:
+        _need_workspace(workspace, cname)
     s, hq, d = q.shape
     nb, bs, hkv, dk = key_cache.shape
     if out.shape != q.shape or dk != d or value_cache.shape != key_cache.shape:
@@ -76,7 +97,7 @@ def _decode_call(cname, out, q, key_cache, value_cache, block_tables, context_le
         raise ValueError("block_tables must be [S, MB] and context_lens [S]")
     mb = block_tables.shape[1]
     if workspace is None:
-        workspace = decode_workspace(s, hq, d, max_context_len, q.device)
+        workspace = _temp_workspace(lambda dv: decode_workspace(s, hq, d, max_context_len, dv), q.device, stream)
     ws_ptr = 0 if workspace is None else _dev(workspace, "workspace")
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     check(cname, getattr(lib(), cname)(
@@ -89,14 +110,16 @@ def _decode_call(cname, out, q, key_cache, value_cache, block_tables, context_le
 
 def pkv_attention_decode(out, q, key_cache, value_cache, block_tables, context_lens, scale,
                          max_context_len, workspace=None, stream=None):
-    """Paged decode attention for one new token per sequence; writes ``out`` [S, Hq, D]."""
+    """Paged decode attention for one new token per sequence; writes ``out`` [S, Hq, D].
+    Without ``workspace``, the call uses a buffer of its own."""
     return _decode_call("pkv_attention_decode", out, q, key_cache, value_cache, block_tables,
-                        context_lens, scale, max_context_len, workspace, stream)
+                        context_lens, scale, max_context_len, workspace, stream, own_workspace=True)
 
 
 def pkv_attention_decode_plan(out, q, key_cache, value_cache, block_tables, context_lens,
                               scale, max_context_len, workspace=None, stream=None):
-    """First launch of ``pkv_attention_decode`` alone (work list from context_lens)."""
+    """First launch of ``pkv_attention_decode`` alone (work list from context_lens).
+    ``workspace`` is required: the later launches read the plan from it."""
     return _decode_call("pkv_attention_decode_plan", out, q, key_cache, value_cache,
                         block_tables, context_lens, scale, max_context_len, workspace, stream)
 
@@ -112,7 +135,9 @@ def pkv_attention_decode_plan_upload(out, q, key_cache, value_cache, block_table
     ``merge_workspace``, the launch also merges the previous step's partials
     (same shapes, another workspace) into ``merge_out``.  With
     ``host_block_tables`` (pinned, [S, MB]), it also copies each row's used
-    entries into ``block_tables``."""
+    entries into ``block_tables``.  ``workspace`` is required (the later launches
+    read the plan from it)."""
+    _need_workspace(workspace, "pkv_attention_decode_plan_upload")
     if host_block_tables is not None:
         if host_block_tables.is_cuda or not host_block_tables.is_pinned() or not host_block_tables.is_contiguous():
             raise TypeError("host_block_tables must be a contiguous pinned host tensor")
@@ -134,10 +159,8 @@ def pkv_attention_decode_plan_upload(out, q, key_cache, value_cache, block_table
         raise ValueError("shape mismatch")
     if block_tables.dim() != 2 or block_tables.shape[0] != s or context_lens.shape != (s,):
         raise ValueError("block_tables must be [S, MB] and context_lens [S]")
-    if workspace is None:
-        workspace = decode_workspace(s, hq, d, max_context_len, q.device)
-    ws_ptr = 0 if workspace is None else _dev(workspace, "workspace")
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    ws_ptr = _dev(workspace, "workspace")
+    ws_bytes = workspace.numel() * workspace.element_size()
     check("pkv_attention_decode_plan_upload", lib().pkv_attention_decode_plan_upload(
         _dev(out, "out"), _dev(q, "q"), _dev(key_cache, "key_cache"), _dev(value_cache, "value_cache"),
         _dev(block_tables, "block_tables", torch.int32), _dev(context_lens, "context_lens", torch.int32),
@@ -151,14 +174,16 @@ def pkv_attention_decode_plan_upload(out, q, key_cache, value_cache, block_table
 
 def pkv_attention_decode_partitions(out, q, key_cache, value_cache, block_tables, context_lens,
                                     scale, max_context_len, workspace=None, stream=None):
-    """Second launch of ``pkv_attention_decode`` alone (partition kernel; needs the plan)."""
+    """Second launch of ``pkv_attention_decode`` alone (partition kernel); ``workspace``
+    is required (the one the plan launch filled)."""
     return _decode_call("pkv_attention_decode_partitions", out, q, key_cache, value_cache,
                         block_tables, context_lens, scale, max_context_len, workspace, stream)
 
 
 def pkv_attention_decode_merge(out, q, key_cache, value_cache, block_tables, context_lens, scale,
                                max_context_len, workspace=None, stream=None):
-    """Third launch of ``pkv_attention_decode`` alone (log-sum-exp merge)."""
+    """Third launch of ``pkv_attention_decode`` alone (log-sum-exp merge); ``workspace``
+    is required (the one the partitions wrote)."""
     return _decode_call("pkv_attention_decode_merge", out, q, key_cache, value_cache, block_tables,
                         context_lens, scale, max_context_len, workspace, stream)
 
@@ -178,7 +203,7 @@ def _append_call(cname, out, q, k_new, v_new, key_cache, value_cache, block_tabl
         raise ValueError("block_tables must be [S, MB] and context_lens [S]")
     mb = block_tables.shape[1]
     if workspace is None:
-        workspace = decode_workspace(s, hq, d, max_context_len, q.device)
+        workspace = _temp_workspace(lambda dv: decode_workspace(s, hq, d, max_context_len, dv), q.device, stream)
     ws_ptr = 0 if workspace is None else _dev(workspace, "workspace")
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     check(cname, getattr(lib(), cname)(
@@ -201,7 +226,9 @@ def pkv_attention_decode_append(out, q, k_new, v_new, key_cache, value_cache, bl
 def pkv_attention_decode_partitions_append(out, q, k_new, v_new, key_cache, value_cache, block_tables,
                                            context_lens, scale, max_context_len, workspace=None,
                                            stream=None):
-    """Partition launch of the append form (after the plan, before the merge)."""
+    """Partition launch of the append form (after the plan, before the merge);
+    ``workspace`` is required (the one the plan launch filled)."""
+    _need_workspace(workspace, "pkv_attention_decode_partitions_append")
     return _append_call("pkv_attention_decode_partitions_append", out, q, k_new, v_new, key_cache,
                         value_cache, block_tables, context_lens, scale, max_context_len, workspace, stream)
 
@@ -302,7 +329,8 @@ def pkv_attention_varlen(out, q, key_cache, value_cache, block_tables, context_l
         raise ValueError("block_tables must be [S, MB] and query_start_loc [S+1]")
     mb = block_tables.shape[1]
     if workspace is None:
-        workspace = varlen_workspace(s, t, hq, hkv, d, max_query_len, max_context_len, q.device)
+        workspace = _temp_workspace(
+            lambda dv: varlen_workspace(s, t, hq, hkv, d, max_query_len, max_context_len, dv), q.device, stream)
     ws_ptr = 0 if workspace is None else _dev(workspace, "workspace")
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     check("pkv_attention_varlen", lib().pkv_attention_varlen(

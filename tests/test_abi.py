@@ -84,6 +84,8 @@ def _decode(**kw):
     (dict(ws=0), PKV_EWORKSPACE),
     (dict(wsb=100), PKV_EWORKSPACE),
     (dict(scale=float("nan")), PKV_EINVAL),
+    (dict(scale=0.0), PKV_EINVAL),                # the softmax scale must be positive
+    (dict(scale=-1.0), PKV_EINVAL),
     (dict(s=-1), PKV_EINVAL),
     (dict(s=0), PKV_OK),                          # empty batch: nothing to launch
 ])
@@ -149,6 +151,8 @@ def _varlen(**kw):
     (dict(ws=0), PKV_EWORKSPACE),
     (dict(wsb=1000), PKV_EWORKSPACE),
     (dict(maxctx=128 * 16 + 1), PKV_EINVAL),
+    (dict(scale=0.0), PKV_EINVAL),                  # prefill rows mask before scaling: scale > 0
+    (dict(scale=-1.0), PKV_EINVAL),
     (dict(t=0), PKV_OK),                            # no query rows: nothing to launch
     (dict(s=0), PKV_OK),
 ])
@@ -353,3 +357,18 @@ def test_append_batch_all_or_nothing():
     assert list(lens) == [16, 17, 6, 6, 6] and tables[0, 1] == -7
     with pytest.raises(pkv.PagedKVError):
         a.append_batch([0, 0], [1, 1])                         # duplicate ids
+
+
+@pytest.mark.parametrize("name", ["pkv_attention_decode_plan", "pkv_attention_decode_partitions",
+                                  "pkv_attention_decode_merge", "pkv_attention_decode_partitions_append",
+                                  "pkv_attention_decode_plan_upload"])
+def test_split_wrappers_need_the_callers_workspace(name):
+    """The split launches read the work list the plan left in the workspace: the
+    Python wrappers refuse to make a fresh (empty) one, before touching any tensor."""
+    with pytest.raises(ValueError, match="workspace is required"):
+        if name == "pkv_attention_decode_partitions_append":
+            getattr(pkv, name)(None, None, None, None, None, None, None, None, 0.125, 100)
+        elif name == "pkv_attention_decode_plan_upload":
+            getattr(pkv, name)(None, None, None, None, None, None, 0.125, 100, None, None, None)
+        else:
+            getattr(pkv, name)(None, None, None, None, None, None, 0.125, 100)
