@@ -8,6 +8,8 @@ Metrics (floating point):
 Element-wise relative error is not used: it is unbounded near zero.
 """
 
+import json
+import os
 import sys
 
 import numpy as np
@@ -16,6 +18,27 @@ import torch
 FP32_ROW_REL = 1e-5
 BF16_ABS = 2e-2
 BF16_ROW_REL = 2e-2
+
+# Every comparison's errors, kept for the run's summary and written one JSON
+# line each to $PKV_PARITY_LOG (default: gpurun_out/parity_margins.jsonl under
+# the repository root), so a run's margins against the bars can be read back.
+RECORDS = []
+_ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _record(what, dtype, max_abs, max_row_rel):
+    bar = FP32_ROW_REL if dtype == "f32" else BF16_ROW_REL
+    rec = {"test": os.environ.get("PYTEST_CURRENT_TEST", "").split(" ")[0], "what": what, "dtype": dtype,
+           "max_abs": max_abs, "max_row_rel": max_row_rel,
+           "frac_of_bar": max(max_row_rel / bar, 0.0 if dtype == "f32" else max_abs / BF16_ABS)}
+    RECORDS.append(rec)
+    path = os.environ.get("PKV_PARITY_LOG") or os.path.join(_ROOT, "gpurun_out", "parity_margins.jsonl")
+    try:
+        os.makedirs(os.path.dirname(path), exist_ok=True)
+        with open(path, "a") as f:
+            f.write(json.dumps(rec) + "\n")
+    except OSError:
+        pass
 
 
 def say(*a):
@@ -58,6 +81,7 @@ def assert_close(got, ref, dtype, what=""):
     assert np.all(np.isfinite(got)), f"{what}: non-finite output"
     a, r = errors(got, ref)
     say(f"  {what}: max_abs={a:.3e} max_row_rel={r:.3e} ({dtype})")
+    _record(what, dtype, a, r)
     if dtype == "f32":
         assert r <= FP32_ROW_REL, f"{what}: fp32 row-relative error {r:.3e} > {FP32_ROW_REL}"
     else:

@@ -50,9 +50,10 @@ def test_graph_replays_equal_eager(form):
     vc = torch.zeros_like(kc)
     slots0 = np.concatenate([np.array(p, np.int32) for p in pre])
     n0 = slots0.size
-    pkv.pkv_write(kc, vc, dev(normal_values_parallel(1, (n0, Hkv, D), dtype)),
-                  dev(normal_values_parallel(2, (n0, Hkv, D), dtype)), dev(slots0))
+    k0, v0 = normal_values_parallel(1, (n0, Hkv, D), dtype), normal_values_parallel(2, (n0, Hkv, D), dtype)
+    pkv.pkv_write(kc, vc, dev(k0), dev(v0), dev(slots0))
     kc2, vc2 = kc.clone(), vc.clone()                      # the eager run's pools
+    exp_k, exp_v = oracle.write_kv(host(kc), host(vc), k0, v0, slots0)   # the oracle's pools
 
     # static buffers the graph reads
     q_b = torch.zeros((S, Hq, D), dtype=tdt, device="cuda")
@@ -86,10 +87,13 @@ def test_graph_replays_equal_eager(form):
             pkv.pkv_attention_decode(out_e, dev(q), kc2, vc2, dev(tables), dev(lens), float(scale), bound,
                                      workspace=ws_e)
         torch.cuda.synchronize()
+        exp_k, exp_v = oracle.write_kv(exp_k, exp_v, kn, vn, np.asarray(slots, np.int32))
         assert host(out_g).tobytes() == host(out_e).tobytes(), f"step {i}: graph output differs"
         assert host(kc).tobytes() == host(kc2).tobytes() and host(vc).tobytes() == host(vc2).tobytes(), i
+        assert host(kc).tobytes() == exp_k.tobytes() and host(vc).tobytes() == exp_v.tobytes(), \
+            f"step {i}: the pool differs from the oracle's writes"
     say(f"  {steps} replays equal to the eager calls byte for byte; contexts now {lens.min()}..{lens.max()}")
-    ref = oracle.decode_attention(q, host(kc), host(vc), tables, lens, scale)
+    ref = oracle.decode_attention(q, exp_k, exp_v, tables, lens, scale)
     assert_close(host_f64(out_g), ref, dtype, f"graph {form} last step")
     graph.close()
 

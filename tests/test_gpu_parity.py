@@ -160,18 +160,23 @@ def test_one_token_context_is_exact(dtype):
 
 
 def test_zero_query_unit_scale_bf16():
-    """q = 0: uniform weights, out = mean of V.  V = sign pattern + small noise: |out| ~ 1."""
+    """q = 0: uniform weights, out = the mean of V over the context (the closed
+    form of equal scores).  V = a sign pattern per (KV head, dim) plus a
+    token-dependent part of half its size, so the mean stays near unit scale
+    and still depends on which tokens are summed.  At long contexts one
+    block's share of a uniform mean is too small for the bf16 bars; dropped or
+    doubled blocks are caught by the peaked sweeps (test_gpu_structural)."""
     say("zero-query unit scale")
     inp = explicit_case(6, "bf16", 32, 8, 128, [1, 17, 600, 2000, 4500])
     rng = np.random.default_rng(6)
     sign = np.where(rng.random((8, 128)) < 0.5, -1.0, 1.0).astype(np.float32)
-    noise = 0.05 * rng.standard_normal(inp["value_cache"].shape).astype(np.float32)
+    per_token = 0.5 * rng.standard_normal(inp["value_cache"].shape).astype(np.float32)
     from workloads import f32_to_bf16_bits
-    inp["value_cache"] = f32_to_bf16_bits(sign[None, None] + noise)
+    inp["value_cache"] = f32_to_bf16_bits(sign[None, None] + per_token)
     inp["q"] = np.zeros_like(inp["q"])
     got = host_f64(gpu_decode(inp))
     ref = oracle_decode(inp)
-    assert np.min(np.abs(ref)) > 0.5
+    assert np.min(np.max(np.abs(ref), axis=-1)) > 0.5
     assert_close(got, ref, "bf16", "zero-query")
 
 

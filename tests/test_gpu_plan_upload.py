@@ -50,6 +50,7 @@ def test_plan_upload_equals_copy_then_plan(append, fuse_merge, ragged):
     perm = rng.permutation(nb).astype(np.int32)
     kc1, vc1 = kc.clone(), vc.clone()              # the pools the fused path runs on
     kc2, vc2 = kc.clone(), vc.clone()              # and the reference path
+    exp = [host(kc), host(vc)]                     # the pool as the oracle's writes leave it
     outs, refs, metas, snaps, keep = [], [], [], [], []
     for step, lo_hi in enumerate([(1, 1500), (400, 3100)]):
         ctx = rng.integers(lo_hi[0], lo_hi[1] + 1, size=S).astype(np.int32)
@@ -92,7 +93,11 @@ def test_plan_upload_equals_copy_then_plan(append, fuse_merge, ragged):
         if not fuse_merge or step == 1:
             pkv.pkv_attention_decode_merge(out, q, kc1, vc1, d_tab, d_lens, float(scale), bound, workspace=ws)
         torch.cuda.synchronize()
-        snaps.append((host(kc1), host(vc1)))        # the pool this step read (the next may append into it)
+        if append:                                   # this step's new rows, written by the oracle
+            exp[:] = oracle.write_kv(exp[0], exp[1], host(kn), host(vn), slots)
+        assert host(kc1).tobytes() == exp[0].tobytes() and host(vc1).tobytes() == exp[1].tobytes(), \
+            f"step {step}: the pool differs from the oracle's writes"
+        snaps.append((exp[0], exp[1]))               # the pool this step read (the next may append into it)
         ref_out = torch.zeros_like(out)
         if append:
             pkv.pkv_attention_decode_append(ref_out, q, kn, vn, kc2, vc2, dev(tables), dev(ctx), float(scale), bound)
@@ -170,8 +175,9 @@ def test_bench_launch_sequence_full_size():
     of each table row by rows; merging the previous step; alternating
     workspaces) then _partitions_append; a plain _merge after the last step.
     Every step's output and the final cache equal the one-call append form run
-    step by step on a copy of the pool, byte for byte; sampled rows of the last
-    step match the oracle."""
+    step by step on a copy of the pool, byte for byte; the final cache equals
+    the pool the oracle's writes of the same rows leave, over the whole pool;
+    sampled rows of the last step match the oracle on that pool."""
     from workloads import SPECS, draw_context_lens, pool_blocks_for
     spec = SPECS["gqa32x8_bf16_s128_ctx512_8192"]
     S, Hq, Hkv, D = spec.num_seqs, spec.num_q_heads, spec.num_kv_heads, spec.head_dim
@@ -187,9 +193,10 @@ def test_bench_launch_sequence_full_size():
     for s in range(S):
         alloc.add_seq(s)
         alloc.append(s, int(ctx0[s]) - 1)
-    kc = dev(normal_values_parallel(11, (nb, 16, Hkv, D), "bf16"))
-    vc = dev(normal_values_parallel(12, (nb, 16, Hkv, D), "bf16"))
+    kc0, vc0 = normal_values_parallel(11, (nb, 16, Hkv, D), "bf16"), normal_values_parallel(12, (nb, 16, Hkv, D), "bf16")
+    kc, vc = dev(kc0), dev(vc0)
     kc_ref, vc_ref = kc.clone(), vc.clone()
+    exp_k, exp_v = kc0, vc0                          # the pool as the oracle's writes leave it
     scale = float(np.float32(1.0 / math.sqrt(D)))
     meta_len = 2 * S + S * MB
     meta_len += -meta_len % 4
@@ -205,8 +212,9 @@ def test_bench_launch_sequence_full_size():
         tables, lens = alloc.block_tables(ids, MB, fill=-1, tables_out=h[2 * S:2 * S + S * MB].reshape(S, MB),
                                           lens_out=h[S:2 * S])
         q = dev(normal_values_parallel(100 + i, (S, Hq, D), "bf16"))
-        kn = dev(normal_values_parallel(200 + i, (S, Hkv, D), "bf16"))
-        vn = dev(normal_values_parallel(300 + i, (S, Hkv, D), "bf16"))
+        kn_h, vn_h = normal_values_parallel(200 + i, (S, Hkv, D), "bf16"), normal_values_parallel(300 + i, (S, Hkv, D), "bf16")
+        kn, vn = dev(kn_h), dev(vn_h)
+        exp_k, exp_v = oracle.write_kv(exp_k, exp_v, kn_h, vn_h, h[:S].copy())
         d_lens, d_tab = dmeta[b][S:2 * S], dmeta[b][2 * S:2 * S + S * MB].view(S, MB)
         merge_kw = dict(merge_out=out[i - 1], merge_workspace=wss[1 - b]) if i > 0 else {}
         pkv.pkv_attention_decode_plan_upload(out[i], q, kc, vc, d_tab, d_lens, scale, bound, stage[b][S:2 * S],
@@ -226,7 +234,9 @@ def test_bench_launch_sequence_full_size():
     for i in range(steps):
         assert host(out[i]).tobytes() == host(refs[i]).tobytes(), f"step {i} differs"
     assert host(kc).tobytes() == host(kc_ref).tobytes() and host(vc).tobytes() == host(vc_ref).tobytes()
+    assert host(kc).tobytes() == exp_k.tobytes() and host(vc).tobytes() == exp_v.tobytes(), \
+        "the pool differs from the oracle's writes"
     tables, lens = last
     idx = np.unique(np.concatenate([np.argsort(lens)[:2], np.argsort(lens)[-2:], rng.choice(S, 6, replace=False)]))
-    ref = oracle.decode_attention(host(qs[-1])[idx], host(kc), host(vc), tables[idx], lens[idx], np.float32(scale))
+    ref = oracle.decode_attention(host(qs[-1])[idx], exp_k, exp_v, tables[idx], lens[idx], np.float32(scale))
     assert_close(host_f64(out[-1])[idx], ref, "bf16", "bench launch sequence, last step")

@@ -7,7 +7,9 @@ the last sharer, which writes in place ("vLLM and PagedAttention", §2
 shareable prefixes with copy-on-write).  The decode over the shared pool must
 be bitwise equal to the decode over a pool where every sequence holds its own
 copy of the prefix (same logical K/V, same reduction order), and match the
-oracle on sampled sequences.
+oracle on sampled sequences.  Both pools are first compared byte for byte,
+over the whole pool, with the pools the oracle's writes and copies build, and
+the oracle reads its own pool.
 """
 
 import math
@@ -65,6 +67,14 @@ def test_prefix_shared_equals_duplicated(dtype):
     assert all(alloc.refcount(b) == S for b in shared_blocks[:93])
     pkv.pkv_copy_blocks(kc, vc, dev(np.ascontiguousarray(pairs, np.int32)))
     pkv.pkv_write(kc, vc, dev(k_tail), dev(v_tail), dev(slots))
+    # the same writes and copies by the oracle, from the same zeroed pool
+    zero = np.zeros((nb, 16, Hkv, D), np.uint16 if dtype == "bf16" else np.float32)
+    ek, ev = oracle.write_kv(zero, zero, k_pre, v_pre, np.array(pre_slots, np.int32))
+    ek, ev = oracle.copy_blocks(ek, ev, pairs)
+    ek, ev = oracle.write_kv(ek, ev, k_tail, v_tail, np.asarray(slots, np.int32))
+    kh, vh = host(kc), host(vc)
+    assert kh.tobytes() == ek.tobytes() and vh.tobytes() == ev.tobytes(), \
+        "shared pool differs from the oracle's writes and copies"
     tables, lens = alloc.block_tables(ids, mb)
     assert np.array_equal(lens, total)
     out_shared = torch.empty((S, Hq, D), dtype=tdt, device="cuda")
@@ -88,6 +98,12 @@ def test_prefix_shared_equals_duplicated(dtype):
         off += int(tails[s])
     pkv.pkv_write(kc2, vc2, dev(np.concatenate(k_log)), dev(np.concatenate(v_log)),
                   dev(np.concatenate(all_slots)))
+    zero2 = np.zeros((nb2, 16, Hkv, D), zero.dtype)
+    ek2, ev2 = oracle.write_kv(zero2, zero2, np.concatenate(k_log), np.concatenate(v_log),
+                               np.concatenate(all_slots))
+    assert host(kc2).tobytes() == ek2.tobytes() and host(vc2).tobytes() == ev2.tobytes(), \
+        "duplicated pool differs from the oracle's writes"
+    del ek2, ev2, zero2
     tables2, lens2 = alloc2.block_tables(ids, mb)
     out_dup = torch.empty_like(out_shared)
     pkv.pkv_attention_decode(out_dup, dev(q), kc2, vc2, dev(tables2), dev(lens2), float(scale),
@@ -95,13 +111,12 @@ def test_prefix_shared_equals_duplicated(dtype):
     torch.cuda.synchronize()
     assert host(out_shared).tobytes() == host(out_dup).tobytes()
 
-    # ---- oracle on sampled sequences (the shared pool as the GPU left it)
+    # ---- oracle on sampled sequences, over the pool the oracle's writes built
     idx = np.unique(np.concatenate([[0, S - 1], np.argsort(total)[-2:],
                                     rng.choice(S, 6, replace=False)]))
-    kh, vh = host(kc), host(vc)
-    ref = oracle.decode_attention(q[idx], kh, vh, tables[idx], lens[idx], scale)
+    ref = oracle.decode_attention(q[idx], ek, ev, tables[idx], lens[idx], scale)
     assert_close(host_f64(out_shared)[idx], ref, dtype, f"prefix-shared {dtype}")
-    # the logical K/V the shared pool holds equals what was written
-    for s in idx[:3]:
-        Kl, Vl = oracle.gather_kv(kh, vh, tables[s], int(lens[s]))
-        assert np.array_equal(Kl, oracle.widen(k_log[s])) and np.array_equal(Vl, oracle.widen(v_log[s]))
+    # the logical K/V that pool holds for every sequence is what each wrote (prefix + tail)
+    for s in range(S):
+        Kl, Vl = oracle.gather_kv(ek, ev, tables[s], int(lens[s]))
+        assert np.array_equal(Kl, oracle.widen(k_log[s])) and np.array_equal(Vl, oracle.widen(v_log[s])), s

@@ -54,14 +54,18 @@ def test_swap_round_trip(dtype):
     alloc.set_host_pool(nh)
     kc = torch.zeros((nb, 16, Hkv, D), dtype=tdt, device="cuda")
     vc = torch.zeros_like(kc)
+    # the oracle's copy of every write and copy-on-write the GPU makes
+    mirror = [host(kc), host(vc)]
 
     def write(sid, n, seed):
         slots, cow = alloc.append(sid, n)
         if cow:
             pkv.pkv_copy_blocks(kc, vc, dev(np.array(cow, np.int32)))
+            mirror[:] = oracle.copy_blocks(mirror[0], mirror[1], cow)
         k = normal_values_parallel(seed, (n, Hkv, D), dtype)
         v = normal_values_parallel(seed + 1, (n, Hkv, D), dtype)
         pkv.pkv_write(kc, vc, dev(k), dev(v), dev(np.array(slots, np.int32)))
+        mirror[:] = oracle.write_kv(mirror[0], mirror[1], k, v, np.array(slots, np.int32))
 
     # sequences 0..S-1; 20..23 are forks of 0..3 with a few private tokens (CoW)
     for s in range(S - 4):
@@ -83,7 +87,9 @@ def test_swap_round_trip(dtype):
         return out, tables, lens
 
     out0, tables0, lens0 = decode()
-    kh0, vh0 = host(kc), host(vc)
+    kh0, vh0 = mirror
+    assert host(kc).tobytes() == kh0.tobytes() and host(vc).tobytes() == vh0.tobytes(), \
+        "the writes and copies differ from the oracle's"
 
     # ---- swap out a group holding a parent with its fork, a fork without its parent, and others
     group = [0, 20, 21, 5, 6, 7, 11, 12]

@@ -155,16 +155,20 @@ def test_varlen_two_partition_prefill_items(name):
 
 
 def test_varlen_unit_scale_zero_query():
-    """q = 0: row r's output is the mean of V over its visible keys (|out| ~ 1)."""
+    """q = 0: row r's output is the mean of V over its visible keys (the closed
+    form of equal scores; V = a sign pattern plus a token-dependent part of half
+    its size, so the means are near unit scale and differ from row to row).
+    Dropped or doubled blocks are caught by the peaked sweeps
+    (test_gpu_structural)."""
     say("varlen zero-query unit scale")
     inp = mixed_case(41, 32, 8, 128, [100, 1, 37], [700, 1200, 37])
     rng = np.random.default_rng(41)
     sign = np.where(rng.random((8, 128)) < 0.5, -1.0, 1.0).astype(np.float32)
-    noise = 0.05 * rng.standard_normal(inp["value_cache"].shape).astype(np.float32)
-    inp["value_cache"] = f32_to_bf16_bits(sign[None, None] + noise)
+    per_token = 0.5 * rng.standard_normal(inp["value_cache"].shape).astype(np.float32)
+    inp["value_cache"] = f32_to_bf16_bits(sign[None, None] + per_token)
     inp["q"] = np.zeros_like(inp["q"])
     ref = oracle_varlen(inp)
-    assert np.min(np.abs(ref)) > 0.5
+    assert np.min(np.max(np.abs(ref), axis=-1)) > 0.5
     assert_close(host_f64(gpu_varlen(inp)), ref, "bf16", "zero-query")
 
 
