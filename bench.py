@@ -24,10 +24,14 @@ rotated step to step so each step's KV reads come from HBM, not the 256 MiB
 last-level cache.
 
 Prints ONE JSON line.  The partition kernel's duration comes from two HIP
-events recorded on the compute stream around it in every EV_EVERY-th timed
-step (each timing event costs the stream a few microseconds, so the other
-launches are not bracketed there); the write (fp32) and merge durations come from a few
-extra steps after the timed region, with events around every launch.
+events recorded on the compute stream around it in every ev_every(K)-th timed
+step, at least ten launches per run (each timing event costs the stream a few
+microseconds, so the other launches are not bracketed there); the write (fp32)
+and merge durations come from a few extra steps after the timed region, with
+events around every launch.  After those, plain read kernels (libpkvprobe.so)
+read the same K/V blocks, in the same order, from the same rotated pools: the
+line reports the partition kernel's KV-read rate against theirs as well as
+against the 8 TB/s peak.
 """
 
 import argparse
@@ -42,7 +46,14 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
-EV_EVERY = 10                                           # timed steps per event-bracketed launch
+
+
+def ev_every(steps):
+    """Timed steps per event-bracketed launch: at least ten bracketed launches
+    per run (every step when there are ten or fewer)."""
+    return max(1, steps // 10)
+
+
 METRIC = "decode tokens/s + KV-read HBM GB/s (% of MI355X peak), bf16 GQA ctx 2k–8k"
 HBM_PEAK_GBPS = 8000.0
 DEFAULT_WORKLOAD = "gqa32x8_bf16_s128_ctx512_8192"
@@ -80,47 +91,61 @@ def parse_args():
                     help="only time one decode step replayed as a HIP graph against the same launches "
                          "made one by one (4-sequence fp32 MHA batch and the default GQA batch)")
     ap.add_argument("--json-out", default=None)
-    ap.add_argument("--traffic-from", nargs=4, metavar="CSV", default=None,
-                    help="rocprofv3 counter_collection CSVs: FETCH_SIZE and WRITE_SIZE of a "
-                         "--steps run, then of a --copy-probe run; writes the per-launch HBM "
-                         "traffic of the partition kernel for later bench lines, and exits")
+    ap.add_argument("--read-probe", action="store_true",
+                    help="only run the plain read kernels over a 1.5 GiB pool (blocks in random order; "
+                         "whole blocks and per-head slices; random and zero-filled data)")
+    ap.add_argument("--traffic-from", nargs=5, metavar="FILE", default=None,
+                    help="rocprofv3 counter_collection CSVs: FETCH_SIZE and WRITE_SIZE of a bench run, "
+                         "then of a --copy-probe run, and that bench run's --json-out line; writes the "
+                         "partition kernel's HBM traffic per algorithmic byte for later bench lines, "
+                         "and exits")
     return ap.parse_args()
 
 
-def traffic_from_counters(paths, workload, W, K):
-    """Per-launch HBM bytes of the partition kernel from rocprofv3 --pmc CSVs.
+def traffic_from_counters(paths, workload):
+    """HBM traffic of the partition kernel per algorithmic byte, from rocprofv3 --pmc CSVs.
 
     FETCH_SIZE / WRITE_SIZE (KiB per dispatch) are scaled by what they read for
-    the copy probe, whose bytes are known (COPY_PROBE_BYTES each way).  The
-    counted run must use the same --warmup W and --steps K as the bench line
-    that reports the figure: the average is taken over the same launches the
-    bench brackets with events (timed steps 0, EV_EVERY, ... after W warmup
-    steps), so it compares with their algorithmic bytes.
+    the copy probe, whose bytes are known (COPY_PROBE_BYTES each way), and
+    averaged over the timed launches of the counted bench run (dispatches W ..
+    W + K - 1 of the kernel, with W and K from that run's JSON line); the
+    algorithmic bytes of the same launches come from that line.  The ratio is
+    stored with the kernel sources' hash and the workload: a later bench line of
+    the same kernel and workload reports traffic = ratio x its own algorithmic
+    bytes per launch, and null once the kernel has changed.
     """
     import csv
 
-    def mean_kib(path, kernel_part, pick=None):
+    fetch, write, cfetch, cwrite, bench_json = paths
+    with open(bench_json) as f:
+        line = json.loads(f.read().strip().splitlines()[-1])
+    W, K = int(line["warmup"]), int(line["steps"])
+    if line["config"]["workload"] != workload:
+        raise SystemExit(f"{bench_json} is a run of {line['config']['workload']}, not {workload}")
+    alg = float(line["roofline"]["algorithmic_bytes_mean_all_timed"])
+
+    def mean_kib(path, kernel_part, timed=False):
         rows = sorted(((int(r["Dispatch_Id"]), float(r["Counter_Value"]))
                        for r in csv.DictReader(open(path)) if kernel_part in r["Kernel_Name"]))
         vals = [v for _, v in rows]
-        if pick is not None:
+        if timed:
             if len(vals) < W + K:
-                raise SystemExit(f"{path}: {len(vals)} dispatches of {kernel_part}, "
-                                 f"fewer than --warmup {W} + --steps {K}")
-            vals = [vals[W + k] for k in range(0, K, EV_EVERY)]
+                raise SystemExit(f"{path}: {len(vals)} dispatches of {kernel_part}, fewer than "
+                                 f"--warmup {W} + --steps {K}")
+            vals = vals[W:W + K]
         if not vals:
             raise SystemExit(f"{path}: no dispatch of {kernel_part}")
         return sum(vals) / len(vals)
 
-    fetch, write, cfetch, cwrite = paths
     kf = COPY_PROBE_BYTES / (mean_kib(cfetch, "copy_blocks_kernel") * 1024)
     kw = COPY_PROBE_BYTES / (mean_kib(cwrite, "copy_blocks_kernel") * 1024)
-    fb = mean_kib(fetch, "decode_partition_mfma_kernel", pick=True) * 1024 * kf
-    wb = mean_kib(write, "decode_partition_mfma_kernel", pick=True) * 1024 * kw
+    fb = mean_kib(fetch, "decode_partition_mfma_kernel", timed=True) * 1024 * kf
+    wb = mean_kib(write, "decode_partition_mfma_kernel", timed=True) * 1024 * kw
     out = {"kernel": "decode_partition_mfma_kernel", "workload": workload,
-           "kernel_source_sha256": kernel_source_hash(), "warmup": W, "steps": K,
+           "kernel_source_sha256": kernel_source_hash(), "counted_warmup": W, "counted_steps": K,
            "fetch_bytes_per_launch": int(fb), "write_bytes_per_launch": int(wb),
-           "traffic_bytes_per_launch": int(fb + wb),
+           "algorithmic_bytes_per_launch": int(alg),
+           "traffic_over_algorithmic": round((fb + wb) / alg, 5),
            "fetch_scale": round(kf, 4), "write_scale": round(kw, 4)}
     with open(TRAFFIC_FILE, "w") as f:
         json.dump(out, f, indent=1)
@@ -337,10 +362,93 @@ def prefix_cache_probe(np, pkv, seed):
                       "append16_us_per_request": round(t_decode / n_req * 1e6, 2)}))
 
 
+def _probe_lib():
+    import ctypes
+    path = os.path.join(ROOT, "paged_kv_cache_360_amd", "libpkvprobe.so")
+    if not os.path.exists(path):
+        return None
+    lib = ctypes.CDLL(path)
+    for fn in (lib.pkv_probe_read_blocks, lib.pkv_probe_read_slices):
+        fn.restype = ctypes.c_int
+    lib.pkv_probe_read_blocks.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
+                                          ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
+    lib.pkv_probe_read_slices.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
+                                          ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
+                                          ctypes.c_void_p]
+    return lib
+
+
+def read_probe_on_blocks(torch, np, kcs, vcs, blk_ids, Hkv, D, es, rounds=4):
+    """Plain read kernels over the K and V of the listed blocks (device pools,
+    rotated like the decode step's), one launch per pool copy and round, the
+    first round untimed.  Returns GB/s for whole blocks and for per-head slices
+    (the partition kernel's pattern), or None without the probe library."""
+    lib = _probe_lib()
+    if lib is None:
+        return None
+    nb = kcs[0].shape[0]
+    assert blk_ids.size > 0 and int(blk_ids.min()) >= 0 and int(blk_ids.max()) < nb, "block id outside the pool"
+    ids = torch.from_numpy(np.ascontiguousarray(blk_ids, np.int32)).cuda()
+    grid = 2048
+    sink = torch.zeros(grid, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+    row_bytes = D * es
+    block_bytes = 16 * Hkv * row_bytes
+    moved = int(blk_ids.size) * 2 * block_bytes
+    res = {"bytes_per_launch": moved, "blocks": int(blk_ids.size)}
+    for name, launch in (
+            ("blocks", lambda r: lib.pkv_probe_read_blocks(kcs[r].data_ptr(), vcs[r].data_ptr(), ids.data_ptr(),
+                                                           int(blk_ids.size), block_bytes, grid, sink.data_ptr(),
+                                                           stream.cuda_stream)),
+            ("slices", lambda r: lib.pkv_probe_read_slices(kcs[r].data_ptr(), vcs[r].data_ptr(), ids.data_ptr(),
+                                                           int(blk_ids.size), Hkv, row_bytes, grid,
+                                                           sink.data_ptr(), stream.cuda_stream))):
+        ts = []
+        for rd in range(rounds):
+            for r in range(len(kcs)):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                rc = launch(r)
+                e1.record(stream)
+                if rc != 0:
+                    raise RuntimeError(f"read probe {name}: HIP error {rc}")
+                if rd > 0:
+                    ts.append((e0, e1))
+        torch.cuda.synchronize()
+        us = [a.elapsed_time(b) * 1e3 for a, b in ts]
+        res[f"{name}_GBps"] = round(moved / (float(np.mean(us)) * 1e-6) / 1e9, 1)
+        res[f"{name}_avg_launch_us"] = round(float(np.mean(us)), 2)
+    res["launches_timed_each"] = (rounds - 1) * len(kcs)
+    return res
+
+
+def read_probe_standalone(torch, np, seed):
+    """The read kernels alone over two 768 MiB pools of 32 KiB blocks (GQA 32/8,
+    head_dim 128, bf16), every block once in a seeded random order, with N(0,1)
+    data and with zeros."""
+    nb, Hkv, D = 24576, 8, 128
+    ids = np.random.default_rng(seed).permutation(nb).astype(np.int32)
+    lines = {}
+    for fill in ("random", "zeros"):
+        kcs, vcs = [], []
+        for _ in range(2):
+            if fill == "random":
+                kcs.append(torch.randn((nb, 16, Hkv, D), device="cuda").to(torch.bfloat16))
+                vcs.append(torch.randn((nb, 16, Hkv, D), device="cuda").to(torch.bfloat16))
+            else:
+                kcs.append(torch.zeros((nb, 16, Hkv, D), dtype=torch.bfloat16, device="cuda"))
+                vcs.append(torch.zeros((nb, 16, Hkv, D), dtype=torch.bfloat16, device="cuda"))
+        lines[fill] = read_probe_on_blocks(torch, np, kcs, vcs, ids, Hkv, D, 2)
+        del kcs, vcs
+        torch.cuda.empty_cache()
+    print(json.dumps({"probe": "read", "pool_blocks": nb, "block_bytes": 16 * Hkv * D * 2, "pool_copies": 2,
+                      "results": lines}))
+
+
 def main():
     args = parse_args()
     if args.traffic_from:
-        return traffic_from_counters(args.traffic_from, args.workload, args.warmup, args.steps)
+        return traffic_from_counters(args.traffic_from, args.workload)
     if args.prefix_cache_probe:
         import numpy as np
 
@@ -380,6 +488,9 @@ def main():
         return
     if args.graph_probe:
         graph_probe(torch, np, pkv, args.seed)
+        return
+    if args.read_probe:
+        read_probe_standalone(torch, np, args.seed)
         return
 
     spec = SPECS[args.workload]
@@ -517,7 +628,7 @@ def main():
         if timed:
             step_lens.append(lens_h.copy())
         r = i % R
-        bracket = detail or (timed and (i - W) % EV_EVERY == 0)
+        bracket = detail or (timed and (i - W) % ev_every(K) == 0)
         ev = events[i - W] if bracket else None
         if detail:
             flush()
@@ -572,7 +683,7 @@ def main():
     torch.cuda.synchronize()
 
     # ---- per-kernel durations and algorithmic bytes --------------------------
-    timed_ev = list(range(0, K, EV_EVERY))             # timed steps whose launch was bracketed
+    timed_ev = list(range(0, K, ev_every(K)))          # timed steps whose launch was bracketed
     t_part = [events[k][1].elapsed_time(events[k][2]) * 1e-3 for k in timed_ev]
     # detail steps: the upload + plan launch (no merge rides along there), plus the
     # write for fp32 (bf16: fused into the partitions); the merge on its own
@@ -598,14 +709,23 @@ def main():
     kv_gbps = sum(kv_b[k] for k in timed_ev) / sum_tp / 1e9
     ms_per_step = wall / K * 1e3
     value = S * K / wall
+    alg_bracketed = float(np.mean([part_b[k] for k in timed_ev]))
 
+    # HBM traffic: the counted ratio of counter bytes to algorithmic bytes for
+    # this kernel source and workload, times this run's algorithmic bytes
     traffic = None
     if os.path.exists(TRAFFIC_FILE):
         with open(TRAFFIC_FILE) as f:
             tr = json.load(f)
         if (tr.get("kernel_source_sha256") == kernel_source_hash() and tr.get("workload") == spec.name
-                and tr.get("warmup") == W and tr.get("steps") == K):
-            traffic = tr.get("traffic_bytes_per_launch")
+                and "traffic_over_algorithmic" in tr):
+            traffic = int(round(tr["traffic_over_algorithmic"] * alg_bracketed))
+
+    # plain read kernels over the same blocks (the contexts of the last step)
+    tables_f, lens_f = alloc.block_tables(ids, MB)
+    blk_ids = np.concatenate([tables_f[s, :-(-int(lens_f[s]) // 16)] for s in range(S)]).astype(np.int32)
+    probe = read_probe_on_blocks(torch, np, kcs, vcs, blk_ids, Hkv, D, es)
+    kv_probe_bytes = int(blk_ids.size) * 2 * 16 * Hkv * D * es
 
     roofline = {
         "kernel": ("decode_partition_mfma_kernel (pkv_attention_decode_partitions_append)" if fused
@@ -616,8 +736,10 @@ def main():
         "unit": "GB/s",
         "frac": round(achieved / HBM_PEAK_GBPS, 4),
         "traffic": traffic,
-        "algorithmic_bytes_per_launch": int(np.mean([part_b[k] for k in timed_ev])),
+        "algorithmic_bytes_per_launch": int(alg_bracketed),
+        "algorithmic_bytes_mean_all_timed": int(np.mean(part_b)),
         "avg_launch_us": round(sum_tp / len(timed_ev) * 1e6, 2),
+        "median_launch_us": round(float(np.median(t_part)) * 1e6, 2),
         "launches_timed": len(timed_ev),
     }
 
@@ -648,10 +770,17 @@ def main():
             "mean_context": round(float(np.mean([l.mean() for l in step_lens])), 1),
             "pool_blocks": nb, "pool_copies": R, "seed": args.seed,
         },
-        "kv_read_GBps": round(kv_gbps, 1),
+        # K/V bytes per partition launch over that launch's time (kernel only) ...
+        "kv_read_GBps_kernel": round(kv_gbps, 1),
         **({"kv_logical_read_GBps": round(sum(logical_b[k] for k in timed_ev) / sum_tp / 1e9, 1),
             "prefix_len": spec.prefix_len, "cow_pairs": int(len(cow_pairs))} if prefix else {}),
-        "kv_read_frac_of_peak": round(kv_gbps / HBM_PEAK_GBPS, 4),
+        "kv_read_frac_of_peak_kernel": round(kv_gbps / HBM_PEAK_GBPS, 4),
+        # ... and over the whole step (wall time per step, every launch and gap included)
+        "kv_read_GBps_step": round(float(np.mean(kv_b)) / (wall / K) / 1e9, 1),
+        "kv_read_frac_of_peak_step": round(float(np.mean(kv_b)) / (wall / K) / 1e9 / HBM_PEAK_GBPS, 4),
+        "read_probe": probe,
+        **({"kv_read_frac_of_read_probe": round(kv_gbps / max(probe["blocks_GBps"], probe["slices_GBps"]), 4)}
+           if probe and not prefix else {}),
         "kernels_us": {
             ("upload_plan" if fused else "upload_plan_write"): round(float(np.mean(t_write)) * 1e6, 2),
             "decode_partitions": round(float(np.mean(t_part)) * 1e6, 2),
@@ -678,7 +807,7 @@ def mixed_main(args, spec):
     One step = host allocation into pinned staging + one H2D copy on a side
     stream + pkv_write of all new rows + pkv_attention_varlen (plan, decode
     partitions, prefill tiles, merge).  The write and attention launches of
-    every EV_EVERY-th timed step are bracketed by events.
+    every ev_every(K)-th timed step are bracketed by events.
     """
     import numpy as np
     import torch
@@ -760,7 +889,7 @@ def mixed_main(args, spec):
             dmeta[b].copy_(stage[b], non_blocking=True)
             h2d_done[b].record(side)
         main.wait_event(h2d_done[b])
-        bracket = timed and (i - W) % EV_EVERY == 0
+        bracket = timed and (i - W) % ev_every(K) == 0
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)] if bracket else None
         if timed:
             lens_log.append(lens_h.copy())

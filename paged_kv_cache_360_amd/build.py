@@ -41,6 +41,10 @@ HOST_FLAGS = ["-O2", "-fPIC", "-std=c++17", "-Wall", "-D__HIP_PLATFORM_AMD__",
 HIP_SOURCES = ["kernels/cache_ops.hip", "kernels/plan.hip", "kernels/decode.hip", "kernels/decode_mfma.hip",
                "kernels/prefill_mfma.hip"]
 HOST_SOURCES = ["api.cpp", "allocator.cpp"]
+# Measurement only: read-bandwidth probes the bench compares the decode kernel
+# with (a library of its own; the attention library does not contain them).
+PROBE_SOURCES = ["probes/read_probe.hip"]
+PROBE_OUT = os.path.join(PKG, "libpkvprobe.so")
 
 
 def _run(cmd, verbose):
@@ -67,12 +71,18 @@ def build(verbose=False, jobs=8):
         obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
         cmds.append([HIPCC, *HOST_FLAGS, "-x", "c++", "-c", os.path.join(CSRC, src), "-o", obj])
         objs.append(obj)
+    probe_objs = []
+    for src in PROBE_SOURCES:
+        obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
+        cmds.append([HIPCC, *HIP_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
+        probe_objs.append(obj)
     with ThreadPoolExecutor(max_workers=max(1, min(jobs, len(cmds)))) as ex:
         list(ex.map(lambda c: _run(c, verbose), cmds))
-    tmp = OUT + ".tmp"
-    _run([HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp, *objs,
-          "-Wl,-soname,libpagedkv.so", f"-Wl,-rpath,{ROCM}/lib"], verbose)
-    shutil.move(tmp, OUT)
+    for out, names, soname in ((OUT, objs, "libpagedkv.so"), (PROBE_OUT, probe_objs, "libpkvprobe.so")):
+        tmp = out + ".tmp"
+        _run([HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp, *names,
+              f"-Wl,-soname,{soname}", f"-Wl,-rpath,{ROCM}/lib"], verbose)
+        shutil.move(tmp, out)
     return OUT
 
 
