@@ -129,6 +129,27 @@ int pkv_attention_decode(void* out, const void* q, const void* key_cache,
                          int32_t max_context_len, pkv_dtype dt, void* workspace,
                          size_t workspace_bytes, void* stream);
 
+/* pkv_attention_decode for callers that cannot allocate device memory: code
+ * under HIP graph capture, serving loops that may not call hipMalloc, harnesses
+ * that forbid allocation.  The workspace is a library-owned device array of
+ * PKV_STATIC_WORKSPACE_BYTES on each GPU the library runs on (its address is
+ * taken at the first call on a device; the array is held until the process
+ * ends); the call allocates nothing.  The arguments are those of
+ * pkv_attention_decode without the workspace.  A call whose workspace
+ * (pkv_decode_workspace_bytes) exceeds PKV_STATIC_WORKSPACE_BYTES returns
+ * PKV_EWORKSPACE and launches nothing.  Every call on one GPU uses that GPU's
+ * one array, whose contents the previous call left: calls that overlap on one
+ * GPU (on different streams or threads) race; order them on one stream.
+ * Errors: those of pkv_attention_decode, PKV_ELAUNCH if the array's address
+ * cannot be taken. */
+#define PKV_STATIC_WORKSPACE_BYTES ((size_t)64 << 20)
+int pkv_attention_decode_noalloc(void* out, const void* q, const void* key_cache,
+                                 const void* value_cache, const int32_t* block_tables,
+                                 const int32_t* context_lens, float scale, int32_t block_size,
+                                 int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                 int32_t num_seqs, int32_t max_blocks_per_seq, int32_t num_blocks,
+                                 int32_t max_context_len, pkv_dtype dt, void* stream);
+
 /* The three launches pkv_attention_decode makes, callable one at a time with the
  * same arguments (so each can be timed or overlapped on its own).
  * _plan: builds the work list in the workspace from context_lens (reads nothing

@@ -25,6 +25,7 @@ PKV_EWORKSPACE = -6
 PKV_ESWAPPED = -7
 BLOCK_SIZE = 16
 PARTITION_TOKENS = 512
+STATIC_WORKSPACE_BYTES = 64 << 20
 
 _i32, _i64, _u64, _f32 = ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64, ctypes.c_float
 _p, _sz = ctypes.c_void_p, ctypes.c_size_t
@@ -37,6 +38,8 @@ SIGNATURES = {
     "pkv_decode_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32]),
     "pkv_attention_decode": (ctypes.c_int, [_p, _p, _p, _p, _p, _p, _f32, _i32, _i32, _i32, _i32, _i32,
                                             _i32, _i32, _i32, ctypes.c_int, _p, _sz, _p]),
+    "pkv_attention_decode_noalloc": (ctypes.c_int, [_p, _p, _p, _p, _p, _p, _f32, _i32, _i32, _i32, _i32, _i32,
+                                                    _i32, _i32, _i32, ctypes.c_int, _p]),
     "pkv_attention_decode_plan": (ctypes.c_int, [_p, _p, _p, _p, _p, _p, _f32, _i32, _i32, _i32, _i32,
                                                  _i32, _i32, _i32, _i32, ctypes.c_int, _p, _sz, _p]),
     "pkv_attention_decode_plan_upload": (ctypes.c_int, [_p, _p, _p, _p, _p, _p, _f32, _i32, _i32, _i32, _i32,

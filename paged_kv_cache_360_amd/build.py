@@ -39,7 +39,7 @@ HOST_FLAGS = ["-O2", "-fPIC", "-std=c++17", "-Wall", "-D__HIP_PLATFORM_AMD__",
               f"-I{ROCM}/include"]
 
 HIP_SOURCES = ["kernels/cache_ops.hip", "kernels/plan.hip", "kernels/decode.hip", "kernels/decode_mfma.hip",
-               "kernels/prefill_mfma.hip"]
+               "kernels/prefill_mfma.hip", "kernels/static_workspace.hip"]
 HOST_SOURCES = ["api.cpp", "allocator.cpp"]
 # Measurement only: read-bandwidth probes the bench compares the decode kernel
 # with (a library of its own; the attention library does not contain them).

@@ -377,6 +377,39 @@ int pkv_attention_decode(PKV_DECODE_ARGS) {
   return pkv::launched(pkv::launch_decode_merge(a, stream), who);
 }
 
+int pkv_attention_decode_noalloc(void* out, const void* q, const void* key_cache, const void* value_cache,
+                                 const int32_t* block_tables, const int32_t* context_lens, float scale,
+                                 int32_t block_size, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                 int32_t num_seqs, int32_t max_blocks_per_seq, int32_t num_blocks,
+                                 int32_t max_context_len, pkv_dtype dt, void* stream) {
+  const char* who = "pkv_attention_decode_noalloc";
+  const size_t cap = pkv::static_workspace_capacity();
+  // Every check before any HIP call: the size against the array, then the
+  // decode checks with a stand-in workspace of the array's size (never read).
+  const size_t need = pkv_decode_workspace_bytes(num_seqs, num_q_heads, head_dim, max_context_len);
+  if (need > cap) {
+    char msg[192];
+    std::snprintf(msg, sizeof(msg), "%s: this batch needs a %zu-byte workspace; the static one holds %zu", who,
+                  need, cap);
+    return fail(PKV_EWORKSPACE, msg);
+  }
+  {
+    pkv::DecodeArgs a{};
+    int rc = prepare_attention(who, a, out, q, key_cache, value_cache, block_tables, context_lens, nullptr,
+                               num_seqs, 1, scale, block_size, num_q_heads, num_kv_heads, head_dim, num_seqs,
+                               max_blocks_per_seq, num_blocks, max_context_len, dt,
+                               reinterpret_cast<void*>(uintptr_t(256)), cap);
+    if (rc != PKV_OK || num_seqs == 0) return rc;
+  }
+  void* ws = nullptr;
+  const int e = pkv::static_workspace(&ws);
+  if (e != 0) return pkv::launched(e, who);
+  // the plan launch clears the ticket counters itself: nothing to reset here
+  return pkv_attention_decode(out, q, key_cache, value_cache, block_tables, context_lens, scale, block_size,
+                              num_q_heads, num_kv_heads, head_dim, num_seqs, max_blocks_per_seq, num_blocks,
+                              max_context_len, dt, ws, cap, stream);
+}
+
 #define PKV_APPEND_ARGS                                                                         \
   void *out, const void *q, const void *k_new, const void *v_new, void *key_cache,               \
       void *value_cache, const int32_t *block_tables, const int32_t *context_lens, float scale,   \

@@ -86,6 +86,12 @@ int launch_decode_partitions(const DecodeArgs& a, void* stream);
 // Log-sum-exp merge of the partials of multi-partition rows (any query length).
 int launch_decode_merge(const DecodeArgs& a, void* stream);
 
+// The decode workspace in a library-owned device array (static_workspace.hip):
+// its size, and its address on the current device, taken once per device
+// (returns 0, or the HIP error of that lookup).
+size_t static_workspace_capacity();
+int static_workspace(void** out);
+
 int launch_lse_merge(void* out, const float* part_m, const float* part_l, const float* part_o,
                      const int32_t* num_parts, int32_t rows, int32_t max_parts, int32_t head_dim,
                      bool bf16, void* stream);
