@@ -60,7 +60,8 @@ DEFAULT_WORKLOAD = "gqa32x8_bf16_s128_ctx512_8192"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_partitions_traffic.json")
 KERNEL_SOURCES = ["paged_kv_cache_360_amd/csrc/kernels/decode_mfma.hip",
                   "paged_kv_cache_360_amd/csrc/kernels/decode_common.hpp",
-                  "paged_kv_cache_360_amd/csrc/kernels/device_common.hpp"]
+                  "paged_kv_cache_360_amd/csrc/kernels/device_common.hpp",
+                  "paged_kv_cache_360_amd/csrc/kernels/plan.hip"]         # the plan shapes the work items
 MFMA_BF16_PEAK_TFLOPS = 2500.0          # MI355X dense bf16 matrix peak
 COPY_PROBE_BYTES = 512 * 1024 * 1024   # pkv_copy_blocks in --copy-probe: read and written per launch
 
@@ -95,7 +96,8 @@ def parse_args():
                     help="only run the plain read kernels over a 1.5 GiB pool (blocks in random order; "
                          "whole blocks and per-head slices; random and zero-filled data)")
     ap.add_argument("--traffic-from", nargs=5, metavar="FILE", default=None,
-                    help="rocprofv3 counter_collection CSVs: FETCH_SIZE and WRITE_SIZE of a bench run, "
+                    help="rocprofv3 counter results (counter_collection CSV or results .db): FETCH_SIZE "
+                         "and WRITE_SIZE of a bench run, "
                          "then of a --copy-probe run, and that bench run's --json-out line; writes the "
                          "partition kernel's HBM traffic per algorithmic byte for later bench lines, "
                          "and exits")
@@ -124,9 +126,20 @@ def traffic_from_counters(paths, workload):
         raise SystemExit(f"{bench_json} is a run of {line['config']['workload']}, not {workload}")
     alg = float(line["roofline"]["algorithmic_bytes_mean_all_timed"])
 
+    def rows_of(path, kernel_part):
+        """(dispatch id, counter value) of the kernel's dispatches: a
+        counter_collection CSV, or the SQLite results database rocprofv3
+        writes by default."""
+        if path.endswith(".db"):
+            import sqlite3
+            con = sqlite3.connect(path)
+            q = "select dispatch_id, value, kernel_name from counters_collection"
+            return [(int(d), float(v)) for d, v, k in con.execute(q) if kernel_part in k]
+        return [(int(r["Dispatch_Id"]), float(r["Counter_Value"]))
+                for r in csv.DictReader(open(path)) if kernel_part in r["Kernel_Name"]]
+
     def mean_kib(path, kernel_part, timed=False):
-        rows = sorted(((int(r["Dispatch_Id"]), float(r["Counter_Value"]))
-                       for r in csv.DictReader(open(path)) if kernel_part in r["Kernel_Name"]))
+        rows = sorted(rows_of(path, kernel_part))
         vals = [v for _, v in rows]
         if timed:
             if len(vals) < W + K:
@@ -360,6 +373,21 @@ def prefix_cache_probe(np, pkv, seed):
                       "served_fraction": round(cached_tokens / prompt_tokens, 4),
                       "admit_us_per_request": round(t_admit / n_req * 1e6, 2),
                       "append16_us_per_request": round(t_decode / n_req * 1e6, 2)}))
+
+
+def partial_slots(np, lens, per_item):
+    """Partial results each decode row's merge combines (1: the row is written
+    directly).  The matrix-core kernel (per_item) writes one partial per work
+    item: items of two 512-token partitions, the last item of a sequence with
+    several split into one-partition pieces when it covers more than one; the
+    vector-ALU kernel writes one per 512-token partition."""
+    nparts = np.maximum(1, -(-lens // 512))
+    if not per_item:
+        return nparts
+    items = -(-nparts // 2)
+    last_blocks = -(-lens // 16) - (items - 1) * 64
+    pieces = np.where((items > 1) & (last_blocks > 32), -(-last_blocks // 32), 1)
+    return items - 1 + pieces
 
 
 def _probe_lib():
@@ -692,18 +720,18 @@ def main():
     kv_b, part_b, merge_b, logical_b = [], [], [], []
     for lens in step_lens:
         lens = lens.astype(np.int64)
-        nparts = -(-lens // 512)
+        slots = partial_slots(np, lens, fused)
         # K/V bytes the launch must bring in: a shared prefix block counts once
         kv = (int(lens.sum()) - (S - 1) * shared_tokens) * 2 * Hkv * D * es
         logical_b.append(int(lens.sum()) * 2 * Hkv * D * es)
-        q_out = S * Hq * D * es + int((nparts == 1).sum()) * Hq * D * es
+        q_out = S * Hq * D * es + int((slots == 1).sum()) * Hq * D * es
         meta = int((4 * -(-lens // 16)).sum()) + 4 * S
-        partials = int(nparts[nparts > 1].sum()) * Hq * (D + 2) * 4
+        partials = int(slots[slots > 1].sum()) * Hq * (D + 2) * 4
         # append form: the new K/V rows are read from the inputs and stored to the cache
         append = 4 * S * Hkv * D * es if fused else 0
         kv_b.append(kv)
         part_b.append(kv + q_out + meta + partials + append)
-        merge_b.append(partials + int((nparts > 1).sum()) * Hq * D * es + 4 * S)
+        merge_b.append(partials + int((slots > 1).sum()) * Hq * D * es + 4 * S)
     sum_tp = sum(t_part)
     achieved = sum(part_b[k] for k in timed_ev) / sum_tp / 1e9
     kv_gbps = sum(kv_b[k] for k in timed_ev) / sum_tp / 1e9
@@ -927,11 +955,11 @@ def mixed_main(args, spec):
     att_b = []
     for lens in lens_log:
         dec = lens[1:].astype(np.int64)
-        nparts = -(-dec // 512)
+        dslots = partial_slots(np, dec, True)
         b = int(dec.sum()) * row_kv + CC * row_kv
         b += 2 * T * Hq * D * es
         pc = -(-keys_chunk // 512)
-        b += 2 * (int(nparts[nparts > 1].sum()) + int(pc[pc > 1].sum())) * Hq * (D + 2) * 4
+        b += 2 * (int(dslots[dslots > 1].sum()) + int(pc[pc > 1].sum())) * Hq * (D + 2) * 4
         att_b.append(b)
     ta = float(np.mean(t_attn))
 

@@ -14,10 +14,20 @@ constexpr int kDecodeThreads = 256;                 // 4 wavefronts per workgrou
 constexpr int kDecodeWaves = kDecodeThreads / kWave;
 constexpr int kPlanThreads = 1024;                  // work-list builder: one workgroup
 // A decode work item covers up to two consecutive 512-token partitions of one
-// (sequence, KV head): the waves keep one state per partition and meet once per
-// item, while each partition still yields its own partial for the merge.
+// (sequence, KV head); on the matrix cores its waves keep one softmax state
+// for the whole item, meet once at its end and write one partial result.
 constexpr int kItemParts = 2;
 constexpr int kItemBlocks = kItemParts * kPartBlocks;
+// Flags in a decode record's partition field (partition numbers stay below
+// 2^16): the item covers that one partition only; the sequence's context
+// length was not clamped, so its new token (position ctx - 1) is the one the
+// append form stores; the item is the sequence's only one.
+constexpr int kOnePartition = 1 << 16;
+constexpr int kAppendable = 1 << 17;
+// (and, for the matrix-core kernel, which writes one partial per item: the
+// item is the sequence's only one, so its result is the output)
+constexpr int kWholeSequence = 1 << 18;
+constexpr int kPartitionMask = kOnePartition - 1;
 
 struct DecodeParams {
   void* out;

@@ -141,8 +141,9 @@ __global__ __launch_bounds__(kMfmaThreads, kMfmaWavesPerSimd) void decode_partit
 
   // One work item as this wave sees it.
   struct Item {
-    int s, part, g, ctx, nparts, b_begin, nmine;  // part: first of the item's partitions
-    int nslots;                                    // partitions the item covers (1 .. kItemParts)
+    int s, part, g, ctx, b_begin, nmine;  // part: first of the item's partitions
+    bool whole;                            // the sequence's only item: its result is the output
+    int slot;                              // else the item's partial: its slot in the row
     int64_t row0;       // first q head (row of q / out) of the KV head group
     int my_id;          // lane k < nmine: id of the wave's k-th block
     int k_lane, v_lane; // this lane's byte offsets inside a block
@@ -167,24 +168,29 @@ __global__ __launch_bounds__(kMfmaThreads, kMfmaWavesPerSimd) void decode_partit
   auto make_item = [&](int tk, int4 r, Item& it) {
     it.g = tk % p.Hkv;
     it.s = r.x;
-    it.part = r.y;
+    it.part = r.y & kPartitionMask;
     it.ctx = r.z;
-    it.nparts = max(1, (it.ctx + kPartTokens - 1) / kPartTokens);
+    it.whole = (r.y & kWholeSequence) != 0;
+    {
+      // slots: the full items in order, then the pieces of the last item
+      const int nparts = max(1, (it.ctx + kPartTokens - 1) / kPartTokens);
+      const int full_end = (nparts + kItemParts - 1) / kItemParts * kItemParts - kItemParts;
+      it.slot = it.part < full_end ? it.part / kItemParts : full_end / kItemParts + (it.part - full_end);
+    }
     const int nblk = (it.ctx + kBlockTokens - 1) / kBlockTokens;
     it.b_begin = it.part * kPartBlocks;
-    const int in_item = min(kItemBlocks, nblk - it.b_begin);
-    it.nslots = max(1, (in_item + kPartBlocks - 1) / kPartBlocks);
+    const int in_item = min((r.y & kOnePartition) ? kPartBlocks : kItemBlocks, nblk - it.b_begin);
     it.nmine = max(0, (in_item - wave + NWAVE - 1) / NWAVE);
     it.row0 = (int64_t)r.w * Hq + (int64_t)it.g * G;  // r.w: the sequence's query row
     it.k_lane = (int)(h * tok_bytes + (it.g * D + 8 * j) * 2);
     it.v_lane = (int)(4 * j * tok_bytes + (it.g * D + EPL * h) * 2);
     it.k_new = -1;
     it.new_row = 0;
-    if (p.knew != nullptr && it.ctx >= 1) {
-      // a context clamped to the workspace bound has no new token to append
-      const int raw = ((const __attribute__((address_space(4))) int*)(const void*)p.ctx)[it.s];
+    if (p.knew != nullptr && it.ctx >= 1 && (r.y & kAppendable)) {
+      // (a context clamped to the workspace bound has no new token to append;
+      // the plan leaves kAppendable out of its records)
       const int bn = (it.ctx - 1) / kBlockTokens - it.b_begin;  // item-relative block
-      if (raw == it.ctx && bn >= 0 && bn < in_item && bn % NWAVE == wave) {
+      if (bn >= 0 && bn < in_item && bn % NWAVE == wave) {
         it.k_new = bn / NWAVE;
         it.new_row = (it.ctx - 1) % kBlockTokens;
       }
@@ -329,10 +335,10 @@ __global__ __launch_bounds__(kMfmaThreads, kMfmaWavesPerSimd) void decode_partit
     }
   };
 
-  // [item parity][partition of the item][wave]
-  __shared__ float s_m[2][kItemParts][NWAVE][G];
-  __shared__ float s_l[2][kItemParts][NWAVE][G];
-  __shared__ float s_o[2][kItemParts][NWAVE][G][D];
+  // [item parity][wave]
+  __shared__ float s_m[2][NWAVE][G];
+  __shared__ float s_l[2][NWAVE][G];
+  __shared__ float s_o[2][NWAVE][G][D];
   __shared__ int s_ticket[2];  // by item parity
 
   // Tickets run two items ahead: while item i is computed the wave already
@@ -340,7 +346,11 @@ __global__ __launch_bounds__(kMfmaThreads, kMfmaWavesPerSimd) void decode_partit
   // Each workgroup's first two tickets are static (blockIdx.x and blockIdx.x +
   // gridDim.x); the counter hands out the rest, from 2 * gridDim.x on, so the
   // launch does not start with every workgroup queueing on one atomic.
+  // The first record is loaded with the ticket count, not after it: its
+  // index blockIdx.x / Hkv is below the list's capacity (the grid is at most
+  // capacity x Hkv), and a workgroup past the count returns before using it.
   const int tk0 = blockIdx.x;
+  const int4 rec0 = load_rec(tk0);
   if (tk0 >= total) return;
   int tk1 = blockIdx.x + gridDim.x;
   bool have1 = tk1 < total;
@@ -351,7 +361,7 @@ __global__ __launch_bounds__(kMfmaThreads, kMfmaWavesPerSimd) void decode_partit
   // masked, so they leave the running state unchanged.
   Blk buf[NBUF];
   Item cur, nxt;
-  make_item(tk0, load_rec(tk0), cur);
+  make_item(tk0, rec0, cur);
   load_ids(cur);
 #pragma unroll
   for (int c = 0; c < NKC; ++c) kn_cur[c] = kn_nxt[c];
@@ -362,32 +372,32 @@ __global__ __launch_bounds__(kMfmaThreads, kMfmaWavesPerSimd) void decode_partit
   int4 rec1 = have1 ? load_rec(tk1) : make_int4(0, 0, 0, 0);
 
   // Cross-wave merge of a finished item whose wave states are in LDS half
-  // `par`: per (partition, head, dim), the four waves' states combined by
-  // log-sum-exp; written to out (single-partition context) or to the partials.
-  // Each wave takes a quarter of the elements.
+  // `par`: per (head, dim), the four waves' states combined by log-sum-exp;
+  // written to out (the sequence's only item) or to the item's partial: one
+  // partial per item, whatever the number of partitions it covers (slot k for
+  // the k-th full item, then one per piece of the last item).
+  // Each thread takes G * D / 256 elements.
   auto merge = [&](const Item& it, int par) {
-    const int nslots = it.nslots;
-    for (int idx = threadIdx.x; idx < nslots * G * D; idx += kMfmaThreads) {
-      const int slot = idx / (G * D);
-      const int hh = (idx / D) % G;
+    for (int idx = threadIdx.x; idx < G * D; idx += kMfmaThreads) {
+      const int hh = idx / D;
       const int d = idx % D;
       float M = -INFINITY;
 #pragma unroll
-      for (int w = 0; w < NWAVE; ++w) M = fmaxf(M, s_m[par][slot][w][hh]);
+      for (int w = 0; w < NWAVE; ++w) M = fmaxf(M, s_m[par][w][hh]);
       float L = 0.f, O = 0.f;
       if (M != -INFINITY) {
 #pragma unroll
         for (int w = 0; w < NWAVE; ++w) {
-          const float f = exp2_fast(s_m[par][slot][w][hh] - M);
-          L = fmaf(s_l[par][slot][w][hh], f, L);
-          O = fmaf(s_o[par][slot][w][hh][d], f, O);
+          const float f = exp2_fast(s_m[par][w][hh] - M);
+          L = fmaf(s_l[par][w][hh], f, L);
+          O = fmaf(s_o[par][w][hh][d], f, O);
         }
       }
       const float r = L > 0.f ? O / L : 0.f;
-      if (it.nparts == 1) {
+      if (it.whole) {
         store_out<true>(p.out, (it.row0 + hh) * D + d, r);
       } else {
-        const int64_t pr = (it.row0 + hh) * p.max_parts + it.part + slot;
+        const int64_t pr = (it.row0 + hh) * p.max_parts + it.slot;
         p.part_o[pr * D + d] = r;
         if (d == 0) {
           p.part_m[pr] = M;
@@ -405,59 +415,64 @@ __global__ __launch_bounds__(kMfmaThreads, kMfmaWavesPerSimd) void decode_partit
   bool pending = false;
   int parity = 0;
   for (;; parity ^= 1) {
-    if (have1) {
-      make_item(tk1, rec1, nxt);
-      load_ids(nxt);
-    }
+    // The next item's record (loaded after the last barrier) is read after
+    // this item's first block, not here: waiting for it here would leave only
+    // the pre-issued first block of each wave in flight.
+    bool nxt_ready = !have1;
+    auto take_next = [&]() {
+      if (!nxt_ready) {
+        make_item(tk1, rec1, nxt);
+        load_ids(nxt);
+        nxt_ready = true;
+      }
+    };
     // (left unset in other lanes: like the ids, its register is written by the
     // atomic alone, so nothing waits for the loads in flight before it is issued)
     int fetched;
     if (threadIdx.x == 0) fetched = atomicAdd(&p.sched[0], 1);  // offset added where it is read
 
-    // Wave state of one partition to LDS (the item's partitions meet at the
-    // barrier), then a fresh state.  The wave's k-th block is block wave + 4k of
-    // the item, so its blocks kSplit*i .. kSplit*(i+1) - 1 belong to the item's
-    // partition i.
-    constexpr int kSplit = kPartBlocks / NWAVE;
+    // The wave's state over its blocks of the item goes to LDS at the end of
+    // the item (the four waves' states meet at the barrier).
     auto reset = [&]() {
       m = -INFINITY;
       l = 0.f;
 #pragma unroll
       for (int e = 0; e < EPL; ++e) acc[e] = f32x4{0.f, 0.f, 0.f, 0.f};
     };
-    auto save = [&](int slot) {
+    auto save = [&]() {
       const float lt = sum_over_rows(l);
       if (h < G) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
 #pragma unroll
-          for (int e = 0; e < EPL; ++e) s_o[parity][slot][wave][h][EPL * (4 * j + i) + e] = acc[e][i];
+          for (int e = 0; e < EPL; ++e) s_o[parity][wave][h][EPL * (4 * j + i) + e] = acc[e][i];
         }
         if (j == 0) {
-          s_m[parity][slot][wave][h] = m;
-          s_l[parity][slot][wave][h] = lt;
+          s_m[parity][wave][h] = m;
+          s_l[parity][wave][h] = lt;
         }
       }
-      reset();
     };
     reset();
-    int saved = 0;  // partitions of this item whose state the wave has stored
     const int rounds = (cur.nmine + NBUF - 1) / NBUF;
     for (int r = 0; r < rounds; ++r) {
 #pragma unroll
       for (int u = 0; u < NBUF; ++u) {
         const int k = r * NBUF + u;
-        if (k > 0 && k % kSplit == 0 && saved < kItemParts) save(saved++);  // uniform
         issue(cur, r * NBUF + u + NBUF - 1, buf[(u + NBUF - 1) % NBUF]);
         if (k == cur.k_new) append(buf[u], cur, k);  // uniform
         compute(buf[u]);
-        if (u == 0 && r == 0 && pending) {
-          merge(prev, parity ^ 1);
-          pending = false;
+        if (u == 0 && r == 0) {
+          take_next();
+          if (pending) {
+            merge(prev, parity ^ 1);
+            pending = false;
+          }
         }
       }
     }
-    if (pending) {  // the wave had no block in this item
+    take_next();    // the wave had no block in this item
+    if (pending) {
       merge(prev, parity ^ 1);
       pending = false;
     }
@@ -478,7 +493,7 @@ __global__ __launch_bounds__(kMfmaThreads, kMfmaWavesPerSimd) void decode_partit
     }
 
     // the partition the wave ended in, and empty states for any it never reached
-    while (saved < done.nslots) save(saved++);
+    save();
     __syncthreads();
     const int tk2 = 2 * (int)gridDim.x + __builtin_amdgcn_readfirstlane(s_ticket[parity]);
     const bool have2 = have1 && tk2 < total;

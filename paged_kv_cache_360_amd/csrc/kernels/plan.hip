@@ -11,10 +11,16 @@
 //
 // Outputs (all in the caller's workspace):
 //  * decode records {sequence, first partition, context, query row}, one per
-//    kItemParts consecutive partitions: every item but a sequence's last (all
-//    full, kItemBlocks blocks) first, then each sequence's last item in
-//    decreasing block count (a counting sort over the kItemBlocks + 1 possible
-//    counts), so the persistent run ends on its shortest items;
+//    kItemParts consecutive partitions.  In front: every item but a sequence's
+//    last (all full, kItemBlocks blocks), and the only item of a sequence with
+//    one item when it has more than kTailBlocks blocks.  Then the tail, in
+//    decreasing block count (a counting sort over the kTailBlocks + 1 possible
+//    counts): the other last items, where the last item of a sequence with
+//    several items is split into one-partition records (first partition field
+//    | kOnePartition) when it covers more than one partition, so that the
+//    persistent run ends on items of at most one partition, the shortest last.
+//    The field also carries kAppendable when the context length was not
+//    clamped, and kWholeSequence on a sequence's only record;
 //  * prefill records, two int4 each: {sequence, first partition, context, first
 //    query row} and {rows, ctx - q + r0 + 1, span, 0} (row i of the group sees
 //    max(0, that + i) keys; negative when the chunk is longer than the context);
@@ -22,10 +28,11 @@
 //    up to the one the group's last row reaches).  The span is 2 when halving
 //    the item count still leaves every compute unit the same number of rounds
 //    of items (then each row writes half the partial results), else 1;
-//  * row_slots[T]: the partial results each query row's merge combines: its
-//    partition count for a decode row, its item count (partitions / span,
-//    rounded up) for a prefill row; 1 for a row written directly (or with no
-//    keys), 0 for rows no sequence owns;
+//  * row_slots[T]: the partial results each query row's merge combines: for a
+//    decode row, its record count when the partition kernel writes one partial
+//    per record (bf16, on the matrix cores), else its partition count (fp32);
+//    its item count (partitions / span, rounded up) for a prefill row; 1 for a
+//    row written directly (or with no keys), 0 for rows no sequence owns;
 //  * sched: both ticket counters reset, and each list's ticket count (records
 //    times KV heads: ticket t is record t / Hkv, KV head t % Hkv).
 // One workgroup; per-thread counts are scanned with lane shuffles and one
@@ -46,8 +53,9 @@ __device__ __forceinline__ void plan_body(
     const int32_t* __restrict__ ctx, const int32_t* __restrict__ qsl, int32_t S, int32_t T,
     int32_t ctx_cap, int32_t Hkv, int32_t rows_per_item, int32_t dec_cap, int32_t pre_cap,
     int32_t num_cus, int32_t* __restrict__ sched, int4* __restrict__ dec, int4* __restrict__ pre,
-    int32_t* __restrict__ row_slots) {
-  constexpr int NBK = kItemBlocks + 1;  // buckets: last-item block count kItemBlocks .. 0
+    int32_t* __restrict__ row_slots, bool record_slots) {
+  constexpr int kTailBlocks = 2 * kPartBlocks;  // largest record sorted into the tail
+  constexpr int NBK = kTailBlocks + 1;          // buckets: tail-record block count kTailBlocks .. 0
   __shared__ int32_t s_wsum[kPlanThreads / kWave][3];  // per wave: full items, prefill records at span 1, 2
   __shared__ int32_t s_bucket[NBK];
   const int t = threadIdx.x;
@@ -60,9 +68,10 @@ __device__ __forceinline__ void plan_body(
   auto first_row = [&](int s) { return qsl ? min(max(qsl[s], 0), T) : s; };
   auto rows_of = [&](int s) { return qsl ? max(0, min(qsl[s + 1], T) - first_row(s)) : 1; };
   auto items_of = [&](int n) { return (n + kItemParts - 1) / kItemParts; };
-  auto last_bucket = [&](int c, int n) {  // 0 for a full last item, kItemBlocks for an empty one
-    return kItemBlocks - ((c + kBlockTokens - 1) / kBlockTokens - (items_of(n) - 1) * kItemBlocks);
+  auto last_blocks = [&](int c, int n) {  // blocks of the last item: kItemBlocks when full, 0 when empty
+    return (c + kBlockTokens - 1) / kBlockTokens - (items_of(n) - 1) * kItemBlocks;
   };
+  auto bucket_of = [&](int blocks) { return kTailBlocks - blocks; };
   // prefill: the keys seen by row r of a sequence with q rows and c keys
   auto row_keys_of = [&](int c, int q, int r) { return max(0, c - q + r + 1); };
 
@@ -70,17 +79,28 @@ __device__ __forceinline__ void plan_body(
   for (int r = t; r < T; r += kPlanThreads) row_slots[r] = 0;  // rows no sequence owns: nothing to merge
   __syncthreads();
   int full = 0, npre = 0, npre2 = 0;
-  int own_c = 0, own_q = 0, own_row0 = 0;  // this thread's (last) sequence, for the write loop
+  int own_c = 0, own_q = 0, own_row0 = 0, own_raw = 0;  // this thread's (last) sequence, for the write loop
   for (int s = s0; s < s1; ++s) {
     const int c = ctx_of(s);
     const int q = rows_of(s);
+    own_raw = ctx[s];
     own_c = c;
     own_q = q;
     own_row0 = first_row(s);
     if (q == 1) {
       const int n = parts_of(c);
-      full += items_of(n) - 1;
-      atomicAdd(&s_bucket[last_bucket(c, n)], 1);
+      const int ni = items_of(n);
+      const int lb = last_blocks(c, n);
+      if (ni == 1) {                 // the sequence's only record
+        if (lb > kTailBlocks) ++full; else atomicAdd(&s_bucket[bucket_of(lb)], 1);
+      } else {
+        full += ni - 1;
+        if (lb > kPartBlocks) {      // the last item in one-partition pieces
+          for (int b = lb; b > 0; b -= kPartBlocks) atomicAdd(&s_bucket[bucket_of(min(b, kPartBlocks))], 1);
+        } else {
+          atomicAdd(&s_bucket[bucket_of(lb)], 1);
+        }
+      }
     } else if (q > 1) {
       for (int r0 = 0; r0 < q; r0 += rows_per_item) {
         const int n = parts_of(row_keys_of(c, q, min(q, r0 + rows_per_item) - 1));
@@ -153,13 +173,35 @@ __device__ __forceinline__ void plan_body(
     const int q = per == 1 ? own_q : rows_of(s);
     if (q != 1) continue;
     const int row0 = per == 1 ? own_row0 : first_row(s);
+    const int app = (per == 1 ? own_raw : ctx[s]) == c ? kAppendable : 0;
     const int n = parts_of(c);
     const int ni = items_of(n);
     for (int k = 0; k < ni - 1; ++k, ++od)
-      if (od < dec_cap) dec[od] = make_int4(s, k * kItemParts, c, row0);
-    const int at = atomicAdd(&s_bucket[last_bucket(c, n)], 1);
-    if (at < dec_cap) dec[at] = make_int4(s, (ni - 1) * kItemParts, c, row0);
-    row_slots[row0] = parts_of(c);
+      if (od < dec_cap) dec[od] = make_int4(s, (k * kItemParts) | app, c, row0);
+    const int lb = last_blocks(c, n);
+    const int p0 = (ni - 1) * kItemParts;
+    int recs = ni;
+    if (ni == 1) {
+      const int4 rec = make_int4(s, p0 | app | kWholeSequence, c, row0);
+      if (lb > kTailBlocks) {
+        if (od < dec_cap) dec[od] = rec;
+        ++od;
+      } else {
+        const int at = atomicAdd(&s_bucket[bucket_of(lb)], 1);
+        if (at < dec_cap) dec[at] = rec;
+      }
+    } else if (lb > kPartBlocks) {
+      int j = 0;
+      for (int b = lb; b > 0; b -= kPartBlocks, ++j) {
+        const int at = atomicAdd(&s_bucket[bucket_of(min(b, kPartBlocks))], 1);
+        if (at < dec_cap) dec[at] = make_int4(s, (p0 + j) | kOnePartition | app, c, row0);
+      }
+      recs = ni - 1 + j;
+    } else {
+      const int at = atomicAdd(&s_bucket[bucket_of(lb)], 1);
+      if (at < dec_cap) dec[at] = make_int4(s, p0 | app, c, row0);
+    }
+    row_slots[row0] = record_slots ? recs : n;
   }
   auto next_prefill = [&](int from) {
     for (int s = from; s < s1; ++s)
@@ -210,8 +252,9 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(
     const int32_t* __restrict__ ctx, const int32_t* __restrict__ qsl, int32_t S, int32_t T,
     int32_t ctx_cap, int32_t Hkv, int32_t rows_per_item, int32_t dec_cap, int32_t pre_cap,
     int32_t num_cus, int32_t* __restrict__ sched, int4* __restrict__ dec, int4* __restrict__ pre,
-    int32_t* __restrict__ row_slots) {
-  plan_body(ctx, qsl, S, T, ctx_cap, Hkv, rows_per_item, dec_cap, pre_cap, num_cus, sched, dec, pre, row_slots);
+    int32_t* __restrict__ row_slots, bool record_slots) {
+  plan_body(ctx, qsl, S, T, ctx_cap, Hkv, rows_per_item, dec_cap, pre_cap, num_cus, sched, dec, pre, row_slots,
+            record_slots);
 }
 
 // Loads in flight per thread in the staging copy (reads cross the host link).
@@ -241,7 +284,7 @@ __global__ __launch_bounds__(kPlanThreads) void upload_plan_kernel(
     int64_t m_rows) {
   if (blockIdx.x == 0) {
     plan_body(host_ctx, nullptr, S, S, ctx_cap, Hkv, /*rows_per_item, unused without prefill rows*/ 1, dec_cap, 0,
-              num_cus, sched, dec, nullptr, row_slots);
+              num_cus, sched, dec, nullptr, row_slots, BF16);
     return;
   }
   if ((int)blockIdx.x <= n_up) {
@@ -295,7 +338,7 @@ int launch_plan(const DecodeArgs& a, void* stream) {
   hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, (hipStream_t)stream, a.ctx, a.qsl,
                      a.num_seqs, a.num_tokens, p.ctx_cap, a.num_kv_heads, prefill_rows_per_item(G),
                      a.dec_cap, a.pre_cap, a.num_cus, a.sched, reinterpret_cast<int4*>(a.dec_recs),
-                     reinterpret_cast<int4*>(a.pre_recs), a.row_slots);
+                     reinterpret_cast<int4*>(a.pre_recs), a.row_slots, a.bf16);
   return (int)hipGetLastError();
 }
 
