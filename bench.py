@@ -832,10 +832,13 @@ def mixed_main(args, spec):
     Sequence 0 holds a context of spec.chunk_ctx tokens whose last spec.chunk_rows
     are the chunk's query rows (written every step into the same slots, so each
     step has the same shape); sequences 1..S append one decode token per step.
-    One step = host allocation into pinned staging + one H2D copy on a side
-    stream + pkv_write of all new rows + pkv_attention_varlen (plan, decode
-    partitions, prefill tiles, merge).  The write and attention launches of
-    every ev_every(K)-th timed step are bracketed by events.
+    One step, all on the compute stream = host allocation into pinned staging
+    + pkv_attention_varlen_plan_upload (the work lists planned from the pinned
+    lengths while the step's slots, lengths and used table entries are copied
+    to the device, one launch) + pkv_write of all new rows from the uploaded
+    slots + pkv_attention_varlen_partitions (decode partitions, prefill tiles,
+    merge).  The upload + plan, write and attention launches of every
+    ev_every(K)-th timed step are bracketed by events.
     """
     import numpy as np
     import torch
@@ -879,20 +882,20 @@ def mixed_main(args, spec):
     scale = float(np.float32(1.0 / math.sqrt(D)))
     qsl = torch.from_numpy(np.concatenate([[0], C + np.arange(S + 1)]).astype(np.int32)).cuda()
 
-    # pinned staging, two sets: [slots T | lens S+1 | tables (S+1)*MB] int32
-    meta_len = T + (S + 1) + (S + 1) * MB
-    stage = [torch.empty(meta_len, dtype=torch.int32, pin_memory=True) for _ in range(2)]
-    dmeta = [torch.empty(meta_len, dtype=torch.int32, device="cuda") for _ in range(2)]
+    # pinned staging, two sets: [slots T | lens S+1 | pad to 16 bytes | tables
+    # (S+1)*MB] int32; the slots and lengths go up as bytes, the tables by rows
+    head = T + (S + 1) + (-(T + S + 1)) % 4
+    meta_len = head + (S + 1) * MB
+    stage = [torch.zeros(meta_len, dtype=torch.int32, pin_memory=True) for _ in range(2)]
+    dmeta = [torch.zeros(meta_len, dtype=torch.int32, device="cuda") for _ in range(2)]
     views = []
     for b in range(2):
         h = stage[b].numpy()
         h[:C] = chunk_slots                               # the chunk rewrites the same slots each step
-        views.append((h[:T], h[T:T + S + 1], h[T + S + 1:].reshape(S + 1, MB)))
+        views.append((h[:T], h[T:T + S + 1], h[head:].reshape(S + 1, MB)))
     ones = np.ones(S, np.int32)
     main = torch.cuda.current_stream()
-    side = torch.cuda.Stream()                            # default priority
-    h2d_done = [torch.cuda.Event() for _ in range(2)]
-    kern_done = [torch.cuda.Event() for _ in range(2)]
+    up_done = [torch.cuda.Event() for _ in range(2)]     # the upload launch of staging set b has run
     events, lens_log = [], []
 
     # direct C-ABI calls with precomputed pointers (as in the decode step)
@@ -903,38 +906,38 @@ def mixed_main(args, spec):
     kc_p = [t.data_ptr() for t in kcs]
     vc_p = [t.data_ptr() for t in vcs]
     dptr = [m.data_ptr() for m in dmeta]
+    sptr = [st.data_ptr() for st in stage]
     qsl_p, ws_p, ws_n, main_h = qsl.data_ptr(), ws.data_ptr(), ws.numel(), main.cuda_stream
 
     def step(i, timed):
         b = i % 2
         slots_h, lens_h, tables_h = views[b]
-        h2d_done[b].synchronize()                         # staging set b is free (copy of step i-2 done)
+        up_done[b].synchronize()                          # staging set b is free (step i-2's upload ran)
         _, pairs = alloc.append_batch(ids[1:], ones, slots_out=slots_h[C:])
         alloc.block_tables(ids, MB, fill=-1, tables_out=tables_h, lens_out=lens_h)
         r = i % R
-        with torch.cuda.stream(side):
-            side.wait_event(kern_done[b])                 # device set b no longer read by step i-2
-            dmeta[b].copy_(stage[b], non_blocking=True)
-            h2d_done[b].record(side)
-        main.wait_event(h2d_done[b])
         bracket = timed and (i - W) % ev_every(K) == 0
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)] if bracket else None
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)] if bracket else None
         if timed:
             lens_log.append(lens_h.copy())
         if bracket:
             ev[0].record(main)
         d = dptr[b]
+        args = (out_p, q0 + i * q_stride, kc_p[r], vc_p[r], d + 4 * head, d + 4 * T, qsl_p, T, C, scale, 16,
+                Hq, Hkv, D, S + 1, MB, nb, max_ctx, pkv.PKV_BF16, ws_p, ws_n)
+        check("pkv_attention_varlen_plan_upload", L.pkv_attention_varlen_plan_upload(
+            *args, sptr[b] + 4 * T, sptr[b], d, 4 * head, sptr[b] + 4 * head, main_h))
+        up_done[b].record(main)
+        if bracket:
+            ev[1].record(main)
         check("pkv_write", L.pkv_write(kc_p[r], vc_p[r], knew0 + i * kv_stride, vnew0 + i * kv_stride, d, T, nb,
                                        16, Hkv, D, pkv.PKV_BF16, main_h))
         if bracket:
-            ev[1].record(main)
-        check("pkv_attention_varlen", L.pkv_attention_varlen(
-            out_p, q0 + i * q_stride, kc_p[r], vc_p[r], d + 4 * (T + S + 1), d + 4 * T, qsl_p, T, C, scale, 16,
-            Hq, Hkv, D, S + 1, MB, nb, max_ctx, pkv.PKV_BF16, ws_p, ws_n, main_h))
-        if bracket:
             ev[2].record(main)
+        check("pkv_attention_varlen_partitions", L.pkv_attention_varlen_partitions(*args, main_h))
+        if bracket:
+            ev[3].record(main)
             events.append(ev)
-        kern_done[b].record(main)
 
     for i in range(W):
         step(i, False)
@@ -944,8 +947,9 @@ def mixed_main(args, spec):
         step(i, True)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    t_write = [e[0].elapsed_time(e[1]) * 1e-3 for e in events]
-    t_attn = [e[1].elapsed_time(e[2]) * 1e-3 for e in events]
+    t_up = [e[0].elapsed_time(e[1]) * 1e-3 for e in events]
+    t_write = [e[1].elapsed_time(e[2]) * 1e-3 for e in events]
+    t_attn = [e[2].elapsed_time(e[3]) * 1e-3 for e in events]
     # algorithmic bytes of the attention call: K/V each row group reads once
     # (decode rows: their context; the chunk: its 4096-token context), q, out,
     # and the partials of rows spanning several partitions
@@ -995,12 +999,13 @@ def mixed_main(args, spec):
         "config": {"workload": spec.name, "chunk_rows": C, "chunk_context": CC, "decode_seqs": S,
                    "num_q_heads": Hq, "num_kv_heads": Hkv, "head_dim": D, "block_size": 16,
                    "partition_tokens": 512, "pool_blocks": nb, "pool_copies": R, "seed": args.seed},
-        "kernels_us": {"write": round(float(np.mean(t_write)) * 1e6, 2),
-                       "varlen_call": round(ta * 1e6, 2)},
+        "kernels_us": {"upload_plan": round(float(np.mean(t_up)) * 1e6, 2),
+                       "write": round(float(np.mean(t_write)) * 1e6, 2),
+                       "varlen_partitions": round(ta * 1e6, 2)},
         "decode_tokens_per_s": round(S * K / wall, 1),
         "prefill_gflop_per_step": round(flops_prefill / 1e9, 2),
         "roofline": {
-            "kernel": "pkv_attention_varlen (plan + decode partitions + prefill tiles + merge)",
+            "kernel": "pkv_attention_varlen_partitions (decode partitions + prefill tiles + merge)",
             "bound": "hbm", "achieved": round(float(np.mean(att_b)) / ta / 1e9, 1),
             "peak": HBM_PEAK_GBPS, "unit": "GB/s",
             "frac": round(float(np.mean(att_b)) / ta / 1e9 / HBM_PEAK_GBPS, 4), "traffic": None,

@@ -157,9 +157,10 @@ int pkv_attention_decode_noalloc(void* out, const void* q, const void* key_cache
  * beside pkv_write -- if the caller orders it before _partitions.  It launches
  * nothing for fp32 when max_context_len <= PKV_PARTITION_TOKENS (the fp32
  * kernel reads no work list, and there is nothing to merge).
- * _partitions: computes every (sequence, KV head, 512-token partition) of the
- * planned work list; writes `out` for sequences with a single partition and the
- * partials (max, sum, normalized output) of the others to the workspace.
+ * _partitions: computes every work item of the planned list (a sequence, a KV
+ * head, one or two 512-token partitions); writes `out` for sequences whose
+ * context one item covers and partial results (max, sum, normalized output)
+ * of the others to the workspace (bf16: one per item; fp32: one per partition).
  * _merge: log-sum-exp merge of those partials into `out` (launches nothing when
  * max_context_len <= PKV_PARTITION_TOKENS).
  * All three take the same workspace; run them in this order.  Errors as
@@ -294,6 +295,39 @@ int pkv_attention_varlen(void* out, const void* q, const void* key_cache, const 
                          int32_t head_dim, int32_t num_seqs, int32_t max_blocks_per_seq,
                          int32_t num_blocks, int32_t max_context_len, pkv_dtype dt, void* workspace,
                          size_t workspace_bytes, void* stream);
+/* pkv_attention_varlen in two calls, for a step whose metadata the host has just
+ * written to page-locked memory ("How vLLM Works?", section 04: the scheduler
+ * batches a prefill chunk with decode rows every step, so the step's launches
+ * should cost little beside the kernels):
+ * _plan_upload: the plan (decode and prefill work lists from host_context_lens,
+ * page-locked, num_seqs values, and from query_start_loc, device) fused with
+ * the upload of the step's metadata in one launch on `stream`, as
+ * pkv_attention_decode_plan_upload does for decode (upload_src -> upload_dst,
+ * upload_bytes a multiple of 16; host_block_tables NULL or page-locked
+ * [num_seqs, max_blocks_per_seq], of which each row's used entries go to
+ * block_tables).  The uploaded slots can feed a pkv_write on the same stream
+ * before _partitions.  num_seqs and num_tokens must be > 0.
+ * _partitions: the launches after the plan (decode partitions, prefill tiles,
+ * log-sum-exp merge), same arguments and workspace.
+ * Results equal pkv_attention_varlen's byte for byte.  Errors as
+ * pkv_attention_varlen, and PKV_EINVAL for host or device buffers of the wrong
+ * kind (checked with the HIP runtime). */
+int pkv_attention_varlen_plan_upload(void* out, const void* q, const void* key_cache, const void* value_cache,
+                                     const int32_t* block_tables, const int32_t* context_lens,
+                                     const int32_t* query_start_loc, int32_t num_tokens, int32_t max_query_len,
+                                     float scale, int32_t block_size, int32_t num_q_heads, int32_t num_kv_heads,
+                                     int32_t head_dim, int32_t num_seqs, int32_t max_blocks_per_seq,
+                                     int32_t num_blocks, int32_t max_context_len, pkv_dtype dt, void* workspace,
+                                     size_t workspace_bytes, const int32_t* host_context_lens,
+                                     const void* upload_src, void* upload_dst, size_t upload_bytes,
+                                     const int32_t* host_block_tables, void* stream);
+int pkv_attention_varlen_partitions(void* out, const void* q, const void* key_cache, const void* value_cache,
+                                    const int32_t* block_tables, const int32_t* context_lens,
+                                    const int32_t* query_start_loc, int32_t num_tokens, int32_t max_query_len,
+                                    float scale, int32_t block_size, int32_t num_q_heads, int32_t num_kv_heads,
+                                    int32_t head_dim, int32_t num_seqs, int32_t max_blocks_per_seq,
+                                    int32_t num_blocks, int32_t max_context_len, pkv_dtype dt, void* workspace,
+                                    size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------ */
 /* Log-sum-exp merge of partial softmax results, one output row per input row.

@@ -23,6 +23,8 @@ from .ops import (  # noqa: F401
     pkv_decode_workspace_bytes,
     decode_workspace,
     pkv_attention_varlen,
+    pkv_attention_varlen_plan_upload,
+    pkv_attention_varlen_partitions,
     pkv_varlen_workspace_bytes,
     varlen_workspace,
     pkv_lse_merge,

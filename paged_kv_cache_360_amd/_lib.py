@@ -57,6 +57,12 @@ SIGNATURES = {
     "pkv_varlen_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32, _i32]),
     "pkv_attention_varlen": (ctypes.c_int, [_p, _p, _p, _p, _p, _p, _p, _i32, _i32, _f32, _i32, _i32, _i32,
                                             _i32, _i32, _i32, _i32, _i32, ctypes.c_int, _p, _sz, _p]),
+    "pkv_attention_varlen_plan_upload": (ctypes.c_int, [_p, _p, _p, _p, _p, _p, _p, _i32, _i32, _f32, _i32, _i32,
+                                                        _i32, _i32, _i32, _i32, _i32, _i32, ctypes.c_int, _p, _sz,
+                                                        _p, _p, _p, _sz, _p, _p]),
+    "pkv_attention_varlen_partitions": (ctypes.c_int, [_p, _p, _p, _p, _p, _p, _p, _i32, _i32, _f32, _i32, _i32,
+                                                       _i32, _i32, _i32, _i32, _i32, _i32, ctypes.c_int, _p, _sz,
+                                                       _p]),
     "pkv_lse_merge": (ctypes.c_int, [_p, _p, _p, _p, _p, _i32, _i32, _i32, ctypes.c_int, _p]),
     "pkv_copy_blocks": (ctypes.c_int, [_p, _p, _p, _i32, _i32, _i32, _i32, _i32, ctypes.c_int, _p]),
     "pkv_swap_blocks": (ctypes.c_int, [_p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32, ctypes.c_int,

@@ -269,6 +269,46 @@ int prepare_attention(const char* who, pkv::DecodeArgs& a, void* out, const void
   return PKV_OK;
 }
 
+// The page-locked host buffers and device targets of a fused upload + plan
+// launch, checked with the HIP runtime; their device addresses on success.
+struct UploadPtrs {
+  const int32_t* hctx = nullptr;
+  const void* src = nullptr;
+  void* dst = nullptr;
+  const int32_t* htab = nullptr;
+};
+int check_upload(const char* who, int32_t num_seqs, int32_t max_blocks_per_seq, const int32_t* block_tables,
+                 const int32_t* host_context_lens, const void* upload_src, void* upload_dst, size_t upload_bytes,
+                 const int32_t* host_block_tables, UploadPtrs& up) {
+  char msg[200];
+  auto bad = [&](const char* what) {
+    std::snprintf(msg, sizeof(msg), "%s: %s", who, what);
+    return fail(PKV_EINVAL, msg);
+  };
+  void* hctx = nullptr;
+  if (!pkv::host_mapped(host_context_lens, (int64_t)num_seqs * 4, &hctx))
+    return bad("host_context_lens must be page-locked host memory");
+  void* src = nullptr;
+  if (upload_bytes > 0) {
+    if (!pkv::host_mapped(upload_src, (int64_t)upload_bytes, &src))
+      return bad("upload_src must be page-locked host memory");
+    if (!pkv::device_readable(upload_dst, (int64_t)upload_bytes)) return bad("upload_dst must be device memory");
+    if (!pkv::aligned16(src) || !pkv::aligned16(upload_dst)) return bad("upload buffers must be 16-byte aligned");
+    up.dst = upload_dst;
+  }
+  void* htab = nullptr;
+  if (host_block_tables != nullptr) {
+    const int64_t tab_bytes = (int64_t)num_seqs * max_blocks_per_seq * 4;
+    if (!pkv::host_mapped(host_block_tables, tab_bytes, &htab))
+      return bad("host_block_tables must be page-locked host memory");
+    if (!pkv::device_readable(block_tables, tab_bytes)) return bad("block_tables must be device memory");
+  }
+  up.hctx = static_cast<const int32_t*>(hctx);
+  up.src = src;
+  up.htab = static_cast<const int32_t*>(htab);
+  return PKV_OK;
+}
+
 }  // namespace
 
 #define PKV_DECODE_ARGS                                                                        \
@@ -308,28 +348,10 @@ int pkv_attention_decode_plan_upload(void* out, const void* q, const void* key_c
     return fail(PKV_EINVAL, "pkv_attention_decode_plan_upload: upload_bytes must be a multiple of 16");
   int rc = prepare_attention(who, a, PKV_DECODE_FWD);
   if (rc != PKV_OK) return rc;
-  void* hctx = nullptr;
-  if (!pkv::host_mapped(host_context_lens, (int64_t)num_seqs * 4, &hctx))
-    return fail(PKV_EINVAL, "pkv_attention_decode_plan_upload: host_context_lens must be page-locked host memory");
-  void* src = nullptr;
-  void* dst = nullptr;
-  if (upload_bytes > 0) {
-    if (!pkv::host_mapped(upload_src, (int64_t)upload_bytes, &src))
-      return fail(PKV_EINVAL, "pkv_attention_decode_plan_upload: upload_src must be page-locked host memory");
-    if (!pkv::device_readable(upload_dst, (int64_t)upload_bytes))
-      return fail(PKV_EINVAL, "pkv_attention_decode_plan_upload: upload_dst must be device memory");
-    dst = upload_dst;
-    if (!pkv::aligned16(src) || !pkv::aligned16(dst))
-      return fail(PKV_EINVAL, "pkv_attention_decode_plan_upload: upload buffers must be 16-byte aligned");
-  }
-  void* htab = nullptr;
-  if (host_block_tables != nullptr) {
-    const int64_t tab_bytes = (int64_t)num_seqs * max_blocks_per_seq * 4;
-    if (!pkv::host_mapped(host_block_tables, tab_bytes, &htab))
-      return fail(PKV_EINVAL, "pkv_attention_decode_plan_upload: host_block_tables must be page-locked host memory");
-    if (!pkv::device_readable(block_tables, tab_bytes))
-      return fail(PKV_EINVAL, "pkv_attention_decode_plan_upload: block_tables must be device memory");
-  }
+  UploadPtrs up{};
+  rc = check_upload(who, num_seqs, max_blocks_per_seq, block_tables, host_context_lens, upload_src, upload_dst,
+                    upload_bytes, host_block_tables, up);
+  if (rc != PKV_OK) return rc;
   pkv::DecodeArgs prev{};
   const pkv::DecodeArgs* prev_p = nullptr;
   if (merge_out != nullptr || merge_workspace != nullptr) {
@@ -343,8 +365,7 @@ int pkv_attention_decode_plan_upload(void* out, const void* q, const void* key_c
     if (rc != PKV_OK) return rc;
     prev_p = &prev;
   }
-  return pkv::launched(pkv::launch_upload_plan(a, static_cast<const int32_t*>(hctx), src, dst,
-                                               (int64_t)upload_bytes, static_cast<const int32_t*>(htab), prev_p,
+  return pkv::launched(pkv::launch_upload_plan(a, up.hctx, up.src, up.dst, (int64_t)upload_bytes, up.htab, prev_p,
                                                stream),
                        who);
 }
@@ -487,6 +508,67 @@ int pkv_attention_varlen(void* out, const void* q, const void* key_cache, const 
   if (rc != PKV_OK || num_seqs == 0 || num_tokens == 0) return rc;
   rc = pkv::launched(pkv::launch_plan(a, stream), who);
   if (rc != PKV_OK) return rc;
+  rc = pkv::launched(pkv::launch_decode_partitions(a, stream), who);
+  if (rc != PKV_OK) return rc;
+  rc = pkv::launched(pkv::launch_prefill(a, stream), who);
+  if (rc != PKV_OK) return rc;
+  return pkv::launched(pkv::launch_decode_merge(a, stream), who);
+}
+
+#define PKV_VARLEN_ARGS                                                                            \
+  void *out, const void *q, const void *key_cache, const void *value_cache,                        \
+      const int32_t *block_tables, const int32_t *context_lens, const int32_t *query_start_loc,     \
+      int32_t num_tokens, int32_t max_query_len, float scale, int32_t block_size, int32_t num_q_heads, \
+      int32_t num_kv_heads, int32_t head_dim, int32_t num_seqs, int32_t max_blocks_per_seq,         \
+      int32_t num_blocks, int32_t max_context_len, pkv_dtype dt, void *workspace, size_t workspace_bytes
+#define PKV_VARLEN_FWD                                                                             \
+  out, q, key_cache, value_cache, block_tables, context_lens, query_start_loc, num_tokens, max_query_len, \
+      scale, block_size, num_q_heads, num_kv_heads, head_dim, num_seqs, max_blocks_per_seq, num_blocks, \
+      max_context_len, dt, workspace, workspace_bytes
+
+namespace {
+int prepare_varlen(const char* who, pkv::DecodeArgs& a, PKV_VARLEN_ARGS) {
+  char msg[160];
+  if (dt != PKV_BF16) {
+    std::snprintf(msg, sizeof(msg), "%s: bf16 only", who);
+    return fail(PKV_EUNSUPPORTED, msg);
+  }
+  if (num_tokens > 0 && num_seqs > 0 && !query_start_loc) {
+    std::snprintf(msg, sizeof(msg), "%s: null query_start_loc", who);
+    return fail(PKV_EINVAL, msg);
+  }
+  return prepare_attention(who, a, out, q, key_cache, value_cache, block_tables, context_lens, query_start_loc,
+                           num_tokens, max_query_len, scale, block_size, num_q_heads, num_kv_heads, head_dim,
+                           num_seqs, max_blocks_per_seq, num_blocks, max_context_len, dt, workspace,
+                           workspace_bytes);
+}
+}  // namespace
+
+int pkv_attention_varlen_plan_upload(PKV_VARLEN_ARGS, const int32_t* host_context_lens, const void* upload_src,
+                                     void* upload_dst, size_t upload_bytes, const int32_t* host_block_tables,
+                                     void* stream) {
+  pkv::DecodeArgs a{};
+  const char* who = "pkv_attention_varlen_plan_upload";
+  if (num_seqs <= 0 || num_tokens <= 0)
+    return fail(PKV_EINVAL, "pkv_attention_varlen_plan_upload: num_seqs and num_tokens must be > 0");
+  if (upload_bytes % 16 != 0 || upload_bytes > (size_t)INT64_MAX)
+    return fail(PKV_EINVAL, "pkv_attention_varlen_plan_upload: upload_bytes must be a multiple of 16");
+  int rc = prepare_varlen(who, a, PKV_VARLEN_FWD);
+  if (rc != PKV_OK) return rc;
+  UploadPtrs up{};
+  rc = check_upload(who, num_seqs, max_blocks_per_seq, block_tables, host_context_lens, upload_src, upload_dst,
+                    upload_bytes, host_block_tables, up);
+  if (rc != PKV_OK) return rc;
+  return pkv::launched(pkv::launch_upload_plan(a, up.hctx, up.src, up.dst, (int64_t)upload_bytes, up.htab, nullptr,
+                                               stream),
+                       who);
+}
+
+int pkv_attention_varlen_partitions(PKV_VARLEN_ARGS, void* stream) {
+  pkv::DecodeArgs a{};
+  const char* who = "pkv_attention_varlen_partitions";
+  int rc = prepare_varlen(who, a, PKV_VARLEN_FWD);
+  if (rc != PKV_OK || num_seqs == 0 || num_tokens == 0) return rc;
   rc = pkv::launched(pkv::launch_decode_partitions(a, stream), who);
   if (rc != PKV_OK) return rc;
   rc = pkv::launched(pkv::launch_prefill(a, stream), who);

@@ -275,16 +275,17 @@ constexpr int kMergeRowsPerBlock = kPlanThreads / kWave;
 // and row counts live in another workspace than the one planned here.
 template <bool BF16, int D>
 __global__ __launch_bounds__(kPlanThreads) void upload_plan_kernel(
-    const int32_t* __restrict__ host_ctx, int32_t S, int32_t ctx_cap, int32_t Hkv, int32_t dec_cap,
-    int32_t num_cus, int32_t* __restrict__ sched, int4* __restrict__ dec, int32_t* __restrict__ row_slots,
+    const int32_t* __restrict__ host_ctx, const int32_t* __restrict__ qsl, int32_t S, int32_t T,
+    int32_t ctx_cap, int32_t Hkv, int32_t rows_per_item, int32_t dec_cap, int32_t pre_cap, int32_t num_cus,
+    int32_t* __restrict__ sched, int4* __restrict__ dec, int4* __restrict__ pre, int32_t* __restrict__ row_slots,
     const uint4* __restrict__ src, uint4* __restrict__ dst, int64_t n16, int32_t n_up,
     const int32_t* __restrict__ host_tables, int32_t* __restrict__ tables, int32_t MB, int32_t n_tab,
     void* __restrict__ m_out, const float* __restrict__ m_pm, const float* __restrict__ m_pl,
     const float* __restrict__ m_po, const int32_t* __restrict__ m_counts, int32_t Hq, int32_t m_max_parts,
     int64_t m_rows) {
   if (blockIdx.x == 0) {
-    plan_body(host_ctx, nullptr, S, S, ctx_cap, Hkv, /*rows_per_item, unused without prefill rows*/ 1, dec_cap, 0,
-              num_cus, sched, dec, nullptr, row_slots, BF16);
+    plan_body(host_ctx, qsl, S, T, ctx_cap, Hkv, rows_per_item, dec_cap, pre_cap, num_cus, sched, dec, pre,
+              row_slots, BF16);
     return;
   }
   if ((int)blockIdx.x <= n_up) {
@@ -361,8 +362,10 @@ int launch_upload_plan(const DecodeArgs& a, const int32_t* host_ctx, const void*
   const int D = merge ? prev->head_dim : a.head_dim;
 #define PKV_UPLOAD_PLAN_LAUNCH(B, DD)                                                                   \
   hipLaunchKernelGGL((upload_plan_kernel<B, DD>), grid, dim3(kPlanThreads), 0, (hipStream_t)stream, host_ctx, \
-                     a.num_seqs, p.ctx_cap, a.num_kv_heads, a.dec_cap, a.num_cus, a.sched,              \
-                     reinterpret_cast<int4*>(a.dec_recs), a.row_slots, reinterpret_cast<const uint4*>(src), \
+                     a.qsl, a.num_seqs, a.num_tokens, p.ctx_cap, a.num_kv_heads,                          \
+                     prefill_rows_per_item(a.num_q_heads / a.num_kv_heads), a.dec_cap, a.pre_cap, a.num_cus, \
+                     a.sched, reinterpret_cast<int4*>(a.dec_recs), reinterpret_cast<int4*>(a.pre_recs),    \
+                     a.row_slots, reinterpret_cast<const uint4*>(src),                                    \
                      reinterpret_cast<uint4*>(dst), n16, n_up, host_tables, const_cast<int32_t*>(a.tables), \
                      a.max_blocks, n_tab, m.out, m.part_m, m.part_l, m.part_o,                            \
                      m.row_slots, m.num_q_heads, m.max_parts, m_rows)

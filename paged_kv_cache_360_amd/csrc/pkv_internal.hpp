@@ -68,7 +68,8 @@ inline int32_t prefill_rows_per_item(int32_t G) { return 256 / G; }
 
 // Work-list plan: decode records, prefill records and per-row merge slot counts.
 int launch_plan(const DecodeArgs& a, void* stream);
-// Decode plan from a page-locked host copy of the context lengths (host_ctx,
+// Plan (decode, or varlen when a.qsl is set: query_start_loc is read from the
+// device) from a page-locked host copy of the context lengths (host_ctx,
 // its device address), fused with a copy of `bytes` (a multiple of 16) from
 // page-locked host memory src to device memory dst (device addresses), with
 // the copy of the used entries of each row of the page-locked host_tables

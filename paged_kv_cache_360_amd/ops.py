@@ -341,6 +341,64 @@ def pkv_attention_varlen(out, q, key_cache, value_cache, block_tables, context_l
     return out
 
 
+def _varlen_args(out, q, key_cache, value_cache, block_tables, context_lens, query_start_loc, scale,
+                 max_query_len, max_context_len, workspace):
+    t, hq, d = q.shape
+    nb, bs, hkv, dk = key_cache.shape
+    if out.shape != q.shape or dk != d or value_cache.shape != key_cache.shape:
+        raise ValueError("shape mismatch")
+    if out.dtype != q.dtype or key_cache.dtype != q.dtype or value_cache.dtype != q.dtype:
+        raise TypeError("q, caches and out must share one dtype")
+    s = context_lens.shape[0]
+    if block_tables.dim() != 2 or block_tables.shape[0] != s or query_start_loc.shape != (s + 1,):
+        raise ValueError("block_tables must be [S, MB] and query_start_loc [S+1]")
+    return (_dev(out, "out"), _dev(q, "q"), _dev(key_cache, "key_cache"), _dev(value_cache, "value_cache"),
+            _dev(block_tables, "block_tables", torch.int32), _dev(context_lens, "context_lens", torch.int32),
+            _dev(query_start_loc, "query_start_loc", torch.int32), t, int(max_query_len), float(scale), bs, hq,
+            hkv, d, s, block_tables.shape[1], nb, int(max_context_len), _dt(q), _dev(workspace, "workspace"),
+            workspace.numel() * workspace.element_size())
+
+
+def pkv_attention_varlen_plan_upload(out, q, key_cache, value_cache, block_tables, context_lens, query_start_loc,
+                                     scale, max_query_len, max_context_len, host_context_lens, upload_src,
+                                     upload_dst, workspace=None, host_block_tables=None, stream=None):
+    """Plan of ``pkv_attention_varlen`` from pinned host lengths, fused with the
+    upload of the pinned ``upload_src`` into ``upload_dst`` (and, with
+    ``host_block_tables``, of each table row's used entries into
+    ``block_tables``); ``workspace`` is required (``_partitions`` reads the plan)."""
+    _need_workspace(workspace, "pkv_attention_varlen_plan_upload")
+    for name, t in (("host_context_lens", host_context_lens), ("upload_src", upload_src)):
+        if not isinstance(t, torch.Tensor) or t.is_cuda or not t.is_pinned() or not t.is_contiguous():
+            raise TypeError(f"{name} must be a contiguous pinned host tensor")
+    if host_block_tables is not None:
+        if host_block_tables.is_cuda or not host_block_tables.is_pinned() or not host_block_tables.is_contiguous():
+            raise TypeError("host_block_tables must be a contiguous pinned host tensor")
+        if host_block_tables.dtype != torch.int32 or tuple(host_block_tables.shape) != tuple(block_tables.shape):
+            raise ValueError("host_block_tables must be int32 of block_tables' shape")
+    if host_context_lens.dtype != torch.int32 or host_context_lens.shape != (context_lens.shape[0],):
+        raise ValueError("host_context_lens must be int32 [num_seqs]")
+    nbytes = upload_src.numel() * upload_src.element_size()
+    if upload_dst.numel() * upload_dst.element_size() != nbytes:
+        raise ValueError("upload_src and upload_dst must have the same byte size")
+    a = _varlen_args(out, q, key_cache, value_cache, block_tables, context_lens, query_start_loc, scale,
+                     max_query_len, max_context_len, workspace)
+    check("pkv_attention_varlen_plan_upload", lib().pkv_attention_varlen_plan_upload(
+        *a, host_context_lens.data_ptr(), upload_src.data_ptr(), _dev(upload_dst, "upload_dst"), nbytes,
+        None if host_block_tables is None else host_block_tables.data_ptr(), _stream(stream)))
+    return out
+
+
+def pkv_attention_varlen_partitions(out, q, key_cache, value_cache, block_tables, context_lens, query_start_loc,
+                                    scale, max_query_len, max_context_len, workspace=None, stream=None):
+    """The launches of ``pkv_attention_varlen`` after its plan (decode partitions,
+    prefill tiles, merge); ``workspace`` is required (the planned one)."""
+    _need_workspace(workspace, "pkv_attention_varlen_partitions")
+    a = _varlen_args(out, q, key_cache, value_cache, block_tables, context_lens, query_start_loc, scale,
+                     max_query_len, max_context_len, workspace)
+    check("pkv_attention_varlen_partitions", lib().pkv_attention_varlen_partitions(*a, _stream(stream)))
+    return out
+
+
 def pkv_lse_merge(out, part_m, part_l, part_o, num_parts, stream=None):
     """Merge partial softmax results (base-2 maxima); ``out`` [rows, D]."""
     rows, maxp, d = part_o.shape

@@ -372,3 +372,29 @@ def test_split_wrappers_need_the_callers_workspace(name):
             getattr(pkv, name)(None, None, None, None, None, None, 0.125, 100, None, None, None)
         else:
             getattr(pkv, name)(None, None, None, None, None, None, 0.125, 100)
+
+
+def test_varlen_split_argument_errors():
+    """pkv_attention_varlen_plan_upload / _partitions refuse bad arguments before
+    any launch (fake device addresses; page-locked checks fail for them)."""
+    L = lib()
+    # out q kc vc tables ctx qsl | T mq scale bs Hq Hkv D S MB NB max_ctx dt | ws ws_bytes
+    base = [FAKE] * 7 + [40, 32, 0.125, 16, 32, 8, 128, 4, 128, 1000, 2048, PKV_BF16, FAKE, 1 << 30]
+
+    def up(args, upload_bytes=64):
+        return L.pkv_attention_varlen_plan_upload(*args, FAKE, FAKE, FAKE, upload_bytes, None, None)
+
+    def with_(i, v):
+        a = list(base)
+        a[i] = v
+        return a
+    assert up(base) == PKV_EINVAL                       # host lengths are not page-locked memory
+    assert up(with_(7, 0)) == PKV_EINVAL                # no query rows
+    assert up(with_(18, PKV_F32)) == PKV_EUNSUPPORTED   # matrix-core path: bf16 only
+    assert up(base, upload_bytes=60) == PKV_EINVAL      # not a multiple of 16
+    assert up(with_(19, 0)) == PKV_EWORKSPACE
+    part = L.pkv_attention_varlen_partitions
+    assert part(*with_(6, 0), None) == PKV_EINVAL       # null query_start_loc
+    assert part(*with_(19, 0), None) == PKV_EWORKSPACE
+    assert part(*with_(9, -1.0), None) == PKV_EINVAL    # negative scale
+    assert part(*with_(7, 0), None) == PKV_OK           # no query rows: nothing to launch

@@ -249,3 +249,78 @@ def test_varlen_full_size_mixed_step_sampled():
     dref = oracle.decode_attention(inp["q"][inp["qsl"][seqs]], inp["key_cache"], inp["value_cache"],
                                    tables[seqs], ctx[seqs], inp["scale"])
     assert_close(got[inp["qsl"][seqs]], dref, "bf16", "decode rows")
+
+
+def test_varlen_plan_upload_equals_one_call():
+    """Two steps of a mixed batch (a 100-row chunk and decode rows) through
+    pkv_attention_varlen_plan_upload (plan from pinned lengths; slots and lengths
+    uploaded as bytes, tables by rows), pkv_write of the uploaded slots and
+    pkv_attention_varlen_partitions: the device metadata equals the staging,
+    outputs equal the one-call varlen on a second copy of the pools byte for
+    byte, both pools equal the pool the oracle's writes build, and sampled rows
+    match the oracle on that pool."""
+    Hq, Hkv, D = 32, 8, 128
+    rng = np.random.default_rng(91)
+    S, C = 21, 100
+    MB = 200
+    nb = S * MB + 8
+    T = C + S - 1
+    kc0 = normal_values_parallel(92, (nb, BLOCK_SIZE, Hkv, D), "bf16")
+    vc0 = normal_values_parallel(93, (nb, BLOCK_SIZE, Hkv, D), "bf16")
+    kc, vc = dev(kc0), dev(vc0)
+    kc2, vc2 = kc.clone(), vc.clone()
+    exp_k, exp_v = kc0, vc0
+    qlens = np.array([C] + [1] * (S - 1), np.int32)
+    qsl_h = np.concatenate([[0], np.cumsum(qlens)]).astype(np.int32)
+    qsl = dev(qsl_h)
+    head = T + S + (-(T + S)) % 4                      # slots | lens, padded to 16 bytes
+    stage = torch.zeros(head + S * MB, dtype=torch.int32, pin_memory=True)
+    dmeta = torch.full((head + S * MB,), -3, dtype=torch.int32, device="cuda")
+    bound = 16 * MB
+    ws = pkv.varlen_workspace(S, T, Hq, Hkv, D, C, bound)
+    scale = float(np.float32(1.0 / math.sqrt(D)))
+    for step, (lo, hi) in enumerate([(1, 1500), (300, 3100)]):
+        ctx = rng.integers(lo, hi + 1, size=S).astype(np.int32)
+        ctx[0] = 700 + 400 * step                       # the chunk's context (its rows are the last C tokens)
+        tables = np.full((S, MB), -1, np.int32)
+        perm = rng.permutation(nb).astype(np.int32)     # distinct blocks within the step
+        off = 0
+        for s in range(S):
+            n = -(-int(ctx[s]) // 16)
+            tables[s, :n] = perm[off:off + n]
+            off += n
+        pos = np.concatenate([ctx[0] - C + np.arange(C), ctx[1:] - 1])          # rows' own positions
+        seq = np.concatenate([np.zeros(C, np.int64), np.arange(1, S)])
+        slots = (tables[seq, pos // 16] * 16 + pos % 16).astype(np.int32)
+        h = stage.numpy()
+        h[:T], h[T:T + S], h[head:] = slots, ctx, tables.reshape(-1)
+        q = dev(normal_values(rng, (T, Hq, D), "bf16"))
+        kn_h, vn_h = normal_values(rng, (T, Hkv, D), "bf16"), normal_values(rng, (T, Hkv, D), "bf16")
+        kn, vn = dev(kn_h), dev(vn_h)
+        say(f"varlen plan_upload step {step}: chunk ctx {ctx[0]}, decode ctx {ctx[1:].min()}..{ctx[1:].max()}")
+        d_slots, d_lens = dmeta[:T], dmeta[T:T + S]
+        d_tab = dmeta[head:].view(S, MB)
+        out = torch.full((T, Hq, D), float("nan"), dtype=torch.bfloat16, device="cuda")
+        pkv.pkv_attention_varlen_plan_upload(out, q, kc, vc, d_tab, d_lens, qsl, scale, C, bound, stage[T:T + S],
+                                             stage[:head], dmeta[:head], workspace=ws,
+                                             host_block_tables=stage[head:].view(S, MB))
+        pkv.pkv_write(kc, vc, kn, vn, d_slots)
+        pkv.pkv_attention_varlen_partitions(out, q, kc, vc, d_tab, d_lens, qsl, scale, C, bound, workspace=ws)
+        ref = torch.full_like(out, float("nan"))
+        pkv.pkv_write(kc2, vc2, kn, vn, dev(slots))
+        pkv.pkv_attention_varlen(ref, q, kc2, vc2, dev(tables), dev(ctx), qsl, scale, C, bound)
+        torch.cuda.synchronize()
+        got_meta = host(dmeta)
+        assert got_meta[:T + S].tobytes() == h[:T + S].tobytes(), "slots / lengths differ from the staging"
+        gt = got_meta[head:].reshape(S, MB)
+        for s in range(S):
+            n = -(-int(ctx[s]) // 16)
+            assert np.array_equal(gt[s, :n], tables[s, :n]), s
+        assert host(out).tobytes() == host(ref).tobytes(), f"step {step}: differs from the one-call varlen"
+        exp_k, exp_v = oracle.write_kv(exp_k, exp_v, kn_h, vn_h, slots)
+        assert host(kc).tobytes() == exp_k.tobytes() and host(vc).tobytes() == exp_v.tobytes()
+        assert host(kc2).tobytes() == exp_k.tobytes() and host(vc2).tobytes() == exp_v.tobytes()
+        rows = np.unique(np.concatenate([[0, 1, 50, C - 1], C + rng.choice(S - 1, 5, replace=False)]))
+        want = oracle.causal_chunk_attention(host(q), exp_k, exp_v, tables, ctx, qsl_h, np.float32(scale))
+        assert_close(host_f64(out)[rows], want[rows], "bf16", f"varlen plan_upload step {step}")
+        torch.cuda.synchronize()                        # the staging is rewritten for the next step
