@@ -136,18 +136,19 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void prefill_mfma_kernel(Decode
   __shared__ __attribute__((aligned(16))) char s_v[kPrefillBufs][kStepTokens * RSV];
   __shared__ int s_ticket[2];
 
-  using TablePtr = const __attribute__((address_space(4))) int*;
   struct Item {
     int s, part, span, g, ctx, qrow0, nrows, key0, b_begin, nblk, nsteps;
-    TablePtr trow;  // the sequence's block table from the item's first block
+    int ids;        // lane k: the id of the item's block k (k < nblk)
     bool valid;
   };
   // Records are written by the plan launch and read-only here: read through the
   // constant address space (scalar loads; waiting for them never waits for the
   // vector loads in flight).
   auto make_item = [&](int tk, Item& it) {
+    // the record's address does not wait for the count of tickets: a ticket
+    // past it reads a record that is not used (no blocks, no rows)
     it.valid = tk < total;
-    const int t = it.valid ? tk : 0;
+    const int t = min(tk, p.pre_cap * p.Hkv - 1);
     const __attribute__((address_space(4))) int* r =
         (const __attribute__((address_space(4))) int*)(const void*)p.pre_recs + 8 * (t / p.Hkv);
     it.g = t % p.Hkv;
@@ -168,7 +169,13 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void prefill_mfma_kernel(Decode
     // ahead of the pair being computed and must never run past the next item;
     // padding steps load nothing and compute nothing
     it.nsteps = max(6, (max(1, (it.nblk + 1) / 2) + NS - 1) / NS * NS);
-    it.trow = (TablePtr)(const void*)(p.tables + (int64_t)it.s * p.MB + it.b_begin);
+    {
+      // the item's block ids, one per lane (an item spans at most 64 blocks),
+      // loaded once; each step then takes its id from a lane, with no memory wait
+      const __amdgpu_buffer_rsrc_t tr = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<int*>(p.tables + (int64_t)it.s * p.MB + it.b_begin), (short)0, it.nblk * 4, kRawBufferWord3);
+      it.ids = __builtin_amdgcn_raw_buffer_load_b32(tr, lane * 4, 0, 0);
+    }
   };
   // q operands (B of the scores) of this wave's columns; rows past the item read
   // zeros through the resource bound.
@@ -213,12 +220,11 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void prefill_mfma_kernel(Decode
     kk = buffer_load_piece<PT>(kr, off, 0);
     vv = buffer_load_piece<PT>(vr, off, 0);
   };
-  // The load stream's position: an item (copied) and a step of it.  Block ids
-  // are scalar loads from the table (written before this launch, read-only
-  // here), which never wait for the vector loads in flight; with each id, the
+  // The load stream's position: an item (copied) and a step of it.  Each step's
+  // block id comes from a lane of the item's id register; with each id, the
   // number of the block's rows inside the context.
   struct Cursor {
-    TablePtr trow;
+    int ids;
     int nblk, ctx_rel, g, step, nsteps;
   };
   struct Ids {
@@ -226,7 +232,7 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void prefill_mfma_kernel(Decode
   };
   auto cursor_of = [&](const Item& it) {
     Cursor c;
-    c.trow = it.trow;
+    c.ids = it.ids;
     c.nblk = it.nblk;
     c.ctx_rel = it.ctx - it.b_begin * kBlockTokens;  // context tokens from the item's first block
     c.g = it.g;
@@ -239,7 +245,7 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void prefill_mfma_kernel(Decode
 #pragma unroll
     for (int j = 0; j < RPT; ++j) {
       const int k = 2 * c.step + wblk[j];
-      ids.v[j] = k < c.nblk ? c.trow[k] : -1;
+      ids.v[j] = k < c.nblk ? __builtin_amdgcn_readlane(c.ids, min(k, kWave - 1)) : -1;
       ids.lim[j] = min(kBlockTokens, c.ctx_rel - k * kBlockTokens);
     }
     return ids;
@@ -258,7 +264,7 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void prefill_mfma_kernel(Decode
   };
 
   bf16x8 qf[CT][NKC], qn[CT][NKC];   // q operands of the current and the next item
-  float m[CT], l[CT];
+  float m[CT], l[CT], mref[CT];      // lazy reference max (log2 units), its finite form
   f32x16 acc[CT][NT];
   int col_keys[CT];                   // keys the column's row sees (0 past the item's rows)
   int min_keys;                       // the least of them over the wave (uniform)
@@ -294,8 +300,8 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void prefill_mfma_kernel(Decode
     // -inf; every step then takes the scale into the exponent's fused
     // multiply-add (-inf stays -inf: the scale is positive).
     const bool masked = t0 + kStepTokens > min_keys;  // uniform over the wave
-    float ms[CT], mref[CT];
-    bool grew = false;
+    float rmax[CT];
+    bool over = false;
 #pragma unroll
     for (int c = 0; c < CT; ++c) {
       if (masked) {
@@ -308,19 +314,22 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void prefill_mfma_kernel(Decode
       float r = sc[c][0];
 #pragma unroll
       for (int i = 1; i < 16; ++i) r = fmaxf(r, sc[c][i]);
-      const float mx = r * p.scale_log2;  // the scale is positive: the max commutes with it
-      const float mb = max_over_halves(mx);
-      const bool up = mb > m[c] + kRescaleLog2;  // -inf + 8 = -inf: the first live step moves it
-      const float mn = up ? mb : m[c];
-      mref[c] = (mn == -INFINITY) ? 0.f : mn;
-      ms[c] = m[c] - mref[c];                     // exponent of the rescale factor
-      m[c] = mn;
-      grew |= up;
+      rmax[c] = r;
+      // this half's tokens exceed the column's reference by more than the lazy
+      // margin (always at the first live step: the reference is -inf; the scale
+      // is positive, so the max commutes with it)
+      over |= r * p.scale_log2 > m[c] + kRescaleLog2;
     }
-    if (__ballot(grew)) {  // some column's reference moved: rescale what was accumulated
+    if (__ballot(over)) {  // move the references of the columns that exceed them
 #pragma unroll
       for (int c = 0; c < CT; ++c) {
-        const float alpha = exp2_fast(ms[c]);
+        const float mb = max_over_halves(rmax[c] * p.scale_log2);  // both halves of the column
+        const bool up = mb > m[c] + kRescaleLog2;
+        const float mn = up ? mb : m[c];
+        const float mr = (mn == -INFINITY) ? 0.f : mn;
+        const float alpha = exp2_fast(m[c] - mr);  // 1 where the reference stays, 0 from -inf
+        mref[c] = mr;
+        m[c] = mn;
         l[c] *= alpha;
 #pragma unroll
         for (int e = 0; e < NT; ++e) acc[c][e] *= alpha;
@@ -367,6 +376,7 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void prefill_mfma_kernel(Decode
 #pragma unroll
     for (int c = 0; c < CT; ++c) {
       m[c] = -INFINITY;
+      mref[c] = 0.f;
       l[c] = 0.f;
       const int r = wave * RPW + c * R + n / G;
       col_keys[c] = r < it.nrows ? max(0, it.key0 + r) : 0;
@@ -437,25 +447,18 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void prefill_mfma_kernel(Decode
   Item cur, n1;
   make_item(blockIdx.x, cur);
   if (!cur.valid) return;
-  make_item(blockIdx.x + grid, n1);
   load_q(cur, qf);
-  load_q(n1, qn);
 
   // The load stream runs ahead of the computation: in cur, then in n1
   // (cs_n1).  Stepping past the end of n1 (only when n1 has the minimum six
   // steps) leaves it pending (cs_wait) until the item switch makes the next
   // n1; that happens before the next issue.  An invalid item has no
-  // blocks (zero-sized loads).  The ids of each position are loaded one issue
-  // ahead (pf_ids, valid when pf_ok), so the issue does not wait for the
-  // scalar loads.
+  // blocks (zero-sized loads).
   Cursor cs = cursor_of(cur);
   bool cs_n1 = false, cs_wait = false;
-  Ids pf_ids;
-  bool pf_ok = false;
   auto issue_next = [&](Stage& st) {
-    const Ids ids = pf_ok ? pf_ids : ids_at(cs);
-    issue_step(cs.g, ids, st);
-    if (++cs.step == cs.nsteps) {
+    issue_step(cs.g, ids_at(cs), st);
+    if (__builtin_expect(++cs.step == cs.nsteps, 0)) {
       if (cs_n1) {
         cs_wait = true;
       } else {
@@ -463,8 +466,6 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void prefill_mfma_kernel(Decode
         cs_n1 = true;
       }
     }
-    pf_ok = !cs_wait;
-    if (pf_ok) pf_ids = ids_at(cs);
   };
 
   // Two steps per barrier: while the pair q, q + 1 runs (reading the LDS
@@ -483,6 +484,10 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void prefill_mfma_kernel(Decode
   }
   stage_to_lds(stg[0], 2);  // steps 0 .. 2 in LDS, 3 and 4 in flight
   issue_next(stg[0]);
+  // the next item is read once the first loads are on their way (the
+  // prologue's five steps stay within cur, which has at least six)
+  make_item(blockIdx.x + grid, n1);
+  load_q(n1, qn);
   __syncthreads();
   int buf = 0, tpar = 0;  // LDS buffer of step 0 of cur
   f32x16 sc[2][CT];       // scores of steps of either parity
@@ -499,13 +504,16 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void prefill_mfma_kernel(Decode
     for (int q = 0; q < cur.nsteps; q += 2) {
       const int b1 = rot(buf, 1), b2 = rot(buf, 2);
       stage_to_lds(stg[1], rot(buf, 3));  // step q + 3 (odd)
-      issue_next(stg[1]);                 // step q + 5
       stage_to_lds(stg[0], rot(buf, 4));  // step q + 4
-      issue_next(stg[0]);                 // step q + 6
       if (q + 2 == cur.nsteps && tid == 0) s_ticket[tpar] = fetched;
       const int t0 = (cur.b_begin + 2 * q) * kBlockTokens;
+      // the scalar work of each issue runs between the steps' vector code
+      // rather than after the barrier, where every wave would queue for the
+      // compute unit's scalar unit at once
       if (2 * q < cur.nblk) softmax_values(sc[0], buf, t0, b1, sc[1]);
+      issue_next(stg[1]);                 // step q + 5
       if (2 * q + 2 < cur.nblk) softmax_values(sc[1], b1, t0 + kStepTokens, b2, sc[0]);
+      issue_next(stg[0]);                 // step q + 6
       __syncthreads();
       buf = b2;
     }
