@@ -452,10 +452,11 @@ def read_probe_on_blocks(torch, np, kcs, vcs, blk_ids, Hkv, D, es, rounds=4):
 
 def read_probe_standalone(torch, np, seed):
     """The read kernels alone over two 768 MiB pools of 32 KiB blocks (GQA 32/8,
-    head_dim 128, bf16), every block once in a seeded random order, with N(0,1)
-    data and with zeros."""
+    head_dim 128, bf16), every block once, in a seeded random order (as a block
+    table scatters them) and in pool order, with N(0,1) data and with zeros."""
     nb, Hkv, D = 24576, 8, 128
-    ids = np.random.default_rng(seed).permutation(nb).astype(np.int32)
+    orders = {"random_order": np.random.default_rng(seed).permutation(nb).astype(np.int32),
+              "pool_order": np.arange(nb, dtype=np.int32)}
     lines = {}
     for fill in ("random", "zeros"):
         kcs, vcs = [], []
@@ -466,7 +467,8 @@ def read_probe_standalone(torch, np, seed):
             else:
                 kcs.append(torch.zeros((nb, 16, Hkv, D), dtype=torch.bfloat16, device="cuda"))
                 vcs.append(torch.zeros((nb, 16, Hkv, D), dtype=torch.bfloat16, device="cuda"))
-        lines[fill] = read_probe_on_blocks(torch, np, kcs, vcs, ids, Hkv, D, 2)
+        for name, ids in orders.items():
+            lines[f"{fill}_{name}"] = read_probe_on_blocks(torch, np, kcs, vcs, ids, Hkv, D, 2)
         del kcs, vcs
         torch.cuda.empty_cache()
     print(json.dumps({"probe": "read", "pool_blocks": nb, "block_bytes": 16 * Hkv * D * 2, "pool_copies": 2,
