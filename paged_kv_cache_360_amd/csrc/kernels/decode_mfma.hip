@@ -46,7 +46,8 @@
 // loads before computing i.
 // Loads go through per-block buffer resources (base = the block, range = its
 // size): the lane offsets are 32-bit, and a block that must not be read gets a
-// zero range, so the prefetch needs no branch.
+// zero range, so the prefetch needs no branch.  Block loads carry the
+// nontemporal hint: each (block, KV head) slice is read once per launch.
 
 #include <hip/hip_runtime.h>
 
@@ -253,9 +254,9 @@ __global__ __launch_bounds__(kMfmaThreads, kMfmaWavesPerSimd) void decode_partit
     const __amdgpu_buffer_rsrc_t vr =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(p.vc + base), (short)0, nrec, kRawBufferWord3);
 #pragma unroll
-    for (int c = 0; c < NKC; ++c) B.k[c] = buffer_load16(kr, it.k_lane + 64 * c, 0);
+    for (int c = 0; c < NKC; ++c) B.k[c] = buffer_load16<kStreamLoad>(kr, it.k_lane + 64 * c, 0);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) B.v[i] = buffer_load_piece<VT>(vr, it.v_lane, i * tok_bytes);
+    for (int i = 0; i < 4; ++i) B.v[i] = buffer_load_piece<VT, kStreamLoad>(vr, it.v_lane, i * tok_bytes);
   };
 
   float m, l;            // reference max of head h (log2 domain, uniform over j); this lane's sum

@@ -51,24 +51,47 @@ __device__ __forceinline__ void widen16(const uint4& r, float* f) {
 __device__ __forceinline__ uint4 load16(const void* p) {
   return *reinterpret_cast<const uint4*>(p);
 }
+// The same with the nontemporal hint (`nt`): for K/V read once per launch.
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 load16_stream(const void* p) {
+  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
 
 // Raw buffer resources (gfx9 descriptor, stride 0): loads at byte offsets at or
 // past the resource's range return zeros without a memory access.
 constexpr int kRawBufferWord3 = 0x00020000;
 
+// Cache policy of a buffer load (its aux operand): kStreamLoad sets the
+// nontemporal hint (`nt`) for data each launch reads once, the K/V blocks.
+// Measured on the partition kernel (interleaved A/B on one box): 6-15% shorter
+// launches, and a plain read of 32 KiB blocks in random order goes from 6.1 to
+// 6.8 TB/s with it.
+constexpr int kCachedLoad = 0;
+constexpr int kStreamLoad = 2;
+
+template <int kPolicy = kCachedLoad>
 __device__ __forceinline__ uint4 buffer_load16(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
-  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, kPolicy));
 }
 
-template <typename T>
-__device__ __forceinline__ T buffer_load_piece(__amdgpu_buffer_rsrc_t r, int voff, int soff);
-template <>
-__device__ __forceinline__ uint4 buffer_load_piece<uint4>(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
-  return buffer_load16(r, voff, soff);
-}
-template <>
-__device__ __forceinline__ uint2 buffer_load_piece<uint2>(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
-  return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0));
+template <typename T, int kPolicy = kCachedLoad>
+struct BufferPiece;
+template <int kPolicy>
+struct BufferPiece<uint4, kPolicy> {
+  static __device__ __forceinline__ uint4 load(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+    return buffer_load16<kPolicy>(r, voff, soff);
+  }
+};
+template <int kPolicy>
+struct BufferPiece<uint2, kPolicy> {
+  static __device__ __forceinline__ uint2 load(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+    return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, kPolicy));
+  }
+};
+template <typename T, int kPolicy = kCachedLoad>
+__device__ __forceinline__ T buffer_load_piece(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+  return BufferPiece<T, kPolicy>::load(r, voff, soff);
 }
 
 // Reductions over the four 16-lane rows of a wave (lanes l, l^16, l^32, l^48)
