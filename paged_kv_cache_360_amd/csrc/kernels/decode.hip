@@ -111,9 +111,9 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_partition_kernel(Decode
     valid = ok ? min(kBlockTokens, ctx - b * kBlockTokens) : 0;
     const int64_t base = (int64_t)(ok ? pb : 0) * blk_bytes + lane_off;
 #pragma unroll
-    for (int i = 0; i < NL; ++i) kr[i] = load16_stream(p.kc + base + (int64_t)i * TPL * tok_bytes);
+    for (int i = 0; i < NL; ++i) kr[i] = load16(p.kc + base + (int64_t)i * TPL * tok_bytes);
 #pragma unroll
-    for (int i = 0; i < NL; ++i) vr[i] = load16_stream(p.vc + base + (int64_t)i * TPL * tok_bytes);
+    for (int i = 0; i < NL; ++i) vr[i] = load16(p.vc + base + (int64_t)i * TPL * tok_bytes);
   };
 
   auto compute = [&](const uint4 (&kr)[NL], const uint4 (&vr)[NL], int valid) {

@@ -28,6 +28,11 @@ constexpr int kAppendable = 1 << 17;
 // item is the sequence's only one, so its result is the output)
 constexpr int kWholeSequence = 1 << 18;
 constexpr int kPartitionMask = kOnePartition - 1;
+// Slot of the plan's ticket header (sched) that is nonzero when some decode
+// sequence's first block is also another decode sequence's first block (a
+// shared prefix, a fork): the partition launch then keeps the default cache
+// policy for its block loads instead of the streaming hint.
+constexpr int kSchedShared = 4;
 
 struct DecodeParams {
   void* out;

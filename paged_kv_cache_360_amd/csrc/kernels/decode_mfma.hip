@@ -47,7 +47,10 @@
 // Loads go through per-block buffer resources (base = the block, range = its
 // size): the lane offsets are 32-bit, and a block that must not be read gets a
 // zero range, so the prefetch needs no branch.  Block loads carry the
-// nontemporal hint: each (block, KV head) slice is read once per launch.
+// nontemporal hint, as each (block, KV head) slice is read once per launch,
+// unless the plan finds sequences sharing their first block (a shared prefix):
+// their blocks are read by several items, and the hint would evict them
+// between those reads.
 
 #include <hip/hip_runtime.h>
 
@@ -117,9 +120,11 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
 // that only loads and the atomic write, and the ticket is consumed while only
 // the zero-sized tail loads are outstanding (vector memory operations complete
 // in order, so any earlier wait would drain the prefetch).
-template <int D, int G>
-__global__ __launch_bounds__(kMfmaThreads, kMfmaWavesPerSimd) void decode_partition_mfma_kernel(
-    DecodeParams p) {
+//
+// kPolicy is the cache policy of the block loads (the kernel below picks it
+// per launch).
+template <int D, int G, int kPolicy>
+__device__ __forceinline__ void decode_partition_body(const DecodeParams& p) {
   constexpr int EPL = D / 16;            // dims per lane in one V row load
   constexpr int WPL = EPL / 2;           // 32-bit words per V row load
   constexpr int NKC = D / 32;            // 16x16x32 MFMAs per block for the scores
@@ -254,9 +259,9 @@ __global__ __launch_bounds__(kMfmaThreads, kMfmaWavesPerSimd) void decode_partit
     const __amdgpu_buffer_rsrc_t vr =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(p.vc + base), (short)0, nrec, kRawBufferWord3);
 #pragma unroll
-    for (int c = 0; c < NKC; ++c) B.k[c] = buffer_load16<kStreamLoad>(kr, it.k_lane + 64 * c, 0);
+    for (int c = 0; c < NKC; ++c) B.k[c] = buffer_load16<kPolicy>(kr, it.k_lane + 64 * c, 0);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) B.v[i] = buffer_load_piece<VT, kStreamLoad>(vr, it.v_lane, i * tok_bytes);
+    for (int i = 0; i < 4; ++i) B.v[i] = buffer_load_piece<VT, kPolicy>(vr, it.v_lane, i * tok_bytes);
   };
 
   float m, l;            // reference max of head h (log2 domain, uniform over j); this lane's sum
@@ -508,6 +513,21 @@ __global__ __launch_bounds__(kMfmaThreads, kMfmaWavesPerSimd) void decode_partit
     rec1 = rec2;
   }
   merge(prev, parity);  // the last item (its closing barrier has passed)
+}
+
+// The block loads stream (nontemporal hint) unless the plan found decode
+// sequences that share their first block (a shared prefix, a fork): then the
+// launch keeps the default policy, so the shared blocks stay in the caches for
+// their other readers.  (A per-item choice costs a branch at every block load,
+// 5% on batches that share nothing.)
+template <int D, int G>
+__global__ __launch_bounds__(kMfmaThreads, kMfmaWavesPerSimd) void decode_partition_mfma_kernel(
+    DecodeParams p) {
+  if (p.sched[kSchedShared] != 0) {
+    decode_partition_body<D, G, kCachedLoad>(p);
+  } else {
+    decode_partition_body<D, G, kStreamLoad>(p);
+  }
 }
 
 template <int D, int G>

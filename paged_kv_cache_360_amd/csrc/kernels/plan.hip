@@ -33,8 +33,12 @@
 //    per record (bf16, on the matrix cores), else its partition count (fp32);
 //    its item count (partitions / span, rounded up) for a prefill row; 1 for a
 //    row written directly (or with no keys), 0 for rows no sequence owns;
-//  * sched: both ticket counters reset, and each list's ticket count (records
-//    times KV heads: ticket t is record t / Hkv, KV head t % Hkv).
+//  * sched: both ticket counters reset, each list's ticket count (records
+//    times KV heads: ticket t is record t / Hkv, KV head t % Hkv), and
+//    sched[kSchedShared]: whether some decode sequence's first block is also
+//    another decode sequence's first block (found through a hash table in LDS
+//    over the first entry of each table row; a hint for the partition launch's
+//    load cache policy only).
 // One workgroup; per-thread counts are scanned with lane shuffles and one
 // exchange of wave totals in LDS.
 
@@ -49,15 +53,27 @@ namespace pkv {
 
 namespace {
 
+// Open-addressing table of first block ids in LDS: a slot holds an id and how
+// many decode sequences start with it.
+constexpr int kShareSlots = 4096;
+constexpr int kShareProbes = 16;
+constexpr int32_t kShareEmpty = INT32_MIN;
+__device__ __forceinline__ int share_hash(int32_t id) {
+  return (int)(((uint32_t)id * 2654435761u) >> 20) & (kShareSlots - 1);
+}
+
 __device__ __forceinline__ void plan_body(
     const int32_t* __restrict__ ctx, const int32_t* __restrict__ qsl, int32_t S, int32_t T,
     int32_t ctx_cap, int32_t Hkv, int32_t rows_per_item, int32_t dec_cap, int32_t pre_cap,
     int32_t num_cus, int32_t* __restrict__ sched, int4* __restrict__ dec, int4* __restrict__ pre,
-    int32_t* __restrict__ row_slots, bool record_slots) {
+    int32_t* __restrict__ row_slots, bool record_slots, const int32_t* __restrict__ tab, int32_t MB) {
   constexpr int kTailBlocks = 2 * kPartBlocks;  // largest record sorted into the tail
   constexpr int NBK = kTailBlocks + 1;          // buckets: tail-record block count kTailBlocks .. 0
   __shared__ int32_t s_wsum[kPlanThreads / kWave][3];  // per wave: full items, prefill records at span 1, 2
   __shared__ int32_t s_bucket[NBK];
+  __shared__ int32_t s_key[kShareSlots];
+  __shared__ int32_t s_cnt[kShareSlots];
+  __shared__ int32_t s_shared_any;
   const int t = threadIdx.x;
   const int per = (S + kPlanThreads - 1) / kPlanThreads;
   const int s0 = min(S, t * per);
@@ -77,9 +93,42 @@ __device__ __forceinline__ void plan_body(
 
   if (t < NBK) s_bucket[t] = 0;
   for (int r = t; r < T; r += kPlanThreads) row_slots[r] = 0;  // rows no sequence owns: nothing to merge
+  for (int k = t; k < kShareSlots; k += kPlanThreads) {
+    s_key[k] = kShareEmpty;
+    s_cnt[k] = 0;
+  }
+  if (t == 0) s_shared_any = 0;
   __syncthreads();
+  // first block id of a decode sequence with keys (a hint only: any value is
+  // safe, it is never dereferenced here)
+  auto first_block = [&](int s) { return tab ? tab[(int64_t)s * MB] : kShareEmpty; };
+  auto share_insert = [&](int32_t id) {
+    if (id == kShareEmpty) return;
+    int h = share_hash(id);
+    for (int k = 0; k < kShareProbes; ++k, h = (h + 1) & (kShareSlots - 1)) {
+      const int32_t prev = atomicCAS(&s_key[h], kShareEmpty, id);
+      if (prev == kShareEmpty || prev == id) {
+        atomicAdd(&s_cnt[h], 1);
+        return;
+      }
+    }
+  };
+  // after the inserts: does another decode sequence start with this id?  (A
+  // probe run that found no slot counts as shared: the cached policy is the
+  // safe default.)
+  auto share_count = [&](int32_t id) {
+    if (id == kShareEmpty) return 1;
+    int h = share_hash(id);
+    for (int k = 0; k < kShareProbes; ++k, h = (h + 1) & (kShareSlots - 1)) {
+      const int32_t key = s_key[h];
+      if (key == id) return s_cnt[h];
+      if (key == kShareEmpty) return 1;
+    }
+    return 2;
+  };
   int full = 0, npre = 0, npre2 = 0;
   int own_c = 0, own_q = 0, own_row0 = 0, own_raw = 0;  // this thread's (last) sequence, for the write loop
+  int32_t own_b0 = kShareEmpty;
   for (int s = s0; s < s1; ++s) {
     const int c = ctx_of(s);
     const int q = rows_of(s);
@@ -87,6 +136,8 @@ __device__ __forceinline__ void plan_body(
     own_c = c;
     own_q = q;
     own_row0 = first_row(s);
+    own_b0 = (q == 1 && c > 0) ? first_block(s) : kShareEmpty;
+    share_insert(own_b0);
     if (q == 1) {
       const int n = parts_of(c);
       const int ni = items_of(n);
@@ -174,6 +225,7 @@ __device__ __forceinline__ void plan_body(
     if (q != 1) continue;
     const int row0 = per == 1 ? own_row0 : first_row(s);
     const int app = (per == 1 ? own_raw : ctx[s]) == c ? kAppendable : 0;
+    if (share_count(per == 1 ? own_b0 : (c > 0 ? first_block(s) : kShareEmpty)) > 1) s_shared_any = 1;
     const int n = parts_of(c);
     const int ni = items_of(n);
     for (int k = 0; k < ni - 1; ++k, ++od)
@@ -245,6 +297,7 @@ __device__ __forceinline__ void plan_body(
     sched[1] = min(num_dec_recs, dec_cap) * Hkv;
     sched[2] = 0;
     sched[3] = min(num_pre, pre_cap) * Hkv;
+    sched[kSchedShared] = s_shared_any;
   }
 }
 
@@ -252,9 +305,9 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(
     const int32_t* __restrict__ ctx, const int32_t* __restrict__ qsl, int32_t S, int32_t T,
     int32_t ctx_cap, int32_t Hkv, int32_t rows_per_item, int32_t dec_cap, int32_t pre_cap,
     int32_t num_cus, int32_t* __restrict__ sched, int4* __restrict__ dec, int4* __restrict__ pre,
-    int32_t* __restrict__ row_slots, bool record_slots) {
+    int32_t* __restrict__ row_slots, bool record_slots, const int32_t* __restrict__ tab, int32_t MB) {
   plan_body(ctx, qsl, S, T, ctx_cap, Hkv, rows_per_item, dec_cap, pre_cap, num_cus, sched, dec, pre, row_slots,
-            record_slots);
+            record_slots, tab, MB);
 }
 
 // Loads in flight per thread in the staging copy (reads cross the host link).
@@ -284,8 +337,10 @@ __global__ __launch_bounds__(kPlanThreads) void upload_plan_kernel(
     const float* __restrict__ m_po, const int32_t* __restrict__ m_counts, int32_t Hq, int32_t m_max_parts,
     int64_t m_rows) {
   if (blockIdx.x == 0) {
+    // first entries of the table rows: from the host copy when this launch
+    // uploads the tables, else from the device tables as they are
     plan_body(host_ctx, qsl, S, T, ctx_cap, Hkv, rows_per_item, dec_cap, pre_cap, num_cus, sched, dec, pre,
-              row_slots, BF16);
+              row_slots, BF16, host_tables ? host_tables : tables, MB);
     return;
   }
   if ((int)blockIdx.x <= n_up) {
@@ -339,7 +394,7 @@ int launch_plan(const DecodeArgs& a, void* stream) {
   hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, (hipStream_t)stream, a.ctx, a.qsl,
                      a.num_seqs, a.num_tokens, p.ctx_cap, a.num_kv_heads, prefill_rows_per_item(G),
                      a.dec_cap, a.pre_cap, a.num_cus, a.sched, reinterpret_cast<int4*>(a.dec_recs),
-                     reinterpret_cast<int4*>(a.pre_recs), a.row_slots, a.bf16);
+                     reinterpret_cast<int4*>(a.pre_recs), a.row_slots, a.bf16, a.tables, a.max_blocks);
   return (int)hipGetLastError();
 }
 
