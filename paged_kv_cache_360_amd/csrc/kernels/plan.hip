@@ -79,10 +79,13 @@ __device__ __forceinline__ void plan_body(
   const int s0 = min(S, t * per);
   const int s1 = min(S, s0 + per);
 
-  auto ctx_of = [&](int s) { return max(0, min(ctx[s], ctx_cap)); };
+  auto clamp_ctx = [&](int raw) { return max(0, min(raw, ctx_cap)); };
+  auto row0_from = [&](int s, int qs) { return qsl ? min(max(qs, 0), T) : s; };
+  auto rows_from = [&](int row0, int qe) { return qsl ? max(0, min(qe, T) - row0) : 1; };
+  auto ctx_of = [&](int s) { return clamp_ctx(ctx[s]); };
   auto parts_of = [&](int keys) { return max(1, (keys + kPartTokens - 1) / kPartTokens); };
-  auto first_row = [&](int s) { return qsl ? min(max(qsl[s], 0), T) : s; };
-  auto rows_of = [&](int s) { return qsl ? max(0, min(qsl[s + 1], T) - first_row(s)) : 1; };
+  auto first_row = [&](int s) { return row0_from(s, qsl ? qsl[s] : 0); };
+  auto rows_of = [&](int s) { return rows_from(first_row(s), qsl ? qsl[s + 1] : 0); };
   auto items_of = [&](int n) { return (n + kItemParts - 1) / kItemParts; };
   auto last_blocks = [&](int c, int n) {  // blocks of the last item: kItemBlocks when full, 0 when empty
     return (c + kBlockTokens - 1) / kBlockTokens - (items_of(n) - 1) * kItemBlocks;
@@ -101,7 +104,7 @@ __device__ __forceinline__ void plan_body(
   __syncthreads();
   // first block id of a decode sequence with keys (a hint only: any value is
   // safe, it is never dereferenced here)
-  auto first_block = [&](int s) { return tab ? tab[(int64_t)s * MB] : kShareEmpty; };
+  auto first_block = [&](int s) { return (tab && MB > 0) ? tab[(int64_t)s * MB] : kShareEmpty; };
   auto share_insert = [&](int32_t id) {
     if (id == kShareEmpty) return;
     int h = share_hash(id);
@@ -130,13 +133,27 @@ __device__ __forceinline__ void plan_body(
   int own_c = 0, own_q = 0, own_row0 = 0, own_raw = 0;  // this thread's (last) sequence, for the write loop
   int32_t own_b0 = kShareEmpty;
   for (int s = s0; s < s1; ++s) {
-    const int c = ctx_of(s);
-    const int q = rows_of(s);
-    own_raw = ctx[s];
+    // the sequence's length, query rows and first table entry read at once,
+    // each exactly once: from host memory, every read that waited on another
+    // would add a round trip over the link
+    // (an absent array's read goes to the length instead, so that all four
+    // loads issue unconditionally, back to back)
+    const bool has_tab = tab != nullptr && MB > 0;
+    const int32_t* p_b0 = has_tab ? tab + (int64_t)s * MB : ctx + s;
+    const int32_t* p_qs = qsl ? qsl + s : ctx + s;
+    const int32_t* p_qe = qsl ? qsl + s + 1 : ctx + s;
+    const int32_t v_b0 = *p_b0, raw = ctx[s], v_qs = *p_qs, v_qe = *p_qe;
+    const int32_t b0 = has_tab ? v_b0 : kShareEmpty;
+    const int qs = qsl ? v_qs : 0;
+    const int qe = qsl ? v_qe : 0;
+    const int c = clamp_ctx(raw);
+    const int row0 = row0_from(s, qs);
+    const int q = rows_from(row0, qe);
+    own_raw = raw;
     own_c = c;
     own_q = q;
-    own_row0 = first_row(s);
-    own_b0 = (q == 1 && c > 0) ? first_block(s) : kShareEmpty;
+    own_row0 = row0;
+    own_b0 = (q == 1 && c > 0) ? b0 : kShareEmpty;
     share_insert(own_b0);
     if (q == 1) {
       const int n = parts_of(c);
@@ -268,9 +285,11 @@ __device__ __forceinline__ void plan_body(
     const int src = __ffsll(pending) - 1;
     const int s = __shfl(ps, src, kWave);
     int cop = __shfl(op, src, kWave);
-    const int c = ctx_of(s);
-    const int q = rows_of(s);
-    const int row0 = first_row(s);
+    // with one sequence per thread, the owner lane's values from the first
+    // loop (no second read of host memory)
+    const int c = per == 1 ? __shfl(own_c, src, kWave) : ctx_of(s);
+    const int q = per == 1 ? __shfl(own_q, src, kWave) : rows_of(s);
+    const int row0 = per == 1 ? __shfl(own_row0, src, kWave) : first_row(s);
     for (int r0 = 0; r0 < q; r0 += rows_per_item) {
       const int nr = min(q, r0 + rows_per_item) - r0;
       const int n = (parts_of(row_keys_of(c, q, r0 + nr - 1)) + span - 1) / span;
