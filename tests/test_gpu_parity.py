@@ -117,6 +117,10 @@ DECODE_CASES = {
     "gqa8_d128_bf16": ("bf16", 16, 2, 128, [5, 260, 777, 2100]),
     "gqa8_d64_f32": ("f32", 16, 2, 64, [5, 260, 777, 2100]),
     "gqa4_d64_bf16": ("bf16", 16, 4, 64, [1, 16, 48, 4097]),
+    # long contexts: more than 64 partial results in a row (the merge's
+    # lane-parallel maxima then take a second round), thousands of table entries
+    "long_gqa4_d64_bf16": ("bf16", 8, 2, 64, [70000, 40961, 3]),
+    "long_gqa4_d64_f32": ("f32", 8, 2, 64, [35000, 33]),
 }
 
 
