@@ -76,6 +76,9 @@ VARLEN_CASES = {
     "gqa8_d64": (32, 4, 64, [33, 32, 1], [33, 600, 3000]),
     # prefill rows only (no decode work), row groups of 64 at partition edges
     "gqa4_d128_item_edges": (32, 8, 128, [64, 65, 128, 63], [64, 577, 640, 1087]),
+    # a chunk deep in a long context (40 partitions: many items per row group,
+    # merged from many slots) beside a long decode row
+    "gqa4_d64_long_context": (16, 4, 64, [160, 1], [20000, 9000]),
 }
 
 
