@@ -17,8 +17,9 @@
 // work items from the plan's list (ticket t = record t / Hkv, KV head t % Hkv);
 // an item is one (sequence, KV head) over one or two consecutive 512-token
 // partitions (partition p is tokens [512p, 512p + 512)).  Wave w takes the
-// item's blocks w, w + 4, ... and keeps one online-softmax state per partition;
-// the four waves' states merge through LDS into one partial per partition.
+// item's blocks w, w + 4, ... and keeps one online-softmax state for the whole
+// item; the four waves' states merge through LDS into one partial result per
+// item (the output itself when the item is the sequence's only one).
 //
 // Per 16-token block, one wave (lane = 16 j + h, h = lane & 15, j = lane >> 4):
 //  scores  S[t][n] = sum_d K[t][d] q[n][d]  (v_mfma_f32_16x16x32_bf16, D/32 of

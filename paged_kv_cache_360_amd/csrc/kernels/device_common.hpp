@@ -51,12 +51,6 @@ __device__ __forceinline__ void widen16(const uint4& r, float* f) {
 __device__ __forceinline__ uint4 load16(const void* p) {
   return *reinterpret_cast<const uint4*>(p);
 }
-// The same with the nontemporal hint (`nt`): for K/V read once per launch.
-typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ uint4 load16_stream(const void* p) {
-  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
-  return make_uint4(v.x, v.y, v.z, v.w);
-}
 
 // Raw buffer resources (gfx9 descriptor, stride 0): loads at byte offsets at or
 // past the resource's range return zeros without a memory access.
