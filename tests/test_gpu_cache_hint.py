@@ -68,3 +68,26 @@ def test_shared_first_block_flag_and_identical_results():
     rows = np.array([0, 1, S - 1])
     ref = oracle.decode_attention(qh[rows], kh, vh, shared[rows], ctx[rows], np.float32(scale))
     assert_close(host_f64(out_shared)[rows], ref, "bf16", "cache hint, shared first block")
+
+
+def test_more_first_blocks_than_hash_slots_keeps_the_cached_policy():
+    """5000 decode sequences with distinct first blocks overflow the plan's
+    4096-slot table: a first block whose probe run finds no slot counts as
+    shared, so the launch keeps the default policy (the safe side); results are
+    unchanged."""
+    S, Hq, Hkv, D, C = 5000, 8, 2, 64, 40
+    say(f"cache hint: {S} sequences of {C} tokens")
+    mb = -(-C // 16)
+    nb = S * mb + 8
+    rng = np.random.default_rng(12)
+    tables = rng.permutation(nb)[:S * mb].astype(np.int32).reshape(S, mb)
+    ctx = np.full(S, C, np.int32)
+    kh = normal_values_parallel(51, (nb, 16, Hkv, D), "bf16")
+    vh = normal_values_parallel(52, (nb, 16, Hkv, D), "bf16")
+    qh = normal_values_parallel(53, (S, Hq, D), "bf16")
+    scale = float(np.float32(1.0 / math.sqrt(D)))
+    out, flag = _decode(tables, ctx, dev(kh), dev(vh), dev(qh), scale, C)
+    assert flag == 1
+    rows = np.array([0, 1, 2047, 4095, 4096, S - 1])
+    ref = oracle.decode_attention(qh[rows], kh, vh, tables[rows], ctx[rows], np.float32(scale))
+    assert_close(host_f64(out)[rows], ref, "bf16", "cache hint, 5000 first blocks")
