@@ -70,6 +70,8 @@ __device__ __forceinline__ void plan_body(
   constexpr int kTailBlocks = 2 * kPartBlocks;  // largest record sorted into the tail
   constexpr int NBK = kTailBlocks + 1;          // buckets: tail-record block count kTailBlocks .. 0
   __shared__ int32_t s_wsum[kPlanThreads / kWave][3];  // per wave: full items, prefill records at span 1, 2
+  __shared__ int32_t s_wpre[kPlanThreads / kWave][3];  // the same summed over the waves before it
+  __shared__ int32_t s_tot[2];                          // prefill records at span 1, 2 over all waves
   __shared__ int32_t s_bucket[NBK];
   __shared__ int32_t s_key[kShareSlots];
   __shared__ int32_t s_cnt[kShareSlots];
@@ -178,7 +180,7 @@ __device__ __forceinline__ void plan_body(
     }
   }
   // Inclusive scans of (full, npre, npre2) over the workgroup: within each
-  // wave by lane shuffles, then across the waves' totals in LDS (one barrier).
+  // wave by lane shuffles, then across the waves' totals by wave 0 (through LDS).
   constexpr int NWV = kPlanThreads / kWave;
   const int lane = t & (kWave - 1);
   const int wv = t / kWave;
@@ -198,28 +200,40 @@ __device__ __forceinline__ void plan_body(
     s_wsum[wv][1] = inc_p;
     s_wsum[wv][2] = inc_p2;
   }
-  __syncthreads();  // (also orders the bucket counts of the loop above)
-  int tot_f = 0, tot_p = 0, tot_p2 = 0;
-  for (int w = 0; w < NWV; ++w) {
-    const int a = s_wsum[w][0], b = s_wsum[w][1], c = s_wsum[w][2];
-    if (w < wv) {
-      inc_f += a;
-      inc_p += b;
-      inc_p2 += c;
+  __syncthreads();  // (also orders the bucket counts and the first-block table of the loop above)
+  // While wave 0 scans: does another decode sequence start with this thread's
+  // sequence's first block?
+  const bool own_shared = per == 1 && share_count(own_b0) > 1;
+  if (own_shared) s_shared_any = 1;
+  if (wv == 0) {
+    // The waves' totals: an exclusive scan over lanes 0 .. NWV-1 (one lane per
+    // wave); the last lane holds the grand totals.
+    static_assert(NWV <= kWave, "one lane per wave");
+    const int a0 = lane < NWV ? s_wsum[lane][0] : 0;
+    const int a1 = lane < NWV ? s_wsum[lane][1] : 0;
+    const int a2 = lane < NWV ? s_wsum[lane][2] : 0;
+    int i0 = a0, i1 = a1, i2 = a2;
+    for (int off = 1; off < kWave; off <<= 1) {
+      const int v0 = __shfl_up(i0, off, kWave);
+      const int v1 = __shfl_up(i1, off, kWave);
+      const int v2 = __shfl_up(i2, off, kWave);
+      if (lane >= off) {
+        i0 += v0;
+        i1 += v1;
+        i2 += v2;
+      }
     }
-    tot_f += a;
-    tot_p += b;
-    tot_p2 += c;
-  }
-  const int num_full = tot_f;
-  // Prefill span: rounds of items per compute unit (one workgroup each) at
-  // span 1 and 2; span 2 when its rounds, each twice as long, take no longer.
-  const int64_t cus = max(1, num_cus);
-  const int64_t rounds1 = ((int64_t)tot_p * Hkv + cus - 1) / cus;
-  const int64_t rounds2 = ((int64_t)tot_p2 * Hkv + cus - 1) / cus;
-  const int span = (rounds1 > 1 && 2 * rounds2 <= rounds1) ? 2 : 1;
-  const int num_pre = span == 2 ? tot_p2 : tot_p;
-  if (wv == 0) {  // bucket start offsets in the decode tail region: a lane-parallel scan
+    if (lane < NWV) {
+      s_wpre[lane][0] = i0 - a0;
+      s_wpre[lane][1] = i1 - a1;
+      s_wpre[lane][2] = i2 - a2;
+    }
+    const int full_total = __shfl(i0, kWave - 1, kWave);
+    if (lane == kWave - 1) {
+      s_tot[0] = i1;
+      s_tot[1] = i2;
+    }
+    // bucket start offsets in the decode tail region: a lane-parallel scan
     static_assert(NBK == kWave + 1, "one bucket per lane plus the empty-item bucket");
     const int c = s_bucket[lane];
     int inc = c;
@@ -227,10 +241,21 @@ __device__ __forceinline__ void plan_body(
       const int v = __shfl_up(inc, off, kWave);
       if (lane >= off) inc += v;
     }
-    s_bucket[lane] = num_full + inc - c;
-    if (lane == kWave - 1) s_bucket[kWave] = num_full + inc;
+    s_bucket[lane] = full_total + inc - c;
+    if (lane == kWave - 1) s_bucket[kWave] = full_total + inc;
   }
   __syncthreads();
+  inc_f += s_wpre[wv][0];
+  inc_p += s_wpre[wv][1];
+  inc_p2 += s_wpre[wv][2];
+  const int tot_p = s_tot[0], tot_p2 = s_tot[1];
+  // Prefill span: rounds of items per compute unit (one workgroup each) at
+  // span 1 and 2; span 2 when its rounds, each twice as long, take no longer.
+  const int64_t cus = max(1, num_cus);
+  const int64_t rounds1 = ((int64_t)tot_p * Hkv + cus - 1) / cus;
+  const int64_t rounds2 = ((int64_t)tot_p2 * Hkv + cus - 1) / cus;
+  const int span = (rounds1 > 1 && 2 * rounds2 <= rounds1) ? 2 : 1;
+  const int num_pre = span == 2 ? tot_p2 : tot_p;
 
   // Writes.  Decode sequences (at most a few records each): every thread writes
   // its own.  Prefill sequences (hundreds of rows and records each): the wave
@@ -242,7 +267,7 @@ __device__ __forceinline__ void plan_body(
     if (q != 1) continue;
     const int row0 = per == 1 ? own_row0 : first_row(s);
     const int app = (per == 1 ? own_raw : ctx[s]) == c ? kAppendable : 0;
-    if (share_count(per == 1 ? own_b0 : (c > 0 ? first_block(s) : kShareEmpty)) > 1) s_shared_any = 1;
+    if (per > 1 && share_count(c > 0 ? first_block(s) : kShareEmpty) > 1) s_shared_any = 1;
     const int n = parts_of(c);
     const int ni = items_of(n);
     for (int k = 0; k < ni - 1; ++k, ++od)
