@@ -13,11 +13,17 @@ namespace pkv {
 constexpr int kDecodeThreads = 256;                 // 4 wavefronts per workgroup
 constexpr int kDecodeWaves = kDecodeThreads / kWave;
 constexpr int kPlanThreads = 1024;                  // work-list builder: one workgroup
-// A decode work item covers up to two consecutive 512-token partitions of one
-// (sequence, KV head); on the matrix cores its waves keep one softmax state
-// for the whole item, meet once at its end and write one partial result.
+// A decode work item covers up to kItemParts consecutive 512-token partitions
+// of one (sequence, KV head), or kLongItemParts for a sequence of at least
+// kLongItemFrom partitions (fewer item boundaries where a sequence has many
+// items); on the matrix cores its waves keep one softmax state for the whole
+// item, meet once at its end and write one partial result.
 constexpr int kItemParts = 2;
-constexpr int kItemBlocks = kItemParts * kPartBlocks;
+constexpr int kLongItemParts = 4;
+constexpr int kLongItemFrom = 9;
+__host__ __device__ inline int item_parts(int nparts) {
+  return nparts >= kLongItemFrom ? kLongItemParts : kItemParts;
+}
 // Flags in a decode record's partition field (partition numbers stay below
 // 2^16): the item covers that one partition only; the sequence's context
 // length was not clamped, so its new token (position ctx - 1) is the one the

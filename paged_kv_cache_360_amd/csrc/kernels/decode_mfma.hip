@@ -133,7 +133,7 @@ __device__ __forceinline__ void decode_partition_body(const DecodeParams& p) {
   constexpr int NBUF = kMfmaPipelineDepth;
   using VT = typename VPiece<D>::T;
   static_assert(G >= 1 && G <= 16, "the q heads of one KV head fill at most 16 MFMA columns");
-  static_assert(kPartBlocks % NWAVE == 0 && kItemBlocks / NWAVE <= kWave,
+  static_assert(kPartBlocks % NWAVE == 0 && kLongItemParts * kPartBlocks / NWAVE <= kWave,
                 "each wave holds its block ids of an item in one register");
 
   const int lane = threadIdx.x & (kWave - 1);
@@ -181,12 +181,14 @@ __device__ __forceinline__ void decode_partition_body(const DecodeParams& p) {
     {
       // slots: the full items in order, then the pieces of the last item
       const int nparts = max(1, (it.ctx + kPartTokens - 1) / kPartTokens);
-      const int full_end = (nparts + kItemParts - 1) / kItemParts * kItemParts - kItemParts;
-      it.slot = it.part < full_end ? it.part / kItemParts : full_end / kItemParts + (it.part - full_end);
+      const int ip = item_parts(nparts);
+      const int full_end = (nparts + ip - 1) / ip * ip - ip;
+      it.slot = it.part < full_end ? it.part / ip : full_end / ip + (it.part - full_end);
     }
     const int nblk = (it.ctx + kBlockTokens - 1) / kBlockTokens;
     it.b_begin = it.part * kPartBlocks;
-    const int in_item = min((r.y & kOnePartition) ? kPartBlocks : kItemBlocks, nblk - it.b_begin);
+    const int in_item = min((r.y & kOnePartition) ? kPartBlocks : item_parts((it.ctx + kPartTokens - 1) / kPartTokens) * kPartBlocks,
+                            nblk - it.b_begin);
     it.nmine = max(0, (in_item - wave + NWAVE - 1) / NWAVE);
     it.row0 = (int64_t)r.w * Hq + (int64_t)it.g * G;  // r.w: the sequence's query row
     it.k_lane = (int)(h * tok_bytes + (it.g * D + 8 * j) * 2);

@@ -11,9 +11,11 @@
 //
 // Outputs (all in the caller's workspace):
 //  * decode records {sequence, first partition, context, query row}, one per
-//    kItemParts consecutive partitions.  In front: every item but a sequence's
-//    last (all full, kItemBlocks blocks), and the only item of a sequence with
-//    one item when it has more than kTailBlocks blocks.  Then the tail, in
+//    item_parts(n) consecutive partitions of a sequence of n partitions (four
+//    when n >= kLongItemFrom, else two).  In front: every item but a sequence's
+//    last, the four-partition ones first (items roughly in decreasing size),
+//    and the only item of a sequence with one item when it has more than
+//    kTailBlocks blocks.  Then the tail, in
 //    decreasing block count (a counting sort over the kTailBlocks + 1 possible
 //    counts): the other last items, where the last item of a sequence with
 //    several items is split into one-partition records (first partition field
@@ -69,9 +71,9 @@ __device__ __forceinline__ void plan_body(
     int32_t* __restrict__ row_slots, bool record_slots, const int32_t* __restrict__ tab, int32_t MB) {
   constexpr int kTailBlocks = 2 * kPartBlocks;  // largest record sorted into the tail
   constexpr int NBK = kTailBlocks + 1;          // buckets: tail-record block count kTailBlocks .. 0
-  __shared__ int32_t s_wsum[kPlanThreads / kWave][3];  // per wave: full items, prefill records at span 1, 2
-  __shared__ int32_t s_wpre[kPlanThreads / kWave][3];  // the same summed over the waves before it
-  __shared__ int32_t s_tot[2];                          // prefill records at span 1, 2 over all waves
+  __shared__ int32_t s_wsum[kPlanThreads / kWave][4];  // per wave: full items, prefill records at span 1, 2
+  __shared__ int32_t s_wpre[kPlanThreads / kWave][4];  // the same summed over the waves before it
+  __shared__ int32_t s_tot[3];                          // prefill records at span 1, 2 over all waves
   __shared__ int32_t s_bucket[NBK];
   __shared__ int32_t s_key[kShareSlots];
   __shared__ int32_t s_cnt[kShareSlots];
@@ -88,9 +90,9 @@ __device__ __forceinline__ void plan_body(
   auto parts_of = [&](int keys) { return max(1, (keys + kPartTokens - 1) / kPartTokens); };
   auto first_row = [&](int s) { return row0_from(s, qsl ? qsl[s] : 0); };
   auto rows_of = [&](int s) { return rows_from(first_row(s), qsl ? qsl[s + 1] : 0); };
-  auto items_of = [&](int n) { return (n + kItemParts - 1) / kItemParts; };
-  auto last_blocks = [&](int c, int n) {  // blocks of the last item: kItemBlocks when full, 0 when empty
-    return (c + kBlockTokens - 1) / kBlockTokens - (items_of(n) - 1) * kItemBlocks;
+  auto items_of = [&](int n) { return (n + item_parts(n) - 1) / item_parts(n); };
+  auto last_blocks = [&](int c, int n) {  // blocks of the last item: a full item's when full, 0 when empty
+    return (c + kBlockTokens - 1) / kBlockTokens - (items_of(n) - 1) * item_parts(n) * kPartBlocks;
   };
   auto bucket_of = [&](int blocks) { return kTailBlocks - blocks; };
   // prefill: the keys seen by row r of a sequence with q rows and c keys
@@ -131,7 +133,9 @@ __device__ __forceinline__ void plan_body(
     }
     return 2;
   };
-  int full = 0, npre = 0, npre2 = 0;
+  // front records: two-partition items (and only items above kTailBlocks),
+  // four-partition items; prefill records at span 1 and 2
+  int full = 0, npre = 0, npre2 = 0, flong = 0;
   int own_c = 0, own_q = 0, own_row0 = 0, own_raw = 0;  // this thread's (last) sequence, for the write loop
   int32_t own_b0 = kShareEmpty;
   for (int s = s0; s < s1; ++s) {
@@ -164,7 +168,7 @@ __device__ __forceinline__ void plan_body(
       if (ni == 1) {                 // the sequence's only record
         if (lb > kTailBlocks) ++full; else atomicAdd(&s_bucket[bucket_of(lb)], 1);
       } else {
-        full += ni - 1;
+        if (item_parts(n) == kLongItemParts) flong += ni - 1; else full += ni - 1;
         if (lb > kPartBlocks) {      // the last item in one-partition pieces
           for (int b = lb; b > 0; b -= kPartBlocks) atomicAdd(&s_bucket[bucket_of(min(b, kPartBlocks))], 1);
         } else {
@@ -179,26 +183,29 @@ __device__ __forceinline__ void plan_body(
       }
     }
   }
-  // Inclusive scans of (full, npre, npre2) over the workgroup: within each
+  // Inclusive scans of (full, npre, npre2, flong) over the workgroup: within each
   // wave by lane shuffles, then across the waves' totals by wave 0 (through LDS).
   constexpr int NWV = kPlanThreads / kWave;
   const int lane = t & (kWave - 1);
   const int wv = t / kWave;
-  int inc_f = full, inc_p = npre, inc_p2 = npre2;
+  int inc_f = full, inc_p = npre, inc_p2 = npre2, inc_l = flong;
   for (int off = 1; off < kWave; off <<= 1) {
     const int vf = __shfl_up(inc_f, off, kWave);
     const int vp = __shfl_up(inc_p, off, kWave);
     const int vp2 = __shfl_up(inc_p2, off, kWave);
+    const int vl = __shfl_up(inc_l, off, kWave);
     if (lane >= off) {
       inc_f += vf;
       inc_p += vp;
       inc_p2 += vp2;
+      inc_l += vl;
     }
   }
   if (lane == kWave - 1) {
     s_wsum[wv][0] = inc_f;
     s_wsum[wv][1] = inc_p;
     s_wsum[wv][2] = inc_p2;
+    s_wsum[wv][3] = inc_l;
   }
   __syncthreads();  // (also orders the bucket counts and the first-block table of the loop above)
   // While wave 0 scans: does another decode sequence start with this thread's
@@ -212,26 +219,31 @@ __device__ __forceinline__ void plan_body(
     const int a0 = lane < NWV ? s_wsum[lane][0] : 0;
     const int a1 = lane < NWV ? s_wsum[lane][1] : 0;
     const int a2 = lane < NWV ? s_wsum[lane][2] : 0;
-    int i0 = a0, i1 = a1, i2 = a2;
+    const int a3 = lane < NWV ? s_wsum[lane][3] : 0;
+    int i0 = a0, i1 = a1, i2 = a2, i3 = a3;
     for (int off = 1; off < kWave; off <<= 1) {
       const int v0 = __shfl_up(i0, off, kWave);
       const int v1 = __shfl_up(i1, off, kWave);
       const int v2 = __shfl_up(i2, off, kWave);
+      const int v3 = __shfl_up(i3, off, kWave);
       if (lane >= off) {
         i0 += v0;
         i1 += v1;
         i2 += v2;
+        i3 += v3;
       }
     }
     if (lane < NWV) {
       s_wpre[lane][0] = i0 - a0;
       s_wpre[lane][1] = i1 - a1;
       s_wpre[lane][2] = i2 - a2;
+      s_wpre[lane][3] = i3 - a3;
     }
-    const int full_total = __shfl(i0, kWave - 1, kWave);
+    const int full_total = __shfl(i0, kWave - 1, kWave) + __shfl(i3, kWave - 1, kWave);
     if (lane == kWave - 1) {
       s_tot[0] = i1;
       s_tot[1] = i2;
+      s_tot[2] = i3;
     }
     // bucket start offsets in the decode tail region: a lane-parallel scan
     static_assert(NBK == kWave + 1, "one bucket per lane plus the empty-item bucket");
@@ -248,7 +260,8 @@ __device__ __forceinline__ void plan_body(
   inc_f += s_wpre[wv][0];
   inc_p += s_wpre[wv][1];
   inc_p2 += s_wpre[wv][2];
-  const int tot_p = s_tot[0], tot_p2 = s_tot[1];
+  inc_l += s_wpre[wv][3];
+  const int tot_p = s_tot[0], tot_p2 = s_tot[1], tot_l = s_tot[2];
   // Prefill span: rounds of items per compute unit (one workgroup each) at
   // span 1 and 2; span 2 when its rounds, each twice as long, take no longer.
   const int64_t cus = max(1, num_cus);
@@ -260,7 +273,8 @@ __device__ __forceinline__ void plan_body(
   // Writes.  Decode sequences (at most a few records each): every thread writes
   // its own.  Prefill sequences (hundreds of rows and records each): the wave
   // takes them one at a time, in each owner's order, and all 64 lanes write.
-  int od = inc_f - full;
+  int od = tot_l + inc_f - full;   // the two-partition front records after all four-partition ones
+  int odl = inc_l - flong;
   for (int s = s0; s < s1; ++s) {
     const int c = per == 1 ? own_c : ctx_of(s);
     const int q = per == 1 ? own_q : rows_of(s);
@@ -270,10 +284,13 @@ __device__ __forceinline__ void plan_body(
     if (per > 1 && share_count(c > 0 ? first_block(s) : kShareEmpty) > 1) s_shared_any = 1;
     const int n = parts_of(c);
     const int ni = items_of(n);
-    for (int k = 0; k < ni - 1; ++k, ++od)
-      if (od < dec_cap) dec[od] = make_int4(s, (k * kItemParts) | app, c, row0);
+    const bool lng = item_parts(n) == kLongItemParts;
+    for (int k = 0; k < ni - 1; ++k) {
+      const int at = lng ? odl++ : od++;
+      if (at < dec_cap) dec[at] = make_int4(s, (k * item_parts(n)) | app, c, row0);
+    }
     const int lb = last_blocks(c, n);
-    const int p0 = (ni - 1) * kItemParts;
+    const int p0 = (ni - 1) * item_parts(n);
     int recs = ni;
     if (ni == 1) {
       const int4 rec = make_int4(s, p0 | app | kWholeSequence, c, row0);
