@@ -117,6 +117,9 @@ DECODE_CASES = {
     "gqa8_d128_bf16": ("bf16", 16, 2, 128, [5, 260, 777, 2100]),
     "gqa8_d64_f32": ("f32", 16, 2, 64, [5, 260, 777, 2100]),
     "gqa4_d64_bf16": ("bf16", 16, 4, 64, [1, 16, 48, 4097]),
+    # around the context at which a sequence's items grow from two partitions
+    # to four (nine partitions: more than 4096 tokens), with ragged last items
+    "item_size_edges_bf16": ("bf16", 32, 8, 128, [4096, 4097, 4607, 4608, 4609, 6144, 6145, 8193]),
     # long contexts: more than 64 partial results in a row (the merge's
     # lane-parallel maxima then take a second round), thousands of table entries
     "long_gqa4_d64_bf16": ("bf16", 8, 2, 64, [70000, 40961, 3]),
