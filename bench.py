@@ -95,6 +95,9 @@ def parse_args():
     ap.add_argument("--read-probe", action="store_true",
                     help="only run the plain read kernels over a 1.5 GiB pool (blocks in random order; "
                          "whole blocks and per-head slices; random and zero-filled data)")
+    ap.add_argument("--lds-probe", action="store_true",
+                    help="only run the chunked-prefill kernel's LDS operand reads by themselves (K, V, both; "
+                         "4, 8 and 16 waves per compute unit)")
     ap.add_argument("--traffic-from", nargs=5, metavar="FILE", default=None,
                     help="rocprofv3 counter results (counter_collection CSV or results .db): FETCH_SIZE "
                          "and WRITE_SIZE of a bench run, "
@@ -475,6 +478,51 @@ def read_probe_standalone(torch, np, seed):
                       "results": lines}))
 
 
+def lds_probe(torch, np):
+    """The chunked-prefill kernel's LDS operand reads by themselves
+    (libpkvprobe.so): one workgroup per compute unit with that kernel's LDS
+    layout at head_dim 128, each wave repeating the K reads (eight 16-byte reads
+    per lane), the transposing V reads (sixteen 8-byte reads per lane) or both,
+    as one wave does in one 32-token step.  Reports the median loop cycles per
+    iteration and wave (s_memtime, the counter the kernel's own step stamps
+    use) and the LDS read rate of the whole device from HIP events."""
+    import ctypes
+    lib = _probe_lib()
+    if lib is None:
+        raise RuntimeError("libpkvprobe.so is not built")
+    fn = lib.pkv_probe_lds_reads
+    fn.restype = ctypes.c_int
+    fn.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
+                   ctypes.c_void_p]
+    grid = torch.cuda.get_device_properties(0).multi_processor_count
+    iters = 20000
+    stream = torch.cuda.current_stream()
+    results = []
+    for waves in (4, 8, 16):
+        sink = torch.zeros(grid * waves * 64, dtype=torch.int32, device="cuda")
+        cyc = torch.zeros(grid * waves, dtype=torch.int64, device="cuda")
+        for mode, name in ((1, "K"), (2, "V"), (3, "K+V")):
+            best = None
+            for _ in range(3):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                rc = fn(mode, waves, iters, grid, sink.data_ptr(), cyc.data_ptr(), stream.cuda_stream)
+                e1.record(stream)
+                if rc != 0:
+                    raise RuntimeError(f"lds probe: error {rc}")
+                torch.cuda.synchronize()
+                ms = e0.elapsed_time(e1)
+                best = ms if best is None else min(best, ms)
+            per_wave = (8 * 1024 if mode & 1 else 0) + (16 * 512 if mode & 2 else 0)
+            cycles = float(np.median(cyc.cpu().numpy())) / iters
+            results.append({"reads": name, "waves_per_cu": waves, "bytes_per_wave_iter": per_wave,
+                            "median_cycles_per_iter": round(cycles, 1),
+                            "bytes_per_cycle_per_cu_if_concurrent": round(waves * per_wave / cycles, 1),
+                            "device_TBps_events": round(grid * waves * per_wave * iters / (best * 1e-3) / 1e12, 2),
+                            "launch_ms": round(best, 3)})
+    print(json.dumps({"probe": "lds_operand_reads", "compute_units": grid, "iters": iters, "results": results}))
+
+
 def main():
     args = parse_args()
     if args.traffic_from:
@@ -521,6 +569,9 @@ def main():
         return
     if args.read_probe:
         read_probe_standalone(torch, np, args.seed)
+        return
+    if args.lds_probe:
+        lds_probe(torch, np)
         return
 
     spec = SPECS[args.workload]

@@ -43,7 +43,7 @@ HIP_SOURCES = ["kernels/cache_ops.hip", "kernels/plan.hip", "kernels/decode.hip"
 HOST_SOURCES = ["api.cpp", "allocator.cpp"]
 # Measurement only: read-bandwidth probes the bench compares the decode kernel
 # with (a library of its own; the attention library does not contain them).
-PROBE_SOURCES = ["probes/read_probe.hip"]
+PROBE_SOURCES = ["probes/read_probe.hip", "probes/lds_probe.hip"]
 PROBE_OUT = os.path.join(PKG, "libpkvprobe.so")
 
 
