@@ -381,14 +381,16 @@ def prefix_cache_probe(np, pkv, seed):
 def partial_slots(np, lens, per_item):
     """Partial results each decode row's merge combines (1: the row is written
     directly).  The matrix-core kernel (per_item) writes one partial per work
-    item: items of two 512-token partitions, the last item of a sequence with
-    several split into one-partition pieces when it covers more than one; the
-    vector-ALU kernel writes one per 512-token partition."""
+    item: items of two 512-token partitions, four for a sequence of nine
+    partitions or more, the last item of a sequence with several split into
+    one-partition pieces when it covers more than one; the vector-ALU kernel
+    writes one per 512-token partition."""
     nparts = np.maximum(1, -(-lens // 512))
     if not per_item:
         return nparts
-    items = -(-nparts // 2)
-    last_blocks = -(-lens // 16) - (items - 1) * 64
+    ip = np.where(nparts >= 9, 4, 2)
+    items = -(-nparts // ip)
+    last_blocks = -(-lens // 16) - (items - 1) * ip * 32
     pieces = np.where((items > 1) & (last_blocks > 32), -(-last_blocks // 32), 1)
     return items - 1 + pieces
 
