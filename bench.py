@@ -483,11 +483,12 @@ def read_probe_standalone(torch, np, seed):
 def lds_probe(torch, np):
     """The chunked-prefill kernel's LDS operand reads by themselves
     (libpkvprobe.so): one workgroup per compute unit with that kernel's LDS
-    layout at head_dim 128, each wave repeating the K reads (eight 16-byte reads
+    layout at head_dim 128 (padded rows, or its unit-column layouts), each wave repeating the K reads (eight 16-byte reads
     per lane), the transposing V reads (sixteen 8-byte reads per lane) or both,
     as one wave does in one 32-token step.  Reports the median loop cycles per
     iteration and wave (s_memtime, the counter the kernel's own step stamps
-    use) and the LDS read rate of the whole device from HIP events."""
+    use) and the LDS read rate of the whole device from HIP events.  "units"
+    lines use the kernel's unit-column layouts instead of padded rows."""
     import ctypes
     lib = _probe_lib()
     if lib is None:
@@ -503,7 +504,7 @@ def lds_probe(torch, np):
     for waves in (4, 8, 16):
         sink = torch.zeros(grid * waves * 64, dtype=torch.int32, device="cuda")
         cyc = torch.zeros(grid * waves, dtype=torch.int64, device="cuda")
-        for mode, name in ((1, "K"), (2, "V"), (3, "K+V")):
+        for mode, name in ((1, "K"), (2, "V"), (3, "K+V"), (5, "K units"), (6, "V units"), (7, "K+V units")):
             best = None
             for _ in range(3):
                 e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)

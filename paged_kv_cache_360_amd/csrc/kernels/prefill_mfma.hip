@@ -31,19 +31,25 @@
 // Each column keeps its own causal mask (token < the keys its row sees), so the
 // diagonal block needs no special case.
 //
-// K and V of each step are loaded once per workgroup (one D/8-byte piece of K
-// and of V per thread and step row), staged through five LDS buffers (K rows
-// padded to D*2 + 16 bytes, V rows to D*2 + 64, which keeps both read patterns
-// free of bank conflicts), and read by every wave.  Rows past the context read
-// as zeros (the block's buffer resource ends at the context), so a V row there
+// K and V of each step are loaded once per workgroup, straight into LDS
+// (buffer loads with the LDS destination: 16 bytes per lane, 1 KiB per wave
+// instruction, no registers and no LDS write instructions on the way), and
+// read by every wave.  In LDS a block's K or V slice is kept in 16-byte units
+// (8 dims of one token) laid out so that both read patterns are free of bank
+// conflicts without padding (see s_k / s_v).  Rows past the context land as
+// zeros (the block's buffer resource ends at the context), so a V row there
 // never meets a zero weight as 0 * NaN.  Each wave computes the scores of step
 // q + 1 while it runs step q's softmax and value products, so the matrix cores
-// work during the vector code.  There is one barrier per two steps: while the
-// pair q, q + 1 runs, steps q + 3 and q + 4 are staged into the buffers of
-// steps q - 2 and q - 1, and the loads of q + 5 and q + 6 are issued, so the
-// load stream runs up to six steps ahead of the computation, across item
-// boundaries: the workgroup keeps the record and the q operand of the next
-// item, so a new item starts with its first steps and q already loaded.
+// work during the vector code.  There is one barrier per four steps, over nine
+// step buffers: while the steps q .. q + 3 run (reading the buffers of steps
+// q .. q + 4), steps q + 5 .. q + 8 load into the buffers of q - 4 .. q - 1,
+// last read before the previous barrier, and each wave waits for its own loads
+// before the next barrier.  Fewer barriers let the eight waves drift apart, so
+// their LDS reads and their arithmetic overlap rather than all waves reading
+// at once after each barrier (one barrier per two steps over seven buffers
+// measured 3-4% slower).  The load stream runs across item boundaries: the
+// workgroup keeps the record and the q operand of the next item, so a new item
+// starts with its first steps and q already loaded.
 //
 // Workgroups take items from the prefill tickets: the first two are static
 // (blockIdx.x and blockIdx.x + gridDim.x), the rest come from the counter.  A row whose
@@ -72,16 +78,11 @@ constexpr int kStepTokens = 2 * kBlockTokens;  // tokens per step (two blocks)
 constexpr int kPrefillWaves = 8;
 constexpr int kPrefillThreads = kPrefillWaves * kWave;
 constexpr int kColTiles = 8 / kPrefillWaves;   // 32-column tiles per wave
-constexpr int kPrefillSteps = 2;               // steps of K/V in flight in registers
-// Barrier interval: two steps, over five LDS buffers (steps q .. q+2 are read
-// while q+3 and q+4 are staged), which lets the waves of a SIMD drift apart
-// within the interval.
-constexpr int kPrefillBufs = 5;
-
-// One thread's piece of a block row: D / 8 bytes.
-template <int D> struct KVPiece;
-template <> struct KVPiece<128> { using T = uint4; };
-template <> struct KVPiece<64> { using T = uint2; };
+constexpr int kPrefillSteps = 4;               // steps per barrier interval
+// LDS buffers of one step each: while steps q .. q+3 are computed (reading the
+// buffers of steps q .. q+4), steps q+5 .. q+8 load into the buffers of
+// q-4 .. q-1; 9 x 16 KiB at head_dim 128.
+constexpr int kPrefillBufs = 9;
 
 // Transposing LDS read of 16-bit data (gfx950): each lane names 8 bytes (four
 // 16-bit values); within each group of 16 lanes, lane i receives value i%4 of
@@ -98,6 +99,12 @@ __device__ __forceinline__ float add_bf16_pair(uint32_t w, float acc) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), __builtin_bit_cast(bf16x2, 0x3F803F80u), acc,
                                          false);
 }
+// Direct-to-LDS buffer load (gfx950): each lane's 16 bytes at voff + soff of
+// the resource land at lds + 16 * lane (lds uniform over the wave); bytes past
+// the resource's range land as zeros.  Counted by vmcnt like any vector load.
+__device__ __forceinline__ void buffer_load_lds16(__amdgpu_buffer_rsrc_t r, char* lds, int voff, int soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voff, soff, 0, 0);
+}
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   const bf16x2 v = {(__bf16)a, (__bf16)b};
   return __builtin_bit_cast(uint32_t, v);
@@ -110,14 +117,9 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void prefill_mfma_kernel(Decode
   constexpr int CT = kColTiles;
   constexpr int R = 32 / G;                // rows per column tile
   constexpr int RPW = CT * R;              // rows per wave
-  constexpr int RSK = D * 2 + 16;          // LDS row strides in bytes: K (16-byte pad)
-  constexpr int RSV = D * 2 + 64;          // and V (64-byte pad)
-  constexpr int PS = D / 8;                // bytes per thread and block row
+  constexpr int BLKB = kBlockTokens * D * 2;  // LDS bytes of one block's K (or V) slice
   constexpr int NS = kPrefillSteps;
-  using PT = typename KVPiece<D>::T;
   static_assert(G >= 1 && G <= 32 && 32 % G == 0, "a tile holds whole rows of G heads");
-  constexpr int RPT = kStepTokens * 16 / kPrefillThreads;  // step rows each thread stages
-  static_assert(RPT >= 1 && kStepTokens * 16 % kPrefillThreads == 0, "16 threads per token row");
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -130,10 +132,15 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void prefill_mfma_kernel(Decode
   const int total = min(p.sched[3], p.pre_cap * p.Hkv);
   const int grid = (int)gridDim.x;
 
-  // [buffer][32 rows x row stride]: step q in buffer q % kPrefillBufs (the
-  // scores of step q + 1 are computed while step q's values are)
-  __shared__ __attribute__((aligned(16))) char s_k[kPrefillBufs][kStepTokens * RSK];
-  __shared__ __attribute__((aligned(16))) char s_v[kPrefillBufs][kStepTokens * RSV];
+  // [buffer][two blocks of 16 token rows]: step q in buffer q % kPrefillBufs.
+  // A block's slice is stored in 16-byte units (8 dims of one token): unit
+  // c * 16 + u holds dims 8c .. 8c+7 of token row u for K, and of token row
+  // u ^ (4 * (c % 4)) for V.  Both read patterns below then spread over all
+  // banks (K: 16 lanes read 16 rows of one unit column, 256 contiguous bytes;
+  // V: the transposing reads take four rows of four unit columns per 16 lanes),
+  // and a 1 KiB direct-to-LDS load (16 bytes per lane) fills four unit columns.
+  __shared__ __attribute__((aligned(16))) char s_k[kPrefillBufs][2 * BLKB];
+  __shared__ __attribute__((aligned(16))) char s_v[kPrefillBufs][2 * BLKB];
   __shared__ int s_ticket[2];
 
   struct Item {
@@ -165,10 +172,10 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void prefill_mfma_kernel(Decode
     it.b_begin = it.part * kPartBlocks;
     it.nblk = it.valid ? max(0, (k_end - k_begin + kBlockTokens - 1) / kBlockTokens) : 0;
     // steps of two blocks, padded to a multiple of NS so that every item starts
-    // on stage slot 0, and to at least 6: the load stream runs up to six steps
-    // ahead of the pair being computed and must never run past the next item;
-    // padding steps load nothing and compute nothing
-    it.nsteps = max(6, (max(1, (it.nblk + 1) / 2) + NS - 1) / NS * NS);
+    // an interval, and to at least 8: the load stream runs up to eight steps
+    // ahead of the interval being computed and must never run past the next
+    // item; padding steps load nothing and compute nothing
+    it.nsteps = max(8, (max(1, (it.nblk + 1) / 2) + NS - 1) / NS * NS);
     {
       // the item's block ids, one per lane (an item spans at most 64 blocks),
       // loaded once; each step then takes its id from a lane, with no memory wait
@@ -192,43 +199,36 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void prefill_mfma_kernel(Decode
     }
   };
 
-  // Cooperative loads: thread t holds the same piece of K and of V of step rows
-  // t / 16 + j * (threads / 16), j < RPT, bytes (t % 16) * PS .. + PS of KV head
-  // g's slice.  A wave's rows lie in one block (wblk[j] of the step's two), so
-  // its loads use one resource.
-  const int st_row = tid / 16;
-  const int st_col = (tid % 16) * PS;
-  constexpr int kRowStride = kPrefillThreads / 16;
-  int wblk[RPT];
+  // Loads straight into LDS: a wave instruction moves 1 KiB, 16 bytes per lane,
+  // into four unit columns of one block's K or V slice (lane i: unit column
+  // i / 16, position i % 16).  A step takes 4 CPB such instructions (K and V,
+  // two blocks, CPB per block slice); this wave issues LPW of them, all in one
+  // block slice: tensor ld_v (K or V), block ld_b of the step, unit columns
+  // 4 (ld_piece + j) .. +3 for j < LPW.
+  constexpr int CPB = D / 32;                      // 1 KiB pieces per block slice
+  constexpr int LPW = 4 * CPB / kPrefillWaves;     // load instructions per wave and step
+  static_assert(LPW >= 1 && 4 * CPB % kPrefillWaves == 0 && CPB % LPW == 0, "whole block slices per wave");
+  const int ld_first = wave * LPW;
+  const bool ld_v = ld_first >= 2 * CPB;
+  const int ld_b = (ld_first / CPB) % 2;
+  const int ld_piece = ld_first % CPB;
+  // per lane and instruction: the byte offset in the block (token row, dims);
+  // the KV head's offset goes in the scalar offset
+  int ld_off[LPW];
 #pragma unroll
-  for (int j = 0; j < RPT; ++j) wblk[j] = __builtin_amdgcn_readfirstlane((st_row + j * kRowStride) / kBlockTokens);
-  struct Stage {
-    PT k[RPT], v[RPT];
-  };
-  // Row `row` (block row row % 16) of block id pb (-1 past the item's blocks),
-  // whose first `lim` rows are in the context: the loads go through resources
-  // that end there (rows past it read zeros), empty for an id outside the pool.
-  auto issue_row = [&](int g, int pb, int lim, int row, PT& kk, PT& vv) {
-    const bool ok = (unsigned)pb < (unsigned)p.NB;
-    const uint64_t base = (uint64_t)(uint32_t)(ok ? pb : 0) * blk_bytes;
-    const int nrec = ok ? lim * (int)tok_bytes : 0;
-    const __amdgpu_buffer_rsrc_t kr =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(p.kc + base), (short)0, nrec, kRawBufferWord3);
-    const __amdgpu_buffer_rsrc_t vr =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(p.vc + base), (short)0, nrec, kRawBufferWord3);
-    const int off = (int)((row % kBlockTokens) * tok_bytes + g * D * 2 + st_col);
-    kk = buffer_load_piece<PT>(kr, off, 0);
-    vv = buffer_load_piece<PT>(vr, off, 0);
-  };
+  for (int j = 0; j < LPW; ++j) {
+    const int c = 4 * (ld_piece + j) + lane / 16;  // unit column: dims 8c .. 8c+7
+    const int u = lane % 16;
+    const int row = ld_v ? u ^ (4 * (c % 4)) : u;
+    ld_off[j] = row * (int)tok_bytes + c * 16;
+  }
+  const char* ld_pool = ld_v ? p.vc : p.kc;
   // The load stream's position: an item (copied) and a step of it.  Each step's
   // block id comes from a lane of the item's id register; with each id, the
   // number of the block's rows inside the context.
   struct Cursor {
     int ids;
     int nblk, ctx_rel, g, step, nsteps;
-  };
-  struct Ids {
-    int v[RPT], lim[RPT];
   };
   auto cursor_of = [&](const Item& it) {
     Cursor c;
@@ -240,27 +240,21 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void prefill_mfma_kernel(Decode
     c.nsteps = it.nsteps;
     return c;
   };
-  auto ids_at = [&](const Cursor& c) {
-    Ids ids;
+  // Loads of the cursor's step into LDS buffer buf.  Each block's buffer
+  // resource ends at the context (rows past it land as zeros, so a V row there
+  // never meets a zero weight as 0 * NaN) and is empty past the item's blocks
+  // or for an id outside the pool.
+  auto issue_step = [&](const Cursor& c, int buf) {
+    const int k = 2 * c.step + ld_b;
+    const int id = __builtin_amdgcn_readlane(c.ids, min(k, kWave - 1));
+    const bool ok = k < c.nblk && (unsigned)id < (unsigned)p.NB;
+    const int lim = min(kBlockTokens, c.ctx_rel - k * kBlockTokens);
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<char*>(ld_pool + (uint64_t)(uint32_t)(ok ? id : 0) * blk_bytes), (short)0,
+        ok ? lim * (int)tok_bytes : 0, kRawBufferWord3);
+    char* dst = (ld_v ? s_v[buf] : s_k[buf]) + ld_b * BLKB + ld_piece * 1024;
 #pragma unroll
-    for (int j = 0; j < RPT; ++j) {
-      const int k = 2 * c.step + wblk[j];
-      ids.v[j] = k < c.nblk ? __builtin_amdgcn_readlane(c.ids, min(k, kWave - 1)) : -1;
-      ids.lim[j] = min(kBlockTokens, c.ctx_rel - k * kBlockTokens);
-    }
-    return ids;
-  };
-  auto issue_step = [&](int g, const Ids& ids, Stage& st) {
-#pragma unroll
-    for (int j = 0; j < RPT; ++j) issue_row(g, ids.v[j], ids.lim[j], st_row + j * kRowStride, st.k[j], st.v[j]);
-  };
-  auto stage_to_lds = [&](const Stage& st, int buf) {
-#pragma unroll
-    for (int j = 0; j < RPT; ++j) {
-      const int row = st_row + j * kRowStride;
-      *reinterpret_cast<PT*>(&s_k[buf][row * RSK + st_col]) = st.k[j];
-      *reinterpret_cast<PT*>(&s_v[buf][row * RSV + st_col]) = st.v[j];
-    }
+    for (int j = 0; j < LPW; ++j) buffer_load_lds16(r, dst + 1024 * j, ld_off[j], c.g * D * 2);
   };
 
   bf16x8 qf[CT][NKC], qn[CT][NKC];   // q operands of the current and the next item
@@ -269,31 +263,41 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void prefill_mfma_kernel(Decode
   int col_keys[CT];                   // keys the column's row sees (0 past the item's rows)
   int min_keys;                       // the least of them over the wave (uniform)
 
+  // This lane's K operand in a step buffer: token n (block n / 16, row n % 16),
+  // dims 16 kc + 8 hh .. +7 = unit column 2 kc + hh, at k_lane + 512 kc.
+  const int k_lane = (n >> 4) * BLKB + hh * 256 + (n & 15) * 16;
+
   // Scores of the step in LDS buffer buf (the matrix products only).
   auto scores = [&](int buf, f32x16 (&sc)[CT]) {
-    const char* kb = s_k[buf];
+    const char* kb = s_k[buf] + k_lane;
 #pragma unroll
     for (int c = 0; c < CT; ++c) sc[c] = f32x16{};
 #pragma unroll
     for (int kc = 0; kc < NKC; ++kc) {
-      const bf16x8 kf = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(kb + n * RSK + 32 * kc + 16 * hh));
+      const bf16x8 kf = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(kb + 512 * kc));
 #pragma unroll
       for (int c = 0; c < CT; ++c) sc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[c][kc], sc[c], 0, 0, 0);
     }
   };
-  // This lane's address in a V buffer for the transposing reads: lane
-  // 16g + 4j + a names token row 4*(g/2) + j (of the 8-row group read), dims
-  // 16*(g%2) + 4a .. +3 of the output tile, so that lane 16g + i receives dim
-  // 16*(g%2) + i = lane%32 of token rows 4*(g/2) + 0..3 = 4*hh + 0..3.
-  const int v_lane = (4 * hh + ((lane >> 2) & 3)) * RSV + (16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2;
+  // This lane's addresses in a V buffer for the transposing reads: lane
+  // 16g + 4j + a names token row 4*(g/2) + j of an 8-row group (rows 0..7 of
+  // a block: v_lane, rows 8..15: v_lane_hi), dims 16*(g%2) + 4a .. +3 of the
+  // output tile, so that lane 16g + i receives dim 16*(g%2) + i = lane%32 of
+  // token rows 4*(g/2) + 0..3 = 4*hh + 0..3.  Those dims are unit column
+  // 4e + cl of output tile e (cl = 2*(g%2) + a/2; bytes 8*(a%2) of the unit),
+  // found at unit (4e + cl) * 16 + (row ^ 4*cl): e adds 1 KiB.
+  const int v_cl = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+  const int v_row = 4 * hh + ((lane >> 2) & 3);
+  const int v_lane = (v_cl * 16 + (v_row ^ (4 * v_cl))) * 16 + (lane & 1) * 8;
+  const int v_lane_hi = (v_cl * 16 + ((v_row + 8) ^ (4 * v_cl))) * 16 + (lane & 1) * 8;
 
   // Softmax and value products of a step from its scores and LDS buffer buf:
   // tokens t0 .. t0+31 (V rows past the context hold zeros); with them, in
   // the same straight-line code, the score products of the next step (K in
   // LDS buffer kbuf, into sn), so that the matrix and vector work interleave.
   auto softmax_values = [&](f32x16 (&sc)[CT], int buf, int t0, int kbuf, f32x16 (&sn)[CT]) {
-    const char* vb = s_v[buf] + v_lane;
-    const char* kb = s_k[kbuf];
+    const char* vb = s_v[buf];
+    const char* kb = s_k[kbuf] + k_lane;
     // softmax per column in base 2: register i holds token 8*(i/4) + 4*hh + i%4.
     // Only steps that reach past some column's keys (the causal edge, the end
     // of the context) need the per-element mask, which sets the raw score to
@@ -355,7 +359,7 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void prefill_mfma_kernel(Decode
       // half of the next step's score products
 #pragma unroll
       for (int kc = s * NKC / 2; kc < (s + 1) * NKC / 2; ++kc) {
-        const bf16x8 kf = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(kb + n * RSK + 32 * kc + 16 * hh));
+        const bf16x8 kf = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(kb + 512 * kc));
 #pragma unroll
         for (int c = 0; c < CT; ++c) sn[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[c][kc], sn[c], 0, 0, 0);
       }
@@ -363,8 +367,8 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void prefill_mfma_kernel(Decode
       // dim 32e + lane%32 (token rows 16s + 4*hh + 0..3, then 8 rows on)
 #pragma unroll
       for (int e = 0; e < NT; ++e) {
-        const uint2 lo = lds_read_tr16(vb + 16 * s * RSV + 64 * e);
-        const uint2 hi = lds_read_tr16(vb + (16 * s + 8) * RSV + 64 * e);
+        const uint2 lo = lds_read_tr16(vb + v_lane + s * BLKB + 1024 * e);
+        const uint2 hi = lds_read_tr16(vb + v_lane_hi + s * BLKB + 1024 * e);
         const bf16x8 av = __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
 #pragma unroll
         for (int c = 0; c < CT; ++c) acc[c][e] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pt[c], acc[c][e], 0, 0, 0);
@@ -442,22 +446,22 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void prefill_mfma_kernel(Decode
 
   // The item queue: cur (being computed) and n1 (record known, q loaded into
   // qn); the ticket after n1 is fetched while cur runs.  The loads run up to
-  // six steps ahead of the pair being computed: into n1 near the end of cur,
-  // never past it.
+  // eight steps ahead of the interval being computed: into n1 near the end of
+  // cur, never past it.
   Item cur, n1;
   make_item(blockIdx.x, cur);
   if (!cur.valid) return;
   load_q(cur, qf);
 
   // The load stream runs ahead of the computation: in cur, then in n1
-  // (cs_n1).  Stepping past the end of n1 (only when n1 has the minimum six
-  // steps) leaves it pending (cs_wait) until the item switch makes the next
+  // (cs_n1).  Stepping past the end of n1 (which has at least eight steps, so
+  // this does not happen with the stream's lookahead) would leave it pending (cs_wait) until the item switch makes the next
   // n1; that happens before the next issue.  An invalid item has no
   // blocks (zero-sized loads).
   Cursor cs = cursor_of(cur);
   bool cs_n1 = false, cs_wait = false;
-  auto issue_next = [&](Stage& st) {
-    issue_step(cs.g, ids_at(cs), st);
+  auto issue_next = [&](int buf) {
+    issue_step(cs, buf);
     if (__builtin_expect(++cs.step == cs.nsteps, 0)) {
       if (cs_n1) {
         cs_wait = true;
@@ -468,27 +472,23 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void prefill_mfma_kernel(Decode
     }
   };
 
-  // Two steps per barrier: while the pair q, q + 1 runs (reading the LDS
-  // buffers of steps q .. q + 2; step q + 1's scores are computed during step
-  // q's softmax and values, step q + 2's during q + 1's), steps q + 3 and q + 4
-  // are staged from the registers their loads landed in, and the loads of
-  // steps q + 5 and q + 6 are issued.
-  static_assert(NS == 2, "two steps per barrier: step s's loads sit in stg[s % 2]");
-  Stage stg[NS];
+  // Four steps per barrier: while steps q .. q + 3 run (reading the LDS
+  // buffers of steps q .. q + 4; step j + 1's scores are computed during step
+  // j's softmax and values), steps q + 5 .. q + 8 load into the buffers of
+  // q - 4 .. q - 1, last read before the previous barrier.  The loads are
+  // issued after the first and the second step's vector code, not right after
+  // the barrier, where every wave would queue for the compute unit's scalar
+  // unit with the same address work at once.  __syncthreads() waits for every
+  // load of this wave (its fence orders all earlier memory operations, the
+  // direct-to-LDS loads included) before the barrier, so the next interval
+  // finds steps q + 4 .. q + 8 in LDS.
+  static_assert(NS == 4 && kPrefillBufs == 9, "four steps per barrier, five more buffers");
 #pragma unroll
-  for (int u = 0; u < NS; ++u) issue_next(stg[u]);
-#pragma unroll
-  for (int u = 0; u < NS; ++u) {
-    stage_to_lds(stg[u], u);
-    issue_next(stg[u]);
-  }
-  stage_to_lds(stg[0], 2);  // steps 0 .. 2 in LDS, 3 and 4 in flight
-  issue_next(stg[0]);
-  // the next item is read once the first loads are on their way (the
-  // prologue's five steps stay within cur, which has at least six)
+  for (int u = 0; u < 5; ++u) issue_next(u);  // steps 0 .. 4 (cur has at least eight)
+  // the next item is read once the first loads are on their way
   make_item(blockIdx.x + grid, n1);
   load_q(n1, qn);
-  __syncthreads();
+  __syncthreads();  // steps 0 .. 4 in LDS (and n1's loads landed)
   int buf = 0, tpar = 0;  // LDS buffer of step 0 of cur
   f32x16 sc[2][CT];       // scores of steps of either parity
   for (;;) {  // one item per iteration
@@ -496,26 +496,22 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void prefill_mfma_kernel(Decode
     if (tid == 0) fetched = atomicAdd(&p.sched[2], 1);  // offset added where it is read
     begin_item(cur);
     if (cur.nblk > 0) scores(buf, sc[0]);
-    // Two steps per barrier: buffers rotate over five; step q in (buf + q) % 5
-    // relative to the pair.  Steps q + 1 and q + 2 were staged in the previous
-    // interval; q + 3 and q + 4 go into the buffers of q - 2 and q - 1, read
-    // last before the previous barrier.
+    // Buffers rotate over nine: step q + k in rot(buf, k) relative to the interval.
     auto rot = [](int b, int k) { return b + k >= kPrefillBufs ? b + k - kPrefillBufs : b + k; };
-    for (int q = 0; q < cur.nsteps; q += 2) {
-      const int b1 = rot(buf, 1), b2 = rot(buf, 2);
-      stage_to_lds(stg[1], rot(buf, 3));  // step q + 3 (odd)
-      stage_to_lds(stg[0], rot(buf, 4));  // step q + 4
-      if (q + 2 == cur.nsteps && tid == 0) s_ticket[tpar] = fetched;
+    for (int q = 0; q < cur.nsteps; q += 4) {
+      const int b1 = rot(buf, 1), b2 = rot(buf, 2), b3 = rot(buf, 3), b4 = rot(buf, 4);
+      if (q + 4 == cur.nsteps && tid == 0) s_ticket[tpar] = fetched;
       const int t0 = (cur.b_begin + 2 * q) * kBlockTokens;
-      // the scalar work of each issue runs between the steps' vector code
-      // rather than after the barrier, where every wave would queue for the
-      // compute unit's scalar unit at once
       if (2 * q < cur.nblk) softmax_values(sc[0], buf, t0, b1, sc[1]);
-      issue_next(stg[1]);                 // step q + 5
+      issue_next(rot(buf, 5));            // step q + 5
+      issue_next(rot(buf, 6));            // step q + 6
       if (2 * q + 2 < cur.nblk) softmax_values(sc[1], b1, t0 + kStepTokens, b2, sc[0]);
-      issue_next(stg[0]);                 // step q + 6
-      __syncthreads();
-      buf = b2;
+      issue_next(rot(buf, 7));            // step q + 7
+      issue_next(rot(buf, 8));            // step q + 8
+      if (2 * q + 4 < cur.nblk) softmax_values(sc[0], b2, t0 + 2 * kStepTokens, b3, sc[1]);
+      if (2 * q + 6 < cur.nblk) softmax_values(sc[1], b3, t0 + 3 * kStepTokens, b4, sc[0]);
+      __syncthreads();  // this interval's loads have landed (the fence waits for them)
+      buf = b4;
     }
     // Switch to n1.  Its q was loaded at the start of this item; the empty asm
     // makes the wait for those loads happen here, once, before the output
