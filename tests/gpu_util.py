@@ -11,6 +11,7 @@ Element-wise relative error is not used: it is unbounded near zero.
 import json
 import os
 import sys
+import tempfile
 
 import numpy as np
 import torch
@@ -20,10 +21,9 @@ BF16_ABS = 2e-2
 BF16_ROW_REL = 2e-2
 
 # Every comparison's errors, kept for the run's summary and written one JSON
-# line each to $PKV_PARITY_LOG (default: gpurun_out/parity_margins.jsonl under
-# the repository root), so a run's margins against the bars can be read back.
+# line each to $PKV_PARITY_LOG (default: pkv_parity_margins.jsonl in the system
+# temporary directory), so a run's margins against the bars can be read back.
 RECORDS = []
-_ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
 def _record(what, dtype, max_abs, max_row_rel):
@@ -32,7 +32,7 @@ def _record(what, dtype, max_abs, max_row_rel):
            "max_abs": max_abs, "max_row_rel": max_row_rel,
            "frac_of_bar": max(max_row_rel / bar, 0.0 if dtype == "f32" else max_abs / BF16_ABS)}
     RECORDS.append(rec)
-    path = os.environ.get("PKV_PARITY_LOG") or os.path.join(_ROOT, "gpurun_out", "parity_margins.jsonl")
+    path = os.environ.get("PKV_PARITY_LOG") or os.path.join(tempfile.gettempdir(), "pkv_parity_margins.jsonl")
     try:
         os.makedirs(os.path.dirname(path), exist_ok=True)
         with open(path, "a") as f:
