@@ -328,6 +328,41 @@ int pkv_attention_varlen_partitions(void* out, const void* q, const void* key_ca
                                     int32_t head_dim, int32_t num_seqs, int32_t max_blocks_per_seq,
                                     int32_t num_blocks, int32_t max_context_len, pkv_dtype dt, void* workspace,
                                     size_t workspace_bytes, void* stream);
+/* pkv_attention_varlen's four launches one by one, for callers that place
+ * them themselves (time them, or put the decode partitions and the prefill
+ * tiles on different streams; "How vLLM Works?", section 04: a step batches
+ * the memory-bound decode rows with the compute-bound prefill chunk).
+ * _plan: the work lists from context_lens and query_start_loc (device); it
+ * also resets the ticket counters, so each step's launches need their own
+ * plan.  _decode_partitions: the one-row sequences' partitions.
+ * _prefill_tiles: the chunk rows' matrix-core tiles.  _merge: the log-sum-exp
+ * merge of every row with more than one partial.  Arguments and workspace as
+ * pkv_attention_varlen; call them in this order on one workspace (the two
+ * middle launches in either order, or concurrently on two streams that meet
+ * before _merge).  Together they equal pkv_attention_varlen byte for byte
+ * (pkv_attention_varlen_partitions is the last three).  Errors as
+ * pkv_attention_varlen.  Ownership: nothing is kept; the caller owns every
+ * buffer. */
+int pkv_attention_varlen_plan(void* out, const void* q, const void* key_cache, const void* value_cache,
+    const int32_t* block_tables, const int32_t* context_lens, const int32_t* query_start_loc, int32_t num_tokens,
+    int32_t max_query_len, float scale, int32_t block_size, int32_t num_q_heads, int32_t num_kv_heads,
+    int32_t head_dim, int32_t num_seqs, int32_t max_blocks_per_seq, int32_t num_blocks, int32_t max_context_len,
+    pkv_dtype dt, void* workspace, size_t workspace_bytes, void* stream);
+int pkv_attention_varlen_decode_partitions(void* out, const void* q, const void* key_cache, const void* value_cache,
+    const int32_t* block_tables, const int32_t* context_lens, const int32_t* query_start_loc, int32_t num_tokens,
+    int32_t max_query_len, float scale, int32_t block_size, int32_t num_q_heads, int32_t num_kv_heads,
+    int32_t head_dim, int32_t num_seqs, int32_t max_blocks_per_seq, int32_t num_blocks, int32_t max_context_len,
+    pkv_dtype dt, void* workspace, size_t workspace_bytes, void* stream);
+int pkv_attention_varlen_prefill_tiles(void* out, const void* q, const void* key_cache, const void* value_cache,
+    const int32_t* block_tables, const int32_t* context_lens, const int32_t* query_start_loc, int32_t num_tokens,
+    int32_t max_query_len, float scale, int32_t block_size, int32_t num_q_heads, int32_t num_kv_heads,
+    int32_t head_dim, int32_t num_seqs, int32_t max_blocks_per_seq, int32_t num_blocks, int32_t max_context_len,
+    pkv_dtype dt, void* workspace, size_t workspace_bytes, void* stream);
+int pkv_attention_varlen_merge(void* out, const void* q, const void* key_cache, const void* value_cache,
+    const int32_t* block_tables, const int32_t* context_lens, const int32_t* query_start_loc, int32_t num_tokens,
+    int32_t max_query_len, float scale, int32_t block_size, int32_t num_q_heads, int32_t num_kv_heads,
+    int32_t head_dim, int32_t num_seqs, int32_t max_blocks_per_seq, int32_t num_blocks, int32_t max_context_len,
+    pkv_dtype dt, void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------ */
 /* Log-sum-exp merge of partial softmax results, one output row per input row.

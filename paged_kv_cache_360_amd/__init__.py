@@ -25,6 +25,10 @@ from .ops import (  # noqa: F401
     pkv_attention_varlen,
     pkv_attention_varlen_plan_upload,
     pkv_attention_varlen_partitions,
+    pkv_attention_varlen_plan,
+    pkv_attention_varlen_decode_partitions,
+    pkv_attention_varlen_prefill_tiles,
+    pkv_attention_varlen_merge,
     pkv_varlen_workspace_bytes,
     varlen_workspace,
     pkv_lse_merge,

@@ -98,6 +98,10 @@ SIGNATURES = {
     "pkv_alloc_num_free_host": (_i32, [_p]),
     "pkv_alloc_host_refcount": (_i32, [_p, _i32]),
 }
+# The varlen launches one by one take the same arguments as their last three together.
+for _name in ("pkv_attention_varlen_plan", "pkv_attention_varlen_decode_partitions",
+              "pkv_attention_varlen_prefill_tiles", "pkv_attention_varlen_merge"):
+    SIGNATURES[_name] = SIGNATURES["pkv_attention_varlen_partitions"]
 
 _lib = None
 

@@ -527,7 +527,7 @@ int pkv_attention_varlen(void* out, const void* q, const void* key_cache, const 
       max_context_len, dt, workspace, workspace_bytes
 
 namespace {
-int prepare_varlen(const char* who, pkv::DecodeArgs& a, PKV_VARLEN_ARGS) {
+static int prepare_varlen(const char* who, pkv::DecodeArgs& a, PKV_VARLEN_ARGS) {
   char msg[160];
   if (dt != PKV_BF16) {
     std::snprintf(msg, sizeof(msg), "%s: bf16 only", who);
@@ -573,6 +573,40 @@ int pkv_attention_varlen_partitions(PKV_VARLEN_ARGS, void* stream) {
   if (rc != PKV_OK) return rc;
   rc = pkv::launched(pkv::launch_prefill(a, stream), who);
   if (rc != PKV_OK) return rc;
+  return pkv::launched(pkv::launch_decode_merge(a, stream), who);
+}
+
+// The launches of pkv_attention_varlen one by one (plan, decode partitions,
+// prefill tiles, merge), in that order on one workspace.
+int pkv_attention_varlen_plan(PKV_VARLEN_ARGS, void* stream) {
+  pkv::DecodeArgs a{};
+  const char* who = "pkv_attention_varlen_plan";
+  int rc = prepare_varlen(who, a, PKV_VARLEN_FWD);
+  if (rc != PKV_OK || num_seqs == 0 || num_tokens == 0) return rc;
+  return pkv::launched(pkv::launch_plan(a, stream), who);
+}
+
+int pkv_attention_varlen_decode_partitions(PKV_VARLEN_ARGS, void* stream) {
+  pkv::DecodeArgs a{};
+  const char* who = "pkv_attention_varlen_decode_partitions";
+  int rc = prepare_varlen(who, a, PKV_VARLEN_FWD);
+  if (rc != PKV_OK || num_seqs == 0 || num_tokens == 0) return rc;
+  return pkv::launched(pkv::launch_decode_partitions(a, stream), who);
+}
+
+int pkv_attention_varlen_prefill_tiles(PKV_VARLEN_ARGS, void* stream) {
+  pkv::DecodeArgs a{};
+  const char* who = "pkv_attention_varlen_prefill_tiles";
+  int rc = prepare_varlen(who, a, PKV_VARLEN_FWD);
+  if (rc != PKV_OK || num_seqs == 0 || num_tokens == 0) return rc;
+  return pkv::launched(pkv::launch_prefill(a, stream), who);
+}
+
+int pkv_attention_varlen_merge(PKV_VARLEN_ARGS, void* stream) {
+  pkv::DecodeArgs a{};
+  const char* who = "pkv_attention_varlen_merge";
+  int rc = prepare_varlen(who, a, PKV_VARLEN_FWD);
+  if (rc != PKV_OK || num_seqs == 0 || num_tokens == 0) return rc;
   return pkv::launched(pkv::launch_decode_merge(a, stream), who);
 }
 

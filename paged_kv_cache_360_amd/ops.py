@@ -399,6 +399,45 @@ def pkv_attention_varlen_partitions(out, q, key_cache, value_cache, block_tables
     return out
 
 
+def _varlen_launch(cname, out, q, key_cache, value_cache, block_tables, context_lens, query_start_loc, scale,
+                   max_query_len, max_context_len, workspace, stream):
+    _need_workspace(workspace, cname)
+    a = _varlen_args(out, q, key_cache, value_cache, block_tables, context_lens, query_start_loc, scale,
+                     max_query_len, max_context_len, workspace)
+    check(cname, getattr(lib(), cname)(*a, _stream(stream)))
+    return out
+
+
+def pkv_attention_varlen_plan(out, q, key_cache, value_cache, block_tables, context_lens, query_start_loc,
+                              scale, max_query_len, max_context_len, workspace=None, stream=None):
+    """First launch of ``pkv_attention_varlen`` alone (work lists, ticket counters reset);
+    ``workspace`` is required: the later launches read the plan from it."""
+    return _varlen_launch("pkv_attention_varlen_plan", out, q, key_cache, value_cache, block_tables, context_lens,
+                          query_start_loc, scale, max_query_len, max_context_len, workspace, stream)
+
+
+def pkv_attention_varlen_decode_partitions(out, q, key_cache, value_cache, block_tables, context_lens,
+                                           query_start_loc, scale, max_query_len, max_context_len, workspace=None,
+                                           stream=None):
+    """The one-row sequences' partitions of a planned varlen step."""
+    return _varlen_launch("pkv_attention_varlen_decode_partitions", out, q, key_cache, value_cache, block_tables,
+                          context_lens, query_start_loc, scale, max_query_len, max_context_len, workspace, stream)
+
+
+def pkv_attention_varlen_prefill_tiles(out, q, key_cache, value_cache, block_tables, context_lens, query_start_loc,
+                                       scale, max_query_len, max_context_len, workspace=None, stream=None):
+    """The chunk rows' matrix-core tiles of a planned varlen step."""
+    return _varlen_launch("pkv_attention_varlen_prefill_tiles", out, q, key_cache, value_cache, block_tables,
+                          context_lens, query_start_loc, scale, max_query_len, max_context_len, workspace, stream)
+
+
+def pkv_attention_varlen_merge(out, q, key_cache, value_cache, block_tables, context_lens, query_start_loc,
+                               scale, max_query_len, max_context_len, workspace=None, stream=None):
+    """The log-sum-exp merge of a planned varlen step (after both kinds of tiles)."""
+    return _varlen_launch("pkv_attention_varlen_merge", out, q, key_cache, value_cache, block_tables, context_lens,
+                          query_start_loc, scale, max_query_len, max_context_len, workspace, stream)
+
+
 def pkv_lse_merge(out, part_m, part_l, part_o, num_parts, stream=None):
     """Merge partial softmax results (base-2 maxima); ``out`` [rows, D]."""
     rows, maxp, d = part_o.shape

@@ -361,7 +361,9 @@ def test_append_batch_all_or_nothing():
 
 @pytest.mark.parametrize("name", ["pkv_attention_decode_plan", "pkv_attention_decode_partitions",
                                   "pkv_attention_decode_merge", "pkv_attention_decode_partitions_append",
-                                  "pkv_attention_decode_plan_upload"])
+                                  "pkv_attention_decode_plan_upload", "pkv_attention_varlen_plan",
+                                  "pkv_attention_varlen_decode_partitions", "pkv_attention_varlen_prefill_tiles",
+                                  "pkv_attention_varlen_merge", "pkv_attention_varlen_partitions"])
 def test_split_wrappers_need_the_callers_workspace(name):
     """The split launches read the work list the plan left in the workspace: the
     Python wrappers refuse to make a fresh (empty) one, before touching any tensor."""
@@ -370,6 +372,8 @@ def test_split_wrappers_need_the_callers_workspace(name):
             getattr(pkv, name)(None, None, None, None, None, None, None, None, 0.125, 100)
         elif name == "pkv_attention_decode_plan_upload":
             getattr(pkv, name)(None, None, None, None, None, None, 0.125, 100, None, None, None)
+        elif name.startswith("pkv_attention_varlen_"):
+            getattr(pkv, name)(None, None, None, None, None, None, None, 0.125, 4, 100)
         else:
             getattr(pkv, name)(None, None, None, None, None, None, 0.125, 100)
 

@@ -254,6 +254,59 @@ def test_varlen_full_size_mixed_step_sampled():
     assert_close(got[inp["qsl"][seqs]], dref, "bf16", "decode rows")
 
 
+@pytest.mark.parametrize("order", ["decode_first", "prefill_first"])
+def test_varlen_launches_one_by_one_equal_one_call(order):
+    """pkv_attention_varlen's four launches made one by one (plan, the decode
+    partitions and the prefill tiles in either order, merge) give the one-call
+    output byte for byte on a mixed batch (a 300-row chunk over 2600 keys and
+    decode rows of 1..3000 keys), which matches the oracle on sampled rows."""
+    Hq, Hkv, D = 32, 8, 128
+    rng = np.random.default_rng(7 if order == "decode_first" else 8)
+    S, C, MB = 12, 300, 200
+    ctx = rng.integers(1, 3001, size=S).astype(np.int32)
+    ctx[0] = 2600
+    qlens = np.array([C] + [1] * (S - 1), np.int32)
+    qsl_h = np.concatenate([[0], np.cumsum(qlens)]).astype(np.int32)
+    T = int(qsl_h[-1])
+    nb = S * MB + 4
+    tables = np.full((S, MB), -1, np.int32)
+    perm = rng.permutation(nb).astype(np.int32)
+    off = 0
+    for s in range(S):
+        n = -(-int(ctx[s]) // 16)
+        tables[s, :n] = perm[off:off + n]
+        off += n
+    kc_h = normal_values_parallel(11, (nb, BLOCK_SIZE, Hkv, D), "bf16")
+    vc_h = normal_values_parallel(12, (nb, BLOCK_SIZE, Hkv, D), "bf16")
+    q_h = normal_values(rng, (T, Hq, D), "bf16")
+    kc, vc, q = dev(kc_h), dev(vc_h), dev(q_h)
+    tab, lens, qsl = dev(tables), dev(ctx), dev(qsl_h)
+    bound = 16 * MB
+    scale = float(np.float32(1.0 / math.sqrt(D)))
+    say(f"varlen one by one ({order}): chunk {C} rows over {ctx[0]} keys, {S - 1} decode rows")
+    ws1 = pkv.varlen_workspace(S, T, Hq, Hkv, D, C, bound)
+    ref = torch.full((T, Hq, D), float("nan"), dtype=torch.bfloat16, device="cuda")
+    pkv.pkv_attention_varlen(ref, q, kc, vc, tab, lens, qsl, scale, C, bound, workspace=ws1)
+    ws2 = pkv.varlen_workspace(S, T, Hq, Hkv, D, C, bound)
+    out = torch.full((T, Hq, D), float("nan"), dtype=torch.bfloat16, device="cuda")
+    args = (out, q, kc, vc, tab, lens, qsl, scale, C, bound)
+    pkv.pkv_attention_varlen_plan(*args, workspace=ws2)
+    middle = [pkv.pkv_attention_varlen_decode_partitions, pkv.pkv_attention_varlen_prefill_tiles]
+    for fn in (middle if order == "decode_first" else middle[::-1]):
+        fn(*args, workspace=ws2)
+    pkv.pkv_attention_varlen_merge(*args, workspace=ws2)
+    torch.cuda.synchronize()
+    assert host(out).tobytes() == host(ref).tobytes()
+    got = host_f64(out)
+    rows = np.array([0, 1, C // 2, C - 1])               # chunk rows: row r sees ctx[0] - C + r + 1 keys
+    ref = oracle.decode_attention(q_h[rows], kc_h, vc_h, np.repeat(tables[:1], len(rows), 0),
+                                  ctx[0] - C + rows + 1, np.float32(scale))
+    assert_close(got[rows], ref, "bf16", "one by one: chunk rows")
+    seqs = np.arange(1, S)
+    dref = oracle.decode_attention(q_h[qsl_h[seqs]], kc_h, vc_h, tables[seqs], ctx[seqs], np.float32(scale))
+    assert_close(got[qsl_h[seqs]], dref, "bf16", "one by one: decode rows")
+
+
 def test_varlen_plan_upload_equals_one_call():
     """Two steps of a mixed batch (a 100-row chunk and decode rows) through
     pkv_attention_varlen_plan_upload (plan from pinned lengths; slots and lengths
