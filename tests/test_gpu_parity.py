@@ -123,6 +123,10 @@ DECODE_CASES = {
     # long contexts: more than 64 partial results in a row (the merge's
     # lane-parallel maxima then take a second round), thousands of table entries
     "long_gqa4_d64_bf16": ("bf16", 8, 2, 64, [70000, 40961, 3]),
+    # 256 partitions in one row (four-partition items throughout), beside a
+    # sequence one token past a partition edge and a one-token sequence
+    "very_long_gqa4_d64_bf16": ("bf16", 4, 1, 64, [131072, 65537, 1]),
+    "very_long_gqa4_d64_f32": ("f32", 4, 1, 64, [131072, 1]),
     "long_gqa4_d64_f32": ("f32", 8, 2, 64, [35000, 33]),
 }
 
