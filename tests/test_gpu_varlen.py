@@ -254,6 +254,37 @@ def test_varlen_full_size_mixed_step_sampled():
     assert_close(got[inp["qsl"][seqs]], dref, "bf16", "decode rows")
 
 
+def test_varlen_long_chunk_many_items_per_cu_sampled():
+    """A 2048-row chunk over 8192 keys (GQA 32/8, D 128): 2048 prefill items of
+    64 rows x 4 heads over two partitions, about eight per compute unit, so each
+    workgroup's load stream runs across item boundaries many times.  Rows at
+    item edges (every 64 rows) and the causal end are compared with the oracle
+    on their truncated contexts; two runs agree bit for bit."""
+    Hq, Hkv, D, C, CC = 32, 8, 128, 2048, 8192
+    rng = np.random.default_rng(2048)
+    ctx = np.array([CC], np.int32)
+    nb = CC // BLOCK_SIZE + 16
+    tables = rng.permutation(nb)[:CC // BLOCK_SIZE].astype(np.int32)[None, :]
+    inp = {
+        "context_lens": ctx, "block_tables": tables, "num_blocks": nb,
+        "qsl": np.array([0, C], np.int32),
+        "key_cache": normal_values_parallel(2049, (nb, BLOCK_SIZE, Hkv, D), "bf16"),
+        "value_cache": normal_values_parallel(2050, (nb, BLOCK_SIZE, Hkv, D), "bf16"),
+        "q": normal_values_parallel(2051, (C, Hq, D), "bf16"),
+        "scale": np.float32(1.0 / math.sqrt(D)),
+        "max_query_len": C,
+    }
+    say(f"varlen long chunk: {C} rows over {CC} keys")
+    got = host_f64(gpu_varlen(inp))
+    again = host_f64(gpu_varlen(inp))
+    assert np.array_equal(got, again), "two runs differ"
+    rows = np.array([0, 1, 63, 64, 127, 128, 511, 512, 1023, 1024, 1535, 1536, 2046, 2047])
+    keys = CC - C + rows + 1
+    ref = oracle.decode_attention(inp["q"][rows], inp["key_cache"], inp["value_cache"],
+                                  np.repeat(tables, len(rows), 0), keys, inp["scale"])
+    assert_close(got[rows], ref, "bf16", "long chunk rows")
+
+
 @pytest.mark.parametrize("order", ["decode_first", "prefill_first"])
 def test_varlen_launches_one_by_one_equal_one_call(order):
     """pkv_attention_varlen's four launches made one by one (plan, the decode
