@@ -254,14 +254,17 @@ def test_varlen_full_size_mixed_step_sampled():
     assert_close(got[inp["qsl"][seqs]], dref, "bf16", "decode rows")
 
 
-def test_varlen_long_chunk_many_items_per_cu_sampled():
-    """A 2048-row chunk over 8192 keys (GQA 32/8, D 128): 2048 prefill items of
-    64 rows x 4 heads over two partitions, about eight per compute unit, so each
-    workgroup's load stream runs across item boundaries many times.  Rows at
-    item edges (every 64 rows) and the causal end are compared with the oracle
-    on their truncated contexts; two runs agree bit for bit."""
-    Hq, Hkv, D, C, CC = 32, 8, 128, 2048, 8192
-    rng = np.random.default_rng(2048)
+@pytest.mark.parametrize("Hq,Hkv,D", [(32, 8, 128), (16, 2, 64), (32, 32, 128)])
+def test_varlen_long_chunk_many_items_per_cu_sampled(Hq, Hkv, D):
+    """A 2048-row chunk over 8192 keys: prefill items of 256/G rows x the G q
+    heads of a KV head over two partitions, four to eight per compute unit
+    (GQA 32/8 D 128: 2048 items; GQA 16/2 D 64, whose waves split the K and V
+    loads between them: 1024; MHA 32 D 128: 2048), so each workgroup's load
+    stream runs across item boundaries many times.  Rows at item edges and the
+    causal end are compared with the oracle on their truncated contexts; two
+    runs agree bit for bit."""
+    C, CC = 2048, 8192
+    rng = np.random.default_rng(2048 + D + Hkv)
     ctx = np.array([CC], np.int32)
     nb = CC // BLOCK_SIZE + 16
     tables = rng.permutation(nb)[:CC // BLOCK_SIZE].astype(np.int32)[None, :]
@@ -274,11 +277,11 @@ def test_varlen_long_chunk_many_items_per_cu_sampled():
         "scale": np.float32(1.0 / math.sqrt(D)),
         "max_query_len": C,
     }
-    say(f"varlen long chunk: {C} rows over {CC} keys")
+    say(f"varlen long chunk: {C} rows over {CC} keys, Hq {Hq} Hkv {Hkv} D {D}")
     got = host_f64(gpu_varlen(inp))
     again = host_f64(gpu_varlen(inp))
     assert np.array_equal(got, again), "two runs differ"
-    rows = np.array([0, 1, 63, 64, 127, 128, 511, 512, 1023, 1024, 1535, 1536, 2046, 2047])
+    rows = np.array([0, 1, 31, 32, 63, 64, 127, 128, 255, 256, 511, 512, 1023, 1024, 1535, 1536, 2046, 2047])
     keys = CC - C + rows + 1
     ref = oracle.decode_attention(inp["q"][rows], inp["key_cache"], inp["value_cache"],
                                   np.repeat(tables, len(rows), 0), keys, inp["scale"])
