@@ -181,6 +181,9 @@ CHUNK_SWEEPS = {
     "edges_gqa32x8": (52, 32, 8, 128, [300, 1, 64, 256], [1300, 2000, 600, 2300]),
     "edges_mha_d64": (53, 32, 32, 64, [256, 256, 100, 1], [2300, 1000, 560, 3000]),
     "edges_gqa8_d64": (54, 32, 4, 64, [200, 33, 1], [2100, 600, 900]),
+    # two prefill items per compute unit (512 rows over 8192 keys: 512 items of
+    # two partitions), so every workgroup's load stream crosses an item boundary
+    "two_items_per_cu_gqa32x8": (55, 32, 8, 128, [512], [8192]),
 }
 
 
